@@ -1,0 +1,249 @@
+"""Python driver for the plain-C SDM oracle (sdm_oracle.c).
+
+TEST INFRASTRUCTURE: only the test-suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It shares no code with the GPU
+library and never calls it.
+
+The C functions are sequential; this driver only splits independent work over
+threads: addressing rows are independent, memories (b, h) are independent, and
+the scan of one memory is independent per slot element because addressing
+never reads the memory.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "sdm_oracle.c")
+LIB = os.path.join(HERE, "liboracle_sdm.so")
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off", "-Wall",
+          "-Wextra", "-Werror"]
+
+
+def build(src: str = SRC, out: str = LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc.  -ffp-contract=off keeps every product and
+    sum a separately rounded IEEE operation, as the C source is written."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-I", HERE, src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class _Cfg(C.Structure):
+    _fields_ = [(n, C.c_int) for n in ("B", "H", "T", "d", "S", "dk", "k", "W", "in_bf16", "state_bf16")]
+
+
+def _ptr(a: np.ndarray):
+    return C.c_void_p(a.ctypes.data)
+
+
+def _cfg_struct(cfg) -> _Cfg:
+    return _Cfg(cfg.B, cfg.H, cfg.T, cfg.d, cfg.S, cfg.dk, cfg.k, cfg.W, int(cfg.in_bf16),
+                int(cfg.state_bf16))
+
+
+def default_threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class Oracle:
+    """Handle on one build of the oracle library (the default build, or a
+    test-made variant at another path)."""
+
+    def __init__(self, path: str | None = None):
+        path = path or LIB
+        if not os.path.exists(path) or (path == LIB and os.path.getmtime(path) < os.path.getmtime(SRC)):
+            if path != LIB:
+                raise FileNotFoundError(path)
+            build()
+        self.path = path
+        L = C.CDLL(path)
+        vp, i32p, f32p = C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_float)
+        L.oracle_bf16_round.argtypes = [C.c_double]
+        L.oracle_bf16_round.restype = C.c_uint16
+        L.oracle_scores.argtypes = [C.POINTER(_Cfg), vp, vp, C.c_long, C.c_long, vp]
+        L.oracle_topk.argtypes = [vp, C.c_int, C.c_int, vp]
+        L.oracle_select.argtypes = [vp, vp, C.c_int, C.c_int, C.c_int, vp, vp]
+        L.oracle_softmax.argtypes = [vp, C.c_int, vp]
+        L.oracle_address.argtypes = [C.POINTER(_Cfg), vp, vp, C.c_long, C.c_long, vp, vp, vp]
+        L.oracle_address_from_scores.argtypes = [C.POINTER(_Cfg), vp, C.c_long, C.c_long, vp, vp, vp]
+        L.oracle_scan.argtypes = [C.POINTER(_Cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, C.c_int, C.c_int,
+                                  C.c_int, C.c_int]
+        for f in ("oracle_scores", "oracle_topk", "oracle_select", "oracle_softmax", "oracle_address",
+                  "oracle_address_from_scores", "oracle_scan"):
+            getattr(L, f).restype = C.c_int
+        del i32p, f32p
+        self.L = L
+
+    # ---- small pieces ----------------------------------------------------
+    def bf16_round(self, x: float) -> int:
+        return int(self.L.oracle_bf16_round(float(x)))
+
+    def topk(self, s: np.ndarray, k: int) -> np.ndarray:
+        s = np.ascontiguousarray(s, np.float32)
+        idx = np.empty(k, np.int32)
+        if self.L.oracle_topk(_ptr(s), s.size, k, _ptr(idx)):
+            raise ValueError("oracle_topk rejected its arguments")
+        return idx
+
+    def select(self, s1, s2, k: int, W: int):
+        s1 = np.ascontiguousarray(s1, np.float32)
+        s2 = np.ascontiguousarray(s2, np.float32)
+        slot = np.empty(W, np.int32)
+        sigma = np.empty(W, np.float32)
+        if self.L.oracle_select(_ptr(s1), _ptr(s2), s1.size, k, W, _ptr(slot), _ptr(sigma)):
+            raise ValueError("oracle_select rejected its arguments")
+        return slot, sigma
+
+    def softmax(self, sigma) -> np.ndarray:
+        sigma = np.ascontiguousarray(sigma, np.float32)
+        w = np.empty(sigma.size, np.float32)
+        if self.L.oracle_softmax(_ptr(sigma), sigma.size, _ptr(w)):
+            raise ValueError("oracle_softmax rejected its arguments")
+        return w
+
+    # ---- row-parallel addressing -----------------------------------------
+    def _rows(self, nrows, fn, threads):
+        threads = threads or default_threads()
+        step = max(1, -(-nrows // (threads * 4)))
+        spans = [(r, min(nrows, r + step)) for r in range(0, nrows, step)]
+        if threads == 1 or len(spans) == 1:
+            rcs = [fn(a, b) for a, b in spans]
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                rcs = list(ex.map(lambda sp: fn(*sp), spans))
+        if any(rcs):
+            raise ValueError("oracle rejected its arguments")
+
+    def scores(self, cfg, q: np.ndarray, subkeys: np.ndarray, rows=None, threads=None) -> np.ndarray:
+        """Scores [R, 2, S] for all rows, or for the row indices given."""
+        cs = _cfg_struct(cfg)
+        q = np.ascontiguousarray(q)
+        subkeys = np.ascontiguousarray(subkeys)
+        if rows is None:
+            R = cfg.B * cfg.T * cfg.H
+            out = np.empty((R, 2, cfg.S), np.float32)
+            self._rows(R, lambda a, b: self.L.oracle_scores(C.byref(cs), _ptr(q), _ptr(subkeys), a, b,
+                                                            C.c_void_p(out.ctypes.data + a * 8 * cfg.S)),
+                       threads)
+            return out
+        rows = np.asarray(rows, np.int64)
+        out = np.empty((rows.size, 2, cfg.S), np.float32)
+        for j, r in enumerate(rows):
+            if self.L.oracle_scores(C.byref(cs), _ptr(q), _ptr(subkeys), int(r), int(r) + 1,
+                                    C.c_void_p(out.ctypes.data + j * 8 * cfg.S)):
+                raise ValueError("oracle_scores rejected its arguments")
+        return out
+
+    def address(self, cfg, q: np.ndarray, subkeys: np.ndarray, rows=None, threads=None):
+        """(idx [R,W] int32, wt [R,W] f32, sigma [R,W] f32) for all rows or the rows given."""
+        cs = _cfg_struct(cfg)
+        W = cfg.W
+        q = np.ascontiguousarray(q)
+        subkeys = np.ascontiguousarray(subkeys)
+        if rows is None:
+            R = cfg.B * cfg.T * cfg.H
+            idx = np.empty((R, W), np.int32)
+            wt = np.empty((R, W), np.float32)
+            sg = np.empty((R, W), np.float32)
+
+            def fn(a, b):
+                o = a * W * 4
+                return self.L.oracle_address(C.byref(cs), _ptr(q), _ptr(subkeys), a, b,
+                                             C.c_void_p(idx.ctypes.data + o), C.c_void_p(wt.ctypes.data + o),
+                                             C.c_void_p(sg.ctypes.data + o))
+
+            self._rows(R, fn, threads)
+            return idx, wt, sg
+        rows = np.asarray(rows, np.int64)
+        idx = np.empty((rows.size, W), np.int32)
+        wt = np.empty((rows.size, W), np.float32)
+        sg = np.empty((rows.size, W), np.float32)
+
+        def fn2(a, b):
+            for j in range(a, b):
+                o = j * W * 4
+                r = int(rows[j])
+                rc = self.L.oracle_address(C.byref(cs), _ptr(q), _ptr(subkeys), r, r + 1,
+                                           C.c_void_p(idx.ctypes.data + o), C.c_void_p(wt.ctypes.data + o),
+                                           C.c_void_p(sg.ctypes.data + o))
+                if rc:
+                    return rc
+            return 0
+
+        self._rows(rows.size, fn2, threads)
+        return idx, wt, sg
+
+    def address_from_scores(self, cfg, scores: np.ndarray, threads=None):
+        """Selection + weights from given scores [R, 2, S]."""
+        cs = _cfg_struct(cfg.replace(B=1, T=scores.shape[0], H=1))
+        scores = np.ascontiguousarray(scores, np.float32)
+        R, W = scores.shape[0], cfg.W
+        idx = np.empty((R, W), np.int32)
+        wt = np.empty((R, W), np.float32)
+        sg = np.empty((R, W), np.float32)
+
+        def fn(a, b):
+            o = a * W * 4
+            return self.L.oracle_address_from_scores(
+                C.byref(cs), C.c_void_p(scores.ctypes.data + a * 8 * cfg.S), 0, b - a,
+                C.c_void_p(idx.ctypes.data + o), C.c_void_p(wt.ctypes.data + o), C.c_void_p(sg.ctypes.data + o))
+
+        self._rows(R, fn, threads)
+        return idx, wt, sg
+
+    # ---- the scan ----------------------------------------------------------
+    def scan(self, cfg, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem, threads=None, e_split=None):
+        """Run the scan; mem [B,H,N,d] is updated in place.  Returns out [B,T,H,d] f32."""
+        cs = _cfg_struct(cfg)
+        arrs = [np.ascontiguousarray(a) for a in (idx_w, wt_w, idx_r, wt_r, v, alpha, beta)]
+        if not (mem.flags.c_contiguous and mem.flags.writeable):
+            raise ValueError("mem must be a writable C-contiguous array")
+        out = np.empty((cfg.B, cfg.T, cfg.H, cfg.d), np.float32)
+        threads = threads or default_threads()
+        units = cfg.B * cfg.H
+        if e_split is None:
+            e_split = max(1, min(cfg.d, -(-threads // units)))
+        bounds = np.linspace(0, cfg.d, e_split + 1).astype(int)
+        jobs = [(b, h, int(bounds[i]), int(bounds[i + 1])) for b in range(cfg.B) for h in range(cfg.H)
+                for i in range(e_split) if bounds[i + 1] > bounds[i]]
+
+        def fn(job):
+            b, h, e0, e1 = job
+            return self.L.oracle_scan(C.byref(cs), *[_ptr(a) for a in arrs], _ptr(mem), _ptr(out), b, h, e0, e1)
+
+        if threads == 1 or len(jobs) == 1:
+            rcs = [fn(j) for j in jobs]
+        else:
+            with ThreadPoolExecutor(threads) as ex:
+                rcs = list(ex.map(fn, jobs))
+        if any(rcs):
+            raise ValueError("oracle_scan rejected its arguments")
+        return out
+
+    def forward(self, cfg, wq, rq, v, alpha, beta, subkeys, mem, threads=None):
+        """Addressing for write and read queries, then the scan.  mem updated in place.
+        Returns (out, (idx_w, wt_w, sigma_w), (idx_r, wt_r, sigma_r))."""
+        aw = self.address(cfg, wq, subkeys, threads=threads)
+        ar = self.address(cfg, rq, subkeys, threads=threads)
+        out = self.scan(cfg, aw[0], aw[1], ar[0], ar[1], v, alpha, beta, mem, threads=threads)
+        return out, aw, ar
+
+
+_default = None
+
+
+def get() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+if __name__ == "__main__":
+    print(build(*sys.argv[1:2]))
