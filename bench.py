@@ -1,0 +1,202 @@
+"""Benchmark of the SDM layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one sdm_forward over the whole batch of the 1.4B-shaped layer
+(B=4 sequences, T=8192 tokens, H=1, slot width d=2048, N=480^2 slots, query
+width 256, k=32, W=64; bf16 queries, values and sub-keys; float32 state and
+arithmetic).  The memory carries over from step to step, as consecutive chunks
+of a long sequence would.  Inputs are seeded synthetic data already resident in
+HBM when the timed region starts.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix, published
+METRIC = "SDM layer tokens/sec (1 GPU) + achieved HBM GB/s vs roofline, 1.4B shape"
+WORKLOAD = 2  # the 1.4B-shaped single layer
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sdm_scan_1p4b_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def scan_bytes_per_launch(cfg) -> int:
+    s = 2 if cfg.state_bf16 else 4
+    return cfg.B * cfg.T * cfg.H * 3 * cfg.W * cfg.d * s
+
+
+def score_flops_per_launch(cfg) -> int:
+    return cfg.B * cfg.T * cfg.H * 2 * cfg.S * cfg.dh * 2
+
+
+def cpu_baseline(cfg, x, budget_s: float):
+    """The oracle, untouched, on a bounded sample of the same workload: the
+    first sequence, its first T' tokens, full slot width and all N slots."""
+    import numpy as np
+
+    import oracle
+    o = oracle.get()
+    threads = oracle.default_threads()
+
+    def run(tn):
+        c = cfg.replace(B=1, T=tn)
+        sl = {k: np.ascontiguousarray(x[k][:1, :tn]) for k in ("wq", "rq", "v", "alpha", "beta")}
+        mem = np.ascontiguousarray(x["mem0"][:1])
+        t0 = time.perf_counter()
+        o.forward(c, sl["wq"], sl["rq"], sl["v"], sl["alpha"], sl["beta"], x["subkeys"], mem, threads=threads)
+        return time.perf_counter() - t0
+
+    tn = 64
+    dt = run(tn)
+    per_tok = dt / tn
+    tn2 = int(min(cfg.T, max(tn, budget_s / max(per_tok, 1e-9))))
+    if tn2 > tn:
+        tn, dt = tn2, run(tn2)
+    return {"value": tn / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"sequence 0, tokens 0..{tn - 1} of {cfg.T} (of {cfg.B * cfg.T} in the batch), full d and N; "
+                      f"{dt:.1f} s wall with {threads} threads (rows and slot elements split over threads)"}
+
+
+def load_traffic(kernel_signature: str):
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary, if
+    it was taken on the kernel as it is now."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_signature") != kernel_signature:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def kernel_signature() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("sdm_scan.hip", "sdm_internal.h"):
+        h.update(open(os.path.join(ROOT, "sparse_memory_linear_pk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 4 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sdm_inputs as gi
+    from sparse_memory_linear_pk_amd import SDM
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": a.numel() * 4, "launches": 5}))
+        return
+
+    cfg = gi.config(WORKLOAD)
+    log(f"generating inputs for {cfg}")
+    t0 = time.perf_counter()
+    x = gi.make_inputs(cfg)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), dtype=torch.float32, device="cuda")
+    layer = SDM.from_config(cfg)
+
+    def step():
+        layer.forward(d["wq"], d["rq"], d["v"], d["alpha"], d["beta"], d["subkeys"], d["mem0"], out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    layer.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        if (i + 1) % 10 == 0:
+            log(f"step {i + 1}/{args.steps}")
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tm = layer.timing()
+    layer.close()
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite output")
+
+    sec = t1 - t0
+    tokens = cfg.B * cfg.T * args.steps
+    scan_ms = tm["ms_scan"] / max(1, tm["n_scan"])
+    score_ms = tm["ms_score"] / max(1, tm["n_score"])
+    sel_ms = tm["ms_select"] / max(1, tm["n_select"])
+    haz_ms = tm["ms_hazard"] / max(1, tm["n_hazard"])
+    nbytes = scan_bytes_per_launch(cfg)
+    achieved = nbytes / (scan_ms * 1e-3) / 1e9
+    sig = kernel_signature()
+    traffic = load_traffic(sig)
+    score_tflops = score_flops_per_launch(cfg) / (score_ms * 1e-3) / 1e12
+    peak_mfma = BF16_MFMA_PEAK_TFLOPS if cfg.in_bf16 else F32_MFMA_PEAK_TFLOPS
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; queries, values and sub-keys bf16, state float32 ~N(0,0.02))",
+        "config": {"workload": "sdm-1.4B layer: B=4 H=1 T=8192 d=2048 N=480^2 dk=256 k=32 W=64, "
+                               "bf16 inputs, float32 state",
+                   "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "sdm_scan", "bytes_per_launch": nbytes, "ms_per_launch": scan_ms},
+        "kernels_ms_per_step": {"pk_score": 2 * score_ms, "pk_topk": 2 * sel_ms, "sdm_hazard": haz_ms,
+                                "sdm_scan": scan_ms},
+        "pk_score": {"tflops": score_tflops, "peak_tflops": peak_mfma, "frac": score_tflops / peak_mfma},
+        "kernel_signature": sig,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * sdm.h -- C ABI of the Sparse Delta Memory (SDM) layer forward pass on AMD
+ * MI355X (gfx950).
+ *
+ * The operation (SDM blog post, lcabannes.github.io/sdm-blogpost, section
+ * "How does SDM work?", its "Write & Read" subsection and the caption of the
+ * figure "The SDM mechanism, end to end"): each (sequence b, head h) owns a
+ * memory of N = S*S slot vectors of width d.  For every token t, in order:
+ *   1. addressing: the write query wq[b,t,h] is split into two halves; half 0
+ *      is scored against sub-key table 0 and half 1 against table 1 (S
+ *      sub-keys each); each half keeps its k best sub-keys; every pair (a, b)
+ *      of survivors is a candidate slot n = a*S + b scored by the float sum of
+ *      its two half scores; the W best candidates are selected and weighted by
+ *      a softmax of their sums.  The read query rq[b,t,h] selects W read slots
+ *      with weights the same way, against the same sub-key tables.
+ *   2. write: the W write slots are decayed by alpha[b,t,h]; the memory's
+ *      prediction vhat = sum_i w_i x_i of v[b,t,h] is formed from the decayed
+ *      slots x_i; each slot becomes x_i + w_i * beta[b,t,h] * (v - vhat).
+ *   3. read: out[b,t,h] = sum_j r_j * M[m_j], after the write of the same token.
+ * Orders are by score descending, then index ascending.  Slots that are not
+ * written keep their value.  All arithmetic is float32; a bf16 state is
+ * rounded to nearest-even when a slot is stored.
+ *
+ * Layouts (row-major, innermost last; all pointers are DEVICE pointers owned
+ * by the caller, 16-byte aligned):
+ *   wq, rq    [B, T, H, dk]    in_dtype
+ *   v         [B, T, H, d]     in_dtype
+ *   alpha     [B, T, H]        float32, the decay of the write-selected slots
+ *   beta      [B, T, H]        float32, the delta-rule step size
+ *   subkeys   [H, 2, S, dk/2]  in_dtype, table 0 then table 1 per head
+ *   mem_inout [B, H, N, d]     state_dtype, slot-major: slot n's d values are
+ *                              contiguous; read as the initial memory and
+ *                              overwritten with the memory after token T-1
+ *   out       [B, T, H, d]     float32
+ *   idx, wt   [B*T*H, W]       int32 slot ids / float32 weights, best first
+ *   scores    [B*T*H, 2, S]    float32 half scores
+ *
+ * Errors: every entry point returns a status and never throws.  Arguments are
+ * checked on the host before anything is launched; on any error nothing is
+ * launched and sdm_last_error() describes it.  NaN/Inf inputs are not checked
+ * and propagate.  Calls are asynchronous on the stream given to sdm_create;
+ * the library never synchronises the stream except in sdm_get_timing.
+ * A handle must not be used from two host threads at once.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDM_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define SDM_API __attribute__((visibility("default")))
+#else
+#define SDM_API
+#endif
+
+typedef struct sdm_ctx* sdm_handle;
+
+typedef enum {
+    SDM_OK = 0,
+    SDM_ERR_INVALID_ARG = 1, /* a null/misaligned pointer, a bad handle, an inconsistent shape */
+    SDM_ERR_UNSUPPORTED = 2, /* a valid shape outside what the kernels implement */
+    SDM_ERR_OOM = 3,         /* device workspace allocation failed */
+    SDM_ERR_DEVICE = 4       /* a HIP runtime error */
+} sdm_status;
+
+typedef enum { SDM_F32 = 0, SDM_BF16 = 1 } sdm_dtype;
+
+typedef struct {
+    int B;      /* sequences */
+    int H;      /* heads: independent memories and sub-key tables per sequence */
+    int T;      /* tokens per call */
+    int d;      /* slot width */
+    int n_sub;  /* S, sub-keys per table; N = S*S slots */
+    int dk;     /* query width; each half is dk/2 */
+    int k;      /* per-half candidates */
+    int W;      /* slots selected per token, for the write and for the read */
+    sdm_dtype in_dtype;    /* wq, rq, v, subkeys */
+    sdm_dtype state_dtype; /* mem_inout */
+} sdm_config;
+
+/* Accumulated device time per kernel (milliseconds) since timing was enabled. */
+typedef struct {
+    double ms_score;   /* sub-key scoring (MFMA) */
+    double ms_select;  /* per-half top-k, top-W, softmax */
+    double ms_hazard;  /* the scan's forwarding plan */
+    double ms_scan;    /* the memory scan */
+    long long n_score, n_select, n_hazard, n_scan; /* launches timed */
+} sdm_timing;
+
+/* Supported shapes: 1 <= k <= min(S, 64); 1 <= W <= min(k*k, 64); S <= 1024;
+ * dk/2 a multiple of 16 and at most 256; d a multiple of 8; N*d*sizeof(state)
+ * below 2^32 bytes per memory. */
+
+/* Validate cfg, allocate the device workspace and bind the HIP stream
+ * (a hipStream_t, NULL for the default stream).  *out receives the handle.
+ * The device is the one current on the calling thread. */
+SDM_API sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out);
+
+/* The whole layer forward for B sequences of T tokens: addressing of wq and rq,
+ * then the scan.  mem_inout is updated in place; out receives the reads. */
+SDM_API sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
+                       const float* beta, const void* subkeys, void* mem_inout, float* out);
+
+/* Free the workspace and the handle.  Waits for the handle's stream first. */
+SDM_API sdm_status sdm_destroy(sdm_handle h);
+
+/* Static text for a status code. */
+SDM_API const char* sdm_status_str(sdm_status s);
+
+/* Text of the last error on the calling host thread ("" if none). */
+SDM_API const char* sdm_last_error(void);
+
+/* Device workspace bytes sdm_create would allocate for cfg. */
+SDM_API sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes);
+
+/* Stage seams (the same kernels sdm_forward runs), for staged checking.
+ * sdm_score:     half scores of the B*T*H rows of q            -> scores
+ * sdm_select:    top-k / outer-sum top-W / softmax of scores   -> idx, wt
+ * sdm_address:   sdm_score then sdm_select, scores kept internal
+ * sdm_scan_with: the scan driven by given write and read addressing */
+SDM_API sdm_status sdm_score(sdm_handle h, const void* q, const void* subkeys, float* scores);
+SDM_API sdm_status sdm_select(sdm_handle h, const float* scores, int32_t* idx, float* wt);
+SDM_API sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t* idx, float* wt);
+SDM_API sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                         const float* wt_r, const void* v, const float* alpha, const float* beta,
+                         void* mem_inout, float* out);
+
+/* Per-kernel timing with HIP events recorded on the handle's stream around
+ * every launch.  sdm_get_timing waits for the recorded events, adds them to the
+ * totals and returns the totals; enabling again resets them. */
+SDM_API sdm_status sdm_set_timing(sdm_handle h, int enable);
+SDM_API sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDM_H */

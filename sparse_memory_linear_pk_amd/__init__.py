@@ -1,0 +1,140 @@
+"""Sparse Delta Memory (SDM) layer forward on AMD MI355X (gfx950).
+
+The layer runs in libsdm.so (hand-written HIP kernels: pk_score on MFMA,
+pk_topk, sdm_hazard and sdm_scan) behind the C ABI in include/sdm.h.  This
+module only checks tensor arguments and passes device pointers; PyTorch is used
+for device memory and the current HIP stream.
+
+    layer = SDM(B=4, H=1, T=8192, d=2048, S=480, dk=256, k=32, W=64,
+                in_bf16=True, state_bf16=False)
+    layer.forward(wq, rq, v, alpha, beta, subkeys, mem, out)   # mem updated in place
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+from ._lib import (SDM_BF16, SDM_F32, Config, SDMError, Timing, check, declared_symbols, lib)
+
+__all__ = ["SDM", "SDMError", "declared_symbols", "lib"]
+
+
+def _ptr(t):
+    """Device pointer of a tensor (or a raw integer address)."""
+    if isinstance(t, int):
+        return C.c_void_p(t)
+    return C.c_void_p(t.data_ptr())
+
+
+class SDM:
+    """One configured layer (the library handle) bound to a HIP stream."""
+
+    def __init__(self, B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False, stream=None):
+        self.shape = dict(B=B, H=H, T=T, d=d, S=S, dk=dk, k=k, W=W)
+        self.in_bf16, self.state_bf16 = bool(in_bf16), bool(state_bf16)
+        self._cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32,
+                           SDM_BF16 if state_bf16 else SDM_F32)
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream()
+        self.stream = stream
+        handle = stream if isinstance(stream, int) else stream.cuda_stream
+        self._h = C.c_void_p()
+        check(lib().sdm_create(C.byref(self._cfg), C.c_void_p(handle), C.byref(self._h)), "sdm_create")
+
+    @classmethod
+    def from_config(cls, cfg, stream=None, **overrides):
+        kw = dict(B=cfg.B, H=cfg.H, T=cfg.T, d=cfg.d, S=cfg.S, dk=cfg.dk, k=cfg.k, W=cfg.W,
+                  in_bf16=cfg.in_bf16, state_bf16=cfg.state_bf16)
+        kw.update(overrides)
+        return cls(stream=stream, **kw)
+
+    # ---- argument checks (shape, dtype, device, contiguity) ------------------
+    def _t(self, t, name, shape, dtype):
+        if isinstance(t, int):
+            return t
+        import torch
+        want = {"in": torch.bfloat16 if self.in_bf16 else torch.float32,
+                "state": torch.bfloat16 if self.state_bf16 else torch.float32,
+                "f32": torch.float32, "i32": torch.int32}[dtype]
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dtype != want:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {want}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return t
+
+    def _dims(self):
+        s = self.shape
+        return s["B"], s["H"], s["T"], s["d"], s["S"], s["dk"], s["k"], s["W"]
+
+    def forward(self, wq, rq, v, alpha, beta, subkeys, mem, out):
+        B, H, T, d, S, dk, k, W = self._dims()
+        args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
+                self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
+                self._t(beta, "beta", (B, T, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
+                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, T, H, d), "f32")]
+        check(lib().sdm_forward(self._h, *[_ptr(a) for a in args]), "sdm_forward")
+
+    def score(self, q, subkeys, scores):
+        B, H, T, d, S, dk, k, W = self._dims()
+        args = [self._t(q, "q", (B, T, H, dk), "in"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
+                self._t(scores, "scores", (B * T * H, 2, S), "f32")]
+        check(lib().sdm_score(self._h, *[_ptr(a) for a in args]), "sdm_score")
+
+    def select(self, scores, idx, wt):
+        B, H, T, d, S, dk, k, W = self._dims()
+        args = [self._t(scores, "scores", (B * T * H, 2, S), "f32"), self._t(idx, "idx", (B * T * H, W), "i32"),
+                self._t(wt, "wt", (B * T * H, W), "f32")]
+        check(lib().sdm_select(self._h, *[_ptr(a) for a in args]), "sdm_select")
+
+    def address(self, q, subkeys, idx, wt):
+        B, H, T, d, S, dk, k, W = self._dims()
+        args = [self._t(q, "q", (B, T, H, dk), "in"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
+                self._t(idx, "idx", (B * T * H, W), "i32"), self._t(wt, "wt", (B * T * H, W), "f32")]
+        check(lib().sdm_address(self._h, *[_ptr(a) for a in args]), "sdm_address")
+
+    def scan_with(self, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem, out):
+        B, H, T, d, S, dk, k, W = self._dims()
+        R = B * T * H
+        args = [self._t(idx_w, "idx_w", (R, W), "i32"), self._t(wt_w, "wt_w", (R, W), "f32"),
+                self._t(idx_r, "idx_r", (R, W), "i32"), self._t(wt_r, "wt_r", (R, W), "f32"),
+                self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
+                self._t(beta, "beta", (B, T, H), "f32"), self._t(mem, "mem", (B, H, S * S, d), "state"),
+                self._t(out, "out", (B, T, H, d), "f32")]
+        check(lib().sdm_scan_with(self._h, *[_ptr(a) for a in args]), "sdm_scan_with")
+
+    # ---- timing ----------------------------------------------------------------
+    def set_timing(self, on: bool = True):
+        check(lib().sdm_set_timing(self._h, int(on)), "sdm_set_timing")
+
+    def timing(self) -> dict:
+        t = Timing()
+        check(lib().sdm_get_timing(self._h, C.byref(t)), "sdm_get_timing")
+        return {f: getattr(t, f) for f, _ in Timing._fields_}
+
+    @staticmethod
+    def workspace_bytes(B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False) -> int:
+        cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32, SDM_BF16 if state_bf16 else SDM_F32)
+        n = C.c_size_t()
+        check(lib().sdm_workspace_bytes(C.byref(cfg), C.byref(n)), "sdm_workspace_bytes")
+        return n.value
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            check(lib().sdm_destroy(self._h), "sdm_destroy")
+            self._h = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -1,0 +1,416 @@
+// Host side of libsdm: the C ABI declared in include/sdm.h.
+//
+// Validates arguments on the host before anything reaches the device, owns the
+// addressing workspace, and launches the kernels in pipeline order on the
+// caller's stream: pk_score + pk_topk for the write queries, the same for the
+// read queries, sdm_hazard, then sdm_scan.  Addressing never reads the memory,
+// so the pipeline has no feedback from the scan.
+#include "sdm.h"
+#include "sdm_internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+namespace {
+
+constexpr uint32_t kMagic = 0x53444d31u; // "SDM1"
+thread_local char g_err[512] = "";
+
+sdm_status fail(sdm_status s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+enum Kind { K_SCORE = 0, K_SELECT = 1, K_HAZARD = 2, K_SCAN = 3 };
+
+struct TimedLaunch {
+    Kind kind;
+    hipEvent_t start, stop;
+};
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+    size_t scores, idx, wt, fwd, total;
+};
+
+Layout layout_of(const sdm_config& c)
+{
+    const size_t rows = (size_t)c.B * c.T * c.H;
+    Layout L;
+    L.scores = align_up(rows * 2 * (size_t)c.n_sub * sizeof(float));
+    L.idx = align_up(rows * (size_t)c.W * sizeof(int32_t));
+    L.wt = align_up(rows * (size_t)c.W * sizeof(float));
+    L.fwd = align_up(rows * (size_t)c.W * sizeof(int32_t));
+    L.total = L.scores + 2 * (L.idx + L.wt + L.fwd);
+    return L;
+}
+
+sdm_status check_config(const sdm_config* c, sdm::ScanPlan* plan)
+{
+    if (!c)
+        return fail(SDM_ERR_INVALID_ARG, "config is NULL");
+    if (c->B < 1 || c->H < 1 || c->T < 1 || c->d < 1 || c->n_sub < 1 || c->dk < 1 || c->k < 1 || c->W < 1)
+        return fail(SDM_ERR_INVALID_ARG, "every size must be >= 1 (B=%d H=%d T=%d d=%d S=%d dk=%d k=%d W=%d)", c->B,
+                    c->H, c->T, c->d, c->n_sub, c->dk, c->k, c->W);
+    if ((c->in_dtype != SDM_F32 && c->in_dtype != SDM_BF16) ||
+        (c->state_dtype != SDM_F32 && c->state_dtype != SDM_BF16))
+        return fail(SDM_ERR_INVALID_ARG, "unknown dtype");
+    if (c->dk % 2)
+        return fail(SDM_ERR_INVALID_ARG, "dk=%d must be even (two halves)", c->dk);
+    if (c->k > c->n_sub)
+        return fail(SDM_ERR_INVALID_ARG, "k=%d exceeds the %d sub-keys of a half", c->k, c->n_sub);
+    if ((long)c->W > (long)c->k * c->k)
+        return fail(SDM_ERR_INVALID_ARG, "W=%d exceeds the k*k=%d candidates", c->W, c->k * c->k);
+    const int dh = c->dk / 2;
+    static const int kHalfWidths[] = {16, 32, 48, 64, 96, 128, 192, 256};
+    bool dh_ok = false;
+    for (int w : kHalfWidths)
+        dh_ok |= dh == w;
+    if (!dh_ok)
+        return fail(SDM_ERR_UNSUPPORTED, "dk/2=%d: supported half widths are 16, 32, 48, 64, 96, 128, 192, 256", dh);
+    if (c->k > 64 || c->W > 64)
+        return fail(SDM_ERR_UNSUPPORTED, "k=%d, W=%d: at most 64 each", c->k, c->W);
+    if (c->n_sub > 1024)
+        return fail(SDM_ERR_UNSUPPORTED, "S=%d: at most 1024 sub-keys per half", c->n_sub);
+    if (c->d % 8)
+        return fail(SDM_ERR_UNSUPPORTED, "d=%d must be a multiple of 8", c->d);
+    const size_t s = c->state_dtype == SDM_BF16 ? 2 : 4;
+    const size_t mem_bytes = (size_t)c->n_sub * c->n_sub * c->d * s;
+    if (mem_bytes >= (1ull << 32))
+        return fail(SDM_ERR_UNSUPPORTED, "one memory is %zu bytes; at most 2^32 - 1", mem_bytes);
+    if ((long)c->B * c->T * c->H > (1l << 31) / 64)
+        return fail(SDM_ERR_UNSUPPORTED, "B*T*H=%ld rows is too many", (long)c->B * c->T * c->H);
+    if (!sdm::plan_scan(c->B, c->H, c->d, c->W, c->state_dtype == SDM_BF16, plan))
+        return fail(SDM_ERR_UNSUPPORTED, "no scan layout for d=%d W=%d", c->d, c->W);
+    return SDM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+} // namespace
+
+struct sdm_ctx {
+    uint32_t magic;
+    sdm_config cfg;
+    hipStream_t stream;
+    int device;
+    sdm::ScanPlan plan;
+    void* block;
+    Layout L;
+    float* scores;
+    int32_t* idx[2];
+    float* wt[2];
+    int32_t* fwd[2];
+    bool timing;
+    std::vector<TimedLaunch> pending;
+    sdm_timing totals;
+};
+
+namespace {
+
+sdm_status check_handle(sdm_handle h)
+{
+    if (!h || h->magic != kMagic)
+        return fail(SDM_ERR_INVALID_ARG, "invalid or destroyed handle");
+    return SDM_OK;
+}
+
+sdm_status hip_fail(hipError_t e, const char* what)
+{
+    return fail(SDM_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Records events around one launch when timing is on.
+struct Timer {
+    sdm_ctx* h;
+    Kind kind;
+    hipEvent_t a = nullptr, b = nullptr;
+    Timer(sdm_ctx* h_, Kind k) : h(h_), kind(k)
+    {
+        if (h->timing && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
+            (void)hipEventRecord(a, h->stream);
+    }
+    ~Timer()
+    {
+        if (a && b) {
+            (void)hipEventRecord(b, h->stream);
+            h->pending.push_back({kind, a, b});
+        }
+    }
+};
+
+sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, float* scores)
+{
+    const sdm_config& c = h->cfg;
+    Timer t(h, K_SCORE);
+    hipError_t e = sdm::launch_pk_score(q, subkeys, scores, (long)c.B * c.T, c.H, c.n_sub, c.dk / 2,
+                                        c.in_dtype == SDM_BF16, h->stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_score launch");
+}
+
+sdm_status run_select(sdm_ctx* h, const float* scores, int32_t* idx, float* wt)
+{
+    const sdm_config& c = h->cfg;
+    Timer t(h, K_SELECT);
+    hipError_t e = sdm::launch_pk_topk(scores, idx, wt, (long)c.B * c.T * c.H, c.n_sub, c.k, c.W, h->stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_topk launch");
+}
+
+sdm_status run_scan(sdm_ctx* h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
+                    const void* v, const float* alpha, const float* beta, void* mem, float* out)
+{
+    const sdm_config& c = h->cfg;
+    {
+        Timer t(h, K_HAZARD);
+        hipError_t e = sdm::launch_sdm_hazard(idx_w, idx_r, h->fwd[0], h->fwd[1], c.B, c.T, c.H, c.W,
+                                              h->plan.epoch, h->stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "sdm_hazard launch");
+    }
+    sdm::ScanArgs a;
+    a.idx_w = idx_w;
+    a.wt_w = wt_w;
+    a.fwd_w = h->fwd[0];
+    a.idx_r = idx_r;
+    a.wt_r = wt_r;
+    a.fwd_r = h->fwd[1];
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.mem = mem;
+    a.out = out;
+    a.B = c.B;
+    a.T = c.T;
+    a.H = c.H;
+    a.d = c.d;
+    a.W = c.W;
+    a.N = (long)c.n_sub * c.n_sub;
+    Timer t(h, K_SCAN);
+    hipError_t e = sdm::launch_sdm_scan(a, h->plan, c.state_dtype == SDM_BF16, c.in_dtype == SDM_BF16, h->stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan launch");
+}
+
+} // namespace
+
+extern "C" {
+
+const char* sdm_status_str(sdm_status s)
+{
+    switch (s) {
+    case SDM_OK: return "ok";
+    case SDM_ERR_INVALID_ARG: return "invalid argument";
+    case SDM_ERR_UNSUPPORTED: return "unsupported shape";
+    case SDM_ERR_OOM: return "out of device memory";
+    case SDM_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+const char* sdm_last_error(void) { return g_err; }
+
+sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes)
+{
+    sdm::ScanPlan plan;
+    sdm_status s = check_config(cfg, &plan);
+    if (s != SDM_OK)
+        return s;
+    if (!bytes)
+        return fail(SDM_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = layout_of(*cfg).total;
+    return SDM_OK;
+}
+
+sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
+{
+    g_err[0] = 0;
+    if (!out)
+        return fail(SDM_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    sdm::ScanPlan plan;
+    sdm_status s = check_config(cfg, &plan);
+    if (s != SDM_OK)
+        return s;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    sdm_ctx* h = new (std::nothrow) sdm_ctx();
+    if (!h)
+        return fail(SDM_ERR_OOM, "host allocation failed");
+    h->cfg = *cfg;
+    h->stream = (hipStream_t)hip_stream;
+    h->device = dev;
+    h->plan = plan;
+    h->L = layout_of(*cfg);
+    h->timing = false;
+    memset(&h->totals, 0, sizeof h->totals);
+    e = hipMalloc(&h->block, h->L.total);
+    if (e != hipSuccess) {
+        delete h;
+        (void)hipGetLastError();
+        return fail(SDM_ERR_OOM, "workspace of %zu bytes: %s", layout_of(*cfg).total, hipGetErrorString(e));
+    }
+    char* p = (char*)h->block;
+    h->scores = (float*)p;
+    p += h->L.scores;
+    for (int set = 0; set < 2; ++set) {
+        h->idx[set] = (int32_t*)p;
+        p += h->L.idx;
+        h->wt[set] = (float*)p;
+        p += h->L.wt;
+        h->fwd[set] = (int32_t*)p;
+        p += h->L.fwd;
+    }
+    h->magic = kMagic;
+    *out = h;
+    return SDM_OK;
+}
+
+sdm_status sdm_destroy(sdm_handle h)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    hipError_t e = hipStreamSynchronize(h->stream);
+    for (auto& tl : h->pending) {
+        (void)hipEventDestroy(tl.start);
+        (void)hipEventDestroy(tl.stop);
+    }
+    hipError_t e2 = hipFree(h->block);
+    h->magic = 0;
+    delete h;
+    if (e != hipSuccess)
+        return hip_fail(e, "hipStreamSynchronize");
+    if (e2 != hipSuccess)
+        return hip_fail(e2, "hipFree");
+    return SDM_OK;
+}
+
+sdm_status sdm_score(sdm_handle h, const void* q, const void* subkeys, float* scores)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!q || !subkeys || !scores)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_score: NULL pointer");
+    if (!aligned16(q) || !aligned16(subkeys) || !aligned4(scores))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_score: q and subkeys must be 16-byte aligned");
+    return run_score(h, q, subkeys, scores);
+}
+
+sdm_status sdm_select(sdm_handle h, const float* scores, int32_t* idx, float* wt)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!scores || !idx || !wt)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_select: NULL pointer");
+    if (!aligned4(scores) || !aligned4(idx) || !aligned4(wt))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_select: pointers must be 4-byte aligned");
+    return run_select(h, scores, idx, wt);
+}
+
+sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t* idx, float* wt)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!q || !subkeys || !idx || !wt)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_address: NULL pointer");
+    if (!aligned16(q) || !aligned16(subkeys) || !aligned4(idx) || !aligned4(wt))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_address: misaligned pointer");
+    s = run_score(h, q, subkeys, h->scores);
+    return s != SDM_OK ? s : run_select(h, h->scores, idx, wt);
+}
+
+sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                         const float* wt_r, const void* v, const float* alpha, const float* beta, void* mem_inout,
+                         float* out)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !v || !alpha || !beta || !mem_inout || !out)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_scan_with: NULL pointer");
+    if (!aligned16(v) || !aligned16(mem_inout) || !aligned16(out) || !aligned4(idx_w) || !aligned4(wt_w) ||
+        !aligned4(idx_r) || !aligned4(wt_r) || !aligned4(alpha) || !aligned4(beta))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_scan_with: misaligned pointer");
+    return run_scan(h, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem_inout, out);
+}
+
+sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
+                       const float* beta, const void* subkeys, void* mem_inout, float* out)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!wq || !rq || !v || !alpha || !beta || !subkeys || !mem_inout || !out)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_forward: NULL pointer");
+    if (!aligned16(wq) || !aligned16(rq) || !aligned16(v) || !aligned16(subkeys) || !aligned16(mem_inout) ||
+        !aligned16(out) || !aligned4(alpha) || !aligned4(beta))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_forward: misaligned pointer");
+    const void* q[2] = {wq, rq};
+    for (int set = 0; set < 2; ++set) {
+        s = run_score(h, q[set], subkeys, h->scores);
+        if (s == SDM_OK)
+            s = run_select(h, h->scores, h->idx[set], h->wt[set]);
+        if (s != SDM_OK)
+            return s;
+    }
+    return run_scan(h, h->idx[0], h->wt[0], h->idx[1], h->wt[1], v, alpha, beta, mem_inout, out);
+}
+
+sdm_status sdm_set_timing(sdm_handle h, int enable)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    for (auto& tl : h->pending) {
+        (void)hipEventDestroy(tl.start);
+        (void)hipEventDestroy(tl.stop);
+    }
+    h->pending.clear();
+    memset(&h->totals, 0, sizeof h->totals);
+    h->timing = enable != 0;
+    return SDM_OK;
+}
+
+sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!t)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_get_timing: NULL pointer");
+    sdm_status rc = SDM_OK;
+    for (auto& tl : h->pending) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(tl.stop);
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, tl.start, tl.stop);
+        if (e != hipSuccess && rc == SDM_OK)
+            rc = hip_fail(e, "timing event");
+        switch (tl.kind) {
+        case K_SCORE: h->totals.ms_score += ms; h->totals.n_score++; break;
+        case K_SELECT: h->totals.ms_select += ms; h->totals.n_select++; break;
+        case K_HAZARD: h->totals.ms_hazard += ms; h->totals.n_hazard++; break;
+        case K_SCAN: h->totals.ms_scan += ms; h->totals.n_scan++; break;
+        }
+        (void)hipEventDestroy(tl.start);
+        (void)hipEventDestroy(tl.stop);
+    }
+    h->pending.clear();
+    *t = h->totals;
+    return rc;
+}
+
+} // extern "C"

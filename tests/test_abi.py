@@ -1,0 +1,85 @@
+"""The C ABI without a GPU: the library loads, exports what include/sdm.h declares,
+and rejects bad arguments on the host before touching a device."""
+import ctypes as C
+
+import pytest
+
+from sparse_memory_linear_pk_amd import _lib
+from sparse_memory_linear_pk_amd._lib import Config, Timing, SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED
+
+EXPECTED = ["sdm_create", "sdm_forward", "sdm_destroy", "sdm_status_str", "sdm_last_error", "sdm_workspace_bytes",
+            "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing"]
+
+
+def _cfg(**kw):
+    base = dict(B=4, H=1, T=8192, d=2048, n_sub=480, dk=256, k=32, W=64, in_dtype=1, state_dtype=0)
+    base.update(kw)
+    return Config(**base)
+
+
+def test_header_declares_the_entry_points():
+    assert sorted(_lib.declared_symbols()) == sorted(EXPECTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _lib.declared_symbols():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = _lib.lib()
+    assert L.sdm_status_str(SDM_OK) == b"ok"
+    assert L.sdm_status_str(SDM_ERR_INVALID_ARG) == b"invalid argument"
+    assert L.sdm_status_str(99) == b"unknown status"
+
+
+def test_workspace_bytes_for_the_1p4b_shape():
+    L = _lib.lib()
+    n = C.c_size_t()
+    assert L.sdm_workspace_bytes(C.byref(_cfg()), C.byref(n)) == SDM_OK
+    rows = 4 * 8192
+    assert n.value >= rows * 2 * 480 * 4 + 2 * 3 * rows * 64 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), SDM_ERR_INVALID_ARG),
+    (dict(dk=255), SDM_ERR_INVALID_ARG),
+    (dict(k=481), SDM_ERR_INVALID_ARG),
+    (dict(k=4, W=17), SDM_ERR_INVALID_ARG),
+    (dict(in_dtype=7), SDM_ERR_INVALID_ARG),
+    (dict(dk=2 * 40), SDM_ERR_UNSUPPORTED),
+    (dict(k=65, W=64), SDM_ERR_UNSUPPORTED),
+    (dict(W=65, k=33), SDM_ERR_UNSUPPORTED),
+    (dict(n_sub=1025), SDM_ERR_UNSUPPORTED),
+    (dict(d=2044), SDM_ERR_UNSUPPORTED),
+    (dict(n_sub=640, d=3840, state_dtype=0), SDM_ERR_UNSUPPORTED),  # 6.3 GB per memory in float32
+])
+def test_bad_configs_are_rejected_on_the_host(kw, status):
+    L = _lib.lib()
+    n = C.c_size_t()
+    assert L.sdm_workspace_bytes(C.byref(_cfg(**kw)), C.byref(n)) == status
+    assert L.sdm_last_error() != b""
+    h = C.c_void_p()
+    assert L.sdm_create(C.byref(_cfg(**kw)), None, C.byref(h)) == status
+    assert h.value is None
+
+
+def test_null_arguments():
+    L = _lib.lib()
+    assert L.sdm_workspace_bytes(None, None) == SDM_ERR_INVALID_ARG
+    assert L.sdm_create(C.byref(_cfg()), None, None) == SDM_ERR_INVALID_ARG
+    for f, n in (("sdm_forward", 8), ("sdm_score", 3), ("sdm_select", 3), ("sdm_address", 4),
+                 ("sdm_scan_with", 9)):
+        assert getattr(L, f)(None, *([None] * n)) == SDM_ERR_INVALID_ARG, f
+    assert L.sdm_destroy(None) == SDM_ERR_INVALID_ARG
+    assert L.sdm_set_timing(None, 1) == SDM_ERR_INVALID_ARG
+    assert L.sdm_get_timing(None, C.byref(Timing())) == SDM_ERR_INVALID_ARG
+    assert b"handle" in L.sdm_last_error()
+
+
+def test_forged_handle_is_rejected():
+    L = _lib.lib()
+    junk = (C.c_uint32 * 64)()
+    assert L.sdm_forward(C.cast(junk, C.c_void_p), *([None] * 8)) == SDM_ERR_INVALID_ARG
+    assert L.sdm_destroy(C.cast(junk, C.c_void_p)) == SDM_ERR_INVALID_ARG
