@@ -42,31 +42,31 @@ def score_flops_per_launch(cfg) -> int:
 
 
 def cpu_baseline(cfg, x, budget_s: float):
-    """The oracle, untouched, on a bounded sample of the same workload: the
-    first sequence, its first T' tokens, full slot width and all N slots."""
+    """The oracle, untouched, on a bounded sample of the same workload: whole
+    sequences (all T tokens, full slot width, all N slots), as many of the B as
+    fit the time budget, at least the first."""
     import numpy as np
 
     import oracle
     o = oracle.get()
     threads = oracle.default_threads()
 
-    def run(tn):
-        c = cfg.replace(B=1, T=tn)
-        sl = {k: np.ascontiguousarray(x[k][:1, :tn]) for k in ("wq", "rq", "v", "alpha", "beta")}
-        mem = np.ascontiguousarray(x["mem0"][:1])
+    def run(nb, tn):
+        c = cfg.replace(B=nb, T=tn)
+        sl = {k: np.ascontiguousarray(x[k][:nb, :tn]) for k in ("wq", "rq", "v", "alpha", "beta")}
+        mem = np.ascontiguousarray(x["mem0"][:nb])
         t0 = time.perf_counter()
         o.forward(c, sl["wq"], sl["rq"], sl["v"], sl["alpha"], sl["beta"], x["subkeys"], mem, threads=threads)
         return time.perf_counter() - t0
 
-    tn = 64
-    dt = run(tn)
-    per_tok = dt / tn
-    tn2 = int(min(cfg.T, max(tn, budget_s / max(per_tok, 1e-9))))
-    if tn2 > tn:
-        tn, dt = tn2, run(tn2)
-    return {"value": tn / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"sequence 0, tokens 0..{tn - 1} of {cfg.T} (of {cfg.B * cfg.T} in the batch), full d and N; "
-                      f"{dt:.1f} s wall with {threads} threads (rows and slot elements split over threads)"}
+    per_tok = run(1, 256) / 256
+    nb = int(max(1, min(cfg.B, budget_s // max(per_tok * cfg.T, 1e-9))))
+    tn = cfg.T if nb > 1 or per_tok * cfg.T <= budget_s else int(max(256, budget_s / per_tok))
+    dt = run(nb, tn)
+    return {"value": nb * tn / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"sequences 0..{nb - 1} of {cfg.B}, tokens 0..{tn - 1} of {cfg.T}, full d and N "
+                      f"({nb * tn} of {cfg.B * cfg.T} tokens); {dt:.1f} s wall with {threads} threads "
+                      f"(addressing rows and slot elements split over threads)"}
 
 
 def load_traffic(kernel_signature: str):

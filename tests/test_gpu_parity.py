@@ -14,8 +14,8 @@ import pytest
 
 import oracle
 import sdm_inputs as gi
-from parity import (as_f32, check_scores, check_selection_exact, compare_index_sets, rel_max_err, scan_tol,
-                    score_error_bound, to_dev, to_host)
+from parity import (as_f32, check_scores, check_selection_exact, compare_index_sets, rel_max_err, rms_max_err,
+                    scan_tol, score_error_bound, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,8 @@ def full_parity(orc, cfg, x, g, label):
     mem = x["mem0"].copy()
     out = orc.scan(cfg, g["idx_w"], g["wt_w"], g["idx_r"], g["wt_r"], x["v"], x["alpha"], x["beta"], mem)
     eo, em = rel_max_err(g["out"], out), rel_max_err(g["mem"], mem)
-    say(f"[{label}] scan: out {eo:.3g}, mem {em:.3g} (tol {scan_tol(cfg)})")
+    say(f"[{label}] scan: out {eo:.3g}, mem {em:.3g} (tol {scan_tol(cfg)}); plain max/RMS: "
+        f"out {rms_max_err(g['out'], out):.3g}, mem {rms_max_err(g['mem'], mem):.3g}")
     assert eo <= scan_tol(cfg) and em <= scan_tol(cfg)
     if excused_rows == 0:
         mem = x["mem0"].copy()
@@ -273,7 +274,8 @@ def sampled_parity(orc, T, cfg, label, n_rows=512, n_elem=16, extra_rows=()):
     v = np.ascontiguousarray(x["v"][..., elems])
     ref_out = orc.scan(c, g["idx_w"], g["wt_w"], g["idx_r"], g["wt_r"], v, x["alpha"], x["beta"], mem0)
     eo, em = rel_max_err(g_out, ref_out), rel_max_err(g_mem, mem0)
-    say(f"[{label}] scan: out {eo:.3g}, mem {em:.3g} (tol {scan_tol(cfg)})")
+    say(f"[{label}] scan: out {eo:.3g}, mem {em:.3g} (tol {scan_tol(cfg)}); plain max/RMS: "
+        f"out {rms_max_err(g_out, ref_out):.3g}, mem {rms_max_err(g_mem, mem0):.3g}")
     assert eo <= scan_tol(cfg) and em <= scan_tol(cfg)
     return g
 
