@@ -160,7 +160,7 @@ def main():
     scan_ms = tm["ms_scan"] / max(1, tm["n_scan"])
     score_ms = tm["ms_score"] / max(1, tm["n_score"])
     sel_ms = tm["ms_select"] / max(1, tm["n_select"])
-    haz_ms = tm["ms_hazard"] / max(1, tm["n_hazard"])
+    plan_ms = tm["ms_plan"] / max(1, tm["n_plan"])
     nbytes = scan_bytes_per_launch(cfg)
     achieved = nbytes / (scan_ms * 1e-3) / 1e9
     sig = kernel_signature()
@@ -187,7 +187,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "sdm_scan", "bytes_per_launch": nbytes, "ms_per_launch": scan_ms},
-        "kernels_ms_per_step": {"pk_score": 2 * score_ms, "pk_topk": 2 * sel_ms, "sdm_hazard": haz_ms,
+        "kernels_ms_per_step": {"pk_score": 2 * score_ms, "pk_topk": 2 * sel_ms, "sdm_plan": plan_ms,
                                 "sdm_scan": scan_ms},
         "pk_score": {"tflops": score_tflops, "peak_tflops": peak_mfma, "frac": score_tflops / peak_mfma},
         "kernel_signature": sig,

@@ -89,9 +89,9 @@ typedef struct {
 typedef struct {
     double ms_score;   /* sub-key scoring (MFMA) */
     double ms_select;  /* per-half top-k, top-W, softmax */
-    double ms_hazard;  /* the scan's forwarding plan */
+    double ms_plan;    /* the scan's plan: packed slot records, forwarding and store decisions */
     double ms_scan;    /* the memory scan */
-    long long n_score, n_select, n_hazard, n_scan; /* launches timed */
+    long long n_score, n_select, n_plan, n_scan; /* launches timed */
 } sdm_timing;
 
 /* Supported shapes: 1 <= k <= min(S, 64); 1 <= W <= min(k*k, 64); S <= 1024;

@@ -1,7 +1,7 @@
 """Sparse Delta Memory (SDM) layer forward on AMD MI355X (gfx950).
 
 The layer runs in libsdm.so (hand-written HIP kernels: pk_score on MFMA,
-pk_topk, sdm_hazard and sdm_scan) behind the C ABI in include/sdm.h.  This
+pk_topk, sdm_plan and sdm_scan) behind the C ABI in include/sdm.h.  This
 module only checks tensor arguments and passes device pointers; PyTorch is used
 for device memory and the current HIP stream.
 

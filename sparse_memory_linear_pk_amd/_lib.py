@@ -27,9 +27,9 @@ class Config(C.Structure):
 
 
 class Timing(C.Structure):
-    _fields_ = [("ms_score", C.c_double), ("ms_select", C.c_double), ("ms_hazard", C.c_double),
+    _fields_ = [("ms_score", C.c_double), ("ms_select", C.c_double), ("ms_plan", C.c_double),
                 ("ms_scan", C.c_double), ("n_score", C.c_longlong), ("n_select", C.c_longlong),
-                ("n_hazard", C.c_longlong), ("n_scan", C.c_longlong)]
+                ("n_plan", C.c_longlong), ("n_scan", C.c_longlong)]
 
 
 def declared_symbols(header: str = HEADER) -> list[str]:

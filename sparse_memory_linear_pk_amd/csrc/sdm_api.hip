@@ -3,7 +3,7 @@
 // Validates arguments on the host before anything reaches the device, owns the
 // addressing workspace, and launches the kernels in pipeline order on the
 // caller's stream: pk_score + pk_topk for the write queries, the same for the
-// read queries, sdm_hazard, then sdm_scan.  Addressing never reads the memory,
+// read queries, sdm_plan, then sdm_scan.  Addressing never reads the memory,
 // so the pipeline has no feedback from the scan.
 #include "sdm.h"
 #include "sdm_internal.h"
@@ -28,7 +28,7 @@ sdm_status fail(sdm_status s, const char* fmt, ...)
     return s;
 }
 
-enum Kind { K_SCORE = 0, K_SELECT = 1, K_HAZARD = 2, K_SCAN = 3 };
+enum Kind { K_SCORE = 0, K_SELECT = 1, K_PLAN = 2, K_SCAN = 3 };
 
 struct TimedLaunch {
     Kind kind;
@@ -38,7 +38,7 @@ struct TimedLaunch {
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t scores, idx, wt, fwd, total;
+    size_t scores, idx, wt, plan, total;
 };
 
 Layout layout_of(const sdm_config& c)
@@ -48,8 +48,8 @@ Layout layout_of(const sdm_config& c)
     L.scores = align_up(rows * 2 * (size_t)c.n_sub * sizeof(float));
     L.idx = align_up(rows * (size_t)c.W * sizeof(int32_t));
     L.wt = align_up(rows * (size_t)c.W * sizeof(float));
-    L.fwd = align_up(rows * (size_t)c.W * sizeof(int32_t));
-    L.total = L.scores + 2 * (L.idx + L.wt + L.fwd);
+    L.plan = align_up(sdm::plan_bytes(c.B, c.H, c.T, c.W));
+    L.total = L.scores + 2 * (L.idx + L.wt) + L.plan;
     return L;
 }
 
@@ -109,7 +109,7 @@ struct sdm_ctx {
     float* scores;
     int32_t* idx[2];
     float* wt[2];
-    int32_t* fwd[2];
+    uint4* plan_buf;
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
@@ -170,19 +170,13 @@ sdm_status run_scan(sdm_ctx* h, const int32_t* idx_w, const float* wt_w, const i
 {
     const sdm_config& c = h->cfg;
     {
-        Timer t(h, K_HAZARD);
-        hipError_t e = sdm::launch_sdm_hazard(idx_w, idx_r, h->fwd[0], h->fwd[1], c.B, c.T, c.H, c.W,
-                                              h->plan.epoch, h->stream);
+        Timer t(h, K_PLAN);
+        hipError_t e = sdm::launch_sdm_plan(idx_w, wt_w, idx_r, wt_r, h->plan_buf, c.B, c.T, c.H, c.W, h->stream);
         if (e != hipSuccess)
-            return hip_fail(e, "sdm_hazard launch");
+            return hip_fail(e, "sdm_plan launch");
     }
     sdm::ScanArgs a;
-    a.idx_w = idx_w;
-    a.wt_w = wt_w;
-    a.fwd_w = h->fwd[0];
-    a.idx_r = idx_r;
-    a.wt_r = wt_r;
-    a.fwd_r = h->fwd[1];
+    a.plan = h->plan_buf;
     a.v = v;
     a.alpha = alpha;
     a.beta = beta;
@@ -267,9 +261,8 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
         p += h->L.idx;
         h->wt[set] = (float*)p;
         p += h->L.wt;
-        h->fwd[set] = (int32_t*)p;
-        p += h->L.fwd;
     }
+    h->plan_buf = (uint4*)p;
     h->magic = kMagic;
     *out = h;
     return SDM_OK;
@@ -402,7 +395,7 @@ sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t)
         switch (tl.kind) {
         case K_SCORE: h->totals.ms_score += ms; h->totals.n_score++; break;
         case K_SELECT: h->totals.ms_select += ms; h->totals.n_select++; break;
-        case K_HAZARD: h->totals.ms_hazard += ms; h->totals.n_hazard++; break;
+        case K_PLAN: h->totals.ms_plan += ms; h->totals.n_plan++; break;
         case K_SCAN: h->totals.ms_scan += ms; h->totals.n_scan++; break;
         }
         (void)hipEventDestroy(tl.start);

@@ -57,17 +57,15 @@ hipError_t launch_pk_score(const void* q, const void* subkeys, float* scores, lo
 hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, long rows, int S, int k, int W,
                           hipStream_t stream);
 
-// Forwarding plan of the scan for tokens in epochs of `epoch` tokens (see sdm_scan.hip).
-hipError_t launch_sdm_hazard(const int32_t* idx_w, const int32_t* idx_r, int32_t* fwd_w, int32_t* fwd_r, int B,
-                             int T, int H, int W, int epoch, hipStream_t stream);
+// The scan's plan: one 16-byte record per (b, h, t, position) packing the write
+// and read slot ids, their weights, where in the scan's LDS ring a slot written
+// too recently to be read from memory is found, and whether a store is superseded.
+size_t plan_bytes(int B, int H, int T, int W);
+hipError_t launch_sdm_plan(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
+                           uint4* plan, int B, int T, int H, int W, hipStream_t stream);
 
 struct ScanArgs {
-    const int32_t* idx_w;
-    const float* wt_w;
-    const int32_t* fwd_w;
-    const int32_t* idx_r;
-    const float* wt_r;
-    const int32_t* fwd_r;
+    const uint4* plan;
     const void* v;
     const float* alpha;
     const float* beta;
@@ -79,20 +77,15 @@ struct ScanArgs {
 
 // Scan launch geometry chosen for a shape.
 struct ScanPlan {
-    int lps;     // lanes sharing one slot (16 bytes each)
-    int waves;   // waves per workgroup
-    int epoch;   // tokens per epoch
-    int grid;    // workgroups
-    int lds;     // dynamic LDS bytes
+    int lps;       // lanes sharing one slot (16 bytes each)
+    int waves;     // waves per workgroup
+    int lookahead; // tokens between a slot read's issue and its use
+    int grid;      // workgroups
+    int lds;       // dynamic LDS bytes
 };
 
 bool plan_scan(int B, int H, int d, int W, bool state_bf16, ScanPlan* plan);
 hipError_t launch_sdm_scan(const ScanArgs& a, const ScanPlan& plan, bool state_bf16, bool in_bf16,
                            hipStream_t stream);
-
-// fwd word layout produced by the hazard kernel and read by the scan
-constexpr int kFwdPosBits = 24;           // (ring position + 1), 0 = read from memory
-constexpr uint32_t kFwdPosMask = (1u << kFwdPosBits) - 1u;
-constexpr uint32_t kFwdSkipStore = 1u << kFwdPosBits; // a later write in the same epoch supersedes this one
 
 } // namespace sdm
