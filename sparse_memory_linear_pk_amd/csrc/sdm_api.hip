@@ -110,6 +110,7 @@ struct sdm_ctx {
     int32_t* idx[2];
     float* wt[2];
     uint4* plan_buf;
+    float2* ab_buf;
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
@@ -171,15 +172,15 @@ sdm_status run_scan(sdm_ctx* h, const int32_t* idx_w, const float* wt_w, const i
     const sdm_config& c = h->cfg;
     {
         Timer t(h, K_PLAN);
-        hipError_t e = sdm::launch_sdm_plan(idx_w, wt_w, idx_r, wt_r, h->plan_buf, c.B, c.T, c.H, c.W, h->stream);
+        hipError_t e = sdm::launch_sdm_plan(idx_w, wt_w, idx_r, wt_r, alpha, beta, h->plan_buf, h->ab_buf, c.B, c.T,
+                                            c.H, c.W, h->stream);
         if (e != hipSuccess)
             return hip_fail(e, "sdm_plan launch");
     }
     sdm::ScanArgs a;
     a.plan = h->plan_buf;
+    a.ab = h->ab_buf;
     a.v = v;
-    a.alpha = alpha;
-    a.beta = beta;
     a.mem = mem;
     a.out = out;
     a.B = c.B;
@@ -263,6 +264,7 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
         p += h->L.wt;
     }
     h->plan_buf = (uint4*)p;
+    h->ab_buf = (float2*)(p + (size_t)cfg->B * cfg->H * cfg->T * cfg->W * sizeof(uint4));
     h->magic = kMagic;
     *out = h;
     return SDM_OK;

@@ -60,15 +60,16 @@ hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, long row
 // The scan's plan: one 16-byte record per (b, h, t, position) packing the write
 // and read slot ids, their weights, where in the scan's LDS ring a slot written
 // too recently to be read from memory is found, and whether a store is superseded.
-size_t plan_bytes(int B, int H, int T, int W);
+// Also writes (alpha, beta) of every token next to each other for the scan.
+size_t plan_bytes(int B, int H, int T, int W); // records followed by the (alpha, beta) pairs
 hipError_t launch_sdm_plan(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
-                           uint4* plan, int B, int T, int H, int W, hipStream_t stream);
+                           const float* alpha, const float* beta, uint4* plan, float2* ab, int B, int T, int H, int W,
+                           hipStream_t stream);
 
 struct ScanArgs {
-    const uint4* plan;
+    const uint4* plan;  // [B*H, T, W] records
+    const float2* ab;   // [B*H, T] (alpha, beta)
     const void* v;
-    const float* alpha;
-    const float* beta;
     void* mem;
     float* out;
     int B, T, H, d, W;
@@ -78,6 +79,7 @@ struct ScanArgs {
 // Scan launch geometry chosen for a shape.
 struct ScanPlan {
     int lps;       // lanes sharing one slot (16 bytes each)
+    int rw;        // slot positions per lane
     int waves;     // waves per workgroup
     int lookahead; // tokens between a slot read's issue and its use
     int grid;      // workgroups

@@ -88,7 +88,10 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(const int32_t* _
                                                               const float* __restrict__ wt_w,
                                                               const int32_t* __restrict__ idx_r,
                                                               const float* __restrict__ wt_r,
-                                                              uint4* __restrict__ plan, int T, int H, int W)
+                                                              const float* __restrict__ alpha,
+                                                              const float* __restrict__ beta,
+                                                              uint4* __restrict__ plan, float2* __restrict__ ab,
+                                                              int T, int H, int W)
 {
     constexpr int P = kLookahead;
     extern __shared__ int32_t s_plan[]; // [span][64] sorted slots, then [span][64] their positions
@@ -126,6 +129,10 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(const int32_t* _
     }
     __syncthreads();
 
+    for (int t = t0 + (int)threadIdx.x; t < t1; t += blockDim.x) {
+        const long o = (long)(b * T + t) * H + h;
+        ab[(long)bh * T + t] = make_float2(alpha[o], beta[o]);
+    }
     const int items = (t1 - t0) * W;
     for (int it = threadIdx.x; it < items; it += blockDim.x) {
         const int t = t0 + it / W, i = it % W;
@@ -163,11 +170,37 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(const int32_t* _
 // the scan
 // ---------------------------------------------------------------------------
 
-constexpr int kScanMaxThreads = 512;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// bf16 bits of the double x rounded once to nearest-even.  x rounds to float
+// first; that can only go wrong when the float lands exactly on a bf16 tie while
+// x was not on it, and then moving the float one ulp towards x settles the tie
+// the way x lies (rounding is monotone and the bf16 tie is a float value).
+__device__ __forceinline__ float settle_bf16_tie(double x)
+{
+    const float f = (float)x;
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0xFFFFu) == 0x8000u) {
+        const double fd = (double)f;
+        if (fd != x)
+            u = (__builtin_fabs(fd) > __builtin_fabs(x)) ? u - 1u : u + 1u;
+    }
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t)); // v_cvt_pk_bf16_f32
+}
+
+// State formats.  `compute_t` is the type of the write path: float for a float32
+// state, double for a bf16 state so that every stored value is the single
+// nearest-even rounding of (nearly) the exact value, as a double reference has it.
 template <class ST> struct StateFmt;
 template <> struct StateFmt<float> {
     static constexpr int VEC = 4;
+    using compute_t = float;
     __device__ static void unpack(const uint4& r, float (&x)[4])
     {
         x[0] = __uint_as_float(r.x);
@@ -182,6 +215,7 @@ template <> struct StateFmt<float> {
 };
 template <> struct StateFmt<uint16_t> { // bfloat16 bits
     static constexpr int VEC = 8;
+    using compute_t = double;
     __device__ static void unpack(const uint4& r, float (&x)[8])
     {
         x[0] = bf16_lo(r.x); x[1] = bf16_hi(r.x);
@@ -189,10 +223,14 @@ template <> struct StateFmt<uint16_t> { // bfloat16 bits
         x[4] = bf16_lo(r.z); x[5] = bf16_hi(r.z);
         x[6] = bf16_lo(r.w); x[7] = bf16_hi(r.w);
     }
-    __device__ static uint4 pack(const float (&x)[8])
+    __device__ static uint4 pack(const double (&x)[8])
     {
-        return make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                          pack_bf16x2(x[6], x[7]));
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            f[q] = settle_bf16_tie(x[q]);
+        return make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]),
+                          pack2_bf16(f[6], f[7]));
     }
 };
 
@@ -247,55 +285,163 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ float xor8(float x)
+// x + (x of lane ^ D), identical in both lanes of every pair (an exactly
+// commutative add): DPP row_ror:8 for D = 8, the gfx950 permlane swaps for 16
+// and 32, ds_bpermute below 8.
+template <int D> __device__ __forceinline__ uint32_t partner32(uint32_t u)
 {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    static_assert(D == 8, "DPP partner only for D = 8");
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float xor16(float x)
+template <int D> __device__ __forceinline__ float bfly(float x)
 {
-    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    if constexpr (D < 8) {
+        return x + __shfl_xor(x, D);
+    } else if constexpr (D == 8) {
+        return x + __uint_as_float(partner32<8>(__float_as_uint(x)));
+    } else if constexpr (D == 16) {
+        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    } else {
+        static_assert(D == 32, "butterfly distance");
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
 }
-__device__ __forceinline__ float xor32(float x)
+template <int D> __device__ __forceinline__ double bfly(double x)
 {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    if constexpr (D < 8) {
+        return x + __shfl_xor(x, D);
+    } else {
+        const uint64_t b = (uint64_t)__double_as_longlong(x);
+        const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
+        if constexpr (D == 8) {
+            const uint64_t p = ((uint64_t)partner32<8>(hi) << 32) | partner32<8>(lo);
+            return x + __longlong_as_double((long long)p);
+        } else {
+            uint32_t a_lo, b_lo, a_hi, b_hi;
+            if constexpr (D == 16) {
+                const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+                const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+                a_lo = sl[0]; b_lo = sl[1]; a_hi = sh[0]; b_hi = sh[1];
+            } else {
+                static_assert(D == 32, "butterfly distance");
+                const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+                const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+                a_lo = sl[0]; b_lo = sl[1]; a_hi = sh[0]; b_hi = sh[1];
+            }
+            return __longlong_as_double((long long)(((uint64_t)a_hi << 32) | a_lo)) +
+                   __longlong_as_double((long long)(((uint64_t)b_hi << 32) | b_lo));
+        }
+    }
+}
+
+// Sum over all 64/LPS lane groups of a wave (lanes sharing lane % LPS).
+template <int LPS, class T> __device__ __forceinline__ T wave_sum(T x)
+{
+    if constexpr (LPS < 64)
+        x = bfly<LPS>(x);
+    if constexpr (2 * LPS < 64)
+        x = bfly<2 * LPS>(x);
+    if constexpr (4 * LPS < 64)
+        x = bfly<4 * LPS>(x);
+    if constexpr (8 * LPS < 64)
+        x = bfly<8 * LPS>(x);
+    if constexpr (16 * LPS < 64)
+        x = bfly<16 * LPS>(x);
+    if constexpr (32 * LPS < 64)
+        x = bfly<32 * LPS>(x);
+    return x;
+}
+
+// Sum of the per-wave partials: lane group g holds partial (g mod p2) (zero past
+// the last wave) and a butterfly over log2(p2) group bits adds them.
+template <int LPS, class T> __device__ __forceinline__ T waves_sum(T x, int p2)
+{
+    if constexpr (LPS < 64)
+        if (p2 > 1) x = bfly<LPS>(x);
+    if constexpr (2 * LPS < 64)
+        if (p2 > 2) x = bfly<2 * LPS>(x);
+    if constexpr (4 * LPS < 64)
+        if (p2 > 4) x = bfly<4 * LPS>(x);
+    if constexpr (8 * LPS < 64)
+        if (p2 > 8) x = bfly<8 * LPS>(x);
+    if constexpr (16 * LPS < 64)
+        if (p2 > 16) x = bfly<16 * LPS>(x);
+    if constexpr (32 * LPS < 64)
+        if (p2 > 32) x = bfly<32 * LPS>(x);
+    return x;
+}
+
+// ds_swizzle in bit mode: lane l of each 32-lane half reads lane ((l & AND) within that half).
+template <int AND> __device__ __forceinline__ uint32_t swz(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, AND);
+}
+template <int AND> __device__ __forceinline__ uint4 swz4(const uint4& v)
+{
+    return make_uint4(swz<AND>(v.x), swz<AND>(v.y), swz<AND>(v.z), swz<AND>(v.w));
+}
+
+// Four per-lane values, each summed over the 8 lane groups of a wave (LPS = 8):
+// one DPP stage, then two transposing permlane16 swaps and one permlane32 swap,
+// so that row r (lanes 16r..16r+15) ends with the total of value r.  Every value
+// goes through the same tree ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)).
+__device__ __forceinline__ float reduce4_to_rows(float v0, float v1, float v2, float v3)
+{
+    v0 = bfly<8>(v0);
+    v1 = bfly<8>(v1);
+    v2 = bfly<8>(v2);
+    v3 = bfly<8>(v3);
+    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+    const float t01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]); // rows 0,2: v0; rows 1,3: v1
+    const float t23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]); // rows 0,2: v2; rows 1,3: v3
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(t01), __float_as_uint(t23), false, false);
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// Sum over the lanes that share `lane % LPS` (the 64/LPS lane groups), the same
-// value in every lane: a xor butterfly, so every lane adds in the same order.
-template <int LPS> __device__ __forceinline__ float group_sum(float x)
+// At most 4 waves per workgroup (1 when a wave holds every position with one
+// position per lane), so each wave may use the whole register file of its SIMD.
+// FAST: float arithmetic, 8 lanes per slot chunk, two positions per lane and
+// exactly 4 waves; sums over slots then use reduce4_to_rows.
+template <class ST, class VT, int LPS, int RW, bool FAST>
+__global__ __launch_bounds__(RW == 2 ? 256 : 64) void sdm_scan_kernel(ScanArgs a)
 {
-#pragma unroll
-    for (int m = LPS; m < 8; m <<= 1)
-        x += __shfl_xor(x, m);
-    x = xor8(x);
-    x = xor16(x);
-    return xor32(x);
-}
-
-template <class ST, class VT, int LPS>
-__global__ __launch_bounds__(kScanMaxThreads) void sdm_scan_kernel(ScanArgs a)
-{
-    static_assert(LPS <= 8, "lane groups are summed with a butterfly from distance LPS up");
     using F = StateFmt<ST>;
+    using CT = typename F::compute_t;
     using VS = VSlice<VT, F::VEC>;
-    constexpr int P = kLookahead, R = kRing;
+    constexpr int P = kLookahead, R = kRing, ZS = P + 1, ZR = 2 * P + 2;
     constexpr int VEC = F::VEC;       // slot elements per lane
     constexpr int DC = LPS * VEC;     // slot elements per workgroup
-    constexpr int GPW = 64 / LPS;     // slot positions per wave
-    constexpr int O_OPS = VEC / 4;    // 16-byte stores per lane for `out`
+    constexpr int GPW = 64 / LPS;     // lane groups per wave
+    static_assert(!FAST || (VEC == 4 && LPS == 8 && RW == 2 && sizeof(CT) == 4), "fast path shape");
+    static_assert(VEC / 4 <= GPW, "out is stored by the first VEC/4 lane groups");
     // vector-memory operations per token: reads issued ahead, then stores
-    constexpr int L_OPS = 2 + VS::V_OPS + 2 + 1; // write slot, read slot, v, alpha, beta, plan record
-    constexpr int C_OPS = O_OPS + 1;             // out (previous token), slot store
+    constexpr int L_OPS = 2 * RW + VS::V_OPS + 1 + RW; // slot reads (write, read), v, alpha|beta, plan records
+    constexpr int C_OPS = RW + 1;                      // slot stores, out
     constexpr int K = (P - 1) * (L_OPS + C_OPS) + C_OPS;
+    static_assert(K <= 63, "more operations in flight than vmcnt can count");
+    // metadata is read by one lane per group (records) or per half-wave (v) and broadcast
+    constexpr int REC_SWZ = 0x1F & ~(LPS - 1); // lane -> first lane of its group
+    constexpr int V_SWZ = LPS - 1;             // lane -> same element in the first group of its half
 
     const int nwv = blockDim.x >> 6;
+    int p2 = 1;
+    while (p2 < nwv)
+        p2 <<= 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane / LPS, el = lane % LPS;
-    const int pos = wave * GPW + g;     // this lane's position in the token's write and read sets
-    const bool act = pos < a.W;
+    const bool rec_lead = el == 0;
+    const bool v_lead = g % (GPW / 2 > 0 ? GPW / 2 : 1) == 0;
     const int T = a.T, H = a.H, W = a.W, d = a.d;
+    int pos[RW];
+    bool act[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        pos[r] = (wave * RW + r) * GPW + g; // this lane's positions in the token's write and read sets
+        act[r] = pos[r] < W;
+    }
     const int nchunk = d / DC;
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const int b = bh / H, h = bh % H;
@@ -305,86 +451,118 @@ __global__ __launch_bounds__(kScanMaxThreads) void sdm_scan_kernel(ScanArgs a)
     const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * row_bytes,
                                                    (uint32_t)((size_t)a.N * row_bytes));
     const __amdgpu_buffer_rsrc_t r_plan = make_rsrc(a.plan + (size_t)bh * T * W, (uint32_t)((size_t)T * W * 16));
-    // v, out: [B, T, H, d], alpha, beta: [B, T, H]; each resource spans sequence b
+    const __amdgpu_buffer_rsrc_t r_ab = make_rsrc(a.ab + (size_t)bh * T, (uint32_t)((size_t)T * 8));
+    // v, out: [B, T, H, d]; each resource spans sequence b
     const size_t tok0 = (size_t)b * T * H;
     const __amdgpu_buffer_rsrc_t r_v = make_rsrc(static_cast<const VT*>(a.v) + tok0 * d,
                                                  (uint32_t)((size_t)T * H * d * sizeof(VT)));
     const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + tok0 * d, (uint32_t)((size_t)T * H * d * 4));
-    const __amdgpu_buffer_rsrc_t r_al = make_rsrc(a.alpha + tok0, (uint32_t)((size_t)T * H * 4));
-    const __amdgpu_buffer_rsrc_t r_be = make_rsrc(a.beta + tok0, (uint32_t)((size_t)T * H * 4));
     const uint32_t v_lane = (uint32_t)(chunk * DC + el * VEC) * (uint32_t)sizeof(VT);
-    const uint32_t o_lane = (uint32_t)(chunk * DC + el * VEC) * 4u;
 
     extern __shared__ uint4 lds[];
-    uint4* ring = lds;                                           // [R*W][LPS]
-    float* red = reinterpret_cast<float*>(lds + R * W * LPS);    // [nwv][LPS][VEC]
-    float* ored = red + nwv * LPS * VEC;                         // [nwv][LPS][VEC]
+    uint4* ring = lds;                                             // [R*W][LPS] stored slot chunks
+    CT* red = reinterpret_cast<CT*>(lds + R * W * LPS);            // [nwv][LPS][VEC] write partials
+    float* ored = reinterpret_cast<float*>(red + nwv * LPS * VEC); // [nwv][LPS][VEC] read partials
 
-    // per-token offsets; tokens outside [0, T) and inactive lanes read past the end
     auto tok_ok = [&](int t) { return t >= 0 && t < T; };
-    auto plan_off = [&](int t) -> uint32_t { return (tok_ok(t) && act) ? (uint32_t)(t * W + pos) * 16u : kOOB; };
 
-    // Ring buffers in registers (indices are compile-time after unrolling):
-    //   slot chunks of token t in [t mod (P+1)], loaded at the end of body t-P-1, used in body t;
-    //   plan record of token t in rec[t mod (2P+2)], loaded at the end of body t-2P-1, used by the
-    //   issue at the end of body t-P-1 (slot ids) and in body t (weights, ring positions).
-    constexpr int ZS = P + 1, ZR = 2 * P + 2;
-    uint4 rec[ZR];
-    uint4 sw[ZS], sr[ZS];
+    // Register rings (indices are constants after unrolling):
+    //   slot chunks, v, gates of token t in [t mod (P+1)]: read at the end of body t-P-1, broadcast
+    //   in body t-1, used in body t;
+    //   plan records of token t in rec[t mod (2P+2)]: read at the end of body t-2P-1, broadcast
+    //   within lane groups in body t-P-1 and used there (slot ids) and in body t.
+    constexpr int S0 = -(2 * P + 1);
+    uint4 rec[ZR][RW];
+    uint4 sw[ZS][RW], sr[ZS][RW];
     VS vv[ZS];
-    float al[ZS], be[ZS];
+    f32x2_t gab[ZS];
 #pragma unroll
     for (int z = 0; z < ZR; ++z)
-        rec[z] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+            rec[z][r] = make_uint4(0, 0, 0, 0);
 
-    // End of body s: reads for token s+P+1 (slot chunks, v, gates) and the plan
-    // record of token s+2P+1.  With s = s0 + ZR*blk + j and s0 = -(2P+1):
-    // s mod ZS = (j+1) mod ZS, (s+P+1) mod ZR = (j+P+2) mod ZR, (s+2P+1) mod ZR = j.
-#define SDM_ISSUE(S_, J_)                                                                                           \
-    {                                                                                                              \
-        const int u_ = (S_) + P + 1;                                                                               \
-        const uint4 ru_ = rec[((J_) + P + 2) % ZR];                                                                \
-        const bool ok_ = tok_ok(u_);                                                                               \
-        const bool oka_ = ok_ && act;                                                                              \
-        constexpr int zs_ = ((J_) + 1) % ZS;                                                                       \
-        sw[zs_] = ld128(r_mem, oka_ ? (ru_.x & kSlotMask) * row_bytes + lane_off : kOOB);                          \
-        sr[zs_] = ld128(r_mem, oka_ ? (ru_.y & kSlotMask) * row_bytes + lane_off : kOOB);                          \
-        const uint32_t ro_ = (uint32_t)(u_ * H + h);                                                               \
-        vv[zs_].load(r_v, ok_ ? ro_ * (uint32_t)d * (uint32_t)sizeof(VT) + v_lane : kOOB);                          \
-        al[zs_] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_al, ok_ ? ro_ * 4u : kOOB, 0, 0));          \
-        be[zs_] = __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_be, ok_ ? ro_ * 4u : kOOB, 0, 0));          \
-        rec[(J_) % ZR] = ld128(r_plan, plan_off((S_) + 2 * P + 1));                                                 \
-    }
+    // End of body s = S0 + ZR*blk + J: reads for token s+P+1 and the plan records of token s+2P+1.
+    // s mod ZS = (J+1) mod ZS, (s+P+1) mod ZR = (J+P+2) mod ZR, (s+2P+1) mod ZR = J mod ZR.
+    auto issue = [&](int s, auto jc) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int zs = (J + 1) % ZS, zu = (J + P + 2) % ZR, zl = J % ZR;
+        const int u = s + P + 1;
+        const bool ok = tok_ok(u);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const uint4 ru = rec[zu][r];
+            const bool oka = ok && act[r];
+            sw[zs][r] = ld128(r_mem, oka ? (ru.x & kSlotMask) * row_bytes + lane_off : kOOB);
+            sr[zs][r] = ld128(r_mem, oka ? (ru.y & kSlotMask) * row_bytes + lane_off : kOOB);
+        }
+        const uint32_t ro = (uint32_t)(u * H + h);
+        vv[zs].load(r_v, (ok && v_lead) ? ro * (uint32_t)d * (uint32_t)sizeof(VT) + v_lane : kOOB);
+        gab[zs] = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  r_ab, (ok && lane == 0) ? (uint32_t)u * 8u : kOOB, 0, 0));
+        const int un = s + 2 * P + 1;
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+            rec[zl][r] = ld128(r_plan, (tok_ok(un) && act[r] && rec_lead) ? (uint32_t)(un * W + pos[r]) * 16u : kOOB);
+    };
+    // After the wait in body s: the records of token s+P+1 and v, gates of token s+1 have
+    // arrived in their leader lanes; hand them to every lane.
+    auto broadcast = [&](auto jc) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int zu = (J + P + 2) % ZR, z1 = (J + 2) % ZS;
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+            rec[zu][r] = swz4<REC_SWZ>(rec[zu][r]);
+#pragma unroll
+        for (int q = 0; q < VS::WORDS; ++q)
+            vv[z1].w[q] = swz<V_SWZ>(vv[z1].w[q]);
+        gab[z1] = (f32x2_t){__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gab[z1][0]))),
+                            __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gab[z1][1])))};
+    };
 
-    // Bodies run from the virtual token s0 = -(2P+1), so the first real records
-    // and slot chunks arrive through the same uniform pattern as every later one;
-    // virtual tokens (s < 0 or s >= T) read zeros and store nothing.  Body T
-    // stores the output of token T-1.
-    constexpr int S0 = -(2 * P + 1);
+    // Bodies run from the virtual token S0, so the first real records and slot
+    // chunks arrive through the same uniform pattern as every later one; virtual
+    // tokens (s < 0 or s >= T) read zeros and store nothing.  Body T stores the
+    // output of token T-1.
     const int blocks = (T + 1 - S0 + ZR - 1) / ZR;
     for (int blk = 0; blk < blocks; ++blk) {
         static_for<ZR>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j = decltype(jc)::value;
+            constexpr int sp = (j + 1) % ZS, zr = (j + 1) % ZR;
             const int s = S0 + blk * ZR + j;
             const bool real = tok_ok(s);
-            const uint4 rs = rec[(j + 1) % ZR];
-            const int sp = (j + 1) % ZS;
 
-            // ---- write: decay this lane's slot, its share of the prediction
-            float x[VEC];
-            {
-                uint4 raw = sw[sp];
+            // ---- write: decay this lane's slots, their share of the prediction
+            CT x[RW][VEC];
+            CT acc[VEC];
+#pragma unroll
+            for (int q = 0; q < VEC; ++q)
+                acc[q] = 0;
+            const CT alpha = (CT)gab[sp][0];
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const uint4 rs = rec[zr][r];
+                uint4 raw = sw[sp][r];
                 const uint32_t fpos = (rs.x >> 20) & 0x7FFu;
                 if (fpos && fpos <= (uint32_t)(R * W))
                     raw = ring[(fpos - 1) * LPS + el];
-                F::unpack(raw, x);
-                const float w = __uint_as_float(rs.z), alpha = al[sp];
-                float acc[VEC];
+                float m[VEC];
+                F::unpack(raw, m);
+                const CT w = (CT)__uint_as_float(rs.z);
 #pragma unroll
                 for (int q = 0; q < VEC; ++q) {
-                    x[q] = alpha * x[q];
-                    acc[q] = group_sum<LPS>(w * x[q]);
+                    x[r][q] = alpha * (CT)m[q];
+                    acc[q] += w * x[r][q];
                 }
+            }
+            if constexpr (FAST) {
+                const float t = reduce4_to_rows(acc[0], acc[1], acc[2], acc[3]);
+                if ((lane & 8) == 0)
+                    red[(wave * LPS + el) * VEC + (lane >> 4)] = t;
+            } else {
+#pragma unroll
+                for (int q = 0; q < VEC; ++q)
+                    acc[q] = wave_sum<LPS>(acc[q]);
                 if (g == 0) {
 #pragma unroll
                     for (int q = 0; q < VEC; ++q)
@@ -392,75 +570,156 @@ __global__ __launch_bounds__(kScanMaxThreads) void sdm_scan_kernel(ScanArgs a)
                 }
             }
             lds_barrier();
-            // ---- the previous token's read is complete in `ored`: every wave sums it, wave 0 stores
-            {
+            // ---- the previous token's read sits in `ored`: wave 0 sums and stores it
+            if constexpr (FAST) {
+                // waves 0..3 read into groups g mod 4; a DPP stage and two transposing
+                // permlane16 swaps leave (o0, o1) in row 0 and (o2, o3) in row 1
+                float o01 = 0.f;
+                if (wave == 0) {
+                    const float4 pv = *reinterpret_cast<const float4*>(ored + ((g & 3) * LPS + el) * VEC);
+                    const float o0 = bfly<8>(pv.x), o1 = bfly<8>(pv.y), o2 = bfly<8>(pv.z), o3 = bfly<8>(pv.w);
+                    const auto s02 = __builtin_amdgcn_permlane16_swap(__float_as_uint(o0), __float_as_uint(o2), false, false);
+                    const auto s13 = __builtin_amdgcn_permlane16_swap(__float_as_uint(o1), __float_as_uint(o3), false, false);
+                    const float t02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+                    const float t13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+                    o01 = t02;
+                    const float o_b = t13;
+                    const int row = lane >> 4;
+                    const bool st_ = (lane & 8) == 0 && row < 2 && tok_ok(s - 1);
+                    const uint32_t oo = st_ ? ((uint32_t)((s - 1) * H + h) * (uint32_t)d + (uint32_t)(chunk * DC + el * VEC + 2 * row)) * 4u : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2_t, (f32x2_t){o01, o_b}), r_out, oo, 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2_t, (f32x2_t){o01, o01}), r_out, kOOB, 0, 0);
+                }
+            } else {
                 float o[VEC];
 #pragma unroll
                 for (int q = 0; q < VEC; ++q)
-                    o[q] = group_sum<LPS>(g < nwv ? ored[(g * LPS + el) * VEC + q] : 0.f);
-                const bool st_ = wave == 0 && g == 0 && tok_ok(s - 1);
-                const uint32_t oo = st_ ? (uint32_t)((s - 1) * H + h) * (uint32_t)d * 4u + o_lane : kOOB;
+                    o[q] = 0.f;
+                if (wave == 0) {
+                    const int pg = g & (p2 - 1);
 #pragma unroll
-                for (int q = 0; q < O_OPS; ++q)
-                    st128(r_out, oo == kOOB ? kOOB : oo + 16u * q,
-                          make_uint4(__float_as_uint(o[4 * q]), __float_as_uint(o[4 * q + 1]),
-                                     __float_as_uint(o[4 * q + 2]), __float_as_uint(o[4 * q + 3])));
-            }
-            // ---- delta-rule write of this lane's slot
-            {
-                const float w = __uint_as_float(rs.z), beta = be[sp];
-                float y[VEC];
-#pragma unroll
-                for (int q = 0; q < VEC; ++q) {
-                    const float vh = group_sum<LPS>(g < nwv ? red[(g * LPS + el) * VEC + q] : 0.f);
-                    y[q] = x[q] + w * (beta * (vv[sp].get(q) - vh));
+                    for (int q = 0; q < VEC; ++q)
+                        o[q] = waves_sum<LPS>(pg < nwv ? ored[(pg * LPS + el) * VEC + q] : 0.f, p2);
                 }
-                const uint4 packed = F::pack(y);
-                if (act)
-                    ring[(((s + 2 * R) % R) * W + pos) * LPS + el] = packed;
-                const bool st_ = real && act && !(rs.x >> 31);
-                st128(r_mem, st_ ? (rs.x & kSlotMask) * row_bytes + lane_off : kOOB, packed);
+                const bool st_ = wave == 0 && g < VEC / 4 && tok_ok(s - 1);
+                const uint32_t oo = st_ ? ((uint32_t)((s - 1) * H + h) * (uint32_t)d + (uint32_t)(chunk * DC + el * VEC)) * 4u + 16u * (uint32_t)(g & 1) : kOOB;
+                uint4 ov;
+                if constexpr (VEC == 8) {
+                    ov = (g & 1) ? make_uint4(__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7]))
+                                 : make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
+                } else {
+                    ov = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3]));
+                }
+                st128(r_out, oo, ov);
+            }
+            // ---- delta-rule write of this lane's slots
+            {
+                CT vh[VEC];
+                if constexpr (FAST) {
+                    const float4 pv = *reinterpret_cast<const float4*>(red + ((g & 3) * LPS + el) * VEC);
+                    vh[0] = bfly<16>(bfly<8>(pv.x));
+                    vh[1] = bfly<16>(bfly<8>(pv.y));
+                    vh[2] = bfly<16>(bfly<8>(pv.z));
+                    vh[3] = bfly<16>(bfly<8>(pv.w));
+                } else {
+                    const int pg = g & (p2 - 1);
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q)
+                        vh[q] = waves_sum<LPS>(pg < nwv ? red[(pg * LPS + el) * VEC + q] : (CT)0, p2);
+                }
+                const CT beta = (CT)gab[sp][1];
+                CT dlt[VEC];
+#pragma unroll
+                for (int q = 0; q < VEC; ++q)
+                    dlt[q] = beta * ((CT)vv[sp].get(q) - vh[q]);
+                const int ring_tok = ((s + 2 * R) % R) * W;
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    const uint4 rs = rec[zr][r];
+                    const CT w = (CT)__uint_as_float(rs.z);
+                    CT y[VEC];
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q)
+                        y[q] = x[r][q] + w * dlt[q];
+                    const uint4 packed = F::pack(y);
+                    if (act[r])
+                        ring[(ring_tok + pos[r]) * LPS + el] = packed;
+                    const bool st_ = real && act[r] && !(rs.x >> 31);
+                    st128(r_mem, st_ ? (rs.x & kSlotMask) * row_bytes + lane_off : kOOB, packed);
+                }
             }
             // the reads for token s+1 were issued at the end of body s-P: retire them
             // and everything issued before them, in every wave
             wait_vmcnt<K>();
             lds_barrier();
-            // ---- read: this lane's read slot, after this token's write
+            broadcast(jc);
+            // ---- read: this lane's read slots, after this token's write
             {
-                uint4 raw = sr[sp];
-                const uint32_t rpos = rs.y >> 20;
-                if (rpos && rpos <= (uint32_t)(R * W))
-                    raw = ring[(rpos - 1) * LPS + el];
-                float y[VEC];
-                F::unpack(raw, y);
-                const float r = __uint_as_float(rs.w);
+                float oa[VEC];
 #pragma unroll
                 for (int q = 0; q < VEC; ++q)
-                    y[q] = group_sum<LPS>(r * y[q]);
-                if (g == 0) {
+                    oa[q] = 0.f;
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    const uint4 rs = rec[zr][r];
+                    uint4 raw = sr[sp][r];
+                    const uint32_t rpos = rs.y >> 20;
+                    if (rpos && rpos <= (uint32_t)(R * W))
+                        raw = ring[(rpos - 1) * LPS + el];
+                    float m[VEC];
+                    F::unpack(raw, m);
+                    const float rw = __uint_as_float(rs.w);
 #pragma unroll
                     for (int q = 0; q < VEC; ++q)
-                        ored[(wave * LPS + el) * VEC + q] = y[q];
+                        oa[q] += rw * m[q];
+                }
+                if constexpr (FAST) {
+                    const float t = reduce4_to_rows(oa[0], oa[1], oa[2], oa[3]);
+                    if ((lane & 8) == 0)
+                        ored[(wave * LPS + el) * VEC + (lane >> 4)] = t;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < VEC; ++q)
+                        oa[q] = wave_sum<LPS>(oa[q]);
+                    if (g == 0) {
+#pragma unroll
+                        for (int q = 0; q < VEC; ++q)
+                            ored[(wave * LPS + el) * VEC + q] = oa[q];
+                    }
                 }
             }
-            SDM_ISSUE(s, j);
+            issue(s, jc);
         });
     }
-#undef SDM_ISSUE
+}
+
+template <class ST, class VT, int RW, bool FAST>
+hipError_t launch_rw(const ScanArgs& a, const ScanPlan& p, hipStream_t stream)
+{
+    dim3 grid((unsigned)p.grid), block((unsigned)(p.waves * 64));
+    if constexpr (FAST) {
+        hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 8, 2, true>), grid, block, p.lds, stream, a);
+        return hipGetLastError();
+    }
+    switch (p.lps) {
+    case 1: hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 1, RW, false>), grid, block, p.lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 2, RW, false>), grid, block, p.lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 4, RW, false>), grid, block, p.lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 8, RW, false>), grid, block, p.lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 template <class ST, class VT>
 hipError_t launch_typed(const ScanArgs& a, const ScanPlan& p, hipStream_t stream)
 {
-    dim3 grid((unsigned)p.grid), block((unsigned)(p.waves * 64));
-    switch (p.lps) {
-    case 1: hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 1>), grid, block, p.lds, stream, a); break;
-    case 2: hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 2>), grid, block, p.lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 4>), grid, block, p.lds, stream, a); break;
-    case 8: hipLaunchKernelGGL((sdm_scan_kernel<ST, VT, 8>), grid, block, p.lds, stream, a); break;
-    default: return hipErrorInvalidValue;
+    if constexpr (sizeof(ST) == 4) {
+        if (p.lps == 8 && p.rw == 2 && p.waves == 4)
+            return launch_rw<ST, VT, 2, true>(a, p, stream);
     }
-    return hipGetLastError();
+    return p.rw == 2 ? launch_rw<ST, VT, 2, false>(a, p, stream) : launch_rw<ST, VT, 1, false>(a, p, stream);
 }
 
 } // namespace
@@ -468,6 +727,7 @@ hipError_t launch_typed(const ScanArgs& a, const ScanPlan& p, hipStream_t stream
 bool plan_scan(int B, int H, int d, int W, bool state_bf16, ScanPlan* plan)
 {
     const int vec = state_bf16 ? 8 : 4;
+    const int ct = state_bf16 ? 8 : 4; // bytes of the write path's arithmetic type
     const long units = (long)B * H;
     int lps = 8;
     // largest chunk that divides d, shrunk while the grid would leave CUs idle
@@ -476,27 +736,30 @@ bool plan_scan(int B, int H, int d, int W, bool state_bf16, ScanPlan* plan)
     if (d % (lps * vec) != 0)
         return false;
     const int gpw = 64 / lps;
-    const int waves = (W + gpw - 1) / gpw;
-    if (waves * 64 > kScanMaxThreads || waves > gpw || kRing * W > 2047)
+    const int rw = W > gpw ? 2 : 1; // slot positions per lane
+    const int waves = (W + gpw * rw - 1) / (gpw * rw);
+    if (waves * 64 > (rw == 2 ? 256 : 64) || waves > gpw || kRing * W > 2047)
         return false;
     plan->lps = lps;
+    plan->rw = rw;
     plan->waves = waves;
     plan->lookahead = kLookahead;
     plan->grid = (int)(units * (d / (lps * vec)));
-    plan->lds = kRing * W * lps * 16 + 2 * waves * lps * vec * 4;
+    plan->lds = kRing * W * lps * 16 + waves * lps * vec * (ct + 4);
     return plan->lds <= 160 * 1024;
 }
 
-size_t plan_bytes(int B, int H, int T, int W) { return (size_t)B * H * T * W * sizeof(uint4); }
+size_t plan_bytes(int B, int H, int T, int W) { return (size_t)B * H * T * (W * sizeof(uint4) + sizeof(float2)); }
 
 hipError_t launch_sdm_plan(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
-                           uint4* plan, int B, int T, int H, int W, hipStream_t stream)
+                           const float* alpha, const float* beta, uint4* plan, float2* ab, int B, int T, int H, int W,
+                           hipStream_t stream)
 {
     const int tiles = (T + kPlanTokens - 1) / kPlanTokens;
     const int span = kPlanTokens + 3 * kLookahead;
     const size_t lds = (size_t)span * 64 * 2 * sizeof(int32_t);
     hipLaunchKernelGGL(sdm_plan_kernel, dim3((unsigned)(tiles * B * H)), dim3(kPlanThreads), lds, stream, idx_w, wt_w,
-                       idx_r, wt_r, plan, T, H, W);
+                       idx_r, wt_r, alpha, beta, plan, ab, T, H, W);
     return hipGetLastError();
 }
 
