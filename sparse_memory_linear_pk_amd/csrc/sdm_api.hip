@@ -41,14 +41,14 @@ struct Layout {
     size_t scores, idx, wt, plan, total;
 };
 
-Layout layout_of(const sdm_config& c)
+Layout layout_of(const sdm_config& c, const sdm::ScanPlan& plan)
 {
     const size_t rows = (size_t)c.B * c.T * c.H;
     Layout L;
     L.scores = align_up(rows * 2 * (size_t)c.n_sub * sizeof(float));
     L.idx = align_up(rows * (size_t)c.W * sizeof(int32_t));
     L.wt = align_up(rows * (size_t)c.W * sizeof(float));
-    L.plan = align_up(sdm::plan_bytes(c.B, c.H, c.T, c.W));
+    L.plan = align_up(sdm::plan_bytes(plan, c.B, c.H, c.T, c.W));
     L.total = L.scores + 2 * (L.idx + L.wt) + L.plan;
     return L;
 }
@@ -88,7 +88,8 @@ sdm_status check_config(const sdm_config* c, sdm::ScanPlan* plan)
         return fail(SDM_ERR_UNSUPPORTED, "one memory is %zu bytes; at most 2^32 - 1", mem_bytes);
     if ((long)c->B * c->T * c->H > (1l << 31) / 64)
         return fail(SDM_ERR_UNSUPPORTED, "B*T*H=%ld rows is too many", (long)c->B * c->T * c->H);
-    if (!sdm::plan_scan(c->B, c->H, c->d, c->W, c->state_dtype == SDM_BF16, plan))
+    if (!sdm::plan_scan(c->B, c->H, c->T, c->d, c->W, (long)c->n_sub * c->n_sub, c->state_dtype == SDM_BF16,
+                         c->in_dtype == SDM_BF16, plan))
         return fail(SDM_ERR_UNSUPPORTED, "no scan layout for d=%d W=%d", c->d, c->W);
     return SDM_OK;
 }
@@ -110,7 +111,6 @@ struct sdm_ctx {
     int32_t* idx[2];
     float* wt[2];
     uint4* plan_buf;
-    float2* ab_buf;
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
@@ -172,14 +172,15 @@ sdm_status run_scan(sdm_ctx* h, const int32_t* idx_w, const float* wt_w, const i
     const sdm_config& c = h->cfg;
     {
         Timer t(h, K_PLAN);
-        hipError_t e = sdm::launch_sdm_plan(idx_w, wt_w, idx_r, wt_r, alpha, beta, h->plan_buf, h->ab_buf, c.B, c.T,
-                                            c.H, c.W, h->stream);
+        hipError_t e = sdm::launch_sdm_plan(h->plan, idx_w, wt_w, idx_r, wt_r, alpha, beta, h->plan_buf, c.B, c.T, c.H,
+                                            c.W, c.d, (long)c.n_sub * c.n_sub, c.in_dtype == SDM_BF16, h->stream);
         if (e != hipSuccess)
             return hip_fail(e, "sdm_plan launch");
     }
     sdm::ScanArgs a;
     a.plan = h->plan_buf;
-    a.ab = h->ab_buf;
+    a.ab = h->plan.staged ? nullptr
+                          : reinterpret_cast<const float2*>(h->plan_buf + (size_t)c.B * c.H * c.T * c.W);
     a.v = v;
     a.mem = mem;
     a.out = out;
@@ -188,6 +189,7 @@ sdm_status run_scan(sdm_ctx* h, const int32_t* idx_w, const float* wt_w, const i
     a.H = c.H;
     a.d = c.d;
     a.W = c.W;
+    a.Tp = h->plan.Tp;
     a.N = (long)c.n_sub * c.n_sub;
     Timer t(h, K_SCAN);
     hipError_t e = sdm::launch_sdm_scan(a, h->plan, c.state_dtype == SDM_BF16, c.in_dtype == SDM_BF16, h->stream);
@@ -220,7 +222,7 @@ sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes)
         return s;
     if (!bytes)
         return fail(SDM_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = layout_of(*cfg).total;
+    *bytes = layout_of(*cfg, plan).total;
     return SDM_OK;
 }
 
@@ -245,14 +247,14 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->stream = (hipStream_t)hip_stream;
     h->device = dev;
     h->plan = plan;
-    h->L = layout_of(*cfg);
+    h->L = layout_of(*cfg, plan);
     h->timing = false;
     memset(&h->totals, 0, sizeof h->totals);
     e = hipMalloc(&h->block, h->L.total);
     if (e != hipSuccess) {
         delete h;
         (void)hipGetLastError();
-        return fail(SDM_ERR_OOM, "workspace of %zu bytes: %s", layout_of(*cfg).total, hipGetErrorString(e));
+        return fail(SDM_ERR_OOM, "workspace of %zu bytes: %s", h->L.total, hipGetErrorString(e));
     }
     char* p = (char*)h->block;
     h->scores = (float*)p;
@@ -264,7 +266,6 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
         p += h->L.wt;
     }
     h->plan_buf = (uint4*)p;
-    h->ab_buf = (float2*)(p + (size_t)cfg->B * cfg->H * cfg->T * cfg->W * sizeof(uint4));
     h->magic = kMagic;
     *out = h;
     return SDM_OK;

@@ -57,37 +57,64 @@ hipError_t launch_pk_score(const void* q, const void* subkeys, float* scores, lo
 hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, long rows, int S, int k, int W,
                           hipStream_t stream);
 
-// The scan's plan: one 16-byte record per (b, h, t, position) packing the write
-// and read slot ids, their weights, where in the scan's LDS ring a slot written
-// too recently to be read from memory is found, and whether a store is superseded.
-// Also writes (alpha, beta) of every token next to each other for the scan.
-size_t plan_bytes(int B, int H, int T, int W); // records followed by the (alpha, beta) pairs
-hipError_t launch_sdm_plan(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
-                           const float* alpha, const float* beta, uint4* plan, float2* ab, int B, int T, int H, int W,
-                           hipStream_t stream);
+// Staged scan (float32 state): constants shared by its plan and its kernel.
+// The kernel steps through tokens in pairs; the slot reads of a pair are issued
+// two pairs ahead, its plan records four pairs ahead.
+namespace staged {
+constexpr int kP = 3;               // a store may be in flight with those of the next kP tokens
+constexpr int kWindow = 7;          // tokens back a forwarded value may come from
+constexpr int kRing = 12;           // tokens of stored values kept for forwarding (> kWindow)
+constexpr int kStages = 6;          // tokens of slot reads in flight or in use (three pairs)
+constexpr int kRecSlots = 12;       // tokens of plan records parked in LDS
+constexpr int kS0 = -8;             // first (virtual) token: the first pair whose records are loaded holds token 0
+constexpr int kPos = 64;            // positions per token (the selection width, padded)
+constexpr int kRecs = kPos + 1;     // plan entries per token: one record per position, then the header
+constexpr int kSlotBits = 21;       // slot id field; the next 10 bits hold a forwarding source
+constexpr uint32_t kDepFlag = 1u;   // header bit (out offset bit 0): the token writes a slot the previous one wrote
+static_assert(kRing == kRecSlots && kRecSlots % kStages == 0 && kRecSlots % 4 == 0 && kS0 % 2 == 0,
+              "slot rings must line up in the unrolled loop");
+static_assert(kRing > kWindow, "forwarding window");
+static_assert(kRing * kPos + 1 <= 1024, "forwarding source field");
+} // namespace staged
 
-struct ScanArgs {
-    const uint4* plan;  // [B*H, T, W] records
-    const float2* ab;   // [B*H, T] (alpha, beta)
-    const void* v;
-    void* mem;
-    float* out;
-    int B, T, H, d, W;
-    long N;
-};
-
-// Scan launch geometry chosen for a shape.
+// Launch geometry of the scan, chosen once per shape.
 struct ScanPlan {
-    int lps;       // lanes sharing one slot (16 bytes each)
+    bool staged;   // staged kernel (float32 state) or the register-ring kernel
+    int lps;       // lanes sharing one slot chunk (16 bytes each)
     int rw;        // slot positions per lane
     int waves;     // waves per workgroup
     int lookahead; // tokens between a slot read's issue and its use
     int grid;      // workgroups
     int lds;       // dynamic LDS bytes
+    int Tp;        // staged: tokens per memory in the plan (T padded with sentinel tokens)
 };
 
-bool plan_scan(int B, int H, int d, int W, bool state_bf16, ScanPlan* plan);
+bool plan_scan(int B, int H, int T, int d, int W, long N, bool state_bf16, bool in_bf16, ScanPlan* plan);
+
+// The plan of a forward: per (b, h, t, position) a 16-byte record with the write
+// and read slot ids, their weights, where a slot written too recently to be read
+// from memory is found instead, and whether its store is superseded; plus the
+// token's gates.  Register-ring format: [B*H][T][W] records, then [B*H][T]
+// (alpha, beta).  Staged format: [B*H][Tp][65]: 64 records (positions past W and
+// tokens past T are sentinels that read nothing and store nothing), then a
+// header (alpha, beta, byte offset of the token's v row, of its out row).
+size_t plan_bytes(const ScanPlan& p, int B, int H, int T, int W);
+hipError_t launch_sdm_plan(const ScanPlan& p, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                           const float* wt_r, const float* alpha, const float* beta, void* plan, int B, int T,
+                           int H, int W, int d, long N, bool in_bf16, hipStream_t stream);
+
+struct ScanArgs {
+    const uint4* plan;  // records (either format)
+    const float2* ab;   // register-ring format: [B*H, T] (alpha, beta)
+    const void* v;
+    void* mem;
+    float* out;
+    int B, T, H, d, W, Tp;
+    long N;
+};
+
 hipError_t launch_sdm_scan(const ScanArgs& a, const ScanPlan& plan, bool state_bf16, bool in_bf16,
                            hipStream_t stream);
+hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& plan, bool in_bf16, hipStream_t stream);
 
 } // namespace sdm

@@ -31,30 +31,13 @@
 // kernel below works out which reads need it and where from.  Two stores of one
 // slot at most P tokens apart may both be in flight, so only the later one is
 // issued; every reader between them is inside the forwarding window.
-#include "sdm_internal.h"
-
-#include <utility>
+#include "scan_device.h"
 
 namespace sdm {
 namespace {
 
-// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), each index a constant expression
-template <class F, int... Js>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, Js...>)
-{
-    (f(std::integral_constant<int, Js>{}), ...);
-}
-template <int N, class F> __device__ __forceinline__ void static_for(F&& f)
-{
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
 constexpr int kLookahead = 6;               // P
 constexpr int kRing = 2 * kLookahead + 1;   // R
-constexpr uint32_t kOOB = 0xFFFFFFF0u;      // a buffer offset past every buffer's end
 
 // Plan record for (b, h, t, position i), 16 bytes:
 //   x: write slot (20 bits) | (1 + ring position of its latest unsettled write) << 20 (11 bits)
@@ -80,43 +63,63 @@ __device__ __forceinline__ int lower_bound64(const int32_t* s, int n)
     return lo;
 }
 
+struct PlanArgs {
+    const int32_t* idx_w;
+    const float* wt_w;
+    const int32_t* idx_r;
+    const float* wt_r;
+    const float* alpha;
+    const float* beta;
+    uint4* plan;
+    float2* ab;        // register-ring format only
+    int T, H, W, d, Tp;
+    uint32_t N;        // slots per memory (the staged sentinel slot id)
+    uint32_t v_bytes;  // bytes of one value element (staged header offsets)
+};
+
 // For every token t and position i: the write slot's latest write by a token in
-// [t - 2P, t) and the read slot's latest write in [t - 2P, t], as ring positions
-// ((t' mod R) * W + i'), and whether a token in (t, t + P] writes the same slot.
-// Write sets are sorted by slot once per token so each lookup is a binary search.
-__global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(const int32_t* __restrict__ idx_w,
-                                                              const float* __restrict__ wt_w,
-                                                              const int32_t* __restrict__ idx_r,
-                                                              const float* __restrict__ wt_r,
-                                                              const float* __restrict__ alpha,
-                                                              const float* __restrict__ beta,
-                                                              uint4* __restrict__ plan, float2* __restrict__ ab,
-                                                              int T, int H, int W)
+// [t - 2P, t) and the read slot's latest write in [t - 2P, t], as (1 + ring
+// position) with ring position (ring slot of t') * stride + i', and whether a
+// token in (t, t + P] writes the same slot.  Write sets are sorted by slot once
+// per token so each lookup is a binary search.
+//   register-ring format: ring slot t' mod (2P+1), stride W, fields 20 + 11/12 bits;
+//   staged format: window kWindow, ring slot (t' - S0) mod 8, stride 64, fields 21 + 10 bits; a
+//   forwarded read names the sentinel slot (nothing to load), bit 31 of y marks a
+//   forwarded write slot (load nothing, still store); sentinel records for
+//   positions >= W and tokens >= T, then a header per token (bit 0 of its out
+//   offset: the token writes a slot the previous token wrote).
+template <int P, int WIN, bool STAGED>
+__global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
 {
-    constexpr int P = kLookahead;
     extern __shared__ int32_t s_plan[]; // [span][64] sorted slots, then [span][64] their positions
-    const int tiles = (T + kPlanTokens - 1) / kPlanTokens;
+    const int T = a.T, H = a.H, W = a.W;
+    const int Tout = STAGED ? a.Tp : T; // tokens written per memory
+    const int tiles = (Tout + kPlanTokens - 1) / kPlanTokens;
     const int bh = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     const int b = bh / H, h = bh % H;
-    const int t0 = tile * kPlanTokens, t1 = min(T, t0 + kPlanTokens);
-    const int lo = max(0, t0 - 2 * P), hi = min(T, t1 + P);
-    const int span = hi - lo;
+    const int t0 = tile * kPlanTokens, t1 = min(Tout, t0 + kPlanTokens);
+    const int lo = max(0, min(T, t0) - WIN), hi = min(T, t1 + P);
+    const int span = max(0, hi - lo);
     int32_t* s_slot = s_plan;
     int32_t* s_pos = s_plan + span * 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    constexpr int kSlotShift = STAGED ? staged::kSlotBits : 20;
+    constexpr uint32_t kSlotField = (1u << kSlotShift) - 1u;
+    const int stride = STAGED ? staged::kPos : W;
+    auto ring_slot = [](int tp) { return STAGED ? (tp - staged::kS0) % staged::kRing : tp % (2 * P + 1); };
 
     // each wave sorts whole write sets by slot (bitonic network across the wave)
     for (int tt = wave; tt < span; tt += nw) {
         const int t = lo + tt;
         int key = 0x7FFFFFFF, pos = lane;
         if (lane < W)
-            key = idx_w[((long)(b * T + t) * H + h) * W + lane];
+            key = a.idx_w[((long)(b * T + t) * H + h) * W + lane];
 #pragma unroll
         for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                const int ok = __shfl_xor(key, stride), op = __shfl_xor(pos, stride);
-                const bool up = (lane & size) == 0, lower = (lane & stride) == 0;
+            for (int stride_ = size >> 1; stride_ > 0; stride_ >>= 1) {
+                const int ok = __shfl_xor(key, stride_), op = __shfl_xor(pos, stride_);
+                const bool up = (lane & size) == 0, lower = (lane & stride_) == 0;
                 const bool take_other = (up == lower) ? (ok < key) : (ok > key);
                 if (take_other) {
                     key = ok;
@@ -129,49 +132,75 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(const int32_t* _
     }
     __syncthreads();
 
-    for (int t = t0 + (int)threadIdx.x; t < t1; t += blockDim.x) {
-        const long o = (long)(b * T + t) * H + h;
-        ab[(long)bh * T + t] = make_float2(alpha[o], beta[o]);
+    if constexpr (!STAGED) {
+        for (int t = t0 + (int)threadIdx.x; t < t1; t += blockDim.x) {
+            const long o = (long)(b * T + t) * H + h;
+            a.ab[(long)bh * T + t] = make_float2(a.alpha[o], a.beta[o]);
+        }
     }
-    const int items = (t1 - t0) * W;
+    const int per_tok = STAGED ? staged::kRecs : W;
+    const int items = (t1 - t0) * per_tok;
     for (int it = threadIdx.x; it < items; it += blockDim.x) {
-        const int t = t0 + it / W, i = it % W;
-        const long o = ((long)(b * T + t) * H + h) * W + i;
-        const int n = idx_w[o], m = idx_r[o];
-        uint32_t fw = 0, fr = 0, skip = 0;
-        for (int tp = t; tp >= max(0, t - 2 * P) && (fw == 0 || fr == 0); --tp) {
-            const int32_t* ss = s_slot + (tp - lo) * 64;
-            if (fw == 0 && tp < t) {
-                const int k = lower_bound64(ss, n);
-                if (k < 64 && ss[k] == n)
-                    fw = (uint32_t)((tp % kRing) * W + s_pos[(tp - lo) * 64 + k]) + 1u;
-            }
-            if (fr == 0) {
-                const int k = lower_bound64(ss, m);
-                if (k < 64 && ss[k] == m)
-                    fr = (uint32_t)((tp % kRing) * W + s_pos[(tp - lo) * 64 + k]) + 1u;
-            }
-        }
-        for (int tq = t + 1; tq <= min(T - 1, t + P) && !skip; ++tq) {
-            const int32_t* ss = s_slot + (tq - lo) * 64;
-            const int k = lower_bound64(ss, n);
-            skip = k < 64 && ss[k] == n;
-        }
+        const int t = t0 + it / per_tok, i = it % per_tok;
         uint4 rec;
-        rec.x = ((uint32_t)n & kSlotMask) | (fw << 20) | (skip << 31);
-        rec.y = ((uint32_t)m & kSlotMask) | (fr << 20);
-        rec.z = __float_as_uint(wt_w[o]);
-        rec.w = __float_as_uint(wt_r[o]);
-        plan[((long)bh * T + t) * W + i] = rec;
+        if (STAGED && i == staged::kPos) { // header
+            const long o = (long)(b * T + t) * H + h;
+            const uint32_t row = (uint32_t)(t * H + h) * (uint32_t)a.d;
+            const bool real = t < T;
+            rec.x = real ? __float_as_uint(a.alpha[o]) : 0u;
+            rec.y = real ? __float_as_uint(a.beta[o]) : 0u;
+            rec.z = (real ? row : (uint32_t)T * H * a.d) * a.v_bytes;
+            rec.w = (real ? row : (uint32_t)T * H * a.d) * 4u;
+            // does the token write a slot the previous token wrote?
+            bool dep = false;
+            if (real && t > 0) {
+                const int32_t* prev = s_slot + (t - 1 - lo) * 64;
+                for (int q = 0; q < W && !dep; ++q) {
+                    const int n = a.idx_w[((long)(b * T + t) * H + h) * W + q];
+                    const int k = lower_bound64(prev, n);
+                    dep = k < 64 && prev[k] == n;
+                }
+            }
+            rec.w |= dep ? staged::kDepFlag : 0u;
+        } else if (STAGED && (t >= T || i >= W)) { // sentinel: slot past the memory, no store, weight 0
+            rec = make_uint4(a.N | (1u << 31), a.N, 0u, 0u);
+        } else {
+            const long o = ((long)(b * T + t) * H + h) * W + i;
+            const int n = a.idx_w[o], m = a.idx_r[o];
+            uint32_t fw = 0, fr = 0, skip = 0;
+            for (int tp = t; tp >= max(0, t - WIN) && (fw == 0 || fr == 0); --tp) {
+                const int32_t* ss = s_slot + (tp - lo) * 64;
+                if (fw == 0 && tp < t) {
+                    const int k = lower_bound64(ss, n);
+                    if (k < 64 && ss[k] == n)
+                        fw = (uint32_t)(ring_slot(tp) * stride + s_pos[(tp - lo) * 64 + k]) + 1u;
+                }
+                if (fr == 0) {
+                    const int k = lower_bound64(ss, m);
+                    if (k < 64 && ss[k] == m)
+                        fr = (uint32_t)(ring_slot(tp) * stride + s_pos[(tp - lo) * 64 + k]) + 1u;
+                }
+            }
+            for (int tq = t + 1; tq <= min(T - 1, t + P) && !skip; ++tq) {
+                const int32_t* ss = s_slot + (tq - lo) * 64;
+                const int k = lower_bound64(ss, n);
+                skip = k < 64 && ss[k] == n;
+            }
+            rec.x = ((uint32_t)n & kSlotField) | (fw << kSlotShift) | (skip << 31);
+            if constexpr (STAGED)
+                rec.y = (fr ? a.N : (uint32_t)m) | (fr << kSlotShift) | ((uint32_t)(fw != 0) << 31);
+            else
+                rec.y = ((uint32_t)m & kSlotField) | (fr << kSlotShift);
+            rec.z = __float_as_uint(a.wt_w[o]);
+            rec.w = __float_as_uint(a.wt_r[o]);
+        }
+        a.plan[((long)bh * Tout + t) * per_tok + i] = rec;
     }
 }
 
 // ---------------------------------------------------------------------------
 // the scan
 // ---------------------------------------------------------------------------
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 bits of the double x rounded once to nearest-even.  x rounds to float
 // first; that can only go wrong when the float lands exactly on a bf16 tie while
@@ -234,15 +263,6 @@ template <> struct StateFmt<uint16_t> { // bfloat16 bits
     }
 };
 
-__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ void st128(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), r, off, 0, 0);
-}
-
 // VEC consecutive values of v (bf16 or float) as raw words, read with V_OPS loads
 template <class VT, int VEC> struct VSlice {
     static constexpr int WORDS = VEC * (int)sizeof(VT) / 4;
@@ -270,71 +290,6 @@ template <class VT, int VEC> struct VSlice {
             return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
     }
 };
-
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding)
-template <int N> __device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// x + (x of lane ^ D), identical in both lanes of every pair (an exactly
-// commutative add): DPP row_ror:8 for D = 8, the gfx950 permlane swaps for 16
-// and 32, ds_bpermute below 8.
-template <int D> __device__ __forceinline__ uint32_t partner32(uint32_t u)
-{
-    static_assert(D == 8, "DPP partner only for D = 8");
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x128, 0xF, 0xF, false);
-}
-template <int D> __device__ __forceinline__ float bfly(float x)
-{
-    if constexpr (D < 8) {
-        return x + __shfl_xor(x, D);
-    } else if constexpr (D == 8) {
-        return x + __uint_as_float(partner32<8>(__float_as_uint(x)));
-    } else if constexpr (D == 16) {
-        const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-    } else {
-        static_assert(D == 32, "butterfly distance");
-        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-    }
-}
-template <int D> __device__ __forceinline__ double bfly(double x)
-{
-    if constexpr (D < 8) {
-        return x + __shfl_xor(x, D);
-    } else {
-        const uint64_t b = (uint64_t)__double_as_longlong(x);
-        const uint32_t lo = (uint32_t)b, hi = (uint32_t)(b >> 32);
-        if constexpr (D == 8) {
-            const uint64_t p = ((uint64_t)partner32<8>(hi) << 32) | partner32<8>(lo);
-            return x + __longlong_as_double((long long)p);
-        } else {
-            uint32_t a_lo, b_lo, a_hi, b_hi;
-            if constexpr (D == 16) {
-                const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-                const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-                a_lo = sl[0]; b_lo = sl[1]; a_hi = sh[0]; b_hi = sh[1];
-            } else {
-                static_assert(D == 32, "butterfly distance");
-                const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-                const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-                a_lo = sl[0]; b_lo = sl[1]; a_hi = sh[0]; b_hi = sh[1];
-            }
-            return __longlong_as_double((long long)(((uint64_t)a_hi << 32) | a_lo)) +
-                   __longlong_as_double((long long)(((uint64_t)b_hi << 32) | b_lo));
-        }
-    }
-}
 
 // Sum over all 64/LPS lane groups of a wave (lanes sharing lane % LPS).
 template <int LPS, class T> __device__ __forceinline__ T wave_sum(T x)
@@ -381,24 +336,6 @@ template <int AND> __device__ __forceinline__ uint32_t swz(uint32_t v)
 template <int AND> __device__ __forceinline__ uint4 swz4(const uint4& v)
 {
     return make_uint4(swz<AND>(v.x), swz<AND>(v.y), swz<AND>(v.z), swz<AND>(v.w));
-}
-
-// Four per-lane values, each summed over the 8 lane groups of a wave (LPS = 8):
-// one DPP stage, then two transposing permlane16 swaps and one permlane32 swap,
-// so that row r (lanes 16r..16r+15) ends with the total of value r.  Every value
-// goes through the same tree ((g0+g1)+(g2+g3))+((g4+g5)+(g6+g7)).
-__device__ __forceinline__ float reduce4_to_rows(float v0, float v1, float v2, float v3)
-{
-    v0 = bfly<8>(v0);
-    v1 = bfly<8>(v1);
-    v2 = bfly<8>(v2);
-    v3 = bfly<8>(v3);
-    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
-    const auto s23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
-    const float t01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]); // rows 0,2: v0; rows 1,3: v1
-    const float t23 = __uint_as_float(s23[0]) + __uint_as_float(s23[1]); // rows 0,2: v2; rows 1,3: v3
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(t01), __float_as_uint(t23), false, false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 // At most 4 waves per workgroup (1 when a wave holds every position with one
@@ -724,11 +661,28 @@ hipError_t launch_typed(const ScanArgs& a, const ScanPlan& p, hipStream_t stream
 
 } // namespace
 
-bool plan_scan(int B, int H, int d, int W, bool state_bf16, ScanPlan* plan)
+bool plan_scan(int B, int H, int T, int d, int W, long N, bool state_bf16, bool in_bf16, ScanPlan* plan)
 {
+    const long units = (long)B * H;
+    const uint64_t v_bytes = in_bf16 ? 2 : 4;
+    if (!state_bf16 && d % 32 == 0 && W <= staged::kPos && N < (1l << staged::kSlotBits) &&
+        (uint64_t)(N + 1) * d * 4 <= (1ull << 32) && ((uint64_t)T * H + 1) * d * 4 <= (1ull << 32) &&
+        ((uint64_t)T * H + 1) * d * v_bytes <= (1ull << 32)) {
+        plan->staged = true;
+        plan->lps = 8;
+        plan->rw = 2;
+        plan->waves = 4;
+        plan->lookahead = staged::kP;
+        plan->grid = (int)(units * (d / 32));
+        plan->lds = 0;
+        // pairs run from S0 to the pair after the one holding T-1; each loads the
+        // records of the pair four ahead
+        const int blocks = (T + 2 - staged::kS0 + staged::kRecSlots - 1) / staged::kRecSlots;
+        plan->Tp = staged::kS0 + blocks * staged::kRecSlots + 8;
+        return true;
+    }
     const int vec = state_bf16 ? 8 : 4;
     const int ct = state_bf16 ? 8 : 4; // bytes of the write path's arithmetic type
-    const long units = (long)B * H;
     int lps = 8;
     // largest chunk that divides d, shrunk while the grid would leave CUs idle
     while (lps > 1 && (d % (lps * vec) != 0 || (lps > 2 && units * (d / (lps * vec)) < 256)))
@@ -740,32 +694,61 @@ bool plan_scan(int B, int H, int d, int W, bool state_bf16, ScanPlan* plan)
     const int waves = (W + gpw * rw - 1) / (gpw * rw);
     if (waves * 64 > (rw == 2 ? 256 : 64) || waves > gpw || kRing * W > 2047)
         return false;
+    plan->staged = false;
     plan->lps = lps;
     plan->rw = rw;
     plan->waves = waves;
     plan->lookahead = kLookahead;
     plan->grid = (int)(units * (d / (lps * vec)));
     plan->lds = kRing * W * lps * 16 + waves * lps * vec * (ct + 4);
+    plan->Tp = T;
     return plan->lds <= 160 * 1024;
 }
 
-size_t plan_bytes(int B, int H, int T, int W) { return (size_t)B * H * T * (W * sizeof(uint4) + sizeof(float2)); }
-
-hipError_t launch_sdm_plan(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
-                           const float* alpha, const float* beta, uint4* plan, float2* ab, int B, int T, int H, int W,
-                           hipStream_t stream)
+size_t plan_bytes(const ScanPlan& p, int B, int H, int T, int W)
 {
-    const int tiles = (T + kPlanTokens - 1) / kPlanTokens;
-    const int span = kPlanTokens + 3 * kLookahead;
-    const size_t lds = (size_t)span * 64 * 2 * sizeof(int32_t);
-    hipLaunchKernelGGL(sdm_plan_kernel, dim3((unsigned)(tiles * B * H)), dim3(kPlanThreads), lds, stream, idx_w, wt_w,
-                       idx_r, wt_r, alpha, beta, plan, ab, T, H, W);
+    if (p.staged)
+        return (size_t)B * H * p.Tp * staged::kRecs * sizeof(uint4);
+    return (size_t)B * H * T * (W * sizeof(uint4) + sizeof(float2));
+}
+
+hipError_t launch_sdm_plan(const ScanPlan& p, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                           const float* wt_r, const float* alpha, const float* beta, void* plan, int B, int T,
+                           int H, int W, int d, long N, bool in_bf16, hipStream_t stream)
+{
+    PlanArgs a;
+    a.idx_w = idx_w;
+    a.wt_w = wt_w;
+    a.idx_r = idx_r;
+    a.wt_r = wt_r;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.plan = static_cast<uint4*>(plan);
+    a.ab = p.staged ? nullptr : reinterpret_cast<float2*>(a.plan + (size_t)B * H * T * W);
+    a.T = T;
+    a.H = H;
+    a.W = W;
+    a.d = d;
+    a.Tp = p.Tp;
+    a.N = (uint32_t)N;
+    a.v_bytes = in_bf16 ? 2u : 4u;
+    const int P = p.staged ? staged::kP : kLookahead, WIN = p.staged ? staged::kWindow : 2 * kLookahead;
+    const int tiles = ((p.staged ? p.Tp : T) + kPlanTokens - 1) / kPlanTokens;
+    const size_t lds = (size_t)(kPlanTokens + WIN + P) * 64 * 2 * sizeof(int32_t);
+    if (p.staged)
+        hipLaunchKernelGGL((sdm_plan_kernel<staged::kP, staged::kWindow, true>), dim3((unsigned)(tiles * B * H)),
+                           dim3(kPlanThreads), lds, stream, a);
+    else
+        hipLaunchKernelGGL((sdm_plan_kernel<kLookahead, 2 * kLookahead, false>), dim3((unsigned)(tiles * B * H)),
+                           dim3(kPlanThreads), lds, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_sdm_scan(const ScanArgs& a, const ScanPlan& plan, bool state_bf16, bool in_bf16,
                            hipStream_t stream)
 {
+    if (plan.staged)
+        return launch_sdm_scan_staged(a, plan, in_bf16, stream);
     if (state_bf16)
         return in_bf16 ? launch_typed<uint16_t, uint16_t>(a, plan, stream) : launch_typed<uint16_t, float>(a, plan, stream);
     return in_bf16 ? launch_typed<float, uint16_t>(a, plan, stream) : launch_typed<float, float>(a, plan, stream);

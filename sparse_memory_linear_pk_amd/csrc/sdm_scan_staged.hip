@@ -1,0 +1,352 @@
+// sdm_scan, staged form: the memory scan of the SDM layer for a float32 state.
+//
+// Per token t of memory (b, h), with write slots n_i, weights w_i, decay alpha,
+// step beta, value v and read slots m_j, weights r_j (SDM blog post, section
+// "How does SDM work?" and the caption of the figure "The SDM mechanism, end
+// to end"):
+//   x_i = alpha * M[n_i];  vhat = sum_i w_i x_i;  M[n_i] = x_i + w_i * beta * (v - vhat)
+//   out = sum_j r_j * M[m_j]                     (after the write of the same token)
+//
+// Work split.  A workgroup of 4 waves owns one (b, h) and 32 consecutive slot
+// elements (128 bytes of every slot row) and walks all T tokens.  A token's 64
+// positions (the W selected slots, padded with sentinels) spread over the waves,
+// 16 each: lane (g, e) of wave w holds elements 4e..4e+3 of positions
+// 16w + g and 16w + 8 + g.  Sums over positions are a transposing reduction
+// inside the wave and one LDS exchange across the waves.
+//
+// Pipeline.  Tokens go in pairs.  At the start of pair k: the read of pair k-1
+// (after its write), then the loads of pair k+2 (its slot rows and v into
+// registers; the plan records of pair k+4 into registers, parked in LDS two pairs
+// later, where the 8 lanes sharing a position read them as a broadcast), then the
+// write of pair k: both tokens' partial sums, one barrier, both updates.  When
+// token 2k+1 writes a slot token 2k writes (a plan flag), its write is redone
+// after token 2k's has landed in the ring.  Two pairs of slot reads stay in
+// flight per wave, enough to cover the memory latency at full bandwidth.
+//
+// Forwarding.  A slot written too recently for its load to see the store comes
+// from a ring of the values stored by the last 8 tokens, which the plan names;
+// such a slot is not loaded (its load reads past the buffer, zeros) and an
+// unforwarded slot names the ring's zero entry, so every read is the sum of a
+// register and one LDS load, without a branch.
+//
+// Ordering.  Every wave issues the same vector-memory operations in the same
+// order for every pair (sentinel records and headers of the virtual tokens
+// before 0 and after T-1 give offsets past their buffers, which read zeros and
+// drop writes), so counted waits (s_waitcnt vmcnt) retire exactly the intended
+// operations: loads and stores retire in issue order.  A barrier after a wait
+// makes every wave's retired stores visible to the loads issued after it.  Two
+// stores of one slot that may be in flight together are never both issued: the
+// plan drops the earlier.
+#include "scan_device.h"
+
+namespace sdm {
+namespace {
+
+using namespace staged;
+
+constexpr int kWaves = 4;
+constexpr int kRecPerWave = 17;                  // 16 records and the header
+constexpr int kEntryU4 = 8;                      // one slot chunk: 8 lanes x 16 bytes
+
+__shared__ __attribute__((aligned(16))) uint4 g_ring[(kRing * kPos + 1) * kEntryU4]; // zero entry, stored chunks
+__shared__ __attribute__((aligned(16))) uint4 g_rec[kRecSlots * kWaves * kRecPerWave + kWaves]; // records, headers; a spare entry per wave
+__shared__ __attribute__((aligned(16))) float4 g_red[2 * kWaves * 8];               // write partials of a pair
+__shared__ __attribute__((aligned(16))) float4 g_ored[2 * kWaves * 8];              // read partials of a pair
+static_assert(kStages == 6, "register rings of three pairs");
+
+// Ring chunk a record field names: entry f - 1 of the ring for f > 0, the zero
+// entry for f = 0 (then the staged chunk holds the value).
+__device__ __forceinline__ const uint4* ring_src(uint32_t field, const uint4* ring_lane)
+{
+    return ring_lane + ((field >> kSlotBits) & 0x3FFu) * kEntryU4;
+}
+
+// Workgroup barrier after this wave's own LDS loads and stores have completed.
+// The loads into the stage buffers are not waited for here: those buffers are
+// private to each wave, and the per-token vmcnt wait retires them.  (A release
+// fence would wait for them.)  The memory clobber keeps the compiler from moving
+// memory accesses across.
+__device__ __forceinline__ void barrier_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Totals over the 4 waves of the per-wave partials of element lane el (the same
+// order in every lane).
+__device__ __forceinline__ float4 sum_waves(const float4* part, int el)
+{
+    const float4 a = part[el], b = part[8 + el], c = part[16 + el], d = part[24 + el];
+    return make_float4((a.x + b.x) + (c.x + d.x), (a.y + b.y) + (c.y + d.y), (a.z + b.z) + (c.z + d.z),
+                       (a.w + b.w) + (c.w + d.w));
+}
+
+__device__ __forceinline__ uint4 add4(const uint4& a, const uint4& b)
+{
+    return make_uint4(__float_as_uint(__uint_as_float(a.x) + __uint_as_float(b.x)),
+                      __float_as_uint(__uint_as_float(a.y) + __uint_as_float(b.y)),
+                      __float_as_uint(__uint_as_float(a.z) + __uint_as_float(b.z)),
+                      __float_as_uint(__uint_as_float(a.w) + __uint_as_float(b.w)));
+}
+
+template <class VT>
+__global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
+{
+    constexpr int ZS = kStages, ZR = kRecSlots, ZL = 4;
+    // Vector-memory operations of a pair, in issue order: 12 loads at its start
+    // (per token of pair k+2 4 slot loads and v; the records of pair k+4), then 2
+    // out stores and 4 slot stores.  vmcnt(18) at the start of pair k leaves only
+    // pair k-1's operations in flight: pair k's data and pair k+2's records have
+    // landed and pair k-2's stores are done.
+    constexpr int K = 18;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int g = lane >> 3, el = lane & 7;
+    const int T = a.T, H = a.H, d = a.d;
+    const uint32_t N = (uint32_t)a.N;
+    const int nchunk = d >> 5;
+    const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    const int b = bh / H;
+    const uint32_t row_bytes = (uint32_t)d * 4u;
+    const uint32_t lane_off = (uint32_t)(chunk * 32 + el * 4) * 4u;
+    const uint32_t tok_bytes = (uint32_t)T * H * d;
+
+    const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * row_bytes,
+                                                   N * row_bytes);
+    const __amdgpu_buffer_rsrc_t r_plan = make_rsrc(a.plan + (size_t)bh * a.Tp * kRecs,
+                                                    (uint32_t)a.Tp * kRecs * 16u);
+    const size_t tok0 = (size_t)b * T * H;
+    const __amdgpu_buffer_rsrc_t r_v = make_rsrc(static_cast<const VT*>(a.v) + tok0 * d, tok_bytes * sizeof(VT));
+    const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + tok0 * d, tok_bytes * 4u);
+
+    // positions of this lane
+    const int pos0 = (wave * 2) * 8 + g, pos1 = pos0 + 8;
+    const uint4* ring_lane = g_ring + el;   // the zero entry
+    uint4* ring_w = g_ring + kEntryU4 + el; // entry 0 of the stored chunks
+    // record loads: lane i < 16 fetches record 16w + i of a token, lane 16 the header
+    const uint32_t rec_lane = lane < 16 ? (uint32_t)(16 * wave + lane) * 16u : (uint32_t)kPos * 16u;
+    const uint32_t v_lane = (uint32_t)(chunk * 32 + el * 4) * (uint32_t)sizeof(VT); // this lane's 4 values of v
+    // out: the 8 lanes of group 0 of wave 0 store 16 bytes each
+    const bool o_lane_ok = wave == 0 && g == 0;
+    const uint32_t o_lane = (uint32_t)(chunk * 32 + el * 4) * 4u;
+    // lanes >= 17 park their (unused) record load in the wave's spare entry; an
+    // index into the one array (not a choice of pointers) keeps the compiler
+    // certain that the store does not touch the stage buffers
+    const bool parks = lane < kRecPerWave;
+    const int spare = kRecSlots * kWaves * kRecPerWave + wave;
+
+    // Sentinels for the virtual tokens before 0: a slot past the memory, no
+    // store, weight 0, nothing forwarded; gates 0 and v, out offsets past their buffers.
+    const uint4 sent_rec = make_uint4(N | (1u << 31), N, 0u, 0u);
+    const uint4 sent_hdr = make_uint4(0u, 0u, tok_bytes * (uint32_t)sizeof(VT), tok_bytes * 4u);
+    const uint4 sent_lane = lane < 16 ? sent_rec : sent_hdr;
+    if (lane < kRecPerWave) {
+#pragma unroll
+        for (int z = 0; z < ZR; ++z)
+            g_rec[(z * kWaves + wave) * kRecPerWave + lane] = sent_lane;
+    }
+    const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+    if (wave == 0 && lane < kEntryU4)
+        g_ring[lane] = zero4;
+    __syncthreads();
+
+    // Per-token state on its way through the pipeline, token t in [(t - S0) mod 6]
+    // (records in [(t - S0) mod 4]):
+    uint4 rl[ZL];          // record loads (lanes < 17), issued four pairs ahead, parked two pairs later
+    uint4 vr[ZS];          // this lane's values of v (bf16: the first 8 bytes), issued two pairs ahead
+    uint4 wset[ZS][2];     // its write slots' chunks (zero when forwarded), issued two pairs ahead
+    uint4 rset[ZS][2];     // its read slots' chunks (zero when forwarded), issued two pairs ahead
+    uint32_t soff[ZS][2];  // store offsets of the write slots (past the memory: no store)
+#pragma unroll
+    for (int z = 0; z < ZL; ++z)
+        rl[z] = sent_lane;
+#pragma unroll
+    for (int z = 0; z < ZS; ++z) {
+        vr[z] = zero4;
+        wset[z][0] = wset[z][1] = rset[z][0] = rset[z][1] = zero4;
+        soff[z][0] = soff[z][1] = kOOB;
+    }
+
+    // this lane's records and the header of the token in record slot Z
+    auto records = [&](auto zc, uint4& r0, uint4& r1, uint4& hd) __attribute__((always_inline)) {
+        const uint4* rw = g_rec + (decltype(zc)::value * kWaves + wave) * kRecPerWave;
+        r0 = rw[g];
+        r1 = rw[8 + g];
+        hd = rw[16];
+    };
+
+    // Write, first half: decay this lane's two slots (x) and leave the wave's share
+    // of the prediction in red.
+    auto partials = [&](const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float (&x0)[4],
+                        float (&x1)[4], float4* red) __attribute__((always_inline)) {
+        const uint4 m0 = add4(ws[0], *ring_src(r0.x, ring_lane));
+        const uint4 m1 = add4(ws[1], *ring_src(r1.x, ring_lane));
+        const float w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z);
+        x0[0] = alpha * __uint_as_float(m0.x); x0[1] = alpha * __uint_as_float(m0.y);
+        x0[2] = alpha * __uint_as_float(m0.z); x0[3] = alpha * __uint_as_float(m0.w);
+        x1[0] = alpha * __uint_as_float(m1.x); x1[1] = alpha * __uint_as_float(m1.y);
+        x1[2] = alpha * __uint_as_float(m1.z); x1[3] = alpha * __uint_as_float(m1.w);
+        float acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            acc[q] = w0 * x0[q] + w1 * x1[q];
+        // row r ends with the wave's total of value r; lanes l and l ^ 8 hold the same one
+        const float t = reduce4_to_rows(acc[0], acc[1], acc[2], acc[3]);
+        reinterpret_cast<float*>(red)[(wave * 8 + el) * 4 + (lane >> 4)] = t;
+    };
+
+    // Write, second half (after the barrier that publishes red): the delta-rule
+    // update of this lane's slots, into the ring entry of the token in ring slot J.
+    auto update = [&](auto jc, const uint4& r0, const uint4& r1, float beta, const uint4& vraw, const float (&x0)[4],
+                      const float (&x1)[4], const float4* red, uint4& p0, uint4& p1) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        const float4 pv = sum_waves(red, el);
+        // pin the use of v here: unpacking it earlier (the compiler would, at the
+        // top of the loop) waits for a load still in flight
+        uint4 u = vraw;
+        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+        float vv[4];
+        if constexpr (sizeof(VT) == 2) {
+            vv[0] = bf16_lo(u.x); vv[1] = bf16_hi(u.x);
+            vv[2] = bf16_lo(u.y); vv[3] = bf16_hi(u.y);
+        } else {
+            vv[0] = __uint_as_float(u.x); vv[1] = __uint_as_float(u.y);
+            vv[2] = __uint_as_float(u.z); vv[3] = __uint_as_float(u.w);
+        }
+        const float vh[4] = {pv.x, pv.y, pv.z, pv.w};
+        const float w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z);
+        float y0[4], y1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float dlt = beta * (vv[q] - vh[q]);
+            y0[q] = x0[q] + w0 * dlt;
+            y1[q] = x1[q] + w1 * dlt;
+        }
+        p0 = make_uint4(__float_as_uint(y0[0]), __float_as_uint(y0[1]), __float_as_uint(y0[2]), __float_as_uint(y0[3]));
+        p1 = make_uint4(__float_as_uint(y1[0]), __float_as_uint(y1[1]), __float_as_uint(y1[2]), __float_as_uint(y1[3]));
+        ring_w[J * kPos * kEntryU4 + pos0 * kEntryU4] = p0;
+        ring_w[J * kPos * kEntryU4 + pos1 * kEntryU4] = p1;
+    };
+
+    // Read: this lane's read slots of the token in record slot Z (after its write),
+    // the wave's share of out left in ored.
+    auto read_phase = [&](auto zc, const uint4 (&rs)[2], float4* ored) __attribute__((always_inline)) {
+        uint4 r0, r1, hd;
+        records(zc, r0, r1, hd);
+        const uint4 q0 = add4(rs[0], *ring_src(r0.y, ring_lane));
+        const uint4 q1 = add4(rs[1], *ring_src(r1.y, ring_lane));
+        const float rw0 = __uint_as_float(r0.w), rw1 = __uint_as_float(r1.w);
+        float oa[4];
+        oa[0] = rw0 * __uint_as_float(q0.x) + rw1 * __uint_as_float(q1.x);
+        oa[1] = rw0 * __uint_as_float(q0.y) + rw1 * __uint_as_float(q1.y);
+        oa[2] = rw0 * __uint_as_float(q0.z) + rw1 * __uint_as_float(q1.z);
+        oa[3] = rw0 * __uint_as_float(q0.w) + rw1 * __uint_as_float(q1.w);
+        const float t = reduce4_to_rows(oa[0], oa[1], oa[2], oa[3]);
+        reinterpret_cast<float*>(ored)[(wave * 8 + el) * 4 + (lane >> 4)] = t;
+    };
+
+    // Issue for token u (record slot Z, register slot S): its slot rows and v, and
+    // the records of token u + 4 into rl[(u - S0) mod 4].
+    auto issue = [&](auto zc, auto sc, int u) __attribute__((always_inline)) {
+        constexpr int S = decltype(sc)::value;
+        uint4 u0, u1, hu;
+        records(zc, u0, u1, hu);
+        const uint32_t ow0 = __umul24(u0.x & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
+        const uint32_t ow1 = __umul24(u1.x & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
+        const uint32_t or0 = __umul24(u0.y & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
+        const uint32_t or1 = __umul24(u1.y & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
+        // a forwarded write slot is not loaded (top bit of y); a forwarded read slot is the sentinel
+        wset[S][0] = ld128(r_mem, (u0.y >> 31) ? kOOB : ow0);
+        wset[S][1] = ld128(r_mem, (u1.y >> 31) ? kOOB : ow1);
+        rset[S][0] = ld128(r_mem, or0);
+        rset[S][1] = ld128(r_mem, or1);
+        soff[S][0] = (u0.x >> 31) ? kOOB : ow0;
+        soff[S][1] = (u1.x >> 31) ? kOOB : ow1;
+        if constexpr (sizeof(VT) == 2) {
+            const i32x2_t w2 = __builtin_amdgcn_raw_buffer_load_b64(r_v, hu.z + v_lane, 0, 0);
+            vr[S] = make_uint4((uint32_t)w2[0], (uint32_t)w2[1], 0u, 0u);
+        } else {
+            vr[S] = ld128(r_v, hu.z + v_lane);
+        }
+        const uint32_t ro = (uint32_t)(u + 4) * (uint32_t)(kRecs * 16) + rec_lane;
+        rl[decltype(zc)::value % ZL] = ld128(r_plan, lane < kRecPerWave ? ro : kOOB);
+    };
+
+    // out of the token in record slot Z from the partials in ored (wave 0 stores)
+    auto store_out = [&](auto zc, const float4* ored) __attribute__((always_inline)) {
+        const uint4 hd = g_rec[(decltype(zc)::value * kWaves + wave) * kRecPerWave + 16];
+        const float4 o = sum_waves(ored, el);
+        st128(r_out, o_lane_ok ? (hd.w & ~kDepFlag) + o_lane : kOOB,
+              make_uint4(__float_as_uint(o.x), __float_as_uint(o.y), __float_as_uint(o.z), __float_as_uint(o.w)));
+    };
+
+    // Pair (s, s+1), s = S0 + ZR*blk + j0: record and ring slots j0, j0+1, register
+    // slots j0 mod 6, j0+1 mod 6.
+    const int blocks = (T + 2 - kS0 + ZR - 1) / ZR;
+    for (int blk = 0; blk < blocks; ++blk) {
+        static_for<ZR / 2>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j0 = 2 * decltype(jc)::value, j1 = j0 + 1;
+            constexpr int n0 = (j0 + 4) % ZR, n1 = (j0 + 5) % ZR;   // pair k+2
+            constexpr int p0 = (j0 + ZR - 2) % ZR, p1 = (j0 + ZR - 1) % ZR; // pair k-1
+            const int s = kS0 + blk * ZR + j0;
+
+            // this pair's slot rows and v and pair k+2's records have landed; every
+            // store of pair k-2 is done and, after the barrier, visible to every wave,
+            // as are pair k-1's ring entries
+            wait_vmcnt<K>();
+            barrier_lds();
+            g_rec[parks ? (n0 * kWaves + wave) * kRecPerWave + lane : spare] = rl[n0 % ZL];
+            g_rec[parks ? (n1 * kWaves + wave) * kRecPerWave + lane : spare] = rl[n1 % ZL];
+
+            // ---- read of pair k-1 (its register slots are then free)
+            read_phase(std::integral_constant<int, p0>{}, rset[p0 % ZS], g_ored);
+            read_phase(std::integral_constant<int, p1>{}, rset[p1 % ZS], g_ored + 32);
+
+            // ---- issue pair k+2 into those register slots
+            issue(std::integral_constant<int, n0>{}, std::integral_constant<int, n0 % ZS>{}, s + 4);
+            issue(std::integral_constant<int, n1>{}, std::integral_constant<int, n1 % ZS>{}, s + 5);
+
+            // ---- write of this pair
+            uint4 a0, a1, ha, b0, b1, hb;
+            records(std::integral_constant<int, j0>{}, a0, a1, ha);
+            records(std::integral_constant<int, j1>{}, b0, b1, hb);
+            float xa0[4], xa1[4], xb0[4], xb1[4];
+            uint4 ya0, ya1, yb0, yb1;
+            partials(wset[j0 % ZS], a0, a1, __uint_as_float(ha.x), xa0, xa1, g_red);
+            partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), xb0, xb1, g_red + 32);
+            barrier_lds();
+            store_out(std::integral_constant<int, p0>{}, g_ored);
+            store_out(std::integral_constant<int, p1>{}, g_ored + 32);
+            update(std::integral_constant<int, j0>{}, a0, a1, __uint_as_float(ha.y), vr[j0 % ZS], xa0, xa1, g_red, ya0, ya1);
+            update(std::integral_constant<int, j1>{}, b0, b1, __uint_as_float(hb.y), vr[j1 % ZS], xb0, xb1, g_red + 32, yb0, yb1);
+            if (__builtin_amdgcn_readfirstlane(hb.w) & kDepFlag) {
+                // token s+1 writes a slot token s writes: redo its write now that
+                // token s's values are in the ring
+                barrier_lds();
+                partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), xb0, xb1, g_red + 32);
+                barrier_lds();
+                update(std::integral_constant<int, j1>{}, b0, b1, __uint_as_float(hb.y), vr[j1 % ZS], xb0, xb1, g_red + 32, yb0, yb1);
+            }
+            st128(r_mem, soff[j0 % ZS][0], ya0);
+            st128(r_mem, soff[j0 % ZS][1], ya1);
+            st128(r_mem, soff[j1 % ZS][0], yb0);
+            st128(r_mem, soff[j1 % ZS][1], yb1);
+        });
+    }
+}
+
+} // namespace
+
+hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& p, bool in_bf16, hipStream_t stream)
+{
+    if (!p.staged || p.waves != kWaves || a.d % 32 != 0 || a.W > kPos)
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)p.grid), block(kWaves * 64);
+    if (in_bf16)
+        hipLaunchKernelGGL(sdm_scan_staged_kernel<uint16_t>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(sdm_scan_staged_kernel<float>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+} // namespace sdm
