@@ -84,7 +84,7 @@ def load_traffic(kernel_signature: str):
 def kernel_signature() -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in ("sdm_scan.hip", "sdm_internal.h"):
+    for f in ("sdm_scan.hip", "sdm_scan_staged.hip", "scan_device.h", "sdm_internal.h"):
         h.update(open(os.path.join(ROOT, "sparse_memory_linear_pk_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
