@@ -108,7 +108,7 @@ def main():
     import torch
 
     import sdm_inputs as gi
-    from sparse_memory_linear_pk_amd import SDM
+    from sparse_memory_linear_pk_amd import SDM, pattern_probe
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -155,6 +155,21 @@ def main():
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
 
+    # The ceiling of the scan's access pattern: the same random 128-byte segment
+    # reads and writes with no arithmetic (scrambles the memory, which is no
+    # longer needed).
+    s_bytes = 2 if cfg.state_bf16 else 4
+    pat = []
+    for i in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pattern_probe(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * s_bytes, cfg.T, cfg.W, seed=i)
+        e1.record()
+        torch.cuda.synchronize()
+        if i:
+            pat.append(e0.elapsed_time(e1))
+    pattern_ms = sum(pat) / len(pat)
+
     sec = t1 - t0
     tokens = cfg.B * cfg.T * args.steps
     scan_ms = tm["ms_scan"] / max(1, tm["n_scan"])
@@ -186,7 +201,12 @@ def main():
                    "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "sdm_scan", "bytes_per_launch": nbytes, "ms_per_launch": scan_ms},
+                     "kernel": "sdm_scan", "bytes_per_launch": nbytes, "ms_per_launch": scan_ms,
+                     "pattern_ceiling": {"achieved": nbytes / (pattern_ms * 1e-3) / 1e9, "unit": "GB/s",
+                                         "ms_per_launch": pattern_ms,
+                                         "frac": (nbytes / (scan_ms * 1e-3)) / (nbytes / (pattern_ms * 1e-3)),
+                                         "what": "sdm_pattern_probe: the scan's random 128-byte segment reads "
+                                                 "and writes (2:1) with no arithmetic; frac = scan / this"}},
         "kernels_ms_per_step": {"pk_score": 2 * score_ms, "pk_topk": 2 * sel_ms, "sdm_plan": plan_ms,
                                 "sdm_scan": scan_ms},
         "pk_score": {"tflops": score_tflops, "peak_tflops": peak_mfma, "frac": score_tflops / peak_mfma},

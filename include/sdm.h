@@ -138,6 +138,19 @@ SDM_API sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float
 SDM_API sdm_status sdm_set_timing(sdm_handle h, int enable);
 SDM_API sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t);
 
+/* Measurement, not part of the layer: the memory traffic of the scan with its
+ * arithmetic taken out.  For each of `memories` memories of `rows` rows of
+ * row_bytes bytes (device pointer mem, 16-byte aligned, row_bytes a multiple of
+ * 128, one memory below 4 GiB) and each of T tokens: W rows read as the write
+ * set, W rows read as the read set and the W write rows stored, each as one
+ * 128-byte segment per workgroup, on rows drawn by a hash of (seed, memory,
+ * token, set, position).  3*W*row_bytes*T*memories bytes move per call; the
+ * contents of mem are scrambled.  Asynchronous on hip_stream (a hipStream_t).
+ * The bandwidth it reaches is what random 128-byte reads and writes in the
+ * scan's 2:1 mix allow on the device, the ceiling of the scan's access pattern. */
+SDM_API sdm_status sdm_pattern_probe(void* mem, int memories, long rows, int row_bytes, int T, int W,
+                                     unsigned seed, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

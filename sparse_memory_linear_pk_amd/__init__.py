@@ -15,7 +15,7 @@ import ctypes as C
 
 from ._lib import (SDM_BF16, SDM_F32, Config, SDMError, Timing, check, declared_symbols, lib)
 
-__all__ = ["SDM", "SDMError", "declared_symbols", "lib"]
+__all__ = ["SDM", "SDMError", "declared_symbols", "lib", "pattern_probe"]
 
 
 def _ptr(t):
@@ -138,3 +138,14 @@ class SDM:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def pattern_probe(mem, memories: int, rows: int, row_bytes: int, T: int, W: int, seed: int = 0, stream=None):
+    """The scan's memory traffic with no arithmetic (sdm_pattern_probe): 3*W*row_bytes*T*memories
+    bytes of random 128-byte row segments, two reads per write.  Scrambles mem."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    check(lib().sdm_pattern_probe(_ptr(mem), memories, rows, row_bytes, T, W, seed, C.c_void_p(handle)),
+          "sdm_pattern_probe")

@@ -117,4 +117,9 @@ hipError_t launch_sdm_scan(const ScanArgs& a, const ScanPlan& plan, bool state_b
                            hipStream_t stream);
 hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& plan, bool in_bf16, hipStream_t stream);
 
+// Measurement only: the scan's traffic pattern without arithmetic on `memories`
+// memories of `rows` rows of row_bytes (a multiple of 128) bytes.
+hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, uint32_t seed,
+                              hipStream_t stream);
+
 } // namespace sdm

@@ -61,6 +61,14 @@ __device__ __forceinline__ const uint4* ring_src(uint32_t field, const uint4* ri
     return ring_lane + ((field >> kSlotBits) & 0x3FFu) * kEntryU4;
 }
 
+// Whether any lane of the wave takes one of its two slots from the ring (a
+// wave-uniform answer; most tokens forward nothing and skip the ring loads).
+__device__ __forceinline__ bool forwards(uint32_t f0, uint32_t f1)
+{
+    constexpr uint32_t kField = 0x3FFu << kSlotBits;
+    return __builtin_amdgcn_ballot_w64(((f0 | f1) & kField) != 0u) != 0u;
+}
+
 // Workgroup barrier after this wave's own LDS loads and stores have completed.
 // The loads into the stage buffers are not waited for here: those buffers are
 // private to each wave, and the per-token vmcnt wait retires them.  (A release
@@ -126,8 +134,7 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     // record loads: lane i < 16 fetches record 16w + i of a token, lane 16 the header
     const uint32_t rec_lane = lane < 16 ? (uint32_t)(16 * wave + lane) * 16u : (uint32_t)kPos * 16u;
     const uint32_t v_lane = (uint32_t)(chunk * 32 + el * 4) * (uint32_t)sizeof(VT); // this lane's 4 values of v
-    // out: the 8 lanes of group 0 of wave 0 store 16 bytes each
-    const bool o_lane_ok = wave == 0 && g == 0;
+    // out: the 8 lanes of group 0 of one wave store 16 bytes each
     const uint32_t o_lane = (uint32_t)(chunk * 32 + el * 4) * 4u;
     // lanes >= 17 park their (unused) record load in the wave's spare entry; an
     // index into the one array (not a choice of pointers) keeps the compiler
@@ -179,8 +186,11 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     // of the prediction in red.
     auto partials = [&](const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float (&x0)[4],
                         float (&x1)[4], float4* red) __attribute__((always_inline)) {
-        const uint4 m0 = add4(ws[0], *ring_src(r0.x, ring_lane));
-        const uint4 m1 = add4(ws[1], *ring_src(r1.x, ring_lane));
+        uint4 m0 = ws[0], m1 = ws[1];
+        if (forwards(r0.x, r1.x)) {
+            m0 = add4(m0, *ring_src(r0.x, ring_lane));
+            m1 = add4(m1, *ring_src(r1.x, ring_lane));
+        }
         const float w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z);
         x0[0] = alpha * __uint_as_float(m0.x); x0[1] = alpha * __uint_as_float(m0.y);
         x0[2] = alpha * __uint_as_float(m0.z); x0[3] = alpha * __uint_as_float(m0.w);
@@ -233,8 +243,11 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     auto read_phase = [&](auto zc, const uint4 (&rs)[2], float4* ored) __attribute__((always_inline)) {
         uint4 r0, r1, hd;
         records(zc, r0, r1, hd);
-        const uint4 q0 = add4(rs[0], *ring_src(r0.y, ring_lane));
-        const uint4 q1 = add4(rs[1], *ring_src(r1.y, ring_lane));
+        uint4 q0 = rs[0], q1 = rs[1];
+        if (forwards(r0.y, r1.y)) {
+            q0 = add4(q0, *ring_src(r0.y, ring_lane));
+            q1 = add4(q1, *ring_src(r1.y, ring_lane));
+        }
         const float rw0 = __uint_as_float(r0.w), rw1 = __uint_as_float(r1.w);
         float oa[4];
         oa[0] = rw0 * __uint_as_float(q0.x) + rw1 * __uint_as_float(q1.x);
@@ -272,11 +285,18 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         rl[decltype(zc)::value % ZL] = ld128(r_plan, lane < kRecPerWave ? ro : kOOB);
     };
 
-    // out of the token in record slot Z from the partials in ored (wave 0 stores)
-    auto store_out = [&](auto zc, const float4* ored) __attribute__((always_inline)) {
-        const uint4 hd = g_rec[(decltype(zc)::value * kWaves + wave) * kRecPerWave + 16];
-        const float4 o = sum_waves(ored, el);
-        st128(r_out, o_lane_ok ? (hd.w & ~kDepFlag) + o_lane : kOOB,
+    // out of the token in record slot Z from the partials in ored: wave `owner`
+    // sums and its group 0 stores; every wave still issues the store (past the
+    // buffer elsewhere), so all waves count the same memory operations
+    auto store_out = [&](auto zc, const float4* ored, int owner) __attribute__((always_inline)) {
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        uint32_t off = kOOB;
+        if (wave == owner) {
+            const uint4 hd = g_rec[(decltype(zc)::value * kWaves + wave) * kRecPerWave + 16];
+            o = sum_waves(ored, el);
+            off = g == 0 ? (hd.w & ~kDepFlag) + o_lane : kOOB;
+        }
+        st128(r_out, off,
               make_uint4(__float_as_uint(o.x), __float_as_uint(o.y), __float_as_uint(o.z), __float_as_uint(o.w)));
     };
 
@@ -315,8 +335,8 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
             partials(wset[j0 % ZS], a0, a1, __uint_as_float(ha.x), xa0, xa1, g_red);
             partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), xb0, xb1, g_red + 32);
             barrier_lds();
-            store_out(std::integral_constant<int, p0>{}, g_ored);
-            store_out(std::integral_constant<int, p1>{}, g_ored + 32);
+            store_out(std::integral_constant<int, p0>{}, g_ored, 0);
+            store_out(std::integral_constant<int, p1>{}, g_ored + 32, 1);
             update(std::integral_constant<int, j0>{}, a0, a1, __uint_as_float(ha.y), vr[j0 % ZS], xa0, xa1, g_red, ya0, ya1);
             update(std::integral_constant<int, j1>{}, b0, b1, __uint_as_float(hb.y), vr[j1 % ZS], xb0, xb1, g_red + 32, yb0, yb1);
             if (__builtin_amdgcn_readfirstlane(hb.w) & kDepFlag) {

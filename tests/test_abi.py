@@ -8,7 +8,8 @@ from sparse_memory_linear_pk_amd import _lib
 from sparse_memory_linear_pk_amd._lib import Config, Timing, SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED
 
 EXPECTED = ["sdm_create", "sdm_forward", "sdm_destroy", "sdm_status_str", "sdm_last_error", "sdm_workspace_bytes",
-            "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing"]
+            "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing",
+            "sdm_pattern_probe"]
 
 
 def _cfg(**kw):
@@ -83,3 +84,17 @@ def test_forged_handle_is_rejected():
     junk = (C.c_uint32 * 64)()
     assert L.sdm_forward(C.cast(junk, C.c_void_p), *([None] * 8)) == SDM_ERR_INVALID_ARG
     assert L.sdm_destroy(C.cast(junk, C.c_void_p)) == SDM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("mem,memories,rows,row_bytes,T,W", [
+    (None, 4, 230400, 8192, 8192, 64),       # no memory
+    (16, 4, 230400, 8192, 8192, 65),         # W past 64
+    (8, 4, 230400, 8192, 8192, 64),          # misaligned
+    (16, 4, 230400, 8000, 8192, 64),         # row not a multiple of 128 bytes
+    (16, 4, 640 * 640, 3840 * 4, 16, 64),    # one memory of 6.3 GB
+    (16, 0, 230400, 8192, 16, 64),           # no memories
+])
+def test_pattern_probe_rejects_bad_arguments_on_the_host(mem, memories, rows, row_bytes, T, W):
+    L = _lib.lib()
+    assert L.sdm_pattern_probe(mem, memories, rows, row_bytes, T, W, 0, None) == SDM_ERR_INVALID_ARG
+    assert L.sdm_last_error().startswith(b"sdm_pattern_probe")
