@@ -52,6 +52,9 @@ constexpr uint32_t kSlotMask = 0xFFFFFu;
 
 constexpr int kPlanTokens = 32;
 constexpr int kPlanThreads = 256;
+constexpr int kFilterWords = 4096; // a 2^17-bit hashed filter of the slots written near a tile
+
+__device__ __forceinline__ uint32_t filter_bit(int n) { return ((uint32_t)n * 2654435761u) >> 15; }
 
 __device__ __forceinline__ int lower_bound64(const int32_t* s, int n)
 {
@@ -91,7 +94,9 @@ struct PlanArgs {
 template <int P, int WIN, bool STAGED>
 __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
 {
-    extern __shared__ int32_t s_plan[]; // [span][64] sorted slots, then [span][64] their positions
+    constexpr int kSpanMax = kPlanTokens + WIN + P;
+    // [span][64] sorted slots, [span][64] their positions, the slot filter, the tile's dependence flags
+    extern __shared__ int32_t s_plan[];
     const int T = a.T, H = a.H, W = a.W;
     const int Tout = STAGED ? a.Tp : T; // tokens written per memory
     const int tiles = (Tout + kPlanTokens - 1) / kPlanTokens;
@@ -102,18 +107,33 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
     const int span = max(0, hi - lo);
     int32_t* s_slot = s_plan;
     int32_t* s_pos = s_plan + span * 64;
+    uint32_t* s_filter = reinterpret_cast<uint32_t*>(s_plan + 2 * kSpanMax * 64);
+    uint32_t* s_dep = s_filter + kFilterWords;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     constexpr int kSlotShift = STAGED ? staged::kSlotBits : 20;
     constexpr uint32_t kSlotField = (1u << kSlotShift) - 1u;
     const int stride = STAGED ? staged::kPos : W;
     auto ring_slot = [](int tp) { return STAGED ? (tp - staged::kS0) % staged::kRing : tp % (2 * P + 1); };
+    auto in_filter = [&](int n) {
+        const uint32_t f = filter_bit(n);
+        return (s_filter[f >> 5] >> (f & 31u)) & 1u;
+    };
+
+    for (int i = threadIdx.x; i < kFilterWords; i += blockDim.x)
+        s_filter[i] = 0u;
+    __syncthreads();
 
     // each wave sorts whole write sets by slot (bitonic network across the wave)
+    // and enters their slots in the filter
     for (int tt = wave; tt < span; tt += nw) {
         const int t = lo + tt;
         int key = 0x7FFFFFFF, pos = lane;
         if (lane < W)
             key = a.idx_w[((long)(b * T + t) * H + h) * W + lane];
+        if (lane < W) {
+            const uint32_t f = filter_bit(key);
+            atomicOr(&s_filter[f >> 5], 1u << (f & 31u));
+        }
 #pragma unroll
         for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
@@ -132,7 +152,22 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
     }
     __syncthreads();
 
-    if constexpr (!STAGED) {
+    if constexpr (STAGED) {
+        // does token t write a slot token t - 1 wrote?  one wave per token, one slot per lane
+        for (int t = t0 + wave; t < t1; t += nw) {
+            bool hit = false;
+            if (t < T && t > 0 && lane < W) {
+                const int n = s_slot[(t - lo) * 64 + lane];
+                const int32_t* prev = s_slot + (t - 1 - lo) * 64;
+                const int k = lower_bound64(prev, n);
+                hit = k < 64 && prev[k] == n;
+            }
+            const bool dep = __builtin_amdgcn_ballot_w64(hit) != 0u;
+            if (lane == 0)
+                s_dep[t - t0] = dep ? 1u : 0u;
+        }
+        __syncthreads();
+    } else {
         for (int t = t0 + (int)threadIdx.x; t < t1; t += blockDim.x) {
             const long o = (long)(b * T + t) * H + h;
             a.ab[(long)bh * T + t] = make_float2(a.alpha[o], a.beta[o]);
@@ -151,40 +186,35 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
             rec.y = real ? __float_as_uint(a.beta[o]) : 0u;
             rec.z = (real ? row : (uint32_t)T * H * a.d) * a.v_bytes;
             rec.w = (real ? row : (uint32_t)T * H * a.d) * 4u;
-            // does the token write a slot the previous token wrote?
-            bool dep = false;
-            if (real && t > 0) {
-                const int32_t* prev = s_slot + (t - 1 - lo) * 64;
-                for (int q = 0; q < W && !dep; ++q) {
-                    const int n = a.idx_w[((long)(b * T + t) * H + h) * W + q];
-                    const int k = lower_bound64(prev, n);
-                    dep = k < 64 && prev[k] == n;
-                }
-            }
-            rec.w |= dep ? staged::kDepFlag : 0u;
+            rec.w |= s_dep[t - t0] ? staged::kDepFlag : 0u;
         } else if (STAGED && (t >= T || i >= W)) { // sentinel: slot past the memory, no store, weight 0
             rec = make_uint4(a.N | (1u << 31), a.N, 0u, 0u);
         } else {
             const long o = ((long)(b * T + t) * H + h) * W + i;
             const int n = a.idx_w[o], m = a.idx_r[o];
             uint32_t fw = 0, fr = 0, skip = 0;
-            for (int tp = t; tp >= max(0, t - WIN) && (fw == 0 || fr == 0); --tp) {
-                const int32_t* ss = s_slot + (tp - lo) * 64;
-                if (fw == 0 && tp < t) {
+            // the filter holds every slot written in [lo, hi): a slot outside it
+            // was written by no token the searches below would find
+            if (in_filter(n)) {
+                for (int tp = t - 1; tp >= max(0, t - WIN) && fw == 0; --tp) {
+                    const int32_t* ss = s_slot + (tp - lo) * 64;
                     const int k = lower_bound64(ss, n);
                     if (k < 64 && ss[k] == n)
                         fw = (uint32_t)(ring_slot(tp) * stride + s_pos[(tp - lo) * 64 + k]) + 1u;
                 }
-                if (fr == 0) {
+                for (int tq = t + 1; tq <= min(T - 1, t + P) && !skip; ++tq) {
+                    const int32_t* ss = s_slot + (tq - lo) * 64;
+                    const int k = lower_bound64(ss, n);
+                    skip = k < 64 && ss[k] == n;
+                }
+            }
+            if (in_filter(m)) {
+                for (int tp = t; tp >= max(0, t - WIN) && fr == 0; --tp) {
+                    const int32_t* ss = s_slot + (tp - lo) * 64;
                     const int k = lower_bound64(ss, m);
                     if (k < 64 && ss[k] == m)
                         fr = (uint32_t)(ring_slot(tp) * stride + s_pos[(tp - lo) * 64 + k]) + 1u;
                 }
-            }
-            for (int tq = t + 1; tq <= min(T - 1, t + P) && !skip; ++tq) {
-                const int32_t* ss = s_slot + (tq - lo) * 64;
-                const int k = lower_bound64(ss, n);
-                skip = k < 64 && ss[k] == n;
             }
             rec.x = ((uint32_t)n & kSlotField) | (fw << kSlotShift) | (skip << 31);
             if constexpr (STAGED)
@@ -734,7 +764,7 @@ hipError_t launch_sdm_plan(const ScanPlan& p, const int32_t* idx_w, const float*
     a.v_bytes = in_bf16 ? 2u : 4u;
     const int P = p.staged ? staged::kP : kLookahead, WIN = p.staged ? staged::kWindow : 2 * kLookahead;
     const int tiles = ((p.staged ? p.Tp : T) + kPlanTokens - 1) / kPlanTokens;
-    const size_t lds = (size_t)(kPlanTokens + WIN + P) * 64 * 2 * sizeof(int32_t);
+    const size_t lds = ((size_t)(kPlanTokens + WIN + P) * 64 * 2 + kFilterWords + kPlanTokens) * sizeof(int32_t);
     if (p.staged)
         hipLaunchKernelGGL((sdm_plan_kernel<staged::kP, staged::kWindow, true>), dim3((unsigned)(tiles * B * H)),
                            dim3(kPlanThreads), lds, stream, a);
