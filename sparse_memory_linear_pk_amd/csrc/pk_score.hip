@@ -7,11 +7,12 @@
 // which runs here on MFMA: v_mfma_f32_32x32x16_bf16 for bf16 inputs and
 // v_mfma_f32_32x32x2_f32 for float32 inputs, accumulating in float32.
 //
-// A workgroup owns 32 rows of one head and one half; its four waves walk the
-// S sub-keys in 32-wide column tiles.  Each lane keeps its slice of the 32 x dh
-// query tile in registers for the whole walk; sub-key tiles are read straight
-// from global memory, where the tables (S*dh elements per half and head) stay
-// resident in L2 across workgroups.
+// bf16: the sub-key tables are first rearranged into MFMA operand order (one
+// contiguous kilobyte per operand load); a workgroup then owns several 32-row
+// query tiles of one head and half, kept in registers, and its four waves walk
+// the S sub-keys in 32-wide column tiles, each operand load serving every row
+// tile.  float32 (the small shapes): one 32-row tile per workgroup, sub-key
+// operands read straight from the table.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -26,58 +27,85 @@ constexpr int kWaves = 4;
 // of the reduction index inside a k-step cancels out): lane l supplies row or
 // column (l % 32) and the reduction slice (l / 32) of the k-step.  Result: lane
 // l holds column (l % 32) of rows 8*(v/4) + 4*(l/32) + (v%4), v = 0..15.
-template <int DH>
+
+// Sub-key tables rearranged once per call into MFMA operand order: for head h,
+// half, column tile ct and k-step kk, the 64 lanes' 16-byte operands are one
+// contiguous kilobyte ([h][half][ct][kk][lane]), so every operand load is
+// coalesced; sub-keys past S are zero.
+__global__ __launch_bounds__(256) void pk_subkey_frag(const uint16_t* __restrict__ subkeys, uint4* __restrict__ frag,
+                                                     int H, int S, int dh)
+{
+    const int ksteps = dh / 16, ctiles = (S + 31) / 32;
+    const long n = (long)H * 2 * ctiles * ksteps * 64;
+    for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
+        const int lane = (int)(e % 64);
+        long r = e / 64;
+        const int kk = (int)(r % ksteps);
+        r /= ksteps;
+        const int ct = (int)(r % ctiles);
+        r /= ctiles; // h * 2 + half
+        const int sk = ct * 32 + (lane & 31);
+        const int c0 = kk * 16 + (lane >> 5) * 8;
+        frag[e] = sk < S ? *reinterpret_cast<const uint4*>(subkeys + (r * S + sk) * (long)dh + c0)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// A workgroup owns RB tiles of 32 rows of one head and half; each wave keeps
+// the RB query tiles in registers and walks every fourth 32-wide sub-key tile,
+// loading its operands once and using them for all RB row tiles.
+template <int DH, int RB>
 __global__ __launch_bounds__(kWaves * 64) void pk_score_bf16(const uint16_t* __restrict__ q,
-                                                           const uint16_t* __restrict__ subkeys,
+                                                           const uint4* __restrict__ frag,
                                                            float* __restrict__ scores, long rows_per_head,
                                                            int H, int S)
 {
     constexpr int KSTEPS = DH / 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 31, kg = lane >> 5;
-    const long tiles = (rows_per_head + 31) / 32;
+    const long blocks = (rows_per_head + 32 * RB - 1) / (32 * RB);
     long bid = blockIdx.x;
     const int half = (int)(bid & 1);
     bid >>= 1;
-    const long rt = bid % tiles;
-    const int h = (int)(bid / tiles);
+    const long rb = bid % blocks;
+    const int h = (int)(bid / blocks);
     const int dk = 2 * DH;
 
-    const long rr = rt * 32 + i;
-    bf16x8_t a[KSTEPS];
-    if (rr < rows_per_head) {
+    bf16x8_t a[RB][KSTEPS];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+        const long rr = (rb * RB + t) * 32 + i;
         const uint16_t* qrow = q + (rr * H + h) * dk + half * DH + kg * 8;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
-            a[kk] = *reinterpret_cast<const bf16x8_t*>(qrow + kk * 16);
-    } else {
+            a[t][kk] = rr < rows_per_head ? *reinterpret_cast<const bf16x8_t*>(qrow + kk * 16) : bf16x8_t{};
+    }
+    const int ctiles = (S + 31) / 32;
+    const uint4* fb = frag + (long)(h * 2 + half) * ctiles * KSTEPS * 64 + lane;
+    // stores through a buffer based at the block's first row: a per-lane offset
+    // (sub-key column, row group) plus a uniform one per row; columns past S
+    // and rows past the end fall outside the buffer and are dropped
+    const long first = ((rb * RB * 32 * H + h) * 2 + half) * (long)S;
+    const long avail = (rows_per_head * H * 2 - ((rb * RB * 32 * H + h) * 2 + half)) * (long)S * 4;
+    const __amdgpu_buffer_rsrc_t out = make_rsrc(scores + first, (uint32_t)(avail < 0x7FFFFFF0L ? avail : 0x7FFFFFF0L));
+    const uint32_t row_bytes = (uint32_t)(H * 2 * S) * 4u;
+    for (int ct = wave; ct < ctiles; ct += kWaves) {
+        bf16x8_t b[KSTEPS];
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
-            a[kk] = bf16x8_t{};
-    }
-    const uint16_t* table = subkeys + ((long)h * 2 + half) * S * DH;
-    const int ctiles = (S + 31) / 32;
-    for (int ct = wave; ct < ctiles; ct += kWaves) {
+            b[kk] = __builtin_bit_cast(bf16x8_t, fb[(ct * KSTEPS + kk) * 64]);
         const int s = ct * 32 + i;
-        f32x16_t acc = {};
-        if (s < S) {
-            const uint16_t* krow = table + (long)s * DH + kg * 8;
+        const uint32_t lane_off = s < S ? (uint32_t)(4 * kg) * row_bytes + (uint32_t)s * 4u : 0x80000000u;
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(krow + kk * 16);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], b, acc, 0, 0, 0);
-            }
-        } else {
+        for (int t = 0; t < RB; ++t) {
+            f32x16_t acc = {};
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], bf16x8_t{}, acc, 0, 0, 0);
-        }
-        if (s < S) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][kk], b[kk], acc, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const long row = rt * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
-                if (row < rows_per_head)
-                    scores[((row * H + h) * 2 + half) * (long)S + s] = acc[v];
+                const uint32_t row_off = (uint32_t)(t * 32 + 8 * (v >> 2) + (v & 3)) * row_bytes;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v]), out, lane_off, row_off, 0);
             }
         }
     }
@@ -134,34 +162,42 @@ __global__ __launch_bounds__(kWaves * 64) void pk_score_f32(const float* __restr
 }
 
 template <int DH>
-hipError_t launch_dh(const void* q, const void* subkeys, float* scores, long rows_per_head, int H, int S,
+hipError_t launch_dh(const void* q, const void* subkeys, void* frag, float* scores, long rows_per_head, int H, int S,
                      bool in_bf16, hipStream_t stream)
 {
-    const long tiles = (rows_per_head + 31) / 32;
-    dim3 grid((unsigned)(tiles * H * 2)), block(kWaves * 64);
-    if (in_bf16)
-        hipLaunchKernelGGL(pk_score_bf16<DH>, grid, block, 0, stream, (const uint16_t*)q,
-                           (const uint16_t*)subkeys, scores, rows_per_head, H, S);
-    else
-        hipLaunchKernelGGL(pk_score_f32<DH>, grid, block, 0, stream, (const float*)q, (const float*)subkeys,
-                           scores, rows_per_head, H, S);
+    if (in_bf16) {
+        constexpr int RB = DH <= 128 ? 4 : 2;
+        const long ctiles = (S + 31) / 32;
+        const long n = (long)H * 2 * ctiles * (DH / 16) * 64;
+        hipLaunchKernelGGL(pk_subkey_frag, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           (const uint16_t*)subkeys, (uint4*)frag, H, S, DH);
+        const long blocks = (rows_per_head + 32 * RB - 1) / (32 * RB);
+        hipLaunchKernelGGL((pk_score_bf16<DH, RB>), dim3((unsigned)(blocks * H * 2)), dim3(kWaves * 64), 0, stream,
+                           (const uint16_t*)q, (const uint4*)frag, scores, rows_per_head, H, S);
+    } else {
+        const long tiles = (rows_per_head + 31) / 32;
+        hipLaunchKernelGGL(pk_score_f32<DH>, dim3((unsigned)(tiles * H * 2)), dim3(kWaves * 64), 0, stream,
+                           (const float*)q, (const float*)subkeys, scores, rows_per_head, H, S);
+    }
     return hipGetLastError();
 }
 
 } // namespace
 
-hipError_t launch_pk_score(const void* q, const void* subkeys, float* scores, long rows_per_head, int H, int S,
-                           int dh, bool in_bf16, hipStream_t stream)
+size_t pk_score_frag_bytes(int H, int S, int dh) { return (size_t)H * 2 * ((S + 31) / 32) * (dh / 16) * 1024; }
+
+hipError_t launch_pk_score(const void* q, const void* subkeys, void* frag, float* scores, long rows_per_head, int H,
+                           int S, int dh, bool in_bf16, hipStream_t stream)
 {
     switch (dh) {
-    case 16: return launch_dh<16>(q, subkeys, scores, rows_per_head, H, S, in_bf16, stream);
-    case 32: return launch_dh<32>(q, subkeys, scores, rows_per_head, H, S, in_bf16, stream);
-    case 48: return launch_dh<48>(q, subkeys, scores, rows_per_head, H, S, in_bf16, stream);
-    case 64: return launch_dh<64>(q, subkeys, scores, rows_per_head, H, S, in_bf16, stream);
-    case 96: return launch_dh<96>(q, subkeys, scores, rows_per_head, H, S, in_bf16, stream);
-    case 128: return launch_dh<128>(q, subkeys, scores, rows_per_head, H, S, in_bf16, stream);
-    case 192: return launch_dh<192>(q, subkeys, scores, rows_per_head, H, S, in_bf16, stream);
-    case 256: return launch_dh<256>(q, subkeys, scores, rows_per_head, H, S, in_bf16, stream);
+    case 16: return launch_dh<16>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
+    case 32: return launch_dh<32>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
+    case 48: return launch_dh<48>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
+    case 64: return launch_dh<64>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
+    case 96: return launch_dh<96>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
+    case 128: return launch_dh<128>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
+    case 192: return launch_dh<192>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
+    case 256: return launch_dh<256>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
     default: return hipErrorInvalidValue;
     }
 }

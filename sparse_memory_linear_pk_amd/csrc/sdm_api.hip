@@ -38,7 +38,7 @@ struct TimedLaunch {
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t scores, idx, wt, plan, total;
+    size_t scores, idx, wt, plan, frag, total;
 };
 
 Layout layout_of(const sdm_config& c, const sdm::ScanPlan& plan)
@@ -49,7 +49,8 @@ Layout layout_of(const sdm_config& c, const sdm::ScanPlan& plan)
     L.idx = align_up(rows * (size_t)c.W * sizeof(int32_t));
     L.wt = align_up(rows * (size_t)c.W * sizeof(float));
     L.plan = align_up(sdm::plan_bytes(plan, c.B, c.H, c.T, c.W));
-    L.total = L.scores + 2 * (L.idx + L.wt) + L.plan;
+    L.frag = align_up(sdm::pk_score_frag_bytes(c.H, c.n_sub, c.dk / 2));
+    L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag;
     return L;
 }
 
@@ -111,6 +112,7 @@ struct sdm_ctx {
     int32_t* idx[2];
     float* wt[2];
     uint4* plan_buf;
+    void* frag;
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
@@ -153,7 +155,7 @@ sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, float* scor
 {
     const sdm_config& c = h->cfg;
     Timer t(h, K_SCORE);
-    hipError_t e = sdm::launch_pk_score(q, subkeys, scores, (long)c.B * c.T, c.H, c.n_sub, c.dk / 2,
+    hipError_t e = sdm::launch_pk_score(q, subkeys, h->frag, scores, (long)c.B * c.T, c.H, c.n_sub, c.dk / 2,
                                         c.in_dtype == SDM_BF16, h->stream);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_score launch");
 }
@@ -266,6 +268,8 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
         p += h->L.wt;
     }
     h->plan_buf = (uint4*)p;
+    p += h->L.plan;
+    h->frag = p;
     h->magic = kMagic;
     *out = h;
     return SDM_OK;

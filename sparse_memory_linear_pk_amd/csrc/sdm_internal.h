@@ -25,10 +25,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return bf16_rne(lo) | (bf16_rne(hi) << 16); }
 
-// order-preserving map from float to uint32 (larger float -> larger key)
+// order-preserving map from float to uint32 (larger float -> larger key); -0
+// and +0 compare equal as floats and get the same key (that of +0)
 __device__ __forceinline__ uint32_t ordered_key(float f)
 {
     uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
@@ -49,8 +51,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // ---------------------------------------------------------------------------
 
 // Half scores of the rows of q ([rows_per_head * H, dk], row r belongs to head r % H)
-// against subkeys [H, 2, S, dh]: scores [rows, 2, S] float32.
-hipError_t launch_pk_score(const void* q, const void* subkeys, float* scores, long rows_per_head, int H,
+// against subkeys [H, 2, S, dh]: scores [rows, 2, S] float32.  frag: workspace of
+// pk_score_frag_bytes for the bf16 path's rearranged sub-key tables.
+size_t pk_score_frag_bytes(int H, int S, int dh);
+hipError_t launch_pk_score(const void* q, const void* subkeys, void* frag, float* scores, long rows_per_head, int H,
                            int S, int dh, bool in_bf16, hipStream_t stream);
 
 // Per-half top-k, outer-sum top-W and softmax weights for `rows` rows of scores.
