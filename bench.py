@@ -32,12 +32,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def scan_bytes_per_launch(cfg) -> int:
+def scan_bytes_per_step(cfg) -> int:
+    """Algorithmic state bytes of one forward: per token and memory, W slots
+    read for the write, W read for the read and W written."""
     s = 2 if cfg.state_bf16 else 4
     return cfg.B * cfg.T * cfg.H * 3 * cfg.W * cfg.d * s
 
 
-def score_flops_per_launch(cfg) -> int:
+def score_flops_per_step(cfg) -> int:
+    """Sub-key scoring of one forward: both query sets, both halves."""
     return cfg.B * cfg.T * cfg.H * 2 * cfg.S * cfg.dh * 2
 
 
@@ -172,15 +175,16 @@ def main():
 
     sec = t1 - t0
     tokens = cfg.B * cfg.T * args.steps
-    scan_ms = tm["ms_scan"] / max(1, tm["n_scan"])
-    score_ms = tm["ms_score"] / max(1, tm["n_score"])
-    sel_ms = tm["ms_select"] / max(1, tm["n_select"])
-    plan_ms = tm["ms_plan"] / max(1, tm["n_plan"])
-    nbytes = scan_bytes_per_launch(cfg)
+    # device time per forward of each kernel (a forward scans in chunks: several
+    # scan launches, with the next chunk's addressing and plan overlapping)
+    per_step = {k: tm[f"ms_{k}"] / args.steps for k in ("score", "select", "plan", "scan")}
+    scan_launches = tm["n_scan"] / args.steps
+    scan_ms = per_step["scan"]
+    nbytes = scan_bytes_per_step(cfg)
     achieved = nbytes / (scan_ms * 1e-3) / 1e9
     sig = kernel_signature()
     traffic = load_traffic(sig)
-    score_tflops = score_flops_per_launch(cfg) / (score_ms * 1e-3) / 1e12
+    score_tflops = score_flops_per_step(cfg) / (per_step["score"] * 1e-3) / 1e12
     peak_mfma = BF16_MFMA_PEAK_TFLOPS if cfg.in_bf16 else F32_MFMA_PEAK_TFLOPS
 
     res = {
@@ -201,14 +205,15 @@ def main():
                    "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "sdm_scan", "bytes_per_launch": nbytes, "ms_per_launch": scan_ms,
+                     "kernel": "sdm_scan", "launches_per_step": scan_launches,
+                     "bytes_per_launch": nbytes / scan_launches, "ms_per_launch": scan_ms / scan_launches,
                      "pattern_ceiling": {"achieved": nbytes / (pattern_ms * 1e-3) / 1e9, "unit": "GB/s",
                                          "ms_per_launch": pattern_ms,
                                          "frac": (nbytes / (scan_ms * 1e-3)) / (nbytes / (pattern_ms * 1e-3)),
                                          "what": "sdm_pattern_probe: the scan's random 128-byte segment reads "
                                                  "and writes (2:1) with no arithmetic; frac = scan / this"}},
-        "kernels_ms_per_step": {"pk_score": 2 * score_ms, "pk_topk": 2 * sel_ms, "sdm_plan": plan_ms,
-                                "sdm_scan": scan_ms},
+        "kernels_ms_per_step": {"pk_score": per_step["score"], "pk_topk": per_step["select"],
+                                "sdm_plan": per_step["plan"], "sdm_scan": scan_ms},
         "pk_score": {"tflops": score_tflops, "peak_tflops": peak_mfma, "frac": score_tflops / peak_mfma},
         "kernel_signature": sig,
     }

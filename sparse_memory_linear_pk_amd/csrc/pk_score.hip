@@ -57,55 +57,63 @@ __global__ __launch_bounds__(256) void pk_subkey_frag(const uint16_t* __restrict
 template <int DH, int RB>
 __global__ __launch_bounds__(kWaves * 64) void pk_score_bf16(const uint16_t* __restrict__ q,
                                                            const uint4* __restrict__ frag,
-                                                           float* __restrict__ scores, long rows_per_head,
-                                                           int H, int S)
+                                                           float* __restrict__ scores, Rows r, int S)
 {
     constexpr int KSTEPS = DH / 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 31, kg = lane >> 5;
-    const long blocks = (rows_per_head + 32 * RB - 1) / (32 * RB);
-    long bid = blockIdx.x;
-    const int half = (int)(bid & 1);
+    const int H = r.H;
+    // blocks of RB*32 tokens never straddle two sequences, so a block's rows are
+    // evenly spaced in memory
+    const int blocks = (r.Tc + 32 * RB - 1) / (32 * RB);
+    int bid = blockIdx.x;
+    const int half = bid & 1;
     bid >>= 1;
-    const long rb = bid % blocks;
-    const int h = (int)(bid / blocks);
+    const int blk = bid % blocks;
+    bid /= blocks;
+    const int b = bid % r.B, h = bid / r.B;
     const int dk = 2 * DH;
+    const int tl0 = blk * RB * 32;                       // first token of the block, within the chunk
+    const int valid = min(RB * 32, r.Tc - tl0);          // tokens of the block inside the chunk
+    const long rr0 = (long)b * r.Ts + r.t0 + tl0;         // its token row (b, t) over the sequences
 
     bf16x8_t a[RB][KSTEPS];
 #pragma unroll
     for (int t = 0; t < RB; ++t) {
-        const long rr = (rb * RB + t) * 32 + i;
-        const uint16_t* qrow = q + (rr * H + h) * dk + half * DH + kg * 8;
+        const int tl = t * 32 + i;
+        const uint16_t* qrow = q + ((rr0 + tl) * H + h) * dk + half * DH + kg * 8;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
-            a[t][kk] = rr < rows_per_head ? *reinterpret_cast<const bf16x8_t*>(qrow + kk * 16) : bf16x8_t{};
+            a[t][kk] = tl < valid ? *reinterpret_cast<const bf16x8_t*>(qrow + kk * 16) : bf16x8_t{};
     }
     const int ctiles = (S + 31) / 32;
     const uint4* fb = frag + (long)(h * 2 + half) * ctiles * KSTEPS * 64 + lane;
-    // stores through a buffer based at the block's first row: a per-lane offset
-    // (sub-key column, row group) plus a uniform one per row; columns past S
-    // and rows past the end fall outside the buffer and are dropped
-    const long first = ((rb * RB * 32 * H + h) * 2 + half) * (long)S;
-    const long avail = (rows_per_head * H * 2 - ((rb * RB * 32 * H + h) * 2 + half)) * (long)S * 4;
-    const __amdgpu_buffer_rsrc_t out = make_rsrc(scores + first, (uint32_t)(avail < 0x7FFFFFF0L ? avail : 0x7FFFFFF0L));
+    // stores through a buffer based at the block's first row that ends with
+    // the last valid row's segment: a per-lane offset (sub-key column, row
+    // group) plus a uniform one per row; rows past the chunk fall outside the
+    // buffer and are dropped (the host keeps 128 rows below 2^31 bytes)
     const uint32_t row_bytes = (uint32_t)(H * 2 * S) * 4u;
+    const __amdgpu_buffer_rsrc_t out = make_rsrc(scores + ((rr0 * H + h) * 2 + half) * (long)S,
+                                                 (uint32_t)(valid - 1) * row_bytes + (uint32_t)S * 4u);
     for (int ct = wave; ct < ctiles; ct += kWaves) {
         bf16x8_t b[KSTEPS];
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
             b[kk] = __builtin_bit_cast(bf16x8_t, fb[(ct * KSTEPS + kk) * 64]);
         const int s = ct * 32 + i;
-        const uint32_t lane_off = s < S ? (uint32_t)(4 * kg) * row_bytes + (uint32_t)s * 4u : 0x80000000u;
+        const uint32_t lane_off = (uint32_t)(4 * kg) * row_bytes + (uint32_t)s * 4u;
 #pragma unroll
         for (int t = 0; t < RB; ++t) {
             f32x16_t acc = {};
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][kk], b[kk], acc, 0, 0, 0);
+            if (s < S) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const uint32_t row_off = (uint32_t)(t * 32 + 8 * (v >> 2) + (v & 3)) * row_bytes;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v]), out, lane_off, row_off, 0);
+                for (int v = 0; v < 16; ++v) {
+                    const uint32_t row_off = (uint32_t)(t * 32 + 8 * (v >> 2) + (v & 3)) * row_bytes;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v]), out, lane_off, row_off, 0);
+                }
             }
         }
     }
@@ -114,24 +122,26 @@ __global__ __launch_bounds__(kWaves * 64) void pk_score_bf16(const uint16_t* __r
 template <int DH>
 __global__ __launch_bounds__(kWaves * 64) void pk_score_f32(const float* __restrict__ q,
                                                           const float* __restrict__ subkeys,
-                                                          float* __restrict__ scores, long rows_per_head, int H,
-                                                          int S)
+                                                          float* __restrict__ scores, Rows r, int S)
 {
     constexpr int KSTEPS = DH / 2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 31, kg = lane >> 5;
-    const long tiles = (rows_per_head + 31) / 32;
-    long bid = blockIdx.x;
-    const int half = (int)(bid & 1);
+    const int H = r.H;
+    const int tiles = (r.Tc + 31) / 32;
+    int bid = blockIdx.x;
+    const int half = bid & 1;
     bid >>= 1;
-    const long rt = bid % tiles;
-    const int h = (int)(bid / tiles);
+    const int tile = bid % tiles;
+    bid /= tiles;
+    const int b = bid % r.B, h = bid / r.B;
     const int dk = 2 * DH;
+    const long rr0 = (long)b * r.Ts + r.t0 + tile * 32; // token row of the tile's first row
+    const int valid = min(32, r.Tc - tile * 32);
 
-    const long rr = rt * 32 + i;
     float a[KSTEPS];
-    if (rr < rows_per_head) {
-        const float* qrow = q + (rr * H + h) * dk + half * DH + kg;
+    if (i < valid) {
+        const float* qrow = q + ((rr0 + i) * H + h) * dk + half * DH + kg;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
             a[kk] = qrow[kk * 2];
@@ -153,31 +163,27 @@ __global__ __launch_bounds__(kWaves * 64) void pk_score_f32(const float* __restr
         if (s < S) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const long row = rt * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
-                if (row < rows_per_head)
-                    scores[((row * H + h) * 2 + half) * (long)S + s] = acc[v];
+                const int row = 8 * (v >> 2) + 4 * kg + (v & 3);
+                if (row < valid)
+                    scores[(((rr0 + row) * H + h) * 2 + half) * (long)S + s] = acc[v];
             }
         }
     }
 }
 
 template <int DH>
-hipError_t launch_dh(const void* q, const void* subkeys, void* frag, float* scores, long rows_per_head, int H, int S,
+hipError_t launch_dh(const void* q, const void* subkeys, const void* frag, float* scores, const Rows& r, int S,
                      bool in_bf16, hipStream_t stream)
 {
     if (in_bf16) {
         constexpr int RB = DH <= 128 ? 4 : 2;
-        const long ctiles = (S + 31) / 32;
-        const long n = (long)H * 2 * ctiles * (DH / 16) * 64;
-        hipLaunchKernelGGL(pk_subkey_frag, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                           (const uint16_t*)subkeys, (uint4*)frag, H, S, DH);
-        const long blocks = (rows_per_head + 32 * RB - 1) / (32 * RB);
-        hipLaunchKernelGGL((pk_score_bf16<DH, RB>), dim3((unsigned)(blocks * H * 2)), dim3(kWaves * 64), 0, stream,
-                           (const uint16_t*)q, (const uint4*)frag, scores, rows_per_head, H, S);
+        const int blocks = (r.Tc + 32 * RB - 1) / (32 * RB);
+        hipLaunchKernelGGL((pk_score_bf16<DH, RB>), dim3((unsigned)(blocks * r.B * r.H * 2)), dim3(kWaves * 64), 0,
+                           stream, (const uint16_t*)q, (const uint4*)frag, scores, r, S);
     } else {
-        const long tiles = (rows_per_head + 31) / 32;
-        hipLaunchKernelGGL(pk_score_f32<DH>, dim3((unsigned)(tiles * H * 2)), dim3(kWaves * 64), 0, stream,
-                           (const float*)q, (const float*)subkeys, scores, rows_per_head, H, S);
+        const int tiles = (r.Tc + 31) / 32;
+        hipLaunchKernelGGL(pk_score_f32<DH>, dim3((unsigned)(tiles * r.B * r.H * 2)), dim3(kWaves * 64), 0, stream,
+                           (const float*)q, (const float*)subkeys, scores, r, S);
     }
     return hipGetLastError();
 }
@@ -186,18 +192,28 @@ hipError_t launch_dh(const void* q, const void* subkeys, void* frag, float* scor
 
 size_t pk_score_frag_bytes(int H, int S, int dh) { return (size_t)H * 2 * ((S + 31) / 32) * (dh / 16) * 1024; }
 
-hipError_t launch_pk_score(const void* q, const void* subkeys, void* frag, float* scores, long rows_per_head, int H,
+hipError_t launch_pk_subkey_frag(const void* subkeys, void* frag, int H, int S, int dh, hipStream_t stream)
+{
+    const long n = (long)pk_score_frag_bytes(H, S, dh) / 16;
+    hipLaunchKernelGGL(pk_subkey_frag, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       (const uint16_t*)subkeys, (uint4*)frag, H, S, dh);
+    return hipGetLastError();
+}
+
+hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag, float* scores, const Rows& r,
                            int S, int dh, bool in_bf16, hipStream_t stream)
 {
+    if (r.count() <= 0)
+        return hipSuccess;
     switch (dh) {
-    case 16: return launch_dh<16>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
-    case 32: return launch_dh<32>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
-    case 48: return launch_dh<48>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
-    case 64: return launch_dh<64>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
-    case 96: return launch_dh<96>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
-    case 128: return launch_dh<128>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
-    case 192: return launch_dh<192>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
-    case 256: return launch_dh<256>(q, subkeys, frag, scores, rows_per_head, H, S, in_bf16, stream);
+    case 16: return launch_dh<16>(q, subkeys, frag, scores, r, S, in_bf16, stream);
+    case 32: return launch_dh<32>(q, subkeys, frag, scores, r, S, in_bf16, stream);
+    case 48: return launch_dh<48>(q, subkeys, frag, scores, r, S, in_bf16, stream);
+    case 64: return launch_dh<64>(q, subkeys, frag, scores, r, S, in_bf16, stream);
+    case 96: return launch_dh<96>(q, subkeys, frag, scores, r, S, in_bf16, stream);
+    case 128: return launch_dh<128>(q, subkeys, frag, scores, r, S, in_bf16, stream);
+    case 192: return launch_dh<192>(q, subkeys, frag, scores, r, S, in_bf16, stream);
+    case 256: return launch_dh<256>(q, subkeys, frag, scores, r, S, in_bf16, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -207,7 +207,7 @@ __device__ void select_w(const uint32_t (&key)[M], const uint32_t (&slot)[M], in
 template <int J, int R>
 __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float* __restrict__ scores,
                                                                    int32_t* __restrict__ idx,
-                                                                   float* __restrict__ wt, long rows, int S,
+                                                                   float* __restrict__ wt, Rows rr, int S,
                                                                    int k, int W, int n_pairs)
 {
     __shared__ uint64_t s_buf[kRowsPerBlock][64];       // compaction scratch, then the winners
@@ -227,9 +227,11 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float
     }
     __syncthreads();
 
-    const long row = (long)blockIdx.x * kRowsPerBlock + wave;
-    if (row >= rows)
+    const long j = (long)blockIdx.x * kRowsPerBlock + wave; // row of the chunk
+    if (j >= rr.count())
         return; // whole wave leaves; no block-level barriers below
+    const long per_seq = (long)rr.Tc * rr.H;
+    const long row = ((j / per_seq) * rr.Ts + rr.t0) * rr.H + j % per_seq; // row (b, t, h) of the call
 
     const float* s = scores + row * 2 * (long)S;
 #pragma unroll
@@ -342,13 +344,13 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float
 }
 
 template <int J>
-hipError_t launch_j(const float* scores, int32_t* idx, float* wt, long rows, int S, int k, int W, int n_pairs,
+hipError_t launch_j(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
                     hipStream_t stream)
 {
-    dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
+    dim3 grid((unsigned)((r.count() + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
 #define SDM_TOPK_R(Rv)                                                                                       \
     if (n_pairs <= 64 * Rv) {                                                                                \
-        hipLaunchKernelGGL((pk_topk_kernel<J, Rv>), grid, block, 0, stream, scores, idx, wt, rows, S, k, W, \
+        hipLaunchKernelGGL((pk_topk_kernel<J, Rv>), grid, block, 0, stream, scores, idx, wt, r, S, k, W,    \
                            n_pairs);                                                                         \
         return hipGetLastError();                                                                            \
     }
@@ -362,10 +364,10 @@ hipError_t launch_j(const float* scores, int32_t* idx, float* wt, long rows, int
 
 } // namespace
 
-hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, long rows, int S, int k, int W,
+hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
                           hipStream_t stream)
 {
-    if (rows <= 0)
+    if (r.count() <= 0)
         return hipSuccess;
     if (k < 1 || k > 64 || W < 1 || W > 64 || W > k * k || k > S)
         return hipErrorInvalidValue;
@@ -375,15 +377,15 @@ hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, long row
     if (n_pairs > kPairsMax)
         return hipErrorInvalidValue;
     if (S <= 64)
-        return launch_j<1>(scores, idx, wt, rows, S, k, W, n_pairs, stream);
+        return launch_j<1>(scores, idx, wt, r, S, k, W, n_pairs, stream);
     if (S <= 128)
-        return launch_j<2>(scores, idx, wt, rows, S, k, W, n_pairs, stream);
+        return launch_j<2>(scores, idx, wt, r, S, k, W, n_pairs, stream);
     if (S <= 256)
-        return launch_j<4>(scores, idx, wt, rows, S, k, W, n_pairs, stream);
+        return launch_j<4>(scores, idx, wt, r, S, k, W, n_pairs, stream);
     if (S <= 512)
-        return launch_j<8>(scores, idx, wt, rows, S, k, W, n_pairs, stream);
+        return launch_j<8>(scores, idx, wt, r, S, k, W, n_pairs, stream);
     if (S <= 1024)
-        return launch_j<16>(scores, idx, wt, rows, S, k, W, n_pairs, stream);
+        return launch_j<16>(scores, idx, wt, r, S, k, W, n_pairs, stream);
     return hipErrorInvalidValue;
 }
 

@@ -37,24 +37,45 @@ struct TimedLaunch {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-struct Layout {
-    size_t scores, idx, wt, plan, frag, total;
+// A forward runs its scan in chunks of kChunkTokens tokens; the addressing and
+// the plan of chunk c + 1 run on a second stream while chunk c scans.
+constexpr int kChunkTokens = 2048;
+
+struct Chunking {
+    int Tc; // tokens per chunk (the last may be shorter)
+    int C;  // chunks
+    int len(const sdm_config& c, int ci) const { return ci + 1 < C ? Tc : c.T - (C - 1) * Tc; }
 };
 
-Layout layout_of(const sdm_config& c, const sdm::ScanPlan& plan)
+Chunking chunking_of(const sdm_config& c)
+{
+    Chunking k;
+    k.Tc = c.T <= kChunkTokens ? c.T : kChunkTokens;
+    k.C = (c.T + k.Tc - 1) / k.Tc;
+    return k;
+}
+
+struct Layout {
+    size_t scores, idx, wt, plan_region, plan, frag, total;
+};
+
+Layout layout_of(const sdm_config& c, const Chunking& k, const sdm::ScanPlan& full, const sdm::ScanPlan& last)
 {
     const size_t rows = (size_t)c.B * c.T * c.H;
     Layout L;
     L.scores = align_up(rows * 2 * (size_t)c.n_sub * sizeof(float));
     L.idx = align_up(rows * (size_t)c.W * sizeof(int32_t));
     L.wt = align_up(rows * (size_t)c.W * sizeof(float));
-    L.plan = align_up(sdm::plan_bytes(plan, c.B, c.H, c.T, c.W));
+    const size_t pf = sdm::plan_bytes(full, c.B, c.H, k.Tc, c.W);
+    const size_t pl = sdm::plan_bytes(last, c.B, c.H, k.len(c, k.C - 1), c.W);
+    L.plan_region = align_up(pf > pl ? pf : pl);
+    L.plan = L.plan_region * k.C;
     L.frag = align_up(sdm::pk_score_frag_bytes(c.H, c.n_sub, c.dk / 2));
     L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag;
     return L;
 }
 
-sdm_status check_config(const sdm_config* c, sdm::ScanPlan* plan)
+sdm_status check_config(const sdm_config* c, sdm::ScanPlan* plan, sdm::ScanPlan* plan_last)
 {
     if (!c)
         return fail(SDM_ERR_INVALID_ARG, "config is NULL");
@@ -87,10 +108,15 @@ sdm_status check_config(const sdm_config* c, sdm::ScanPlan* plan)
     const size_t mem_bytes = (size_t)c->n_sub * c->n_sub * c->d * s;
     if (mem_bytes >= (1ull << 32))
         return fail(SDM_ERR_UNSUPPORTED, "one memory is %zu bytes; at most 2^32 - 1", mem_bytes);
+    if ((long)c->H * c->n_sub * 2 * 4 * 128 >= (1l << 31))
+        return fail(SDM_ERR_UNSUPPORTED, "H*S=%ld: at most 2^21 - 1", (long)c->H * c->n_sub);
     if ((long)c->B * c->T * c->H > (1l << 31) / 64)
         return fail(SDM_ERR_UNSUPPORTED, "B*T*H=%ld rows is too many", (long)c->B * c->T * c->H);
-    if (!sdm::plan_scan(c->B, c->H, c->T, c->d, c->W, (long)c->n_sub * c->n_sub, c->state_dtype == SDM_BF16,
-                         c->in_dtype == SDM_BF16, plan))
+    const Chunking k = chunking_of(*c);
+    const long N = (long)c->n_sub * c->n_sub;
+    if (!sdm::plan_scan(c->B, c->H, k.Tc, c->d, c->W, N, c->state_dtype == SDM_BF16, c->in_dtype == SDM_BF16, plan) ||
+        !sdm::plan_scan(c->B, c->H, k.len(*c, k.C - 1), c->d, c->W, N, c->state_dtype == SDM_BF16,
+                        c->in_dtype == SDM_BF16, plan_last))
         return fail(SDM_ERR_UNSUPPORTED, "no scan layout for d=%d W=%d", c->d, c->W);
     return SDM_OK;
 }
@@ -103,9 +129,13 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 struct sdm_ctx {
     uint32_t magic;
     sdm_config cfg;
-    hipStream_t stream;
+    hipStream_t stream;  // the caller's: scans run here
+    hipStream_t aux;     // addressing and plans of a chunked forward (default priority)
+    hipEvent_t e_start;  // the caller's stream reached the forward
+    std::vector<hipEvent_t> e_plan; // chunk c's plan is written
     int device;
-    sdm::ScanPlan plan;
+    Chunking ck;
+    sdm::ScanPlan plan, plan_last; // scan layout of a full chunk and of the last chunk
     void* block;
     Layout L;
     float* scores;
@@ -132,70 +162,113 @@ sdm_status hip_fail(hipError_t e, const char* what)
     return fail(SDM_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Records events around one launch when timing is on.
+// Records events around one launch, on the stream it runs on, when timing is on.
 struct Timer {
     sdm_ctx* h;
     Kind kind;
+    hipStream_t st;
     hipEvent_t a = nullptr, b = nullptr;
-    Timer(sdm_ctx* h_, Kind k) : h(h_), kind(k)
+    Timer(sdm_ctx* h_, Kind k, hipStream_t s) : h(h_), kind(k), st(s)
     {
         if (h->timing && hipEventCreate(&a) == hipSuccess && hipEventCreate(&b) == hipSuccess)
-            (void)hipEventRecord(a, h->stream);
+            (void)hipEventRecord(a, st);
     }
     ~Timer()
     {
         if (a && b) {
-            (void)hipEventRecord(b, h->stream);
+            (void)hipEventRecord(b, st);
             h->pending.push_back({kind, a, b});
         }
     }
 };
 
-sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, float* scores)
+sdm::Rows all_rows(const sdm_config& c) { return sdm::Rows{c.B, c.H, c.T, c.T, 0}; }
+
+sdm::Rows chunk_rows(const sdm_ctx* h, int ci)
 {
     const sdm_config& c = h->cfg;
-    Timer t(h, K_SCORE);
-    hipError_t e = sdm::launch_pk_score(q, subkeys, h->frag, scores, (long)c.B * c.T, c.H, c.n_sub, c.dk / 2,
-                                        c.in_dtype == SDM_BF16, h->stream);
+    return sdm::Rows{c.B, c.H, h->ck.len(c, ci), c.T, ci * h->ck.Tc};
+}
+
+// frag: rearrange the sub-key tables first (once per call that scores)
+sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, float* scores, const sdm::Rows& r,
+                     hipStream_t st, bool frag)
+{
+    const sdm_config& c = h->cfg;
+    const bool bf16 = c.in_dtype == SDM_BF16;
+    Timer t(h, K_SCORE, st);
+    hipError_t e = hipSuccess;
+    if (frag && bf16)
+        e = sdm::launch_pk_subkey_frag(subkeys, h->frag, c.H, c.n_sub, c.dk / 2, st);
+    if (e == hipSuccess)
+        e = sdm::launch_pk_score(q, subkeys, h->frag, scores, r, c.n_sub, c.dk / 2, bf16, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_score launch");
 }
 
-sdm_status run_select(sdm_ctx* h, const float* scores, int32_t* idx, float* wt)
+sdm_status run_select(sdm_ctx* h, const float* scores, int32_t* idx, float* wt, const sdm::Rows& r, hipStream_t st)
 {
     const sdm_config& c = h->cfg;
-    Timer t(h, K_SELECT);
-    hipError_t e = sdm::launch_pk_topk(scores, idx, wt, (long)c.B * c.T * c.H, c.n_sub, c.k, c.W, h->stream);
+    Timer t(h, K_SELECT, st);
+    hipError_t e = sdm::launch_pk_topk(scores, idx, wt, r, c.n_sub, c.k, c.W, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_topk launch");
 }
 
-sdm_status run_scan(sdm_ctx* h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
-                    const void* v, const float* alpha, const float* beta, void* mem, float* out)
+const sdm::ScanPlan& plan_of(const sdm_ctx* h, int ci) { return ci + 1 < h->ck.C ? h->plan : h->plan_last; }
+
+uint4* plan_region(const sdm_ctx* h, int ci)
+{
+    return reinterpret_cast<uint4*>(reinterpret_cast<char*>(h->plan_buf) + (size_t)ci * h->L.plan_region);
+}
+
+sdm_status run_plan(sdm_ctx* h, int ci, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                    const float* wt_r, const float* alpha, const float* beta, hipStream_t st)
 {
     const sdm_config& c = h->cfg;
-    {
-        Timer t(h, K_PLAN);
-        hipError_t e = sdm::launch_sdm_plan(h->plan, idx_w, wt_w, idx_r, wt_r, alpha, beta, h->plan_buf, c.B, c.T, c.H,
-                                            c.W, c.d, (long)c.n_sub * c.n_sub, c.in_dtype == SDM_BF16, h->stream);
-        if (e != hipSuccess)
-            return hip_fail(e, "sdm_plan launch");
-    }
+    Timer t(h, K_PLAN, st);
+    hipError_t e = sdm::launch_sdm_plan(plan_of(h, ci), idx_w, wt_w, idx_r, wt_r, alpha, beta, plan_region(h, ci),
+                                        chunk_rows(h, ci), c.W, c.d, (long)c.n_sub * c.n_sub, c.in_dtype == SDM_BF16,
+                                        st);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_plan launch");
+}
+
+sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hipStream_t st)
+{
+    const sdm_config& c = h->cfg;
+    const sdm::ScanPlan& p = plan_of(h, ci);
+    const sdm::Rows r = chunk_rows(h, ci);
+    const size_t first = (size_t)r.t0 * c.H * c.d; // element of token t0 in sequence 0
     sdm::ScanArgs a;
-    a.plan = h->plan_buf;
-    a.ab = h->plan.staged ? nullptr
-                          : reinterpret_cast<const float2*>(h->plan_buf + (size_t)c.B * c.H * c.T * c.W);
-    a.v = v;
+    a.plan = plan_region(h, ci);
+    a.ab = p.staged ? nullptr : reinterpret_cast<const float2*>(a.plan + (size_t)c.B * c.H * r.Tc * c.W);
+    a.v = static_cast<const char*>(v) + first * (c.in_dtype == SDM_BF16 ? 2 : 4);
     a.mem = mem;
-    a.out = out;
+    a.out = out + first;
     a.B = c.B;
-    a.T = c.T;
+    a.T = r.Tc;
+    a.Ts = c.T;
     a.H = c.H;
     a.d = c.d;
     a.W = c.W;
-    a.Tp = h->plan.Tp;
+    a.Tp = p.Tp;
     a.N = (long)c.n_sub * c.n_sub;
-    Timer t(h, K_SCAN);
-    hipError_t e = sdm::launch_sdm_scan(a, h->plan, c.state_dtype == SDM_BF16, c.in_dtype == SDM_BF16, h->stream);
+    Timer t(h, K_SCAN, st);
+    hipError_t e = sdm::launch_sdm_scan(a, p, c.state_dtype == SDM_BF16, c.in_dtype == SDM_BF16, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan launch");
+}
+
+// The addressing of both query sets for chunk ci, then its plan.
+sdm_status run_chunk_front(sdm_ctx* h, int ci, const void* wq, const void* rq, const float* alpha, const float* beta,
+                           const void* subkeys, hipStream_t st)
+{
+    const sdm::Rows r = chunk_rows(h, ci);
+    const void* q[2] = {wq, rq};
+    sdm_status s = SDM_OK;
+    for (int set = 0; set < 2 && s == SDM_OK; ++set) {
+        s = run_score(h, q[set], subkeys, h->scores, r, st, ci == 0 && set == 0);
+        if (s == SDM_OK)
+            s = run_select(h, h->scores, h->idx[set], h->wt[set], r, st);
+    }
+    return s == SDM_OK ? run_plan(h, ci, h->idx[0], h->wt[0], h->idx[1], h->wt[1], alpha, beta, st) : s;
 }
 
 } // namespace
@@ -218,13 +291,13 @@ const char* sdm_last_error(void) { return g_err; }
 
 sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes)
 {
-    sdm::ScanPlan plan;
-    sdm_status s = check_config(cfg, &plan);
+    sdm::ScanPlan plan, plan_last;
+    sdm_status s = check_config(cfg, &plan, &plan_last);
     if (s != SDM_OK)
         return s;
     if (!bytes)
         return fail(SDM_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = layout_of(*cfg, plan).total;
+    *bytes = layout_of(*cfg, chunking_of(*cfg), plan, plan_last).total;
     return SDM_OK;
 }
 
@@ -234,8 +307,8 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     if (!out)
         return fail(SDM_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    sdm::ScanPlan plan;
-    sdm_status s = check_config(cfg, &plan);
+    sdm::ScanPlan plan, plan_last;
+    sdm_status s = check_config(cfg, &plan, &plan_last);
     if (s != SDM_OK)
         return s;
     int dev = 0;
@@ -249,7 +322,11 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->stream = (hipStream_t)hip_stream;
     h->device = dev;
     h->plan = plan;
-    h->L = layout_of(*cfg, plan);
+    h->plan_last = plan_last;
+    h->ck = chunking_of(*cfg);
+    h->L = layout_of(*cfg, h->ck, plan, plan_last);
+    h->aux = nullptr;
+    h->e_start = nullptr;
     h->timing = false;
     memset(&h->totals, 0, sizeof h->totals);
     e = hipMalloc(&h->block, h->L.total);
@@ -270,6 +347,26 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->plan_buf = (uint4*)p;
     p += h->L.plan;
     h->frag = p;
+    if (h->ck.C > 1) {
+        e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&h->e_start, hipEventDisableTiming);
+        h->e_plan.assign(h->ck.C, nullptr);
+        for (int ci = 0; ci < h->ck.C && e == hipSuccess; ++ci)
+            e = hipEventCreateWithFlags(&h->e_plan[ci], hipEventDisableTiming);
+        if (e != hipSuccess) {
+            for (hipEvent_t ev : h->e_plan)
+                if (ev)
+                    (void)hipEventDestroy(ev);
+            if (h->e_start)
+                (void)hipEventDestroy(h->e_start);
+            if (h->aux)
+                (void)hipStreamDestroy(h->aux);
+            (void)hipFree(h->block);
+            delete h;
+            return hip_fail(e, "stream or event creation");
+        }
+    }
     h->magic = kMagic;
     *out = h;
     return SDM_OK;
@@ -281,6 +378,14 @@ sdm_status sdm_destroy(sdm_handle h)
     if (s != SDM_OK)
         return s;
     hipError_t e = hipStreamSynchronize(h->stream);
+    if (h->aux) {
+        const hipError_t ea = hipStreamSynchronize(h->aux);
+        e = e == hipSuccess ? ea : e;
+        for (hipEvent_t ev : h->e_plan)
+            (void)hipEventDestroy(ev);
+        (void)hipEventDestroy(h->e_start);
+        (void)hipStreamDestroy(h->aux);
+    }
     for (auto& tl : h->pending) {
         (void)hipEventDestroy(tl.start);
         (void)hipEventDestroy(tl.stop);
@@ -304,7 +409,7 @@ sdm_status sdm_score(sdm_handle h, const void* q, const void* subkeys, float* sc
         return fail(SDM_ERR_INVALID_ARG, "sdm_score: NULL pointer");
     if (!aligned16(q) || !aligned16(subkeys) || !aligned4(scores))
         return fail(SDM_ERR_INVALID_ARG, "sdm_score: q and subkeys must be 16-byte aligned");
-    return run_score(h, q, subkeys, scores);
+    return run_score(h, q, subkeys, scores, all_rows(h->cfg), h->stream, true);
 }
 
 sdm_status sdm_select(sdm_handle h, const float* scores, int32_t* idx, float* wt)
@@ -316,7 +421,7 @@ sdm_status sdm_select(sdm_handle h, const float* scores, int32_t* idx, float* wt
         return fail(SDM_ERR_INVALID_ARG, "sdm_select: NULL pointer");
     if (!aligned4(scores) || !aligned4(idx) || !aligned4(wt))
         return fail(SDM_ERR_INVALID_ARG, "sdm_select: pointers must be 4-byte aligned");
-    return run_select(h, scores, idx, wt);
+    return run_select(h, scores, idx, wt, all_rows(h->cfg), h->stream);
 }
 
 sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t* idx, float* wt)
@@ -328,8 +433,8 @@ sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t
         return fail(SDM_ERR_INVALID_ARG, "sdm_address: NULL pointer");
     if (!aligned16(q) || !aligned16(subkeys) || !aligned4(idx) || !aligned4(wt))
         return fail(SDM_ERR_INVALID_ARG, "sdm_address: misaligned pointer");
-    s = run_score(h, q, subkeys, h->scores);
-    return s != SDM_OK ? s : run_select(h, h->scores, idx, wt);
+    s = run_score(h, q, subkeys, h->scores, all_rows(h->cfg), h->stream, true);
+    return s != SDM_OK ? s : run_select(h, h->scores, idx, wt, all_rows(h->cfg), h->stream);
 }
 
 sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
@@ -344,7 +449,12 @@ sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, 
     if (!aligned16(v) || !aligned16(mem_inout) || !aligned16(out) || !aligned4(idx_w) || !aligned4(wt_w) ||
         !aligned4(idx_r) || !aligned4(wt_r) || !aligned4(alpha) || !aligned4(beta))
         return fail(SDM_ERR_INVALID_ARG, "sdm_scan_with: misaligned pointer");
-    return run_scan(h, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem_inout, out);
+    for (int ci = 0; ci < h->ck.C && s == SDM_OK; ++ci) {
+        s = run_plan(h, ci, idx_w, wt_w, idx_r, wt_r, alpha, beta, h->stream);
+        if (s == SDM_OK)
+            s = run_scan(h, ci, v, mem_inout, out, h->stream);
+    }
+    return s;
 }
 
 sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
@@ -358,15 +468,34 @@ sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void*
     if (!aligned16(wq) || !aligned16(rq) || !aligned16(v) || !aligned16(subkeys) || !aligned16(mem_inout) ||
         !aligned16(out) || !aligned4(alpha) || !aligned4(beta))
         return fail(SDM_ERR_INVALID_ARG, "sdm_forward: misaligned pointer");
-    const void* q[2] = {wq, rq};
-    for (int set = 0; set < 2; ++set) {
-        s = run_score(h, q[set], subkeys, h->scores);
-        if (s == SDM_OK)
-            s = run_select(h, h->scores, h->idx[set], h->wt[set]);
+    if (h->ck.C == 1) {
+        s = run_chunk_front(h, 0, wq, rq, alpha, beta, subkeys, h->stream);
+        return s == SDM_OK ? run_scan(h, 0, v, mem_inout, out, h->stream) : s;
+    }
+    // Chunked: the addressing and plan of every chunk go to the aux stream in
+    // order, after whatever the caller's stream holds before this call (its
+    // inputs, and earlier calls' scans of the plans about to be rewritten); the
+    // scan of chunk c waits for its plan on the caller's stream, so chunk c + 1's
+    // addressing runs while chunk c scans.
+    hipError_t e = hipEventRecord(h->e_start, h->stream);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(h->aux, h->e_start, 0);
+    if (e != hipSuccess)
+        return hip_fail(e, "stream ordering");
+    for (int ci = 0; ci < h->ck.C; ++ci) {
+        s = run_chunk_front(h, ci, wq, rq, alpha, beta, subkeys, h->aux);
+        if (s != SDM_OK)
+            return s;
+        e = hipEventRecord(h->e_plan[ci], h->aux);
+        if (e == hipSuccess)
+            e = hipStreamWaitEvent(h->stream, h->e_plan[ci], 0);
+        if (e != hipSuccess)
+            return hip_fail(e, "stream ordering");
+        s = run_scan(h, ci, v, mem_inout, out, h->stream);
         if (s != SDM_OK)
             return s;
     }
-    return run_scan(h, h->idx[0], h->wt[0], h->idx[1], h->wt[1], v, alpha, beta, mem_inout, out);
+    return SDM_OK;
 }
 
 sdm_status sdm_set_timing(sdm_handle h, int enable)

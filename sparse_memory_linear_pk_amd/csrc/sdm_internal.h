@@ -50,15 +50,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // launchers (all asynchronous on `stream`; they return the launch status)
 // ---------------------------------------------------------------------------
 
-// Half scores of the rows of q ([rows_per_head * H, dk], row r belongs to head r % H)
-// against subkeys [H, 2, S, dh]: scores [rows, 2, S] float32.  frag: workspace of
-// pk_score_frag_bytes for the bf16 path's rearranged sub-key tables.
+// Rows of a call.  The per-token tensors are [B, Ts, H, ...]; a launch covers the
+// Tc tokens t0 .. t0 + Tc - 1 of every sequence (a chunk of the call, or all of
+// it with Tc = Ts, t0 = 0).  Row (b, t, h) is (b * Ts + t) * H + h.
+struct Rows {
+    int B, H, Tc, Ts, t0;
+    __host__ __device__ long count() const { return (long)B * Tc * H; }
+};
+
+// Sub-key tables [H, 2, S, dh] (bf16) rearranged into MFMA operand order in
+// frag (pk_score_frag_bytes); pk_score's bf16 path reads them from there.
 size_t pk_score_frag_bytes(int H, int S, int dh);
-hipError_t launch_pk_score(const void* q, const void* subkeys, void* frag, float* scores, long rows_per_head, int H,
+hipError_t launch_pk_subkey_frag(const void* subkeys, void* frag, int H, int S, int dh, hipStream_t stream);
+
+// Half scores of the rows of q ([B, Ts, H, dk]) against subkeys [H, 2, S, dh]
+// (float32 inputs) or frag (bf16 inputs): scores [B*Ts*H, 2, S] float32, only the
+// covered rows written.
+hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag, float* scores, const Rows& r,
                            int S, int dh, bool in_bf16, hipStream_t stream);
 
-// Per-half top-k, outer-sum top-W and softmax weights for `rows` rows of scores.
-hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, long rows, int S, int k, int W,
+// Per-half top-k, outer-sum top-W and softmax weights of the covered rows:
+// scores [B*Ts*H, 2, S] -> idx, wt [B*Ts*H, W].
+hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
                           hipStream_t stream);
 
 // Staged scan (float32 state): constants shared by its plan and its kernel.
@@ -103,17 +116,22 @@ bool plan_scan(int B, int H, int T, int d, int W, long N, bool state_bf16, bool 
 // tokens past T are sentinels that read nothing and store nothing), then a
 // header (alpha, beta, byte offset of the token's v row, of its out row).
 size_t plan_bytes(const ScanPlan& p, int B, int H, int T, int W);
+// idx/wt [B*Ts*H, W] and alpha/beta [B, Ts, H] are read at the covered rows; the
+// plan describes the Tc tokens of the chunk, whose v and out rows it names
+// relative to token t0.
 hipError_t launch_sdm_plan(const ScanPlan& p, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
-                           const float* wt_r, const float* alpha, const float* beta, void* plan, int B, int T,
-                           int H, int W, int d, long N, bool in_bf16, hipStream_t stream);
+                           const float* wt_r, const float* alpha, const float* beta, void* plan, const Rows& r,
+                           int W, int d, long N, bool in_bf16, hipStream_t stream);
 
+// One chunk's scan: T tokens per memory (the chunk length); v and out point at
+// token t0 of sequence 0 and advance Ts tokens per sequence.
 struct ScanArgs {
     const uint4* plan;  // records (either format)
     const float2* ab;   // register-ring format: [B*H, T] (alpha, beta)
     const void* v;
     void* mem;
     float* out;
-    int B, T, H, d, W, Tp;
+    int B, T, Ts, H, d, W, Tp;
     long N;
 };
 

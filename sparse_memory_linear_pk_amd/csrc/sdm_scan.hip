@@ -76,6 +76,7 @@ struct PlanArgs {
     uint4* plan;
     float2* ab;        // register-ring format only
     int T, H, W, d, Tp;
+    int Ts, t0;        // tokens per sequence of idx, wt, alpha, beta; the chunk's first token
     uint32_t N;        // slots per memory (the staged sentinel slot id)
     uint32_t v_bytes;  // bytes of one value element (staged header offsets)
 };
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
         const int t = lo + tt;
         int key = 0x7FFFFFFF, pos = lane;
         if (lane < W)
-            key = a.idx_w[((long)(b * T + t) * H + h) * W + lane];
+            key = a.idx_w[((long)b * a.Ts + a.t0 + t) * H * W + (long)h * W + lane];
         if (lane < W) {
             const uint32_t f = filter_bit(key);
             atomicOr(&s_filter[f >> 5], 1u << (f & 31u));
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
         __syncthreads();
     } else {
         for (int t = t0 + (int)threadIdx.x; t < t1; t += blockDim.x) {
-            const long o = (long)(b * T + t) * H + h;
+            const long o = ((long)b * a.Ts + a.t0 + t) * H + h;
             a.ab[(long)bh * T + t] = make_float2(a.alpha[o], a.beta[o]);
         }
     }
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
         const int t = t0 + it / per_tok, i = it % per_tok;
         uint4 rec;
         if (STAGED && i == staged::kPos) { // header
-            const long o = (long)(b * T + t) * H + h;
+            const long o = ((long)b * a.Ts + a.t0 + t) * H + h;
             const uint32_t row = (uint32_t)(t * H + h) * (uint32_t)a.d;
             const bool real = t < T;
             rec.x = real ? __float_as_uint(a.alpha[o]) : 0u;
@@ -190,7 +191,7 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
         } else if (STAGED && (t >= T || i >= W)) { // sentinel: slot past the memory, no store, weight 0
             rec = make_uint4(a.N | (1u << 31), a.N, 0u, 0u);
         } else {
-            const long o = ((long)(b * T + t) * H + h) * W + i;
+            const long o = (((long)b * a.Ts + a.t0 + t) * H + h) * W + i;
             const int n = a.idx_w[o], m = a.idx_r[o];
             uint32_t fw = 0, fr = 0, skip = 0;
             // the filter holds every slot written in [lo, hi): a slot outside it
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(RW == 2 ? 256 : 64) void sdm_scan_kernel(ScanArgs a
     const __amdgpu_buffer_rsrc_t r_plan = make_rsrc(a.plan + (size_t)bh * T * W, (uint32_t)((size_t)T * W * 16));
     const __amdgpu_buffer_rsrc_t r_ab = make_rsrc(a.ab + (size_t)bh * T, (uint32_t)((size_t)T * 8));
     // v, out: [B, T, H, d]; each resource spans sequence b
-    const size_t tok0 = (size_t)b * T * H;
+    const size_t tok0 = (size_t)b * a.Ts * H;
     const __amdgpu_buffer_rsrc_t r_v = make_rsrc(static_cast<const VT*>(a.v) + tok0 * d,
                                                  (uint32_t)((size_t)T * H * d * sizeof(VT)));
     const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + tok0 * d, (uint32_t)((size_t)T * H * d * 4));
@@ -743,9 +744,10 @@ size_t plan_bytes(const ScanPlan& p, int B, int H, int T, int W)
 }
 
 hipError_t launch_sdm_plan(const ScanPlan& p, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
-                           const float* wt_r, const float* alpha, const float* beta, void* plan, int B, int T,
-                           int H, int W, int d, long N, bool in_bf16, hipStream_t stream)
+                           const float* wt_r, const float* alpha, const float* beta, void* plan, const Rows& r,
+                           int W, int d, long N, bool in_bf16, hipStream_t stream)
 {
+    const int B = r.B, H = r.H, T = r.Tc;
     PlanArgs a;
     a.idx_w = idx_w;
     a.wt_w = wt_w;
@@ -756,6 +758,8 @@ hipError_t launch_sdm_plan(const ScanPlan& p, const int32_t* idx_w, const float*
     a.plan = static_cast<uint4*>(plan);
     a.ab = p.staged ? nullptr : reinterpret_cast<float2*>(a.plan + (size_t)B * H * T * W);
     a.T = T;
+    a.Ts = r.Ts;
+    a.t0 = r.t0;
     a.H = H;
     a.W = W;
     a.d = d;

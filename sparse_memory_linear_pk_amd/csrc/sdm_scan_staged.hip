@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
                                                    N * row_bytes);
     const __amdgpu_buffer_rsrc_t r_plan = make_rsrc(a.plan + (size_t)bh * a.Tp * kRecs,
                                                     (uint32_t)a.Tp * kRecs * 16u);
-    const size_t tok0 = (size_t)b * T * H;
+    const size_t tok0 = (size_t)b * a.Ts * H;
     const __amdgpu_buffer_rsrc_t r_v = make_rsrc(static_cast<const VT*>(a.v) + tok0 * d, tok_bytes * sizeof(VT));
     const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + tok0 * d, tok_bytes * 4u);
 
