@@ -37,45 +37,59 @@ struct TimedLaunch {
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// A forward runs its scan in chunks of kChunkTokens tokens; the addressing and
-// the plan of chunk c + 1 run on a second stream while chunk c scans.
-constexpr int kChunkTokens = 2048;
+// A forward longer than kChunk tokens runs its scan in chunks: a first one of
+// kChunk / 2 tokens, then kChunk each, the last taking any remainder shorter
+// than kChunk / 2.  The addressing and plan of chunk c + 1 run on a second
+// stream while chunk c scans (under a running scan they take about a third of
+// the scan's time per token), so only the first, short chunk's preparation is
+// exposed.
+constexpr int kChunk = 2048;
 
 struct Chunking {
-    int Tc; // tokens per chunk (the last may be shorter)
-    int C;  // chunks
-    int len(const sdm_config& c, int ci) const { return ci + 1 < C ? Tc : c.T - (C - 1) * Tc; }
+    std::vector<int> start; // first token of each chunk, then T
+    int C() const { return (int)start.size() - 1; }
+    int t0(int ci) const { return start[ci]; }
+    int len(int ci) const { return start[ci + 1] - start[ci]; }
 };
 
 Chunking chunking_of(const sdm_config& c)
 {
     Chunking k;
-    k.Tc = c.T <= kChunkTokens ? c.T : kChunkTokens;
-    k.C = (c.T + k.Tc - 1) / k.Tc;
-    return k;
+    k.start.push_back(0);
+    int t = c.T <= kChunk ? c.T : kChunk / 2;
+    while (true) {
+        if (c.T - t < kChunk / 2)
+            t = c.T;
+        k.start.push_back(t);
+        if (t == c.T)
+            return k;
+        t += kChunk < c.T - t ? kChunk : c.T - t;
+    }
 }
 
 struct Layout {
-    size_t scores, idx, wt, plan_region, plan, frag, total;
+    size_t scores, idx, wt, plan, frag, total;
+    std::vector<size_t> plan_off; // byte offset of each chunk's plan
 };
 
-Layout layout_of(const sdm_config& c, const Chunking& k, const sdm::ScanPlan& full, const sdm::ScanPlan& last)
+Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::ScanPlan>& plans)
 {
     const size_t rows = (size_t)c.B * c.T * c.H;
     Layout L;
     L.scores = align_up(rows * 2 * (size_t)c.n_sub * sizeof(float));
     L.idx = align_up(rows * (size_t)c.W * sizeof(int32_t));
     L.wt = align_up(rows * (size_t)c.W * sizeof(float));
-    const size_t pf = sdm::plan_bytes(full, c.B, c.H, k.Tc, c.W);
-    const size_t pl = sdm::plan_bytes(last, c.B, c.H, k.len(c, k.C - 1), c.W);
-    L.plan_region = align_up(pf > pl ? pf : pl);
-    L.plan = L.plan_region * k.C;
+    L.plan = 0;
+    for (int ci = 0; ci < k.C(); ++ci) {
+        L.plan_off.push_back(L.plan);
+        L.plan += align_up(sdm::plan_bytes(plans[ci], c.B, c.H, k.len(ci), c.W));
+    }
     L.frag = align_up(sdm::pk_score_frag_bytes(c.H, c.n_sub, c.dk / 2));
     L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag;
     return L;
 }
 
-sdm_status check_config(const sdm_config* c, sdm::ScanPlan* plan, sdm::ScanPlan* plan_last)
+sdm_status check_config(const sdm_config* c, std::vector<sdm::ScanPlan>* plans)
 {
     if (!c)
         return fail(SDM_ERR_INVALID_ARG, "config is NULL");
@@ -114,10 +128,11 @@ sdm_status check_config(const sdm_config* c, sdm::ScanPlan* plan, sdm::ScanPlan*
         return fail(SDM_ERR_UNSUPPORTED, "B*T*H=%ld rows is too many", (long)c->B * c->T * c->H);
     const Chunking k = chunking_of(*c);
     const long N = (long)c->n_sub * c->n_sub;
-    if (!sdm::plan_scan(c->B, c->H, k.Tc, c->d, c->W, N, c->state_dtype == SDM_BF16, c->in_dtype == SDM_BF16, plan) ||
-        !sdm::plan_scan(c->B, c->H, k.len(*c, k.C - 1), c->d, c->W, N, c->state_dtype == SDM_BF16,
-                        c->in_dtype == SDM_BF16, plan_last))
-        return fail(SDM_ERR_UNSUPPORTED, "no scan layout for d=%d W=%d", c->d, c->W);
+    plans->assign(k.C(), sdm::ScanPlan{});
+    for (int ci = 0; ci < k.C(); ++ci)
+        if (!sdm::plan_scan(c->B, c->H, k.len(ci), c->d, c->W, N, c->state_dtype == SDM_BF16, c->in_dtype == SDM_BF16,
+                            &(*plans)[ci]))
+            return fail(SDM_ERR_UNSUPPORTED, "no scan layout for d=%d W=%d", c->d, c->W);
     return SDM_OK;
 }
 
@@ -135,7 +150,7 @@ struct sdm_ctx {
     std::vector<hipEvent_t> e_plan; // chunk c's plan is written
     int device;
     Chunking ck;
-    sdm::ScanPlan plan, plan_last; // scan layout of a full chunk and of the last chunk
+    std::vector<sdm::ScanPlan> plans; // scan layout of each chunk
     void* block;
     Layout L;
     float* scores;
@@ -187,7 +202,7 @@ sdm::Rows all_rows(const sdm_config& c) { return sdm::Rows{c.B, c.H, c.T, c.T, 0
 sdm::Rows chunk_rows(const sdm_ctx* h, int ci)
 {
     const sdm_config& c = h->cfg;
-    return sdm::Rows{c.B, c.H, h->ck.len(c, ci), c.T, ci * h->ck.Tc};
+    return sdm::Rows{c.B, c.H, h->ck.len(ci), c.T, h->ck.t0(ci)};
 }
 
 // frag: rearrange the sub-key tables first (once per call that scores)
@@ -213,11 +228,11 @@ sdm_status run_select(sdm_ctx* h, const float* scores, int32_t* idx, float* wt, 
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_topk launch");
 }
 
-const sdm::ScanPlan& plan_of(const sdm_ctx* h, int ci) { return ci + 1 < h->ck.C ? h->plan : h->plan_last; }
+const sdm::ScanPlan& plan_of(const sdm_ctx* h, int ci) { return h->plans[ci]; }
 
 uint4* plan_region(const sdm_ctx* h, int ci)
 {
-    return reinterpret_cast<uint4*>(reinterpret_cast<char*>(h->plan_buf) + (size_t)ci * h->L.plan_region);
+    return reinterpret_cast<uint4*>(reinterpret_cast<char*>(h->plan_buf) + h->L.plan_off[ci]);
 }
 
 sdm_status run_plan(sdm_ctx* h, int ci, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
@@ -291,13 +306,13 @@ const char* sdm_last_error(void) { return g_err; }
 
 sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes)
 {
-    sdm::ScanPlan plan, plan_last;
-    sdm_status s = check_config(cfg, &plan, &plan_last);
+    std::vector<sdm::ScanPlan> plans;
+    sdm_status s = check_config(cfg, &plans);
     if (s != SDM_OK)
         return s;
     if (!bytes)
         return fail(SDM_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = layout_of(*cfg, chunking_of(*cfg), plan, plan_last).total;
+    *bytes = layout_of(*cfg, chunking_of(*cfg), plans).total;
     return SDM_OK;
 }
 
@@ -307,8 +322,8 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     if (!out)
         return fail(SDM_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
-    sdm::ScanPlan plan, plan_last;
-    sdm_status s = check_config(cfg, &plan, &plan_last);
+    std::vector<sdm::ScanPlan> plans;
+    sdm_status s = check_config(cfg, &plans);
     if (s != SDM_OK)
         return s;
     int dev = 0;
@@ -321,10 +336,9 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->cfg = *cfg;
     h->stream = (hipStream_t)hip_stream;
     h->device = dev;
-    h->plan = plan;
-    h->plan_last = plan_last;
+    h->plans = plans;
     h->ck = chunking_of(*cfg);
-    h->L = layout_of(*cfg, h->ck, plan, plan_last);
+    h->L = layout_of(*cfg, h->ck, plans);
     h->aux = nullptr;
     h->e_start = nullptr;
     h->timing = false;
@@ -347,12 +361,12 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->plan_buf = (uint4*)p;
     p += h->L.plan;
     h->frag = p;
-    if (h->ck.C > 1) {
+    if (h->ck.C() > 1) {
         e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&h->e_start, hipEventDisableTiming);
-        h->e_plan.assign(h->ck.C, nullptr);
-        for (int ci = 0; ci < h->ck.C && e == hipSuccess; ++ci)
+        h->e_plan.assign(h->ck.C(), nullptr);
+        for (int ci = 0; ci < h->ck.C() && e == hipSuccess; ++ci)
             e = hipEventCreateWithFlags(&h->e_plan[ci], hipEventDisableTiming);
         if (e != hipSuccess) {
             for (hipEvent_t ev : h->e_plan)
@@ -449,7 +463,7 @@ sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, 
     if (!aligned16(v) || !aligned16(mem_inout) || !aligned16(out) || !aligned4(idx_w) || !aligned4(wt_w) ||
         !aligned4(idx_r) || !aligned4(wt_r) || !aligned4(alpha) || !aligned4(beta))
         return fail(SDM_ERR_INVALID_ARG, "sdm_scan_with: misaligned pointer");
-    for (int ci = 0; ci < h->ck.C && s == SDM_OK; ++ci) {
+    for (int ci = 0; ci < h->ck.C() && s == SDM_OK; ++ci) {
         s = run_plan(h, ci, idx_w, wt_w, idx_r, wt_r, alpha, beta, h->stream);
         if (s == SDM_OK)
             s = run_scan(h, ci, v, mem_inout, out, h->stream);
@@ -468,7 +482,7 @@ sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void*
     if (!aligned16(wq) || !aligned16(rq) || !aligned16(v) || !aligned16(subkeys) || !aligned16(mem_inout) ||
         !aligned16(out) || !aligned4(alpha) || !aligned4(beta))
         return fail(SDM_ERR_INVALID_ARG, "sdm_forward: misaligned pointer");
-    if (h->ck.C == 1) {
+    if (h->ck.C() == 1) {
         s = run_chunk_front(h, 0, wq, rq, alpha, beta, subkeys, h->stream);
         return s == SDM_OK ? run_scan(h, 0, v, mem_inout, out, h->stream) : s;
     }
@@ -482,7 +496,7 @@ sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void*
         e = hipStreamWaitEvent(h->aux, h->e_start, 0);
     if (e != hipSuccess)
         return hip_fail(e, "stream ordering");
-    for (int ci = 0; ci < h->ck.C; ++ci) {
+    for (int ci = 0; ci < h->ck.C(); ++ci) {
         s = run_chunk_front(h, ci, wq, rq, alpha, beta, subkeys, h->aux);
         if (s != SDM_OK)
             return s;

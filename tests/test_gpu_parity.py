@@ -209,6 +209,53 @@ def test_chunked_calls_are_bitwise_equal(T):
     assert np.array_equal(to_host(mem), g["mem"])
 
 
+# Forwards longer than 2048 tokens scan in several launches (512, 2048, ...
+# tokens) while the next chunk's addressing runs on a second stream.
+CHUNKED = {
+    "f32_state_f32_in": _edge(T=2600, B=2, H=2, d=32, S=32, k=6, W=16),
+    "f32_state_bf16_in": _edge(T=2700, B=1, H=3, d=64, S=48, k=8, W=24, in_bf16=True),
+    "bf16_state": _edge(T=2600, B=2, H=1, d=64, S=32, k=6, W=16, in_bf16=True, state_bf16=True),
+}
+
+
+@pytest.mark.parametrize("name", list(CHUNKED))
+def test_chunked_forward_parity(orc, T, name):
+    """Every row and element of a forward that the library splits into chunks,
+    with queries that repeat across the chunk boundaries (slots written just
+    before a boundary are read and rewritten just after it)."""
+    cfg = CHUNKED[name]
+    x = gi.make_inputs(cfg)
+    rng = np.random.default_rng(11)
+    pats = x["wq"][:, :6].copy()
+    for t0 in (500, 512, 2555, 2560):
+        if t0 + 24 <= cfg.T:
+            x["wq"][:, t0:t0 + 24] = pats[:, rng.integers(0, 6, 24)]
+            x["rq"][:, t0:t0 + 24] = pats[:, rng.integers(0, 6, 24)]
+    say(f"[chunked {name}] {cfg}")
+    g = run_gpu(T, cfg, x)
+    full_parity(orc, cfg, x, g, f"chunked {name}")
+
+
+def test_chunked_forward_is_bitwise_one_launch_per_call(T):
+    """The library's chunking changes no bit: one forward of 2600 tokens equals
+    two forwards of 1300 (each scanned in a single launch)."""
+    from sparse_memory_linear_pk_amd import SDM
+    cfg = CHUNKED["f32_state_bf16_in"].replace(T=2600)
+    x = gi.make_inputs(cfg)
+    g = run_gpu(T, cfg, x, stages=False)
+    mem = to_dev(x["mem0"])
+    outs = []
+    for sl in (slice(0, 1300), slice(1300, 2600)):
+        c = cfg.replace(T=sl.stop - sl.start)
+        xs = {k: to_dev(np.ascontiguousarray(v[:, sl])) for k, v in x.items() if k in ("wq", "rq", "v", "alpha", "beta")}
+        out = T.empty((c.B, c.T, c.H, c.d), dtype=T.float32, device="cuda")
+        with SDM.from_config(c) as layer:
+            layer.forward(xs["wq"], xs["rq"], xs["v"], xs["alpha"], xs["beta"], to_dev(x["subkeys"]), mem, out)
+        outs.append(to_host(out))
+    assert np.array_equal(np.concatenate(outs, axis=1), g["out"])
+    assert np.array_equal(to_host(mem), g["mem"])
+
+
 def test_permuted_elements_are_bitwise_permuted(T):
     cfg = gi.config(1, T=40, B=1, H=2)
     x = gi.make_inputs(cfg)
