@@ -118,4 +118,55 @@ __device__ __forceinline__ float reduce4_to_rows(float v0, float v1, float v2, f
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// The float whose nearest-even bf16 rounding is that of the double x (one
+// rounding of x to bf16).  x rounds to float
+// first; that can only go wrong when the float lands exactly on a bf16 tie while
+// x was not on it, and then moving the float one ulp towards x settles the tie
+// the way x lies (rounding is monotone and the bf16 tie is a float value).
+__device__ __forceinline__ float settle_bf16_tie(double x)
+{
+    const float f = (float)x;
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0xFFFFu) == 0x8000u) {
+        const double fd = (double)f;
+        if (fd != x)
+            u = (__builtin_fabs(fd) > __builtin_fabs(x)) ? u - 1u : u + 1u;
+    }
+    return __uint_as_float(u);
+}
+
+// reduce4_to_rows for doubles: the same tree, the permlane swaps applied to
+// both 32-bit halves of every value.
+__device__ __forceinline__ void swap_rows_d(double a, double b, bool rows32, double& x, double& y)
+{
+    const uint64_t ua = (uint64_t)__double_as_longlong(a), ub = (uint64_t)__double_as_longlong(b);
+    uint32_t xl, yl, xh, yh;
+    if (rows32) {
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)ua, (uint32_t)ub, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32), false, false);
+        xl = lo[0]; yl = lo[1]; xh = hi[0]; yh = hi[1];
+    } else {
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)ua, (uint32_t)ub, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32), false, false);
+        xl = lo[0]; yl = lo[1]; xh = hi[0]; yh = hi[1];
+    }
+    x = __longlong_as_double((long long)(((uint64_t)xh << 32) | xl));
+    y = __longlong_as_double((long long)(((uint64_t)yh << 32) | yl));
+}
+
+__device__ __forceinline__ double reduce4_to_rows(double v0, double v1, double v2, double v3)
+{
+    v0 = bfly<8>(v0);
+    v1 = bfly<8>(v1);
+    v2 = bfly<8>(v2);
+    v3 = bfly<8>(v3);
+    double a, b;
+    swap_rows_d(v0, v1, false, a, b);
+    const double t01 = a + b; // rows 0,2: v0; rows 1,3: v1
+    swap_rows_d(v2, v3, false, a, b);
+    const double t23 = a + b; // rows 0,2: v2; rows 1,3: v3
+    swap_rows_d(t01, t23, true, a, b);
+    return a + b;
+}
+
 } // namespace sdm

@@ -74,7 +74,7 @@ hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag,
 hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
                           hipStream_t stream);
 
-// Staged scan (float32 state): constants shared by its plan and its kernel.
+// Staged scan: constants shared by its plan and its kernel.
 // The kernel steps through tokens in pairs; the slot reads of a pair are issued
 // two pairs ahead, its plan records four pairs ahead.
 namespace staged {
@@ -96,7 +96,7 @@ static_assert(kRing * kPos + 1 <= 1024, "forwarding source field");
 
 // Launch geometry of the scan, chosen once per shape.
 struct ScanPlan {
-    bool staged;   // staged kernel (float32 state) or the register-ring kernel
+    bool staged;   // staged kernel (128-byte segments) or the register-ring kernel
     int lps;       // lanes sharing one slot chunk (16 bytes each)
     int rw;        // slot positions per lane
     int waves;     // waves per workgroup
@@ -137,7 +137,8 @@ struct ScanArgs {
 
 hipError_t launch_sdm_scan(const ScanArgs& a, const ScanPlan& plan, bool state_bf16, bool in_bf16,
                            hipStream_t stream);
-hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& plan, bool in_bf16, hipStream_t stream);
+hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& plan, bool state_bf16, bool in_bf16,
+                                  hipStream_t stream);
 
 // Measurement only: the scan's traffic pattern without arithmetic on `memories`
 // memories of `rows` rows of row_bytes (a multiple of 128) bytes.

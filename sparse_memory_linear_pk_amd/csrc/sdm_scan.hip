@@ -233,22 +233,6 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
 // the scan
 // ---------------------------------------------------------------------------
 
-// bf16 bits of the double x rounded once to nearest-even.  x rounds to float
-// first; that can only go wrong when the float lands exactly on a bf16 tie while
-// x was not on it, and then moving the float one ulp towards x settles the tie
-// the way x lies (rounding is monotone and the bf16 tie is a float value).
-__device__ __forceinline__ float settle_bf16_tie(double x)
-{
-    const float f = (float)x;
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0xFFFFu) == 0x8000u) {
-        const double fd = (double)f;
-        if (fd != x)
-            u = (__builtin_fabs(fd) > __builtin_fabs(x)) ? u - 1u : u + 1u;
-    }
-    return __uint_as_float(u);
-}
-
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b)
 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t)); // v_cvt_pk_bf16_f32
@@ -696,15 +680,16 @@ bool plan_scan(int B, int H, int T, int d, int W, long N, bool state_bf16, bool 
 {
     const long units = (long)B * H;
     const uint64_t v_bytes = in_bf16 ? 2 : 4;
-    if (!state_bf16 && d % 32 == 0 && W <= staged::kPos && N < (1l << staged::kSlotBits) &&
-        (uint64_t)(N + 1) * d * 4 <= (1ull << 32) && ((uint64_t)T * H + 1) * d * 4 <= (1ull << 32) &&
+    const uint64_t s_bytes = state_bf16 ? 2 : 4;
+    if ((d * s_bytes) % 128 == 0 && W <= staged::kPos && N < (1l << staged::kSlotBits) &&
+        (uint64_t)(N + 1) * d * s_bytes <= (1ull << 32) && ((uint64_t)T * H + 1) * d * 4 <= (1ull << 32) &&
         ((uint64_t)T * H + 1) * d * v_bytes <= (1ull << 32)) {
         plan->staged = true;
         plan->lps = 8;
         plan->rw = 2;
         plan->waves = 4;
         plan->lookahead = staged::kP;
-        plan->grid = (int)(units * (d / 32));
+        plan->grid = (int)(units * (d * s_bytes / 128));
         plan->lds = 0;
         // pairs run from S0 to the pair after the one holding T-1; each loads the
         // records of the pair four ahead
@@ -782,7 +767,7 @@ hipError_t launch_sdm_scan(const ScanArgs& a, const ScanPlan& plan, bool state_b
                            hipStream_t stream)
 {
     if (plan.staged)
-        return launch_sdm_scan_staged(a, plan, in_bf16, stream);
+        return launch_sdm_scan_staged(a, plan, state_bf16, in_bf16, stream);
     if (state_bf16)
         return in_bf16 ? launch_typed<uint16_t, uint16_t>(a, plan, stream) : launch_typed<uint16_t, float>(a, plan, stream);
     return in_bf16 ? launch_typed<float, uint16_t>(a, plan, stream) : launch_typed<float, float>(a, plan, stream);

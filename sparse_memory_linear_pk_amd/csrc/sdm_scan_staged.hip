@@ -1,4 +1,5 @@
-// sdm_scan, staged form: the memory scan of the SDM layer for a float32 state.
+// sdm_scan, staged form: the memory scan of the SDM layer for a float32 or a
+// bf16 state.
 //
 // Per token t of memory (b, h), with write slots n_i, weights w_i, decay alpha,
 // step beta, value v and read slots m_j, weights r_j (SDM blog post, section
@@ -6,13 +7,17 @@
 // to end"):
 //   x_i = alpha * M[n_i];  vhat = sum_i w_i x_i;  M[n_i] = x_i + w_i * beta * (v - vhat)
 //   out = sum_j r_j * M[m_j]                     (after the write of the same token)
+// A float32 state is updated in float32.  A bf16 state is updated in double
+// and rounded once, to nearest-even, when a slot is stored (every stored value
+// is then the correctly rounded exact result, as the double reference has it);
+// the read sees the stored values and sums in float32.
 //
-// Work split.  A workgroup of 4 waves owns one (b, h) and 32 consecutive slot
-// elements (128 bytes of every slot row) and walks all T tokens.  A token's 64
-// positions (the W selected slots, padded with sentinels) spread over the waves,
-// 16 each: lane (g, e) of wave w holds elements 4e..4e+3 of positions
-// 16w + g and 16w + 8 + g.  Sums over positions are a transposing reduction
-// inside the wave and one LDS exchange across the waves.
+// Work split.  A workgroup of 4 waves owns one (b, h) and 128 bytes of every
+// slot row (32 float32 or 64 bf16 elements) and walks all T tokens.  A token's
+// 64 positions (the W selected slots, padded with sentinels) spread over the
+// waves, 16 each: lane (g, e) of wave w holds the 16 bytes e of positions
+// 16w + g and 16w + 8 + g (E = 4 or 8 elements).  Sums over positions are a
+// transposing reduction inside the wave and one LDS exchange across the waves.
 //
 // Pipeline.  Tokens go in pairs.  At the start of pair k: the read of pair k-1
 // (after its write), then the loads of pair k+2 (its slot rows and v into
@@ -24,10 +29,10 @@
 // flight per wave, enough to cover the memory latency at full bandwidth.
 //
 // Forwarding.  A slot written too recently for its load to see the store comes
-// from a ring of the values stored by the last 8 tokens, which the plan names;
+// from a ring of the values stored by the last 12 tokens, which the plan names;
 // such a slot is not loaded (its load reads past the buffer, zeros) and an
-// unforwarded slot names the ring's zero entry, so every read is the sum of a
-// register and one LDS load, without a branch.
+// unforwarded slot names the ring's zero entry, so a read is the sum of a
+// register and, when any lane of the wave forwards, one LDS load.
 //
 // Ordering.  Every wave issues the same vector-memory operations in the same
 // order for every pair (sentinel records and headers of the virtual tokens
@@ -46,16 +51,17 @@ using namespace staged;
 
 constexpr int kWaves = 4;
 constexpr int kRecPerWave = 17;                  // 16 records and the header
-constexpr int kEntryU4 = 8;                      // one slot chunk: 8 lanes x 16 bytes
+constexpr int kEntryU4 = 8;                      // one slot segment: 8 lanes x 16 bytes
+constexpr int kPartU4 = kWaves * 8 * 4;          // room for one token's partials ([wave][el][E], <= 8 doubles)
 
-__shared__ __attribute__((aligned(16))) uint4 g_ring[(kRing * kPos + 1) * kEntryU4]; // zero entry, stored chunks
+__shared__ __attribute__((aligned(16))) uint4 g_ring[(kRing * kPos + 1) * kEntryU4]; // zero entry, stored segments
 __shared__ __attribute__((aligned(16))) uint4 g_rec[kRecSlots * kWaves * kRecPerWave + kWaves]; // records, headers; a spare entry per wave
-__shared__ __attribute__((aligned(16))) float4 g_red[2 * kWaves * 8];               // write partials of a pair
-__shared__ __attribute__((aligned(16))) float4 g_ored[2 * kWaves * 8];              // read partials of a pair
+__shared__ __attribute__((aligned(16))) float4 g_red[2 * kPartU4];                  // write partials of a pair
+__shared__ __attribute__((aligned(16))) float4 g_ored[2 * kPartU4];                 // read partials of a pair
 static_assert(kStages == 6, "register rings of three pairs");
 
-// Ring chunk a record field names: entry f - 1 of the ring for f > 0, the zero
-// entry for f = 0 (then the staged chunk holds the value).
+// Ring entry a record field names: entry f - 1 of the ring for f > 0, the zero
+// entry for f = 0 (then the staged segment holds the value).
 __device__ __forceinline__ const uint4* ring_src(uint32_t field, const uint4* ring_lane)
 {
     return ring_lane + ((field >> kSlotBits) & 0x3FFu) * kEntryU4;
@@ -79,63 +85,126 @@ __device__ __forceinline__ void barrier_lds()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Totals over the 4 waves of the per-wave partials of element lane el (the same
-// order in every lane).
-__device__ __forceinline__ float4 sum_waves(const float4* part, int el)
+// The 16 bytes of state a lane owns in one slot segment: 4 float32 or 8 bf16
+// values, unpacked to float32 for the arithmetic and packed back with one
+// nearest-even rounding per value.
+template <class ST> struct Cell;
+template <> struct Cell<float> {
+    static constexpr int E = 4;
+    using CT = float; // type of the write arithmetic
+    __device__ static uint4 pack(const float (&x)[4])
+    {
+        return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
+    }
+    __device__ static void unpack(const uint4& u, float (&x)[4])
+    {
+        x[0] = __uint_as_float(u.x);
+        x[1] = __uint_as_float(u.y);
+        x[2] = __uint_as_float(u.z);
+        x[3] = __uint_as_float(u.w);
+    }
+};
+template <> struct Cell<uint16_t> {
+    static constexpr int E = 8;
+    using CT = double;
+    __device__ static void unpack(const uint4& u, float (&x)[8])
+    {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    }
+    // v_cvt_pk_bf16_f32: nearest-even, NaN stays a quiet NaN
+    __device__ static uint32_t pack2(float lo, float hi)
+    {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+    }
+    __device__ static uint4 pack(const double (&x)[8])
+    {
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            f[q] = settle_bf16_tie(x[q]);
+        return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
+    }
+};
+
+// Totals over the 4 waves of the per-wave partials ([wave][el][E] values of
+// type X) of element lane el, in the same order in every lane.
+template <int E, class X>
+__device__ __forceinline__ void sum_waves(const float4* part, int el, X (&t)[E])
 {
-    const float4 a = part[el], b = part[8 + el], c = part[16 + el], d = part[24 + el];
-    return make_float4((a.x + b.x) + (c.x + d.x), (a.y + b.y) + (c.y + d.y), (a.z + b.z) + (c.z + d.z),
-                       (a.w + b.w) + (c.w + d.w));
+    const X* p = reinterpret_cast<const X*>(part);
+#pragma unroll
+    for (int q = 0; q < E; ++q)
+        t[q] = (p[(0 * 8 + el) * E + q] + p[(1 * 8 + el) * E + q]) + (p[(2 * 8 + el) * E + q] + p[(3 * 8 + el) * E + q]);
 }
 
-__device__ __forceinline__ uint4 add4(const uint4& a, const uint4& b)
+// The wave's totals over its 8 lane groups of the E values of every lane, left
+// in part ([wave][el][E] values of type X); lanes l and l ^ 8 write the same.
+template <int E, class X>
+__device__ __forceinline__ void reduce_to_part(const X (&v)[E], float4* part, int wave, int el, int lane)
 {
-    return make_uint4(__float_as_uint(__uint_as_float(a.x) + __uint_as_float(b.x)),
-                      __float_as_uint(__uint_as_float(a.y) + __uint_as_float(b.y)),
-                      __float_as_uint(__uint_as_float(a.z) + __uint_as_float(b.z)),
-                      __float_as_uint(__uint_as_float(a.w) + __uint_as_float(b.w)));
+    X* p = reinterpret_cast<X*>(part);
+#pragma unroll
+    for (int c = 0; c < E / 4; ++c) {
+        // row r (lanes 16r .. 16r+15) ends with the total of value 4c + r
+        const X t = reduce4_to_rows(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+        p[(wave * 8 + el) * E + 4 * c + (lane >> 4)] = t;
+    }
 }
 
-template <class VT>
+// ST: state element (float or bf16 bits), VT: v element (float or bf16 bits).
+template <class ST, class VT>
 __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
 {
+    using C = Cell<ST>;
+    using CT = typename C::CT;                       // type of the write arithmetic
+    constexpr int E = C::E;                          // state elements per lane
+    constexpr int SEG = 128 / (int)sizeof(ST);       // state elements of a workgroup's segment
+    constexpr int VB = E * (int)sizeof(VT);          // bytes of v per lane and token: 8, 16 or 32
+    constexpr int NV = VB <= 16 ? 1 : 2;             // v loads per token
+    constexpr int NO = E / 4;                        // out stores per token (16 bytes each)
     constexpr int ZS = kStages, ZR = kRecSlots, ZL = 4;
-    // Vector-memory operations of a pair, in issue order: 12 loads at its start
-    // (per token of pair k+2 4 slot loads and v; the records of pair k+4), then 2
-    // out stores and 4 slot stores.  vmcnt(18) at the start of pair k leaves only
-    // pair k-1's operations in flight: pair k's data and pair k+2's records have
-    // landed and pair k-2's stores are done.
-    constexpr int K = 18;
+    // Vector-memory operations of a pair, in issue order: at its start the loads
+    // (per token of pair k+2 4 slot loads and NV of v; the records of pair k+4),
+    // then 2*NO out stores and 4 slot stores.  vmcnt(K) at the start of pair k
+    // leaves only pair k-1's operations in flight: pair k's data and pair k+2's
+    // records have landed and pair k-2's stores are done.
+    constexpr int K = 2 * (4 + NV) + 2 + 2 * NO + 4;
+    static_assert(K <= 63, "vmcnt");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int g = lane >> 3, el = lane & 7;
     const int T = a.T, H = a.H, d = a.d;
     const uint32_t N = (uint32_t)a.N;
-    const int nchunk = d >> 5;
+    const int nchunk = d / SEG;
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const int b = bh / H;
-    const uint32_t row_bytes = (uint32_t)d * 4u;
-    const uint32_t lane_off = (uint32_t)(chunk * 32 + el * 4) * 4u;
-    const uint32_t tok_bytes = (uint32_t)T * H * d;
+    const uint32_t row_bytes = (uint32_t)d * (uint32_t)sizeof(ST);
+    const uint32_t lane_off = (uint32_t)chunk * 128u + (uint32_t)el * 16u;
+    const uint32_t tok_elems = (uint32_t)T * H * d;
 
     const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * row_bytes,
                                                    N * row_bytes);
     const __amdgpu_buffer_rsrc_t r_plan = make_rsrc(a.plan + (size_t)bh * a.Tp * kRecs,
                                                     (uint32_t)a.Tp * kRecs * 16u);
     const size_t tok0 = (size_t)b * a.Ts * H;
-    const __amdgpu_buffer_rsrc_t r_v = make_rsrc(static_cast<const VT*>(a.v) + tok0 * d, tok_bytes * sizeof(VT));
-    const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + tok0 * d, tok_bytes * 4u);
+    const __amdgpu_buffer_rsrc_t r_v = make_rsrc(static_cast<const VT*>(a.v) + tok0 * d, tok_elems * sizeof(VT));
+    const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + tok0 * d, tok_elems * 4u);
 
     // positions of this lane
     const int pos0 = (wave * 2) * 8 + g, pos1 = pos0 + 8;
     const uint4* ring_lane = g_ring + el;   // the zero entry
-    uint4* ring_w = g_ring + kEntryU4 + el; // entry 0 of the stored chunks
+    uint4* ring_w = g_ring + kEntryU4 + el; // entry 0 of the stored segments
     // record loads: lane i < 16 fetches record 16w + i of a token, lane 16 the header
     const uint32_t rec_lane = lane < 16 ? (uint32_t)(16 * wave + lane) * 16u : (uint32_t)kPos * 16u;
-    const uint32_t v_lane = (uint32_t)(chunk * 32 + el * 4) * (uint32_t)sizeof(VT); // this lane's 4 values of v
-    // out: the 8 lanes of group 0 of one wave store 16 bytes each
-    const uint32_t o_lane = (uint32_t)(chunk * 32 + el * 4) * 4u;
+    const uint32_t elem0 = (uint32_t)(chunk * SEG + el * E);  // this lane's first element
+    const uint32_t v_lane = elem0 * (uint32_t)sizeof(VT);
+    const uint32_t o_lane = elem0 * 4u; // out: the 8 lanes of group 0 of one wave store E floats each
     // lanes >= 17 park their (unused) record load in the wave's spare entry; an
     // index into the one array (not a choice of pointers) keeps the compiler
     // certain that the store does not touch the stage buffers
@@ -145,7 +214,7 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     // Sentinels for the virtual tokens before 0: a slot past the memory, no
     // store, weight 0, nothing forwarded; gates 0 and v, out offsets past their buffers.
     const uint4 sent_rec = make_uint4(N | (1u << 31), N, 0u, 0u);
-    const uint4 sent_hdr = make_uint4(0u, 0u, tok_bytes * (uint32_t)sizeof(VT), tok_bytes * 4u);
+    const uint4 sent_hdr = make_uint4(0u, 0u, tok_elems * (uint32_t)sizeof(VT), tok_elems * 4u);
     const uint4 sent_lane = lane < 16 ? sent_rec : sent_hdr;
     if (lane < kRecPerWave) {
 #pragma unroll
@@ -160,16 +229,18 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     // Per-token state on its way through the pipeline, token t in [(t - S0) mod 6]
     // (records in [(t - S0) mod 4]):
     uint4 rl[ZL];          // record loads (lanes < 17), issued four pairs ahead, parked two pairs later
-    uint4 vr[ZS];          // this lane's values of v (bf16: the first 8 bytes), issued two pairs ahead
-    uint4 wset[ZS][2];     // its write slots' chunks (zero when forwarded), issued two pairs ahead
-    uint4 rset[ZS][2];     // its read slots' chunks (zero when forwarded), issued two pairs ahead
+    uint4 vr[ZS][NV];      // this lane's values of v (8 bytes: the first half), issued two pairs ahead
+    uint4 wset[ZS][2];     // its write slots' segments (zero when forwarded), issued two pairs ahead
+    uint4 rset[ZS][2];     // its read slots' segments (zero when forwarded), issued two pairs ahead
     uint32_t soff[ZS][2];  // store offsets of the write slots (past the memory: no store)
 #pragma unroll
     for (int z = 0; z < ZL; ++z)
         rl[z] = sent_lane;
 #pragma unroll
     for (int z = 0; z < ZS; ++z) {
-        vr[z] = zero4;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            vr[z][i] = zero4;
         wset[z][0] = wset[z][1] = rset[z][0] = rset[z][1] = zero4;
         soff[z][0] = soff[z][1] = kOOB;
     }
@@ -182,58 +253,83 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         hd = rw[16];
     };
 
-    // Write, first half: decay this lane's two slots (x) and leave the wave's share
-    // of the prediction in red.
-    auto partials = [&](const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float (&x0)[4],
-                        float (&x1)[4], float4* red) __attribute__((always_inline)) {
-        uint4 m0 = ws[0], m1 = ws[1];
-        if (forwards(r0.x, r1.x)) {
-            m0 = add4(m0, *ring_src(r0.x, ring_lane));
-            m1 = add4(m1, *ring_src(r1.x, ring_lane));
-        }
-        const float w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z);
-        x0[0] = alpha * __uint_as_float(m0.x); x0[1] = alpha * __uint_as_float(m0.y);
-        x0[2] = alpha * __uint_as_float(m0.z); x0[3] = alpha * __uint_as_float(m0.w);
-        x1[0] = alpha * __uint_as_float(m1.x); x1[1] = alpha * __uint_as_float(m1.y);
-        x1[2] = alpha * __uint_as_float(m1.z); x1[3] = alpha * __uint_as_float(m1.w);
-        float acc[4];
+    // The values of this lane's two slots: the staged segments plus, for a
+    // forwarded slot, its ring entry (one of the two is zero).
+    auto slot_values = [&](const uint4 (&ss)[2], uint32_t f0, uint32_t f1, float (&m0)[E], float (&m1)[E])
+        __attribute__((always_inline)) {
+        C::unpack(ss[0], m0);
+        C::unpack(ss[1], m1);
+        if (forwards(f0, f1)) {
+            float r0[E], r1[E];
+            C::unpack(*ring_src(f0, ring_lane), r0);
+            C::unpack(*ring_src(f1, ring_lane), r1);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            acc[q] = w0 * x0[q] + w1 * x1[q];
-        // row r ends with the wave's total of value r; lanes l and l ^ 8 hold the same one
-        const float t = reduce4_to_rows(acc[0], acc[1], acc[2], acc[3]);
-        reinterpret_cast<float*>(red)[(wave * 8 + el) * 4 + (lane >> 4)] = t;
+            for (int q = 0; q < E; ++q) {
+                m0[q] += r0[q];
+                m1[q] += r1[q];
+            }
+        }
+    };
+
+    // Write, first half: this lane's share of the prediction of the decayed
+    // slots, summed over the wave into red.
+    auto partials = [&](const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float4* red)
+        __attribute__((always_inline)) {
+        float m0[E], m1[E];
+        slot_values(ws, r0.x, r1.x, m0, m1);
+        const CT w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z), al = alpha;
+        CT acc[E];
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+            acc[q] = w0 * (al * (CT)m0[q]) + w1 * (al * (CT)m1[q]);
+        reduce_to_part<E, CT>(acc, red, wave, el, lane);
     };
 
     // Write, second half (after the barrier that publishes red): the delta-rule
-    // update of this lane's slots, into the ring entry of the token in ring slot J.
-    auto update = [&](auto jc, const uint4& r0, const uint4& r1, float beta, const uint4& vraw, const float (&x0)[4],
-                      const float (&x1)[4], const float4* red, uint4& p0, uint4& p1) __attribute__((always_inline)) {
+    // update of this lane's slots (the decayed values formed again, exactly as
+    // above), stored into the ring entry of the token in ring slot J.
+    auto update = [&](auto jc, const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float beta,
+                      const uint4 (&vraw)[NV], const float4* red, uint4& p0, uint4& p1) __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;
-        const float4 pv = sum_waves(red, el);
+        CT vh[E];
+        sum_waves<E, CT>(red, el, vh);
         // pin the use of v here: unpacking it earlier (the compiler would, at the
         // top of the loop) waits for a load still in flight
-        uint4 u = vraw;
-        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-        float vv[4];
-        if constexpr (sizeof(VT) == 2) {
-            vv[0] = bf16_lo(u.x); vv[1] = bf16_hi(u.x);
-            vv[2] = bf16_lo(u.y); vv[3] = bf16_hi(u.y);
-        } else {
-            vv[0] = __uint_as_float(u.x); vv[1] = __uint_as_float(u.y);
-            vv[2] = __uint_as_float(u.z); vv[3] = __uint_as_float(u.w);
-        }
-        const float vh[4] = {pv.x, pv.y, pv.z, pv.w};
-        const float w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z);
-        float y0[4], y1[4];
+        uint4 u[NV];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float dlt = beta * (vv[q] - vh[q]);
-            y0[q] = x0[q] + w0 * dlt;
-            y1[q] = x1[q] + w1 * dlt;
+        for (int i = 0; i < NV; ++i) {
+            u[i] = vraw[i];
+            asm volatile("" : "+v"(u[i].x), "+v"(u[i].y), "+v"(u[i].z), "+v"(u[i].w));
         }
-        p0 = make_uint4(__float_as_uint(y0[0]), __float_as_uint(y0[1]), __float_as_uint(y0[2]), __float_as_uint(y0[3]));
-        p1 = make_uint4(__float_as_uint(y1[0]), __float_as_uint(y1[1]), __float_as_uint(y1[2]), __float_as_uint(y1[3]));
+        float vv[E];
+        if constexpr (sizeof(VT) == 2) {
+            const uint32_t w[4] = {u[0].x, u[0].y, u[0].z, u[0].w};
+#pragma unroll
+            for (int i = 0; i < E / 2; ++i) {
+                vv[2 * i] = bf16_lo(w[i]);
+                vv[2 * i + 1] = bf16_hi(w[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                vv[4 * i] = __uint_as_float(u[i].x);
+                vv[4 * i + 1] = __uint_as_float(u[i].y);
+                vv[4 * i + 2] = __uint_as_float(u[i].z);
+                vv[4 * i + 3] = __uint_as_float(u[i].w);
+            }
+        }
+        float m0[E], m1[E];
+        slot_values(ws, r0.x, r1.x, m0, m1);
+        const CT w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z), al = alpha, be = beta;
+        CT y0[E], y1[E];
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+            const CT dlt = be * ((CT)vv[q] - vh[q]);
+            y0[q] = (al * (CT)m0[q]) + w0 * dlt;
+            y1[q] = (al * (CT)m1[q]) + w1 * dlt;
+        }
+        p0 = C::pack(y0);
+        p1 = C::pack(y1);
         ring_w[J * kPos * kEntryU4 + pos0 * kEntryU4] = p0;
         ring_w[J * kPos * kEntryU4 + pos1 * kEntryU4] = p1;
     };
@@ -243,19 +339,14 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     auto read_phase = [&](auto zc, const uint4 (&rs)[2], float4* ored) __attribute__((always_inline)) {
         uint4 r0, r1, hd;
         records(zc, r0, r1, hd);
-        uint4 q0 = rs[0], q1 = rs[1];
-        if (forwards(r0.y, r1.y)) {
-            q0 = add4(q0, *ring_src(r0.y, ring_lane));
-            q1 = add4(q1, *ring_src(r1.y, ring_lane));
-        }
+        float q0[E], q1[E];
+        slot_values(rs, r0.y, r1.y, q0, q1);
         const float rw0 = __uint_as_float(r0.w), rw1 = __uint_as_float(r1.w);
-        float oa[4];
-        oa[0] = rw0 * __uint_as_float(q0.x) + rw1 * __uint_as_float(q1.x);
-        oa[1] = rw0 * __uint_as_float(q0.y) + rw1 * __uint_as_float(q1.y);
-        oa[2] = rw0 * __uint_as_float(q0.z) + rw1 * __uint_as_float(q1.z);
-        oa[3] = rw0 * __uint_as_float(q0.w) + rw1 * __uint_as_float(q1.w);
-        const float t = reduce4_to_rows(oa[0], oa[1], oa[2], oa[3]);
-        reinterpret_cast<float*>(ored)[(wave * 8 + el) * 4 + (lane >> 4)] = t;
+        float oa[E];
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+            oa[q] = rw0 * q0[q] + rw1 * q1[q];
+        reduce_to_part<E, float>(oa, ored, wave, el, lane);
     };
 
     // Issue for token u (record slot Z, register slot S): its slot rows and v, and
@@ -275,29 +366,37 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         rset[S][1] = ld128(r_mem, or1);
         soff[S][0] = (u0.x >> 31) ? kOOB : ow0;
         soff[S][1] = (u1.x >> 31) ? kOOB : ow1;
-        if constexpr (sizeof(VT) == 2) {
+        if constexpr (VB == 8) {
             const i32x2_t w2 = __builtin_amdgcn_raw_buffer_load_b64(r_v, hu.z + v_lane, 0, 0);
-            vr[S] = make_uint4((uint32_t)w2[0], (uint32_t)w2[1], 0u, 0u);
+            vr[S][0] = make_uint4((uint32_t)w2[0], (uint32_t)w2[1], 0u, 0u);
         } else {
-            vr[S] = ld128(r_v, hu.z + v_lane);
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                vr[S][i] = ld128(r_v, hu.z + v_lane + 16u * i);
         }
         const uint32_t ro = (uint32_t)(u + 4) * (uint32_t)(kRecs * 16) + rec_lane;
         rl[decltype(zc)::value % ZL] = ld128(r_plan, lane < kRecPerWave ? ro : kOOB);
     };
 
     // out of the token in record slot Z from the partials in ored: wave `owner`
-    // sums and its group 0 stores; every wave still issues the store (past the
+    // sums and its group 0 stores; every wave still issues the stores (past the
     // buffer elsewhere), so all waves count the same memory operations
     auto store_out = [&](auto zc, const float4* ored, int owner) __attribute__((always_inline)) {
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        float o[E];
+#pragma unroll
+        for (int q = 0; q < E; ++q)
+            o[q] = 0.f;
         uint32_t off = kOOB;
         if (wave == owner) {
             const uint4 hd = g_rec[(decltype(zc)::value * kWaves + wave) * kRecPerWave + 16];
-            o = sum_waves(ored, el);
+            sum_waves<E, float>(ored, el, o);
             off = g == 0 ? (hd.w & ~kDepFlag) + o_lane : kOOB;
         }
-        st128(r_out, off,
-              make_uint4(__float_as_uint(o.x), __float_as_uint(o.y), __float_as_uint(o.z), __float_as_uint(o.w)));
+#pragma unroll
+        for (int i = 0; i < NO; ++i)
+            st128(r_out, off == kOOB ? kOOB : off + 16u * i,
+                  make_uint4(__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]), __float_as_uint(o[4 * i + 2]),
+                             __float_as_uint(o[4 * i + 3])));
     };
 
     // Pair (s, s+1), s = S0 + ZR*blk + j0: record and ring slots j0, j0+1, register
@@ -320,7 +419,7 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
 
             // ---- read of pair k-1 (its register slots are then free)
             read_phase(std::integral_constant<int, p0>{}, rset[p0 % ZS], g_ored);
-            read_phase(std::integral_constant<int, p1>{}, rset[p1 % ZS], g_ored + 32);
+            read_phase(std::integral_constant<int, p1>{}, rset[p1 % ZS], g_ored + kPartU4);
 
             // ---- issue pair k+2 into those register slots
             issue(std::integral_constant<int, n0>{}, std::integral_constant<int, n0 % ZS>{}, s + 4);
@@ -330,22 +429,24 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
             uint4 a0, a1, ha, b0, b1, hb;
             records(std::integral_constant<int, j0>{}, a0, a1, ha);
             records(std::integral_constant<int, j1>{}, b0, b1, hb);
-            float xa0[4], xa1[4], xb0[4], xb1[4];
             uint4 ya0, ya1, yb0, yb1;
-            partials(wset[j0 % ZS], a0, a1, __uint_as_float(ha.x), xa0, xa1, g_red);
-            partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), xb0, xb1, g_red + 32);
+            partials(wset[j0 % ZS], a0, a1, __uint_as_float(ha.x), g_red);
+            partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), g_red + kPartU4);
             barrier_lds();
             store_out(std::integral_constant<int, p0>{}, g_ored, 0);
-            store_out(std::integral_constant<int, p1>{}, g_ored + 32, 1);
-            update(std::integral_constant<int, j0>{}, a0, a1, __uint_as_float(ha.y), vr[j0 % ZS], xa0, xa1, g_red, ya0, ya1);
-            update(std::integral_constant<int, j1>{}, b0, b1, __uint_as_float(hb.y), vr[j1 % ZS], xb0, xb1, g_red + 32, yb0, yb1);
+            store_out(std::integral_constant<int, p1>{}, g_ored + kPartU4, 1);
+            update(std::integral_constant<int, j0>{}, wset[j0 % ZS], a0, a1, __uint_as_float(ha.x),
+                   __uint_as_float(ha.y), vr[j0 % ZS], g_red, ya0, ya1);
+            update(std::integral_constant<int, j1>{}, wset[j1 % ZS], b0, b1, __uint_as_float(hb.x),
+                   __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1);
             if (__builtin_amdgcn_readfirstlane(hb.w) & kDepFlag) {
                 // token s+1 writes a slot token s writes: redo its write now that
                 // token s's values are in the ring
                 barrier_lds();
-                partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), xb0, xb1, g_red + 32);
+                partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), g_red + kPartU4);
                 barrier_lds();
-                update(std::integral_constant<int, j1>{}, b0, b1, __uint_as_float(hb.y), vr[j1 % ZS], xb0, xb1, g_red + 32, yb0, yb1);
+                update(std::integral_constant<int, j1>{}, wset[j1 % ZS], b0, b1, __uint_as_float(hb.x),
+                       __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1);
             }
             st128(r_mem, soff[j0 % ZS][0], ya0);
             st128(r_mem, soff[j0 % ZS][1], ya1);
@@ -357,15 +458,24 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
 
 } // namespace
 
-hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& p, bool in_bf16, hipStream_t stream)
+hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& p, bool state_bf16, bool in_bf16,
+                                  hipStream_t stream)
 {
-    if (!p.staged || p.waves != kWaves || a.d % 32 != 0 || a.W > kPos)
+    const int seg = state_bf16 ? 64 : 32;
+    if (!p.staged || p.waves != kWaves || a.d % seg != 0 || a.W > kPos)
         return hipErrorInvalidValue;
     dim3 grid((unsigned)p.grid), block(kWaves * 64);
-    if (in_bf16)
-        hipLaunchKernelGGL(sdm_scan_staged_kernel<uint16_t>, grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL(sdm_scan_staged_kernel<float>, grid, block, 0, stream, a);
+    if (state_bf16) {
+        if (in_bf16)
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, uint16_t>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, float>), grid, block, 0, stream, a);
+    } else {
+        if (in_bf16)
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, uint16_t>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, float>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
