@@ -121,12 +121,23 @@ template <> struct Cell<uint16_t> {
     {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
     }
+    // One rounding of each double to bf16: through float, which is exact unless
+    // the float lands on a bf16 tie (1 in 2^16); only then, for the whole wave,
+    // the tie is settled the way the double lies.
     __device__ static uint4 pack(const double (&x)[8])
     {
         float f[8];
+        bool tie = false;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-            f[q] = settle_bf16_tie(x[q]);
+        for (int q = 0; q < 8; ++q) {
+            f[q] = (float)x[q];
+            tie |= (__float_as_uint(f[q]) & 0xFFFFu) == 0x8000u;
+        }
+        if (__builtin_amdgcn_ballot_w64(tie) != 0u) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                f[q] = settle_bf16_tie(x[q]);
+        }
         return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
     }
 };
@@ -280,8 +291,12 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         const CT w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z), al = alpha;
         CT acc[E];
 #pragma unroll
-        for (int q = 0; q < E; ++q)
-            acc[q] = w0 * (al * (CT)m0[q]) + w1 * (al * (CT)m1[q]);
+        for (int q = 0; q < E; ++q) {
+            if constexpr (sizeof(CT) == 8) // w m is exact in double: the decay comes out of the sum
+                acc[q] = al * (w0 * (CT)m0[q] + w1 * (CT)m1[q]);
+            else
+                acc[q] = w0 * (al * (CT)m0[q]) + w1 * (al * (CT)m1[q]);
+        }
         reduce_to_part<E, CT>(acc, red, wave, el, lane);
     };
 
