@@ -92,6 +92,78 @@ def kernel_signature() -> str:
     return h.hexdigest()[:16]
 
 
+def decode_bench(args, cfg):
+    """One token per sequence per call over a persistent memory: sdm_step, timed
+    over consecutive tokens of the same synthetic sequences, and sdm_forward of
+    one token for comparison."""
+    import numpy as np
+    import torch
+
+    import sdm_inputs as gi
+    from sparse_memory_linear_pk_amd import SDM
+
+    steps = max(args.steps, 64)
+    c = cfg.replace(T=steps + args.warmup)
+    log(f"generating inputs for {c}")
+    x = gi.make_inputs(c)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    tok = [{k: d[k][:, t].contiguous() for k in ("wq", "rq", "v", "alpha", "beta")} for t in range(c.T)]
+    out = torch.empty((c.B, c.H, c.d), dtype=torch.float32, device="cuda")
+    layer = SDM.from_config(c)
+    for t in range(args.warmup):
+        layer.step(tok[t]["wq"], tok[t]["rq"], tok[t]["v"], tok[t]["alpha"], tok[t]["beta"], d["subkeys"], d["mem0"], out)
+    torch.cuda.synchronize()
+    layer.set_timing(True)
+    t0 = time.perf_counter()
+    for t in range(args.warmup, c.T):
+        layer.step(tok[t]["wq"], tok[t]["rq"], tok[t]["v"], tok[t]["alpha"], tok[t]["beta"], d["subkeys"], d["mem0"], out)
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    tm = layer.timing()
+    layer.close()
+    # the same tokens through a one-token forward
+    one = SDM.from_config(c.replace(T=1))
+    o1 = torch.empty((c.B, 1, c.H, c.d), dtype=torch.float32, device="cuda")
+    x1 = [{k: v.unsqueeze(1) for k, v in tk.items()} for tk in tok]
+    for t in range(args.warmup):
+        one.forward(x1[t]["wq"], x1[t]["rq"], x1[t]["v"], x1[t]["alpha"], x1[t]["beta"], d["subkeys"], d["mem0"], o1)
+    torch.cuda.synchronize()
+    f0 = time.perf_counter()
+    for t in range(args.warmup, c.T):
+        one.forward(x1[t]["wq"], x1[t]["rq"], x1[t]["v"], x1[t]["alpha"], x1[t]["beta"], d["subkeys"], d["mem0"], o1)
+    torch.cuda.synchronize()
+    fsec = time.perf_counter() - f0
+    one.close()
+    s_bytes = 2 if c.state_bf16 else 4
+    step_bytes = c.B * c.H * 3 * c.W * c.d * s_bytes
+    dev_ms = tm["ms_step"] / max(1, tm["n_step"])
+    res = {
+        "metric": "SDM decode step tokens/sec (1 GPU), sdm_step",
+        "value": c.B * steps / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3 / steps,
+        "higher_is_better": True,
+        "dtype": "f32",
+        "data": "synthetic (seeded), consecutive tokens of the workload's sequences",
+        "config": {"workload": f"sdm-{c.name} decode: B={c.B} H={c.H} d={c.d} N={c.S}^2 dk={c.dk} k={c.k} W={c.W}, "
+                               f"one token per sequence per step"},
+        "step_device_us": dev_ms * 1e3,
+        "step_state_bytes": step_bytes,
+        "step_device_GBps": step_bytes / (dev_ms * 1e-3) / 1e9,
+        "forward_T1_ms_per_step": fsec * 1e3 / steps,
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +174,8 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD,
                     help="workload index (default 2, the 1.4B shape the metric is quoted on; 3 long-context, "
                          "4 8B-shaped: bf16 state)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decode step (sdm_step, one token per sequence per call) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 4 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -127,6 +201,8 @@ def main():
         return
 
     cfg = gi.config(args.workload)
+    if args.decode:
+        return decode_bench(args, cfg)
     log(f"generating inputs for {cfg}")
     t0 = time.perf_counter()
     x = gi.make_inputs(cfg)

@@ -92,6 +92,8 @@ typedef struct {
     double ms_plan;    /* the scan's plan: packed slot records, forwarding and store decisions */
     double ms_scan;    /* the memory scan */
     long long n_score, n_select, n_plan, n_scan; /* launches timed */
+    double ms_step;    /* decode steps (sdm_step), both of their kernels */
+    long long n_step;  /* steps timed */
 } sdm_timing;
 
 /* Supported shapes: 1 <= k <= min(S, 64); 1 <= W <= min(k*k, 64); S <= 1024;
@@ -107,6 +109,18 @@ SDM_API sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handl
  * then the scan.  mem_inout is updated in place; out receives the reads. */
 SDM_API sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                        const float* beta, const void* subkeys, void* mem_inout, float* out);
+
+/* One token of the layer over a persistent memory (decode): the same operation
+ * as sdm_forward with T = 1 for B sequences and H heads, in two launches sized
+ * for a single token; T consecutive steps leave exactly the memory and outputs
+ * of one T-token forward.  Tensors of the token: wq, rq [B, H, dk] in_dtype;
+ * v [B, H, d] in_dtype; alpha, beta [B, H] float32; out [B, H, d] float32;
+ * subkeys and mem_inout as for sdm_forward.  The handle's T is not used.
+ * SDM_ERR_UNSUPPORTED unless d * sizeof(state) is a multiple of 128 bytes.
+ * (SDM blog post, section "How does SDM work?": the per-token update whose
+ * cost does not grow with the sequence.) */
+SDM_API sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
+                            const float* beta, const void* subkeys, void* mem_inout, float* out);
 
 /* Free the workspace and the handle.  Waits for the handle's stream first. */
 SDM_API sdm_status sdm_destroy(sdm_handle h);

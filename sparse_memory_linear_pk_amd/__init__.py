@@ -78,6 +78,15 @@ class SDM:
                 self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, T, H, d), "f32")]
         check(lib().sdm_forward(self._h, *[_ptr(a) for a in args]), "sdm_forward")
 
+    def step(self, wq, rq, v, alpha, beta, subkeys, mem, out):
+        """One token (decode): wq, rq [B, H, dk], v [B, H, d], alpha, beta [B, H], out [B, H, d]."""
+        B, H, T, d, S, dk, k, W = self._dims()
+        args = [self._t(wq, "wq", (B, H, dk), "in"), self._t(rq, "rq", (B, H, dk), "in"),
+                self._t(v, "v", (B, H, d), "in"), self._t(alpha, "alpha", (B, H), "f32"),
+                self._t(beta, "beta", (B, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
+                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, H, d), "f32")]
+        check(lib().sdm_step(self._h, *[_ptr(a) for a in args]), "sdm_step")
+
     def score(self, q, subkeys, scores):
         B, H, T, d, S, dk, k, W = self._dims()
         args = [self._t(q, "q", (B, T, H, dk), "in"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),

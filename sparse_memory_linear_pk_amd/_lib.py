@@ -29,7 +29,8 @@ class Config(C.Structure):
 class Timing(C.Structure):
     _fields_ = [("ms_score", C.c_double), ("ms_select", C.c_double), ("ms_plan", C.c_double),
                 ("ms_scan", C.c_double), ("n_score", C.c_longlong), ("n_select", C.c_longlong),
-                ("n_plan", C.c_longlong), ("n_scan", C.c_longlong)]
+                ("n_plan", C.c_longlong), ("n_scan", C.c_longlong), ("ms_step", C.c_double),
+                ("n_step", C.c_longlong)]
 
 
 def declared_symbols(header: str = HEADER) -> list[str]:
@@ -53,6 +54,7 @@ def lib() -> C.CDLL:
     sig = {
         "sdm_create": ([C.POINTER(Config), vp, C.POINTER(C.c_void_p)], C.c_int),
         "sdm_forward": ([h, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
+        "sdm_step": ([h, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
         "sdm_destroy": ([h], C.c_int),
         "sdm_status_str": ([C.c_int], C.c_char_p),
         "sdm_last_error": ([], C.c_char_p),

@@ -28,7 +28,7 @@ sdm_status fail(sdm_status s, const char* fmt, ...)
     return s;
 }
 
-enum Kind { K_SCORE = 0, K_SELECT = 1, K_PLAN = 2, K_SCAN = 3 };
+enum Kind { K_SCORE = 0, K_SELECT = 1, K_PLAN = 2, K_SCAN = 3, K_STEP = 4 };
 
 struct TimedLaunch {
     Kind kind;
@@ -512,6 +512,29 @@ sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void*
     return SDM_OK;
 }
 
+sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
+                    const float* beta, const void* subkeys, void* mem_inout, float* out)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!wq || !rq || !v || !alpha || !beta || !subkeys || !mem_inout || !out)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_step: NULL pointer");
+    if (!aligned16(wq) || !aligned16(rq) || !aligned16(v) || !aligned16(subkeys) || !aligned16(mem_inout) ||
+        !aligned16(out) || !aligned4(alpha) || !aligned4(beta))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_step: misaligned pointer");
+    const sdm_config& c = h->cfg;
+    if (!sdm::step_supported(c.d, c.state_dtype == SDM_BF16))
+        return fail(SDM_ERR_UNSUPPORTED, "sdm_step: d=%d: a slot row must be a multiple of 128 bytes", c.d);
+    // the slot ids and weights of both query sets go to the first 2*B*H*W
+    // entries of the forward's addressing workspace
+    Timer t(h, K_STEP, h->stream);
+    hipError_t e = sdm::launch_sdm_step(wq, rq, v, alpha, beta, subkeys, mem_inout, out, h->idx[0], h->wt[0], c.B,
+                                        c.H, c.d, c.n_sub, c.dk / 2, c.k, c.W, c.in_dtype == SDM_BF16,
+                                        c.state_dtype == SDM_BF16, h->stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_step launch");
+}
+
 sdm_status sdm_set_timing(sdm_handle h, int enable)
 {
     sdm_status s = check_handle(h);
@@ -547,6 +570,7 @@ sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t)
         case K_SELECT: h->totals.ms_select += ms; h->totals.n_select++; break;
         case K_PLAN: h->totals.ms_plan += ms; h->totals.n_plan++; break;
         case K_SCAN: h->totals.ms_scan += ms; h->totals.n_scan++; break;
+        case K_STEP: h->totals.ms_step += ms; h->totals.n_step++; break;
         }
         (void)hipEventDestroy(tl.start);
         (void)hipEventDestroy(tl.stop);

@@ -140,6 +140,14 @@ hipError_t launch_sdm_scan(const ScanArgs& a, const ScanPlan& plan, bool state_b
 hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& plan, bool state_bf16, bool in_bf16,
                                   hipStream_t stream);
 
+// One token over a persistent memory (sdm_step): tensors [B, H, ...] of the
+// token; idx/wt: workspace of 2*B*H*W entries each.  Needs d * sizeof(state) a
+// multiple of 128 bytes.
+bool step_supported(int d, bool state_bf16);
+hipError_t launch_sdm_step(const void* wq, const void* rq, const void* v, const float* alpha, const float* beta,
+                           const void* subkeys, void* mem, float* out, int32_t* idx, float* wt, int B, int H, int d,
+                           int S, int dh, int k, int W, bool in_bf16, bool state_bf16, hipStream_t stream);
+
 // Measurement only: the scan's traffic pattern without arithmetic on `memories`
 // memories of `rows` rows of row_bytes (a multiple of 128) bytes.
 hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, uint32_t seed,

@@ -42,7 +42,7 @@
 // makes every wave's retired stores visible to the loads issued after it.  Two
 // stores of one slot that may be in flight together are never both issued: the
 // plan drops the earlier.
-#include "scan_device.h"
+#include "scan_cell.h"
 
 namespace sdm {
 namespace {
@@ -83,88 +83,6 @@ __device__ __forceinline__ bool forwards(uint32_t f0, uint32_t f1)
 __device__ __forceinline__ void barrier_lds()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// The 16 bytes of state a lane owns in one slot segment: 4 float32 or 8 bf16
-// values, unpacked to float32 for the arithmetic and packed back with one
-// nearest-even rounding per value.
-template <class ST> struct Cell;
-template <> struct Cell<float> {
-    static constexpr int E = 4;
-    using CT = float; // type of the write arithmetic
-    __device__ static uint4 pack(const float (&x)[4])
-    {
-        return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
-    }
-    __device__ static void unpack(const uint4& u, float (&x)[4])
-    {
-        x[0] = __uint_as_float(u.x);
-        x[1] = __uint_as_float(u.y);
-        x[2] = __uint_as_float(u.z);
-        x[3] = __uint_as_float(u.w);
-    }
-};
-template <> struct Cell<uint16_t> {
-    static constexpr int E = 8;
-    using CT = double;
-    __device__ static void unpack(const uint4& u, float (&x)[8])
-    {
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = bf16_lo(w[i]);
-            x[2 * i + 1] = bf16_hi(w[i]);
-        }
-    }
-    // v_cvt_pk_bf16_f32: nearest-even, NaN stays a quiet NaN
-    __device__ static uint32_t pack2(float lo, float hi)
-    {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-    }
-    // One rounding of each double to bf16: through float, which is exact unless
-    // the float lands on a bf16 tie (1 in 2^16); only then, for the whole wave,
-    // the tie is settled the way the double lies.
-    __device__ static uint4 pack(const double (&x)[8])
-    {
-        float f[8];
-        bool tie = false;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            f[q] = (float)x[q];
-            tie |= (__float_as_uint(f[q]) & 0xFFFFu) == 0x8000u;
-        }
-        if (__builtin_amdgcn_ballot_w64(tie) != 0u) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                f[q] = settle_bf16_tie(x[q]);
-        }
-        return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7]));
-    }
-};
-
-// Totals over the 4 waves of the per-wave partials ([wave][el][E] values of
-// type X) of element lane el, in the same order in every lane.
-template <int E, class X>
-__device__ __forceinline__ void sum_waves(const float4* part, int el, X (&t)[E])
-{
-    const X* p = reinterpret_cast<const X*>(part);
-#pragma unroll
-    for (int q = 0; q < E; ++q)
-        t[q] = (p[(0 * 8 + el) * E + q] + p[(1 * 8 + el) * E + q]) + (p[(2 * 8 + el) * E + q] + p[(3 * 8 + el) * E + q]);
-}
-
-// The wave's totals over its 8 lane groups of the E values of every lane, left
-// in part ([wave][el][E] values of type X); lanes l and l ^ 8 write the same.
-template <int E, class X>
-__device__ __forceinline__ void reduce_to_part(const X (&v)[E], float4* part, int wave, int el, int lane)
-{
-    X* p = reinterpret_cast<X*>(part);
-#pragma unroll
-    for (int c = 0; c < E / 4; ++c) {
-        // row r (lanes 16r .. 16r+15) ends with the total of value 4c + r
-        const X t = reduce4_to_rows(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
-        p[(wave * 8 + el) * E + 4 * c + (lane >> 4)] = t;
-    }
 }
 
 // ST: state element (float or bf16 bits), VT: v element (float or bf16 bits).
@@ -291,12 +209,8 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         const CT w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z), al = alpha;
         CT acc[E];
 #pragma unroll
-        for (int q = 0; q < E; ++q) {
-            if constexpr (sizeof(CT) == 8) // w m is exact in double: the decay comes out of the sum
-                acc[q] = al * (w0 * (CT)m0[q] + w1 * (CT)m1[q]);
-            else
-                acc[q] = w0 * (al * (CT)m0[q]) + w1 * (al * (CT)m1[q]);
-        }
+        for (int q = 0; q < E; ++q)
+            acc[q] = predict2<CT>(al, w0, m0[q], w1, m1[q]);
         reduce_to_part<E, CT>(acc, red, wave, el, lane);
     };
 
@@ -339,9 +253,9 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         CT y0[E], y1[E];
 #pragma unroll
         for (int q = 0; q < E; ++q) {
-            const CT dlt = be * ((CT)vv[q] - vh[q]);
-            y0[q] = (al * (CT)m0[q]) + w0 * dlt;
-            y1[q] = (al * (CT)m1[q]) + w1 * dlt;
+            const CT dlt = delta<CT>(be, vv[q], vh[q]);
+            y0[q] = updated<CT>(al, m0[q], w0, dlt);
+            y1[q] = updated<CT>(al, m1[q], w1, dlt);
         }
         p0 = C::pack(y0);
         p1 = C::pack(y1);
@@ -360,7 +274,7 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         float oa[E];
 #pragma unroll
         for (int q = 0; q < E; ++q)
-            oa[q] = rw0 * q0[q] + rw1 * q1[q];
+            oa[q] = read2(rw0, q0[q], rw1, q1[q]);
         reduce_to_part<E, float>(oa, ored, wave, el, lane);
     };
 
