@@ -217,6 +217,24 @@ inline int pair_count(int k, int W)
     return n;
 }
 
+// Step 1 for one half by one wave: the half's sorted top k into val[lane] and
+// sub[lane] (scores and sub-key indices, 64 entries; lanes past k hold padding).
+template <int J>
+__device__ inline void select_half(const float* s, int S, int k, int lane, uint64_t* buf, float* val, uint32_t* sub)
+{
+    const uint64_t x = half_sorted_topk<J>(s, S, k, lane, buf);
+    val[lane] = key_value((uint32_t)(x >> 32));
+    sub[lane] = ~(uint32_t)x;
+}
+
+// Step 2 by one wave, from both halves' sorted lists (val, sub: 2 x 64, in
+// LDS and visible to the wave): idx_row, wt_row receive the W slots and
+// weights, best first.  buf: 64 entries of the wave's LDS scratch.
+template <int R>
+__device__ inline void select_from_lists(int S, int k, int W, int n_pairs, const uint16_t* s_pairs, int lane,
+                                         uint64_t* buf, const float (*val)[64], const uint32_t (*sub)[64],
+                                         int32_t* idx_row, float* wt_row);
+
 // The selection of one row by one wave: s holds the row's half scores (S of
 // half 0, then S of half 1; global or LDS); buf, val, sub are the wave's LDS
 // scratch (64 entries each, val and sub 2 x 64); idx_row, wt_row receive the W
@@ -227,12 +245,17 @@ __device__ inline void select_row(const float* s, int S, int k, int W, int n_pai
                                   int32_t* idx_row, float* wt_row)
 {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint64_t x = half_sorted_topk<J>(s + h * S, S, k, lane, buf);
-        val[h][lane] = key_value((uint32_t)(x >> 32));
-        sub[h][lane] = ~(uint32_t)x;
-    }
+    for (int h = 0; h < 2; ++h)
+        select_half<J>(s + h * S, S, k, lane, buf, val[h], sub[h]);
     wave_sync_lds();
+    select_from_lists<R>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
+}
+
+template <int R>
+__device__ inline void select_from_lists(int S, int k, int W, int n_pairs, const uint16_t* s_pairs, int lane,
+                                         uint64_t* buf, const float (*val)[64], const uint32_t (*sub)[64],
+                                         int32_t* idx_row, float* wt_row)
+{
 
     // restricted candidates
     uint32_t key[R], slot[R];

@@ -3,8 +3,11 @@
 // The same operation as sdm_forward with T = 1 (SDM blog post, section "How
 // does SDM work?" and the caption of the figure "The SDM mechanism, end to
 // end": addressing of the write and read queries, the decay and delta-rule
-// write of the W write slots, then the softmax-weighted read), in two launches
-// sized for a single token:
+// write of the W write slots, then the softmax-weighted read).  For bf16
+// queries with 128-wide halves (the workload shapes) and a grid of at most one
+// workgroup per CU it is one launch, step_fused_kernel: every workgroup of a
+// memory forms that memory's addressing itself, then scans its 128 bytes of the
+// rows.  Otherwise two launches sized for a single token:
 //
 //  1. step_address_kernel: one workgroup per (b, h) scores both queries of the
 //     token on the matrix cores, with the instruction, operand layout and
@@ -114,10 +117,13 @@ struct StepScanArgs {
     long N;
 };
 
-// One token: lane (g, e) of wave w holds the 16 bytes e of write and read
-// positions 16w + g and 16w + 8 + g, as in the staged scan.
+// One token for the workgroup's 128 bytes of the rows of memory bh: lane
+// (g, e) of wave w holds the 16 bytes e of write and read positions 16w + g
+// and 16w + 8 + g, as in the staged scan.  widx/wwt, ridx/rwt: the token's W
+// write and read slots and weights (global memory or LDS).
 template <class ST, class VT>
-__global__ __launch_bounds__(kWaves * 64) void step_scan_kernel(StepScanArgs a)
+__device__ void step_scan_body(const StepScanArgs& a, int bh, int chunk, const int32_t* widx, const float* wwt,
+                               const int32_t* ridx, const float* rwt)
 {
     using C = Cell<ST>;
     using CT = typename C::CT;
@@ -131,15 +137,12 @@ __global__ __launch_bounds__(kWaves * 64) void step_scan_kernel(StepScanArgs a)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 3, el = lane & 7;
-    const int nchunk = a.d / SEG;
-    const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const int W = a.W;
     const uint32_t row_bytes = (uint32_t)a.d * (uint32_t)sizeof(ST);
     const uint32_t lane_off = (uint32_t)chunk * 128u + (uint32_t)el * 16u;
     const __amdgpu_buffer_rsrc_t r_mem =
         make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * row_bytes, (uint32_t)a.N * row_bytes);
     const int pos[2] = {wave * 16 + g, wave * 16 + 8 + g};
-    const long wrow = (long)bh * W, rrow = ((long)a.B * a.H + bh) * W;
 
     int32_t ws[2], rs[2];
     float ww[2], rw[2];
@@ -147,10 +150,10 @@ __global__ __launch_bounds__(kWaves * 64) void step_scan_kernel(StepScanArgs a)
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const bool live = pos[p] < W;
-        ws[p] = live ? a.idx[wrow + pos[p]] : -1;
-        rs[p] = live ? a.idx[rrow + pos[p]] : -1;
-        ww[p] = live ? a.wt[wrow + pos[p]] : 0.f;
-        rw[p] = live ? a.wt[rrow + pos[p]] : 0.f;
+        ws[p] = live ? widx[pos[p]] : -1;
+        rs[p] = live ? ridx[pos[p]] : -1;
+        ww[p] = live ? wwt[pos[p]] : 0.f;
+        rw[p] = live ? rwt[pos[p]] : 0.f;
         wv[p] = ld128(r_mem, live ? (uint32_t)ws[p] * row_bytes + lane_off : kOOB);
         rv[p] = ld128(r_mem, live ? (uint32_t)rs[p] * row_bytes + lane_off : kOOB);
     }
@@ -240,6 +243,49 @@ __global__ __launch_bounds__(kWaves * 64) void step_scan_kernel(StepScanArgs a)
     }
 }
 
+template <class ST, class VT>
+__global__ __launch_bounds__(kWaves * 64) void step_scan_kernel(StepScanArgs a)
+{
+    const int nchunk = a.d / (128 / (int)sizeof(ST));
+    const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    const long wrow = (long)bh * a.W, rrow = ((long)a.B * a.H + bh) * a.W;
+    step_scan_body<ST, VT>(a, bh, chunk, a.idx + wrow, a.wt + wrow, a.idx + rrow, a.wt + rrow);
+}
+
+// The whole step in one launch, for bf16 queries: every workgroup of memory bh
+// forms bh's addressing itself (the same scores and selection as
+// step_address_kernel, the four half selections on the four waves at once, the
+// two top-W selections on two of them), then scans its 128 bytes.  The
+// repeated addressing runs in parallel, so it adds no latency.
+template <int DH, int J, int R, class ST>
+__global__ __launch_bounds__(kWaves * 64) void step_fused_kernel(StepArgs a, StepScanArgs c)
+{
+    extern __shared__ float s_sc[]; // [query][half][S]
+    __shared__ uint64_t s_buf[kWaves][64];
+    __shared__ float s_val[2][2][64];
+    __shared__ uint32_t s_sub[2][2][64];
+    __shared__ uint16_t s_pairs[pksel::kPairsMax];
+    __shared__ int32_t s_idx[2][64];
+    __shared__ float s_wt[2][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nchunk = c.d / (128 / (int)sizeof(ST));
+    const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    pksel::fill_pairs(s_pairs, a.k, a.W);
+    step_scores<DH, true>(a, bh, s_sc, lane, wave);
+    __syncthreads();
+    {
+        const int q = wave >> 1, half = wave & 1; // waves 0, 1: write query; 2, 3: read query
+        pksel::select_half<J>(s_sc + (q * 2 + half) * a.S, a.S, a.k, lane, s_buf[wave], s_val[q][half],
+                              s_sub[q][half]);
+    }
+    __syncthreads();
+    if (wave < 2)
+        pksel::select_from_lists<R>(a.S, a.k, a.W, a.n_pairs, s_pairs, lane, s_buf[wave], s_val[wave], s_sub[wave],
+                                    s_idx[wave], s_wt[wave]);
+    __syncthreads();
+    step_scan_body<ST, uint16_t>(c, bh, chunk, s_idx[0], s_wt[0], s_idx[1], s_wt[1]);
+}
+
 template <int DH, bool BF16, int J>
 hipError_t launch_address_j(const StepArgs& a, hipStream_t stream)
 {
@@ -301,12 +347,25 @@ hipError_t launch_sdm_step(const void* wq, const void* rq, const void* v, const 
     StepArgs sa{wq, rq, subkeys, idx, wt, B, H, S, k, W, pksel::pair_count(k, W)};
     if (sa.n_pairs > pksel::kPairsMax)
         return hipErrorInvalidValue;
-    hipError_t e = in_bf16 ? launch_address<true>(sa, dh, stream) : launch_address<false>(sa, dh, stream);
-    if (e != hipSuccess)
-        return e;
     StepScanArgs ca{idx, wt, alpha, beta, v, mem, out, B, H, d, W, (long)S * S};
     const int nchunk = d * (state_bf16 ? 2 : 4) / 128;
     dim3 grid((unsigned)(B * H * nchunk)), block(kWaves * 64);
+    // one launch for the workload shapes (bf16 queries, 128-wide halves) when
+    // every workgroup has a CU of its own (more would repeat the addressing on
+    // shared CUs, which costs more than the second launch saves)
+    if (in_bf16 && dh == 128 && S > 256 && sa.n_pairs <= 256 && B * H * nchunk <= 256) {
+        const size_t lds = (size_t)4 * S * sizeof(float);
+        if (S <= 512)
+            hipLaunchKernelGGL((state_bf16 ? step_fused_kernel<128, 8, 4, uint16_t> : step_fused_kernel<128, 8, 4, float>),
+                               grid, block, lds, stream, sa, ca);
+        else
+            hipLaunchKernelGGL((state_bf16 ? step_fused_kernel<128, 16, 4, uint16_t> : step_fused_kernel<128, 16, 4, float>),
+                               grid, block, lds, stream, sa, ca);
+        return hipGetLastError();
+    }
+    hipError_t e = in_bf16 ? launch_address<true>(sa, dh, stream) : launch_address<false>(sa, dh, stream);
+    if (e != hipSuccess)
+        return e;
     if (state_bf16) {
         if (in_bf16)
             hipLaunchKernelGGL((step_scan_kernel<uint16_t, uint16_t>), grid, block, 0, stream, ca);
