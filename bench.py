@@ -40,8 +40,9 @@ def scan_bytes_per_step(cfg) -> int:
 
 
 def score_flops_per_step(cfg) -> int:
-    """Sub-key scoring of one forward: both query sets, both halves."""
-    return cfg.B * cfg.T * cfg.H * 2 * cfg.S * cfg.dh * 2
+    """Sub-key scoring of one forward: 2 query sets x 2 halves x S sub-keys x dh
+    multiply-adds of 2 FLOP, per row."""
+    return cfg.B * cfg.T * cfg.H * 2 * 2 * cfg.S * cfg.dh * 2
 
 
 def cpu_baseline(cfg, x, budget_s: float):
