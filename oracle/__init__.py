@@ -26,10 +26,21 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contrac
           "-Wextra", "-Werror"]
 
 
+GRAD_SRC = os.path.join(HERE, "sdm_oracle_grad.c")
+GRAD_LIB = os.path.join(HERE, "liboracle_sdm_grad.so")
+
+
 def build(src: str = SRC, out: str = LIB, extra_flags=()) -> str:
     """Compile the oracle with gcc.  -ffp-contract=off keeps every product and
     sum a separately rounded IEEE operation, as the C source is written."""
     cmd = ["gcc", *CFLAGS, *extra_flags, "-I", HERE, src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def build_grad(src: str = GRAD_SRC, out: str = GRAD_LIB, fwd_src: str = SRC, extra_flags=()) -> str:
+    """Compile the gradient oracle together with the forward it replays."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-I", HERE, src, fwd_src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -235,7 +246,104 @@ class Oracle:
         return out, aw, ar
 
 
+class GradOracle:
+    """Handle on one build of the gradient oracle (sdm_oracle_grad.c)."""
+
+    def __init__(self, path: str | None = None):
+        path = path or GRAD_LIB
+        if path == GRAD_LIB and (not os.path.exists(path) or os.path.getmtime(path) < max(
+                os.path.getmtime(GRAD_SRC), os.path.getmtime(SRC))):
+            build_grad()
+        if not os.path.exists(path):
+            raise FileNotFoundError(path)
+        self.path = path
+        L = C.CDLL(path)
+        vp = C.c_void_p
+        L.oracle_scan_grad.argtypes = [C.POINTER(_Cfg)] + [vp] * 15 + [C.c_int, C.c_int]
+        L.oracle_weights_f64.argtypes = [C.POINTER(_Cfg), vp, vp, C.c_int, vp, vp]
+        L.oracle_address_grad.argtypes = [C.POINTER(_Cfg), vp, vp, C.c_long, C.c_long, vp, vp, vp, vp, vp]
+        for f in ("oracle_scan_grad", "oracle_weights_f64", "oracle_address_grad", "oracle_scan"):
+            getattr(L, f).restype = C.c_int
+        L.oracle_scan.argtypes = [C.POINTER(_Cfg), vp, vp, vp, vp, vp, vp, vp, vp, vp, C.c_int, C.c_int,
+                                  C.c_int, C.c_int]
+        self.L = L
+
+    def scan_forward(self, cfg, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem):
+        """The forward scan of this build's own copy of the forward oracle (mem updated in place,
+        any state kind including float64).  Returns out [B,T,H,d] f32."""
+        cs = _cfg_struct(cfg)
+        arrs = [np.ascontiguousarray(a) for a in (idx_w, wt_w, idx_r, wt_r, v, alpha, beta)]
+        out = np.empty((cfg.B, cfg.T, cfg.H, cfg.d), np.float32)
+        for b in range(cfg.B):
+            for h in range(cfg.H):
+                if self.L.oracle_scan(C.byref(cs), *[_ptr(a) for a in arrs], _ptr(mem), _ptr(out), b, h, 0, cfg.d):
+                    raise ValueError("oracle_scan rejected its arguments")
+        return out
+
+    def scan_grad(self, cfg, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem0, dout, dmem_final, threads=None):
+        """Gradients of the scan.  Returns dict with dmem0 [B,H,N,d], dv [B,T,H,d], dalpha, dbeta [B,T,H],
+        dwt_w, dwt_r [B*T*H, W], all float64."""
+        cs = _cfg_struct(cfg)
+        arrs = [np.ascontiguousarray(a) for a in (idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem0)]
+        dout = np.ascontiguousarray(dout, np.float32)
+        R = cfg.B * cfg.T * cfg.H
+        g = {"dmem0": np.array(dmem_final, np.float64, copy=True, order="C"),
+             "dv": np.zeros((cfg.B, cfg.T, cfg.H, cfg.d)), "dalpha": np.zeros((cfg.B, cfg.T, cfg.H)),
+             "dbeta": np.zeros((cfg.B, cfg.T, cfg.H)), "dwt_w": np.zeros((R, cfg.W)), "dwt_r": np.zeros((R, cfg.W))}
+        outs = [g[k] for k in ("dmem0", "dv", "dalpha", "dbeta", "dwt_w", "dwt_r")]
+
+        def fn(job):
+            b, h = job
+            return self.L.oracle_scan_grad(C.byref(cs), *[_ptr(a) for a in arrs], _ptr(dout),
+                                           *[_ptr(a) for a in outs], b, h)
+
+        jobs = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+        threads = threads or default_threads()
+        if threads == 1 or len(jobs) == 1:
+            rcs = [fn(j) for j in jobs]
+        else:
+            with ThreadPoolExecutor(min(threads, len(jobs))) as ex:
+                rcs = list(ex.map(fn, jobs))
+        if any(rcs):
+            raise ValueError("oracle_scan_grad rejected its arguments")
+        return g
+
+    def weights_f64(self, cfg, q_row, subkeys, h, slots) -> np.ndarray:
+        cs = _cfg_struct(cfg)
+        q_row = np.ascontiguousarray(q_row, np.float64)
+        subkeys = np.ascontiguousarray(subkeys, np.float64)
+        slots = np.ascontiguousarray(slots, np.int32)
+        w = np.empty(cfg.W, np.float64)
+        if self.L.oracle_weights_f64(C.byref(cs), _ptr(q_row), _ptr(subkeys), int(h), _ptr(slots), _ptr(w)):
+            raise ValueError("oracle_weights_f64 rejected its arguments")
+        return w
+
+    def address_grad(self, cfg, q, subkeys, idx, sigma, dwt):
+        """(dq [R, dk], dsub [H,2,S,dh]) in float64 for all rows."""
+        cs = _cfg_struct(cfg)
+        q = np.ascontiguousarray(q)
+        subkeys = np.ascontiguousarray(subkeys)
+        idx = np.ascontiguousarray(idx, np.int32)
+        sigma = np.ascontiguousarray(sigma, np.float32)
+        dwt = np.ascontiguousarray(dwt, np.float64)
+        R = cfg.B * cfg.T * cfg.H
+        dq = np.zeros((R, cfg.dk))
+        dsub = np.zeros((cfg.H, 2, cfg.S, cfg.dk // 2))
+        if self.L.oracle_address_grad(C.byref(cs), _ptr(q), _ptr(subkeys), 0, R, _ptr(idx), _ptr(sigma), _ptr(dwt),
+                                      _ptr(dq), _ptr(dsub)):
+            raise ValueError("oracle_address_grad rejected its arguments")
+        return dq, dsub
+
+
 _default = None
+_default_grad = None
+
+
+def get_grad() -> GradOracle:
+    global _default_grad
+    if _default_grad is None:
+        _default_grad = GradOracle()
+    return _default_grad
 
 
 def get() -> Oracle:

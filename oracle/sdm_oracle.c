@@ -58,14 +58,20 @@ static double load_in(const void* p, size_t i, int bf16)
     return bf16 ? bf16_to_double(((const uint16_t*)p)[i]) : (double)((const float*)p)[i];
 }
 
-static double load_state(const void* mem, size_t i, int bf16)
+/* State storage kinds: 0 float32, 1 bf16 bits, 2 float64 (no rounding at
+ * store; used only to check derivatives by finite differences). */
+static double load_state(const void* mem, size_t i, int kind)
 {
-    return load_in(mem, i, bf16);
+    if (kind == 2)
+        return ((const double*)mem)[i];
+    return load_in(mem, i, kind);
 }
 
-static void store_state(void* mem, size_t i, double x, int bf16)
+static void store_state(void* mem, size_t i, double x, int kind)
 {
-    if (bf16)
+    if (kind == 2)
+        ((double*)mem)[i] = x;
+    else if (kind)
         ((uint16_t*)mem)[i] = oracle_bf16_round(x);
     else
         ((float*)mem)[i] = (float)x; /* nearest-even */

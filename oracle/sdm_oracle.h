@@ -45,7 +45,7 @@ extern "C" {
 typedef struct {
     int B, H, T, d, S, dk, k, W;
     int in_bf16;    /* q, v, subkeys are bf16 bits when 1, float32 when 0 */
-    int state_bf16; /* mem is bf16 bits when 1, float32 when 0 */
+    int state_bf16; /* mem is bf16 bits when 1, float32 when 0, float64 when 2 (finite-difference checks) */
 } oracle_cfg;
 
 /* bf16 bits nearest (ties to even) to a double; NaN -> quiet NaN. */
