@@ -165,6 +165,97 @@ def decode_bench(args, cfg):
     print(json.dumps(res))
 
 
+def train_bench(args, cfg):
+    """One training step of the layer: sdm_forward_train (the forward, logging every write
+    slot's old value), then sdm_backward (the reverse walk, the softmax derivative, query and
+    sub-key gradients), with the gradient buffer of the initial memory zeroed first.  The
+    backward restores the memory, so every step starts from the same one."""
+    import numpy as np
+    import torch
+
+    import sdm_inputs as gi
+    from sparse_memory_linear_pk_amd import SDM
+
+    if cfg.state_bf16:
+        raise SystemExit("the backward pass is built for a float32 state; use the 1.4B-shaped workload")
+    log(f"generating inputs for {cfg}")
+    x = gi.make_inputs(cfg)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    f32 = dict(dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    dout = torch.randn((cfg.B, cfg.T, cfg.H, cfg.d), generator=gen, **f32)
+    out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32)
+    log_buf = torch.empty((cfg.B, cfg.T, cfg.H, cfg.W, cfg.d), **f32)
+    dmem = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), **f32)
+    g = {"dwq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32), "drq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32),
+         "dv": torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32), "dalpha": torch.empty((cfg.B, cfg.T, cfg.H), **f32),
+         "dbeta": torch.empty((cfg.B, cfg.T, cfg.H), **f32), "dsub": torch.empty((cfg.H, 2, cfg.S, cfg.dh), **f32)}
+    layer = SDM.from_config(cfg)
+    mem_check = d["mem0"][0, 0, :4096].clone()
+
+    def step():
+        dmem.zero_()
+        layer.forward_train(d["wq"], d["rq"], d["v"], d["alpha"], d["beta"], d["subkeys"], d["mem0"], out, log_buf)
+        layer.backward(d["wq"], d["rq"], d["v"], d["alpha"], d["beta"], d["subkeys"], d["mem0"], log_buf, dout, dmem,
+                       g["dwq"], g["drq"], g["dv"], g["dalpha"], g["dbeta"], g["dsub"])
+
+    steps = max(1, min(args.steps, 10))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    layer.set_timing(True)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+        log(f"train step {i + 1}/{steps}")
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    tm = layer.timing()
+    layer.close()
+    if not torch.equal(d["mem0"][0, 0, :4096], mem_check):
+        raise RuntimeError("the backward did not restore the memory")
+    for k, v in g.items():
+        if not torch.isfinite(v).all():
+            raise RuntimeError(f"non-finite {k}")
+    tokens = cfg.B * cfg.T
+    wd4 = cfg.W * cfg.d * 4
+    bwd_bytes = tokens * cfg.H * 7 * wd4     # reads M, G (read slots), G, log (write slots); writes G, G, M
+    fwd_bytes = tokens * cfg.H * 4 * wd4     # 2W rows read, W written, W logged
+    bwd_ms = tm["ms_bwd_scan"] / max(1, tm["n_bwd_scan"])
+    fwd_ms = tm["ms_train"] / max(1, tm["n_train"])
+    res = {
+        "metric": "SDM layer training step tokens/sec (1 GPU): sdm_forward_train + sdm_backward",
+        "value": tokens * steps / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded inputs as for the forward; upstream gradient of out ~N(0,1), none of the final memory)",
+        "config": {"workload": f"sdm-{cfg.name} layer training step: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} "
+                               f"N={cfg.S}^2 dk={cfg.dk} k={cfg.k} W={cfg.W}", "global_batch": cfg.B,
+                   "seq_len": cfg.T, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "grad_scan", "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
+                     "peak": 8000.0, "unit": "GB/s", "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / 8000.0,
+                     "traffic": None, "bytes_per_launch": bwd_bytes, "ms_per_launch": bwd_ms},
+        "kernels_ms_per_step": {"train_scan": fwd_ms, "train_scan_GBps": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+                                "pk_score": tm["ms_score"] / steps, "pk_topk": tm["ms_select"] / steps,
+                                "grad_scan": bwd_ms, "grad_rows": tm["ms_bwd_rows"] / steps,
+                                "grad_subkeys": tm["ms_bwd_sub"] / steps},
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +268,8 @@ def main():
                          "4 8B-shaped: bf16 state)")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode step (sdm_step, one token per sequence per call) instead of the forward")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step (sdm_forward_train + sdm_backward) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 4 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -204,6 +297,8 @@ def main():
     cfg = gi.config(args.workload)
     if args.decode:
         return decode_bench(args, cfg)
+    if args.train:
+        return train_bench(args, cfg)
     log(f"generating inputs for {cfg}")
     t0 = time.perf_counter()
     x = gi.make_inputs(cfg)

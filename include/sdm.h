@@ -94,6 +94,11 @@ typedef struct {
     long long n_score, n_select, n_plan, n_scan; /* launches timed */
     double ms_step;    /* decode steps (sdm_step), both of their kernels */
     long long n_step;  /* steps timed */
+    double ms_train;     /* the logging scan of sdm_forward_train */
+    double ms_bwd_scan;  /* the reverse walk of sdm_backward */
+    double ms_bwd_rows;  /* per-row reduction, softmax derivative, query gradients */
+    double ms_bwd_sub;   /* sub-key gradients */
+    long long n_train, n_bwd_scan, n_bwd_rows, n_bwd_sub;
 } sdm_timing;
 
 /* Supported shapes: 1 <= k <= min(S, 64); 1 <= W <= min(k*k, 64); S <= 1024;
@@ -111,8 +116,8 @@ SDM_API sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, con
                        const float* beta, const void* subkeys, void* mem_inout, float* out);
 
 /* One token of the layer over a persistent memory (decode): the same operation
- * as sdm_forward with T = 1 for B sequences and H heads, in two launches sized
- * for a single token; T consecutive steps leave exactly the memory and outputs
+ * as sdm_forward with T = 1 for B sequences and H heads, in one or two launches
+ * sized for a single token; T consecutive steps leave exactly the memory and outputs
  * of one T-token forward.  Tensors of the token: wq, rq [B, H, dk] in_dtype;
  * v [B, H, d] in_dtype; alpha, beta [B, H] float32; out [B, H, d] float32;
  * subkeys and mem_inout as for sdm_forward.  The handle's T is not used.
@@ -121,6 +126,47 @@ SDM_API sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, con
  * cost does not grow with the sequence.) */
 SDM_API sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                             const float* beta, const void* subkeys, void* mem_inout, float* out);
+
+/* Training forward: exactly sdm_forward's memory and outputs, and the value of
+ * every write slot before its write, saved to log [B, T, H, W, d] (float32;
+ * entry ((b*T + t)*H + h)*W + i is write position i of token t, best first),
+ * which sdm_backward consumes.  The log holds B*T*H*W*d*4 bytes (17.2 GB for
+ * B=4, T=8192, H=1, W=64, d=2048), owned by the caller.  The scan runs as T
+ * consecutive one-token steps of each memory (the decode step's arithmetic),
+ * one launch for the call.  SDM_ERR_UNSUPPORTED unless the state is float32
+ * and d is a multiple of 32.  (SDM blog post, section "How does SDM work?":
+ * the decay and delta-rule write whose inputs the log keeps.) */
+SDM_API sdm_status sdm_forward_train(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
+                                     const float* beta, const void* subkeys, void* mem_inout, float* out, void* log);
+
+/* Device bytes sdm_backward allocates on its first call on a handle (kept
+ * until sdm_destroy): per-column partial sums [B*T*H, d/32, 2W+2], dense
+ * softmax-derivative rows [2, B*T*H, 2, S] and split sub-key sums, all float32. */
+SDM_API sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* bytes);
+
+/* Backward pass of sdm_forward_train, by reverse-mode differentiation of the
+ * forward (SDM blog post, section "How does SDM work?", its "Write & Read"
+ * subsection and the caption of the figure "The SDM mechanism, end to end"):
+ * the selected slots are held fixed (top-k and top-W are piecewise constant),
+ * and the rounding of stored values is passed straight through.
+ * Inputs as given to sdm_forward_train (wq, rq, v, alpha, beta, subkeys), and:
+ *   mem_inout  float32 [B, H, N, d]: the memory sdm_forward_train left; the
+ *              reverse walk restores it, bit for bit, to the memory before it
+ *   log        that call's log [B, T, H, W, d], read only
+ *   dout       float32 [B, T, H, d]: dL/d(out)
+ *   dmem_inout float32 [B, H, N, d]: in dL/d(final memory) (zeros if the
+ *              loss does not use it), out dL/d(initial memory)
+ * Outputs, float32, overwritten: dwq, drq [B, T, H, dk]; dv [B, T, H, d];
+ * dalpha, dbeta [B, T, H]; dsubkeys [H, 2, S, dk/2].
+ * The addressing of both query sets is recomputed by the forward's kernels, so
+ * the slots are those the forward used.  Allocates its workspace on the first
+ * call (sdm_backward_workspace_bytes).  Deterministic: every sum has a fixed
+ * order.  SDM_ERR_UNSUPPORTED unless the state is float32 and d is a multiple
+ * of 32. */
+SDM_API sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
+                                const float* beta, const void* subkeys, void* mem_inout, const void* log,
+                                const float* dout, float* dmem_inout, float* dwq, float* drq, float* dv,
+                                float* dalpha, float* dbeta, float* dsubkeys);
 
 /* Free the workspace and the handle.  Waits for the handle's stream first. */
 SDM_API sdm_status sdm_destroy(sdm_handle h);

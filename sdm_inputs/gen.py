@@ -14,6 +14,7 @@ CHUNK = 1 << 22
 
 # tensor ids
 _WQ, _RQ, _V, _ALPHA, _BETA, _SUBKEYS, _MEM0, _CENTROIDS, _PICK_W, _PICK_R, _NOISE_W, _NOISE_R = range(1, 13)
+_DOUT, _DMEM = 13, 14
 
 
 @dataclasses.dataclass(frozen=True)
@@ -192,3 +193,10 @@ def make_inputs(cfg: Config, seed: int = 0, threads=None, with_mem0: bool = True
     if with_mem0:
         out["mem0"] = make_mem0(cfg, seed, threads)
     return out
+
+
+def make_upstream_grads(cfg: Config, seed: int = 0, dmem_std: float = 0.1, threads=None) -> dict:
+    """Seeded upstream gradients for a backward pass: dout [B, T, H, d] ~ N(0, 1) and
+    dmem [B, H, N, d] ~ N(0, dmem_std) (the gradient reaching the final memory), float32."""
+    return {"dout": normal_f32((cfg.B, cfg.T, cfg.H, cfg.d), seed, _DOUT, 1.0, threads),
+            "dmem": normal_f32((cfg.B, cfg.H, cfg.N, cfg.d), seed, _DMEM, dmem_std, threads)}

@@ -87,6 +87,31 @@ class SDM:
                 self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, H, d), "f32")]
         check(lib().sdm_step(self._h, *[_ptr(a) for a in args]), "sdm_step")
 
+    def forward_train(self, wq, rq, v, alpha, beta, subkeys, mem, out, log):
+        """sdm_forward, and every write slot's value before its write into log [B, T, H, W, d] float32."""
+        B, H, T, d, S, dk, k, W = self._dims()
+        args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
+                self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
+                self._t(beta, "beta", (B, T, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
+                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, T, H, d), "f32"),
+                self._t(log, "log", (B, T, H, W, d), "f32")]
+        check(lib().sdm_forward_train(self._h, *[_ptr(a) for a in args]), "sdm_forward_train")
+
+    def backward(self, wq, rq, v, alpha, beta, subkeys, mem, log, dout, dmem, dwq, drq, dv, dalpha, dbeta, dsubkeys):
+        """Gradients of sdm_forward_train: mem is restored to the initial memory and dmem goes from
+        dL/d(final memory) to dL/d(initial memory); the other gradients are written."""
+        B, H, T, d, S, dk, k, W = self._dims()
+        args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
+                self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
+                self._t(beta, "beta", (B, T, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
+                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(log, "log", (B, T, H, W, d), "f32"),
+                self._t(dout, "dout", (B, T, H, d), "f32"), self._t(dmem, "dmem", (B, H, S * S, d), "f32"),
+                self._t(dwq, "dwq", (B, T, H, dk), "f32"), self._t(drq, "drq", (B, T, H, dk), "f32"),
+                self._t(dv, "dv", (B, T, H, d), "f32"), self._t(dalpha, "dalpha", (B, T, H), "f32"),
+                self._t(dbeta, "dbeta", (B, T, H), "f32"),
+                self._t(dsubkeys, "dsubkeys", (H, 2, S, dk // 2), "f32")]
+        check(lib().sdm_backward(self._h, *[_ptr(a) for a in args]), "sdm_backward")
+
     def score(self, q, subkeys, scores):
         B, H, T, d, S, dk, k, W = self._dims()
         args = [self._t(q, "q", (B, T, H, dk), "in"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
@@ -129,6 +154,13 @@ class SDM:
         cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32, SDM_BF16 if state_bf16 else SDM_F32)
         n = C.c_size_t()
         check(lib().sdm_workspace_bytes(C.byref(cfg), C.byref(n)), "sdm_workspace_bytes")
+        return n.value
+
+    @staticmethod
+    def backward_workspace_bytes(B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False) -> int:
+        cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32, SDM_BF16 if state_bf16 else SDM_F32)
+        n = C.c_size_t()
+        check(lib().sdm_backward_workspace_bytes(C.byref(cfg), C.byref(n)), "sdm_backward_workspace_bytes")
         return n.value
 
     def close(self):

@@ -30,7 +30,9 @@ class Timing(C.Structure):
     _fields_ = [("ms_score", C.c_double), ("ms_select", C.c_double), ("ms_plan", C.c_double),
                 ("ms_scan", C.c_double), ("n_score", C.c_longlong), ("n_select", C.c_longlong),
                 ("n_plan", C.c_longlong), ("n_scan", C.c_longlong), ("ms_step", C.c_double),
-                ("n_step", C.c_longlong)]
+                ("n_step", C.c_longlong), ("ms_train", C.c_double), ("ms_bwd_scan", C.c_double),
+                ("ms_bwd_rows", C.c_double), ("ms_bwd_sub", C.c_double), ("n_train", C.c_longlong),
+                ("n_bwd_scan", C.c_longlong), ("n_bwd_rows", C.c_longlong), ("n_bwd_sub", C.c_longlong)]
 
 
 def declared_symbols(header: str = HEADER) -> list[str]:
@@ -55,6 +57,9 @@ def lib() -> C.CDLL:
         "sdm_create": ([C.POINTER(Config), vp, C.POINTER(C.c_void_p)], C.c_int),
         "sdm_forward": ([h, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
         "sdm_step": ([h, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
+        "sdm_forward_train": ([h, vp, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
+        "sdm_backward_workspace_bytes": ([C.POINTER(Config), C.POINTER(C.c_size_t)], C.c_int),
+        "sdm_backward": ([h] + [vp] * 16, C.c_int),
         "sdm_destroy": ([h], C.c_int),
         "sdm_status_str": ([C.c_int], C.c_char_p),
         "sdm_last_error": ([], C.c_char_p),

@@ -28,7 +28,8 @@ sdm_status fail(sdm_status s, const char* fmt, ...)
     return s;
 }
 
-enum Kind { K_SCORE = 0, K_SELECT = 1, K_PLAN = 2, K_SCAN = 3, K_STEP = 4 };
+enum Kind { K_SCORE = 0, K_SELECT = 1, K_PLAN = 2, K_SCAN = 3, K_STEP = 4, K_TRAIN = 5, K_BWD_SCAN = 6,
+            K_BWD_ROWS = 7, K_BWD_SUB = 8 };
 
 struct TimedLaunch {
     Kind kind;
@@ -161,6 +162,12 @@ struct sdm_ctx {
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
+    // backward workspace, allocated by the first sdm_backward call
+    void* bwd_block;
+    float* part;
+    float* ds;
+    float* sub_part;
+    int nsplit;
 };
 
 namespace {
@@ -286,6 +293,29 @@ sdm_status run_chunk_front(sdm_ctx* h, int ci, const void* wq, const void* rq, c
     return s == SDM_OK ? run_plan(h, ci, h->idx[0], h->wt[0], h->idx[1], h->wt[1], alpha, beta, st) : s;
 }
 
+// Scores and selection of both query sets for every row of the call, on st.
+sdm_status run_address_all(sdm_ctx* h, const void* wq, const void* rq, const void* subkeys, hipStream_t st)
+{
+    const sdm::Rows r = all_rows(h->cfg);
+    const void* q[2] = {wq, rq};
+    sdm_status s = SDM_OK;
+    for (int set = 0; set < 2 && s == SDM_OK; ++set) {
+        s = run_score(h, q[set], subkeys, h->scores, r, st, set == 0);
+        if (s == SDM_OK)
+            s = run_select(h, h->scores, h->idx[set], h->wt[set], r, st);
+    }
+    return s;
+}
+
+sdm_status check_train_shape(const sdm_config& c, const char* who)
+{
+    if (c.state_dtype != SDM_F32)
+        return fail(SDM_ERR_UNSUPPORTED, "%s: the backward pass is built for a float32 state", who);
+    if (c.d % 32)
+        return fail(SDM_ERR_UNSUPPORTED, "%s: d=%d must be a multiple of 32 (128-byte slot columns)", who, c.d);
+    return SDM_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -342,6 +372,9 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->aux = nullptr;
     h->e_start = nullptr;
     h->timing = false;
+    h->bwd_block = nullptr;
+    h->part = h->ds = h->sub_part = nullptr;
+    h->nsplit = 0;
     memset(&h->totals, 0, sizeof h->totals);
     e = hipMalloc(&h->block, h->L.total);
     if (e != hipSuccess) {
@@ -405,6 +438,10 @@ sdm_status sdm_destroy(sdm_handle h)
         (void)hipEventDestroy(tl.stop);
     }
     hipError_t e2 = hipFree(h->block);
+    if (h->bwd_block) {
+        const hipError_t e3 = hipFree(h->bwd_block);
+        e2 = e2 == hipSuccess ? e3 : e2;
+    }
     h->magic = 0;
     delete h;
     if (e != hipSuccess)
@@ -535,6 +572,141 @@ sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v,
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_step launch");
 }
 
+sdm_status sdm_forward_train(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
+                             const float* beta, const void* subkeys, void* mem_inout, float* out, void* log)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!wq || !rq || !v || !alpha || !beta || !subkeys || !mem_inout || !out || !log)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_forward_train: NULL pointer");
+    if (!aligned16(wq) || !aligned16(rq) || !aligned16(v) || !aligned16(subkeys) || !aligned16(mem_inout) ||
+        !aligned16(out) || !aligned16(log) || !aligned4(alpha) || !aligned4(beta))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_forward_train: misaligned pointer");
+    const sdm_config& c = h->cfg;
+    if ((s = check_train_shape(c, "sdm_forward_train")) != SDM_OK)
+        return s;
+    if ((s = run_address_all(h, wq, rq, subkeys, h->stream)) != SDM_OK)
+        return s;
+    Timer t(h, K_TRAIN, h->stream);
+    hipError_t e = sdm::launch_sdm_train_scan(h->idx[0], h->wt[0], h->idx[1], h->wt[1], v, alpha, beta, mem_inout, out,
+                                              log, c.B, c.H, c.T, c.d, c.W, (long)c.n_sub * c.n_sub,
+                                              c.in_dtype == SDM_BF16, c.state_dtype == SDM_BF16, h->stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "train scan launch");
+}
+
+sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* bytes)
+{
+    std::vector<sdm::ScanPlan> plans;
+    sdm_status s = check_config(cfg, &plans);
+    if (s != SDM_OK)
+        return s;
+    if (!bytes)
+        return fail(SDM_ERR_INVALID_ARG, "bytes is NULL");
+    if ((s = check_train_shape(*cfg, "sdm_backward_workspace_bytes")) != SDM_OK)
+        return s;
+    const sdm_config& c = *cfg;
+    const size_t rows = (size_t)c.B * c.T * c.H;
+    const int nsplit = sdm::grad_sub_splits(c.B, c.H, c.T, c.n_sub, c.dk / 2);
+    *bytes = align_up(sdm::grad_part_floats(c.B, c.H, c.T, c.d, c.W) * 4) + align_up(2 * rows * 2 * c.n_sub * 4) +
+             align_up((size_t)nsplit * c.H * 2 * c.n_sub * (c.dk / 2) * 4);
+    return SDM_OK;
+}
+
+sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
+                        const float* beta, const void* subkeys, void* mem_inout, const void* log, const float* dout,
+                        float* dmem_inout, float* dwq, float* drq, float* dv, float* dalpha, float* dbeta,
+                        float* dsubkeys)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!wq || !rq || !v || !alpha || !beta || !subkeys || !mem_inout || !log || !dout || !dmem_inout || !dwq ||
+        !drq || !dv || !dalpha || !dbeta || !dsubkeys)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_backward: NULL pointer");
+    if (!aligned16(wq) || !aligned16(rq) || !aligned16(v) || !aligned16(subkeys) || !aligned16(mem_inout) ||
+        !aligned16(log) || !aligned16(dout) || !aligned16(dmem_inout) || !aligned16(dv) || !aligned4(dwq) ||
+        !aligned4(drq) || !aligned4(alpha) || !aligned4(beta) || !aligned4(dalpha) || !aligned4(dbeta) ||
+        !aligned4(dsubkeys))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_backward: misaligned pointer");
+    const sdm_config& c = h->cfg;
+    if ((s = check_train_shape(c, "sdm_backward")) != SDM_OK)
+        return s;
+    const size_t rows = (size_t)c.B * c.T * c.H;
+    if (!h->bwd_block) {
+        size_t bytes = 0;
+        if ((s = sdm_backward_workspace_bytes(&c, &bytes)) != SDM_OK)
+            return s;
+        hipError_t e = hipMalloc(&h->bwd_block, bytes);
+        if (e != hipSuccess) {
+            h->bwd_block = nullptr;
+            (void)hipGetLastError();
+            return fail(SDM_ERR_OOM, "backward workspace of %zu bytes: %s", bytes, hipGetErrorString(e));
+        }
+        char* p = (char*)h->bwd_block;
+        h->part = (float*)p;
+        p += align_up(sdm::grad_part_floats(c.B, c.H, c.T, c.d, c.W) * 4);
+        h->ds = (float*)p;
+        p += align_up(2 * rows * 2 * c.n_sub * 4);
+        h->sub_part = (float*)p;
+        h->nsplit = sdm::grad_sub_splits(c.B, c.H, c.T, c.n_sub, c.dk / 2);
+    }
+    // the forward's slots and weights, recomputed by the same kernels
+    if ((s = run_address_all(h, wq, rq, subkeys, h->stream)) != SDM_OK)
+        return s;
+    sdm::GradArgs a;
+    a.B = c.B;
+    a.H = c.H;
+    a.T = c.T;
+    a.d = c.d;
+    a.S = c.n_sub;
+    a.dh = c.dk / 2;
+    a.W = c.W;
+    a.in_bf16 = c.in_dtype == SDM_BF16;
+    a.mem = static_cast<float*>(mem_inout);
+    a.G = dmem_inout;
+    a.log = static_cast<const float*>(log);
+    for (int set = 0; set < 2; ++set) {
+        a.idx[set] = h->idx[set];
+        a.wt[set] = h->wt[set];
+    }
+    a.q[0] = wq;
+    a.q[1] = rq;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.subkeys = subkeys;
+    a.dout = dout;
+    a.dv = dv;
+    a.dalpha = dalpha;
+    a.dbeta = dbeta;
+    a.dq[0] = dwq;
+    a.dq[1] = drq;
+    a.dsub = dsubkeys;
+    a.part = h->part;
+    a.ds = h->ds;
+    a.sub_part = h->sub_part;
+    a.nsplit = h->nsplit;
+    hipError_t e;
+    {
+        Timer t(h, K_BWD_SCAN, h->stream);
+        e = sdm::launch_grad_scan(a, h->stream);
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "backward scan launch");
+    {
+        Timer t(h, K_BWD_ROWS, h->stream);
+        e = sdm::launch_grad_rows(a, h->stream);
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "backward rows launch");
+    {
+        Timer t(h, K_BWD_SUB, h->stream);
+        e = sdm::launch_grad_subkeys(a, h->stream);
+    }
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sub-key gradient launch");
+}
+
 sdm_status sdm_set_timing(sdm_handle h, int enable)
 {
     sdm_status s = check_handle(h);
@@ -571,6 +743,10 @@ sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t)
         case K_PLAN: h->totals.ms_plan += ms; h->totals.n_plan++; break;
         case K_SCAN: h->totals.ms_scan += ms; h->totals.n_scan++; break;
         case K_STEP: h->totals.ms_step += ms; h->totals.n_step++; break;
+        case K_TRAIN: h->totals.ms_train += ms; h->totals.n_train++; break;
+        case K_BWD_SCAN: h->totals.ms_bwd_scan += ms; h->totals.n_bwd_scan++; break;
+        case K_BWD_ROWS: h->totals.ms_bwd_rows += ms; h->totals.n_bwd_rows++; break;
+        case K_BWD_SUB: h->totals.ms_bwd_sub += ms; h->totals.n_bwd_sub++; break;
         }
         (void)hipEventDestroy(tl.start);
         (void)hipEventDestroy(tl.stop);

@@ -148,6 +148,45 @@ hipError_t launch_sdm_step(const void* wq, const void* rq, const void* v, const 
                            const void* subkeys, void* mem, float* out, int32_t* idx, float* wt, int B, int H, int d,
                            int S, int dh, int k, int W, bool in_bf16, bool state_bf16, hipStream_t stream);
 
+// The forward scan of a whole call as consecutive steps, saving every write
+// slot's value before its write to log [rows, W, d] (state type).  Rows are
+// (b, t, h); idx/wt [rows, W].
+hipError_t launch_sdm_train_scan(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
+                                 const void* v, const float* alpha, const float* beta, void* mem, float* out,
+                                 void* log, int B, int H, int T, int d, int W, long N, bool in_bf16, bool state_bf16,
+                                 hipStream_t stream);
+
+// The backward pass (float32 state; d a multiple of 32).
+struct GradArgs {
+    int B, H, T, d, S, dh, W;
+    bool in_bf16;
+    float* mem;                          // [B*H, N, d]: memory after the forward in, before it out
+    float* G;                            // [B*H, N, d]: dL/d(memory after) in, dL/d(memory before) out
+    const float* log;                    // [rows, W, d]
+    const int32_t* idx[2];               // write, read slots [rows, W]
+    const float* wt[2];                  // their weights
+    const void* q[2];                    // wq, rq [rows, dk]
+    const void* v;                       // [rows, d]
+    const float* alpha;                  // [rows]
+    const float* beta;                   // [rows]
+    const void* subkeys;                 // [H, 2, S, dh]
+    const float* dout;                   // [rows, d]
+    float* dv;                           // [rows, d]
+    float* dalpha;                       // [rows]
+    float* dbeta;                        // [rows]
+    float* dq[2];                        // dwq, drq [rows, dk]
+    float* dsub;                         // [H, 2, S, dh]
+    float* part;                         // workspace: [rows, d/32, 2W+2]
+    float* ds;                           // workspace: [2, rows, 2, S]
+    float* sub_part;                     // workspace: [nsplit, H, 2, S, dh]
+    int nsplit;
+};
+size_t grad_part_floats(int B, int H, int T, int d, int W);
+int grad_sub_splits(int B, int H, int T, int S, int dh);
+hipError_t launch_grad_scan(const GradArgs& a, hipStream_t stream);
+hipError_t launch_grad_rows(const GradArgs& a, hipStream_t stream);
+hipError_t launch_grad_subkeys(const GradArgs& a, hipStream_t stream);
+
 // Measurement only: the scan's traffic pattern without arithmetic on `memories`
 // memories of `rows` rows of row_bytes (a multiple of 128) bytes.
 hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, uint32_t seed,

@@ -9,7 +9,7 @@ from sparse_memory_linear_pk_amd._lib import Config, Timing, SDM_OK, SDM_ERR_INV
 
 EXPECTED = ["sdm_create", "sdm_forward", "sdm_destroy", "sdm_status_str", "sdm_last_error", "sdm_workspace_bytes",
             "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing",
-            "sdm_pattern_probe", "sdm_step"]
+            "sdm_pattern_probe", "sdm_step", "sdm_forward_train", "sdm_backward_workspace_bytes", "sdm_backward"]
 
 
 def _cfg(**kw):
@@ -71,7 +71,7 @@ def test_null_arguments():
     assert L.sdm_workspace_bytes(None, None) == SDM_ERR_INVALID_ARG
     assert L.sdm_create(C.byref(_cfg()), None, None) == SDM_ERR_INVALID_ARG
     for f, n in (("sdm_forward", 8), ("sdm_score", 3), ("sdm_select", 3), ("sdm_address", 4),
-                 ("sdm_scan_with", 9), ("sdm_step", 8)):
+                 ("sdm_scan_with", 9), ("sdm_step", 8), ("sdm_forward_train", 9), ("sdm_backward", 16)):
         assert getattr(L, f)(None, *([None] * n)) == SDM_ERR_INVALID_ARG, f
     assert L.sdm_destroy(None) == SDM_ERR_INVALID_ARG
     assert L.sdm_set_timing(None, 1) == SDM_ERR_INVALID_ARG
@@ -98,3 +98,22 @@ def test_pattern_probe_rejects_bad_arguments_on_the_host(mem, memories, rows, ro
     L = _lib.lib()
     assert L.sdm_pattern_probe(mem, memories, rows, row_bytes, T, W, 0, None) == SDM_ERR_INVALID_ARG
     assert L.sdm_last_error().startswith(b"sdm_pattern_probe")
+
+
+def test_backward_workspace_for_the_1p4b_shape():
+    """Column partials (2W+2 floats per row and 128-byte column), dense dsigma rows of both query
+    sets, and the split sub-key sums."""
+    L = _lib.lib()
+    n = C.c_size_t()
+    assert L.sdm_backward_workspace_bytes(C.byref(_cfg()), C.byref(n)) == SDM_OK
+    rows = 4 * 8192
+    assert n.value >= rows * 64 * 130 * 4 + 2 * rows * 2 * 480 * 4
+
+
+@pytest.mark.parametrize("kw", [dict(state_dtype=1, n_sub=240), dict(d=2040)])
+def test_backward_rejects_what_it_does_not_build(kw):
+    """A bf16 state, and slot rows that are not whole 128-byte float32 columns."""
+    L = _lib.lib()
+    n = C.c_size_t()
+    assert L.sdm_backward_workspace_bytes(C.byref(_cfg(**kw)), C.byref(n)) == SDM_ERR_UNSUPPORTED
+    assert b"sdm_backward" in L.sdm_last_error()
