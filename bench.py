@@ -191,7 +191,7 @@ def train_bench(args, cfg):
     gen = torch.Generator(device="cuda").manual_seed(7)
     dout = torch.randn((cfg.B, cfg.T, cfg.H, cfg.d), generator=gen, **f32)
     out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32)
-    log_buf = torch.empty((cfg.B, cfg.T, cfg.H, cfg.W, cfg.d), **f32)
+    log_buf = torch.empty((cfg.B, cfg.H, cfg.T, cfg.W, cfg.d), **f32)
     dmem = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), **f32)
     g = {"dwq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32), "drq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32),
          "dv": torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32), "dalpha": torch.empty((cfg.B, cfg.T, cfg.H), **f32),
@@ -228,7 +228,7 @@ def train_bench(args, cfg):
     bwd_bytes = tokens * cfg.H * 7 * wd4     # reads M, G (read slots), G, log (write slots); writes G, G, M
     fwd_bytes = tokens * cfg.H * 4 * wd4     # 2W rows read, W written, W logged
     bwd_ms = tm["ms_bwd_scan"] / max(1, tm["n_bwd_scan"])
-    fwd_ms = tm["ms_train"] / max(1, tm["n_train"])
+    fwd_ms = tm["ms_train"] / steps  # the forward's scan launches (one per chunk)
     res = {
         "metric": "SDM layer training step tokens/sec (1 GPU): sdm_forward_train + sdm_backward",
         "value": tokens * steps / sec,

@@ -127,15 +127,15 @@ SDM_API sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, con
 SDM_API sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                             const float* beta, const void* subkeys, void* mem_inout, float* out);
 
-/* Training forward: exactly sdm_forward's memory and outputs, and the value of
- * every write slot before its write, saved to log [B, T, H, W, d] (float32;
- * entry ((b*T + t)*H + h)*W + i is write position i of token t, best first),
- * which sdm_backward consumes.  The log holds B*T*H*W*d*4 bytes (17.2 GB for
- * B=4, T=8192, H=1, W=64, d=2048), owned by the caller.  The scan runs as T
- * consecutive one-token steps of each memory (the decode step's arithmetic),
- * one launch for the call.  SDM_ERR_UNSUPPORTED unless the state is float32
- * and d is a multiple of 32.  (SDM blog post, section "How does SDM work?":
- * the decay and delta-rule write whose inputs the log keeps.) */
+/* Training forward: exactly sdm_forward's memory and outputs (the same
+ * launches; the scan also stores), and the bits of every write slot before its
+ * write, saved to log [B, H, T, W, d] (float32; entry ((b*H + h)*T + t)*W + i
+ * is write position i of token t, best first), which sdm_backward consumes.
+ * The log holds B*H*T*W*d*4 bytes (17.2 GB for B=4, H=1, T=8192, W=64,
+ * d=2048), owned by the caller.  SDM_ERR_UNSUPPORTED unless the state is
+ * float32, d is a multiple of 32 and one memory's log of a scan chunk (up to
+ * 3071 tokens) stays below 4 GiB.  (SDM blog post, section "How does SDM
+ * work?": the decay and delta-rule write whose inputs the log keeps.) */
 SDM_API sdm_status sdm_forward_train(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                                      const float* beta, const void* subkeys, void* mem_inout, float* out, void* log);
 
@@ -152,7 +152,7 @@ SDM_API sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* b
  * Inputs as given to sdm_forward_train (wq, rq, v, alpha, beta, subkeys), and:
  *   mem_inout  float32 [B, H, N, d]: the memory sdm_forward_train left; the
  *              reverse walk restores it, bit for bit, to the memory before it
- *   log        that call's log [B, T, H, W, d], read only
+ *   log        that call's log [B, H, T, W, d], read only
  *   dout       float32 [B, T, H, d]: dL/d(out)
  *   dmem_inout float32 [B, H, N, d]: in dL/d(final memory) (zeros if the
  *              loss does not use it), out dL/d(initial memory)

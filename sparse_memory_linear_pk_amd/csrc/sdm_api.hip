@@ -253,7 +253,8 @@ sdm_status run_plan(sdm_ctx* h, int ci, const int32_t* idx_w, const float* wt_w,
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_plan launch");
 }
 
-sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hipStream_t st)
+sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hipStream_t st, void* log = nullptr,
+                    Kind kind = K_SCAN)
 {
     const sdm_config& c = h->cfg;
     const sdm::ScanPlan& p = plan_of(h, ci);
@@ -265,6 +266,7 @@ sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hi
     a.v = static_cast<const char*>(v) + first * (c.in_dtype == SDM_BF16 ? 2 : 4);
     a.mem = mem;
     a.out = out + first;
+    a.log = log ? static_cast<char*>(log) + (size_t)r.t0 * c.W * c.d * 4u : nullptr;
     a.B = c.B;
     a.T = r.Tc;
     a.Ts = c.T;
@@ -273,7 +275,7 @@ sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hi
     a.W = c.W;
     a.Tp = p.Tp;
     a.N = (long)c.n_sub * c.n_sub;
-    Timer t(h, K_SCAN, st);
+    Timer t(h, kind, st);
     hipError_t e = sdm::launch_sdm_scan(a, p, c.state_dtype == SDM_BF16, c.in_dtype == SDM_BF16, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan launch");
 }
@@ -307,12 +309,19 @@ sdm_status run_address_all(sdm_ctx* h, const void* wq, const void* rq, const voi
     return s;
 }
 
+sdm_status forward_impl(sdm_ctx* h, const void* wq, const void* rq, const void* v, const float* alpha,
+                        const float* beta, const void* subkeys, void* mem_inout, float* out, void* log);
+
 sdm_status check_train_shape(const sdm_config& c, const char* who)
 {
     if (c.state_dtype != SDM_F32)
         return fail(SDM_ERR_UNSUPPORTED, "%s: the backward pass is built for a float32 state", who);
     if (c.d % 32)
         return fail(SDM_ERR_UNSUPPORTED, "%s: d=%d must be a multiple of 32 (128-byte slot columns)", who, c.d);
+    const Chunking k = chunking_of(c);
+    for (int ci = 0; ci < k.C(); ++ci)
+        if ((uint64_t)k.len(ci) * c.W * c.d * 4u >= (1ull << 32) - 16u)
+            return fail(SDM_ERR_UNSUPPORTED, "%s: one memory's log of a %d-token chunk exceeds 4 GiB", who, k.len(ci));
     return SDM_OK;
 }
 
@@ -519,9 +528,22 @@ sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void*
     if (!aligned16(wq) || !aligned16(rq) || !aligned16(v) || !aligned16(subkeys) || !aligned16(mem_inout) ||
         !aligned16(out) || !aligned4(alpha) || !aligned4(beta))
         return fail(SDM_ERR_INVALID_ARG, "sdm_forward: misaligned pointer");
+    return forward_impl(h, wq, rq, v, alpha, beta, subkeys, mem_inout, out, nullptr);
+}
+
+} // extern "C"
+
+namespace {
+
+// The forward's launches; with log, the scans also keep every write slot's old value.
+sdm_status forward_impl(sdm_ctx* h, const void* wq, const void* rq, const void* v, const float* alpha,
+                        const float* beta, const void* subkeys, void* mem_inout, float* out, void* log)
+{
+    sdm_status s = SDM_OK;
+    const Kind kind = log ? K_TRAIN : K_SCAN;
     if (h->ck.C() == 1) {
         s = run_chunk_front(h, 0, wq, rq, alpha, beta, subkeys, h->stream);
-        return s == SDM_OK ? run_scan(h, 0, v, mem_inout, out, h->stream) : s;
+        return s == SDM_OK ? run_scan(h, 0, v, mem_inout, out, h->stream, log, kind) : s;
     }
     // Chunked: the addressing and plan of every chunk go to the aux stream in
     // order, after whatever the caller's stream holds before this call (its
@@ -542,12 +564,16 @@ sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, const void*
             e = hipStreamWaitEvent(h->stream, h->e_plan[ci], 0);
         if (e != hipSuccess)
             return hip_fail(e, "stream ordering");
-        s = run_scan(h, ci, v, mem_inout, out, h->stream);
+        s = run_scan(h, ci, v, mem_inout, out, h->stream, log, kind);
         if (s != SDM_OK)
             return s;
     }
     return SDM_OK;
 }
+
+} // namespace
+
+extern "C" {
 
 sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                     const float* beta, const void* subkeys, void* mem_inout, float* out)
@@ -586,13 +612,7 @@ sdm_status sdm_forward_train(sdm_handle h, const void* wq, const void* rq, const
     const sdm_config& c = h->cfg;
     if ((s = check_train_shape(c, "sdm_forward_train")) != SDM_OK)
         return s;
-    if ((s = run_address_all(h, wq, rq, subkeys, h->stream)) != SDM_OK)
-        return s;
-    Timer t(h, K_TRAIN, h->stream);
-    hipError_t e = sdm::launch_sdm_train_scan(h->idx[0], h->wt[0], h->idx[1], h->wt[1], v, alpha, beta, mem_inout, out,
-                                              log, c.B, c.H, c.T, c.d, c.W, (long)c.n_sub * c.n_sub,
-                                              c.in_dtype == SDM_BF16, c.state_dtype == SDM_BF16, h->stream);
-    return e == hipSuccess ? SDM_OK : hip_fail(e, "train scan launch");
+    return forward_impl(h, wq, rq, v, alpha, beta, subkeys, mem_inout, out, log);
 }
 
 sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* bytes)

@@ -83,27 +83,56 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
     const bool live[2] = {pos[0] < W, pos[1] < W};
     const int e0 = col * 32 + el * E; // this lane's first element of the row
 
-    for (int t = a.T - 1; t >= 0; --t) {
-        const long row = ((long)b * a.T + t) * a.H + h;
+    // Everything of a token that does not depend on the state (its slots and
+    // weights, the log of its write slots, dout, v and the gates) is fetched one
+    // token ahead, so that a token starts with its slot loads.
+    struct Meta {
         int32_t ws[2], rs[2];
         float ww[2], rw[2];
-        uint4 rv[2], rg[2], wg[2], wo[2];
+        uint4 wo[2];
+        float go[E], vv[E];
+        float al, be;
+    };
+    auto fetch = [&](int t, Meta& m) __attribute__((always_inline)) {
+        const long row = ((long)b * a.T + t) * a.H + h;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            ws[p] = live[p] ? a.idx[0][row * W + pos[p]] : -1;
-            rs[p] = live[p] ? a.idx[1][row * W + pos[p]] : -1;
-            ww[p] = live[p] ? a.wt[0][row * W + pos[p]] : 0.f;
-            rw[p] = live[p] ? a.wt[1][row * W + pos[p]] : 0.f;
+            m.ws[p] = live[p] ? a.idx[0][row * W + pos[p]] : -1;
+            m.rs[p] = live[p] ? a.idx[1][row * W + pos[p]] : -1;
+            m.ww[p] = live[p] ? a.wt[0][row * W + pos[p]] : 0.f;
+            m.rw[p] = live[p] ? a.wt[1][row * W + pos[p]] : 0.f;
+            m.wo[p] = live[p] ? *reinterpret_cast<const uint4*>(a.log + (((size_t)bh * a.T + t) * W + pos[p]) * a.d + e0)
+                              : make_uint4(0u, 0u, 0u, 0u);
+        }
+        load4(a.dout + (size_t)row * a.d + e0, m.go);
+        load4(static_cast<const VT*>(a.v) + (size_t)row * a.d + e0, m.vv);
+        m.al = a.alpha[row];
+        m.be = a.beta[row];
+    };
+    Meta cur;
+    fetch(a.T - 1, cur);
+
+    for (int t = a.T - 1; t >= 0; --t) {
+        const long row = ((long)b * a.T + t) * a.H + h;
+        const int32_t ws[2] = {cur.ws[0], cur.ws[1]}, rs[2] = {cur.rs[0], cur.rs[1]};
+        const float ww[2] = {cur.ww[0], cur.ww[1]}, rw[2] = {cur.rw[0], cur.rw[1]};
+        const uint4 wo[2] = {cur.wo[0], cur.wo[1]};
+        uint4 rv[2], rg[2], wg[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
             rv[p] = ld128(r_mem, live[p] ? (uint32_t)rs[p] * row_bytes + lane_off : kOOB);
             rg[p] = ld128(r_g, live[p] ? (uint32_t)rs[p] * row_bytes + lane_off : kOOB);
             wg[p] = ld128(r_g, live[p] ? (uint32_t)ws[p] * row_bytes + lane_off : kOOB);
-            wo[p] = live[p] ? *reinterpret_cast<const uint4*>(a.log + ((size_t)row * W + pos[p]) * a.d + e0)
-                            : make_uint4(0u, 0u, 0u, 0u);
         }
         float go[E], vv[E];
-        load4(a.dout + (size_t)row * a.d + e0, go);
-        load4(static_cast<const VT*>(a.v) + (size_t)row * a.d + e0, vv);
-        const float al = a.alpha[row], be = a.beta[row];
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+            go[q] = cur.go[q];
+            vv[q] = cur.vv[q];
+        }
+        const float al = cur.al, be = cur.be;
+        if (t > 0)
+            fetch(t - 1, cur);
         float* part = a.part + ((size_t)row * ncol + col) * P;
 
         // the read: the memory holds its state after token t's write

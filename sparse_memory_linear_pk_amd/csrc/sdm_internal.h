@@ -131,6 +131,8 @@ struct ScanArgs {
     const void* v;
     void* mem;
     float* out;
+    void* log;          // null, or the write slots' values before each write: memory (b, h) at
+                        // log + (b*H + h)*Ts*W*d, token t of the chunk at + t*W*d (staged form only)
     int B, T, Ts, H, d, W, Tp;
     long N;
 };
@@ -148,21 +150,13 @@ hipError_t launch_sdm_step(const void* wq, const void* rq, const void* v, const 
                            const void* subkeys, void* mem, float* out, int32_t* idx, float* wt, int B, int H, int d,
                            int S, int dh, int k, int W, bool in_bf16, bool state_bf16, hipStream_t stream);
 
-// The forward scan of a whole call as consecutive steps, saving every write
-// slot's value before its write to log [rows, W, d] (state type).  Rows are
-// (b, t, h); idx/wt [rows, W].
-hipError_t launch_sdm_train_scan(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
-                                 const void* v, const float* alpha, const float* beta, void* mem, float* out,
-                                 void* log, int B, int H, int T, int d, int W, long N, bool in_bf16, bool state_bf16,
-                                 hipStream_t stream);
-
 // The backward pass (float32 state; d a multiple of 32).
 struct GradArgs {
     int B, H, T, d, S, dh, W;
     bool in_bf16;
     float* mem;                          // [B*H, N, d]: memory after the forward in, before it out
     float* G;                            // [B*H, N, d]: dL/d(memory after) in, dL/d(memory before) out
-    const float* log;                    // [rows, W, d]
+    const float* log;                    // [B*H, T, W, d]
     const int32_t* idx[2];               // write, read slots [rows, W]
     const float* wt[2];                  // their weights
     const void* q[2];                    // wq, rq [rows, dk]

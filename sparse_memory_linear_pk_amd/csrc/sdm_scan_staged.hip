@@ -34,6 +34,11 @@
 // unforwarded slot names the ring's zero entry, so a read is the sum of a
 // register and, when any lane of the wave forwards, one LDS load.
 //
+// Log.  For training, the kernel can also store every write slot's value before
+// its write (the staged segment, or the ring entry it was forwarded from, bit for
+// bit) to a log that the reverse pass restores the memory from: four more stores
+// per pair, issued after the slot stores.
+//
 // Ordering.  Every wave issues the same vector-memory operations in the same
 // order for every pair (sentinel records and headers of the virtual tokens
 // before 0 and after T-1 give offsets past their buffers, which read zeros and
@@ -85,8 +90,9 @@ __device__ __forceinline__ void barrier_lds()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// ST: state element (float or bf16 bits), VT: v element (float or bf16 bits).
-template <class ST, class VT>
+// ST: state element (float or bf16 bits), VT: v element (float or bf16 bits),
+// LOG: also store the write slots' values before the write to a.log.
+template <class ST, class VT, bool LOG>
 __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
 {
     using C = Cell<ST>;
@@ -99,10 +105,10 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     constexpr int ZS = kStages, ZR = kRecSlots, ZL = 4;
     // Vector-memory operations of a pair, in issue order: at its start the loads
     // (per token of pair k+2 4 slot loads and NV of v; the records of pair k+4),
-    // then 2*NO out stores and 4 slot stores.  vmcnt(K) at the start of pair k
-    // leaves only pair k-1's operations in flight: pair k's data and pair k+2's
-    // records have landed and pair k-2's stores are done.
-    constexpr int K = 2 * (4 + NV) + 2 + 2 * NO + 4;
+    // then 2*NO out stores, 4 slot stores and, with LOG, 4 log stores.  vmcnt(K)
+    // at the start of pair k leaves only pair k-1's operations in flight: pair
+    // k's data and pair k+2's records have landed and pair k-2's stores are done.
+    constexpr int K = 2 * (4 + NV) + 2 + 2 * NO + 4 + (LOG ? 4 : 0);
     static_assert(K <= 63, "vmcnt");
 
     const int lane = threadIdx.x & 63;
@@ -124,9 +130,16 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     const size_t tok0 = (size_t)b * a.Ts * H;
     const __amdgpu_buffer_rsrc_t r_v = make_rsrc(static_cast<const VT*>(a.v) + tok0 * d, tok_elems * sizeof(VT));
     const __amdgpu_buffer_rsrc_t r_out = make_rsrc(a.out + tok0 * d, tok_elems * 4u);
+    // the log of this memory's tokens of the call: one row of W segments per token
+    const uint32_t log_tok = (uint32_t)a.W * row_bytes;
+    const __amdgpu_buffer_rsrc_t r_log =
+        make_rsrc(LOG ? static_cast<const char*>(a.log) + (size_t)bh * a.Ts * log_tok : nullptr,
+                  LOG ? (uint32_t)T * log_tok : 0u);
 
     // positions of this lane
     const int pos0 = (wave * 2) * 8 + g, pos1 = pos0 + 8;
+    const uint32_t lpos0 = pos0 < a.W ? (uint32_t)pos0 * row_bytes + lane_off : kOOB;
+    const uint32_t lpos1 = pos1 < a.W ? (uint32_t)pos1 * row_bytes + lane_off : kOOB;
     const uint4* ring_lane = g_ring + el;   // the zero entry
     uint4* ring_w = g_ring + kEntryU4 + el; // entry 0 of the stored segments
     // record loads: lane i < 16 fetches record 16w + i of a token, lane 16 the header
@@ -214,11 +227,28 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         reduce_to_part<E, CT>(acc, red, wave, el, lane);
     };
 
+    // The stored bits of this lane's two write slots before the write: the staged
+    // segment, or the ring entry a forwarded slot comes from.
+    auto old_bits = [&](const uint4 (&ss)[2], uint32_t f0, uint32_t f1, uint4& o0, uint4& o1)
+        __attribute__((always_inline)) {
+        constexpr uint32_t kField = 0x3FFu << kSlotBits;
+        o0 = ss[0];
+        o1 = ss[1];
+        if (forwards(f0, f1)) {
+            if (f0 & kField)
+                o0 = *ring_src(f0, ring_lane);
+            if (f1 & kField)
+                o1 = *ring_src(f1, ring_lane);
+        }
+    };
+
     // Write, second half (after the barrier that publishes red): the delta-rule
     // update of this lane's slots (the decayed values formed again, exactly as
-    // above), stored into the ring entry of the token in ring slot J.
+    // above), stored into the ring entry of the token in ring slot J; with LOG,
+    // the slots' bits before the update in o0, o1.
     auto update = [&](auto jc, const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float beta,
-                      const uint4 (&vraw)[NV], const float4* red, uint4& p0, uint4& p1) __attribute__((always_inline)) {
+                      const uint4 (&vraw)[NV], const float4* red, uint4& p0, uint4& p1, uint4& o0, uint4& o1)
+        __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;
         CT vh[E];
         sum_waves<E, CT>(red, el, vh);
@@ -249,6 +279,8 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         }
         float m0[E], m1[E];
         slot_values(ws, r0.x, r1.x, m0, m1);
+        if constexpr (LOG)
+            old_bits(ws, r0.x, r1.x, o0, o1);
         const CT w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z), al = alpha, be = beta;
         CT y0[E], y1[E];
 #pragma unroll
@@ -358,16 +390,16 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
             uint4 a0, a1, ha, b0, b1, hb;
             records(std::integral_constant<int, j0>{}, a0, a1, ha);
             records(std::integral_constant<int, j1>{}, b0, b1, hb);
-            uint4 ya0, ya1, yb0, yb1;
+            uint4 ya0, ya1, yb0, yb1, oa0, oa1, ob0, ob1;
             partials(wset[j0 % ZS], a0, a1, __uint_as_float(ha.x), g_red);
             partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), g_red + kPartU4);
             barrier_lds();
             store_out(std::integral_constant<int, p0>{}, g_ored, 0);
             store_out(std::integral_constant<int, p1>{}, g_ored + kPartU4, 1);
             update(std::integral_constant<int, j0>{}, wset[j0 % ZS], a0, a1, __uint_as_float(ha.x),
-                   __uint_as_float(ha.y), vr[j0 % ZS], g_red, ya0, ya1);
+                   __uint_as_float(ha.y), vr[j0 % ZS], g_red, ya0, ya1, oa0, oa1);
             update(std::integral_constant<int, j1>{}, wset[j1 % ZS], b0, b1, __uint_as_float(hb.x),
-                   __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1);
+                   __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1, ob0, ob1);
             if (__builtin_amdgcn_readfirstlane(hb.w) & kDepFlag) {
                 // token s+1 writes a slot token s writes: redo its write now that
                 // token s's values are in the ring
@@ -375,12 +407,21 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
                 partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), g_red + kPartU4);
                 barrier_lds();
                 update(std::integral_constant<int, j1>{}, wset[j1 % ZS], b0, b1, __uint_as_float(hb.x),
-                       __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1);
+                       __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1, ob0, ob1);
             }
             st128(r_mem, soff[j0 % ZS][0], ya0);
             st128(r_mem, soff[j0 % ZS][1], ya1);
             st128(r_mem, soff[j1 % ZS][0], yb0);
             st128(r_mem, soff[j1 % ZS][1], yb1);
+            if constexpr (LOG) {
+                // tokens outside [0, T) and positions past W log nothing (offsets past the buffer)
+                const uint32_t la = (s >= 0 && s < T) ? (uint32_t)s * log_tok : kOOB;
+                const uint32_t lb = (s + 1 >= 0 && s + 1 < T) ? (uint32_t)(s + 1) * log_tok : kOOB;
+                st128(r_log, la == kOOB || lpos0 == kOOB ? kOOB : la + lpos0, oa0);
+                st128(r_log, la == kOOB || lpos1 == kOOB ? kOOB : la + lpos1, oa1);
+                st128(r_log, lb == kOOB || lpos0 == kOOB ? kOOB : lb + lpos0, ob0);
+                st128(r_log, lb == kOOB || lpos1 == kOOB ? kOOB : lb + lpos1, ob1);
+            }
         });
     }
 }
@@ -394,16 +435,24 @@ hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& p, bool sta
     if (!p.staged || p.waves != kWaves || a.d % seg != 0 || a.W > kPos)
         return hipErrorInvalidValue;
     dim3 grid((unsigned)p.grid), block(kWaves * 64);
-    if (state_bf16) {
+    if (a.log) {
+        // the log of a call: float32 state, and one memory's tokens of a chunk addressable by 32-bit offsets
+        if (state_bf16 || (uint64_t)a.T * a.W * a.d * 4u >= (1ull << 32) - 16u)
+            return hipErrorInvalidValue;
         if (in_bf16)
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, uint16_t>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, uint16_t, true>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, float>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, float, true>), grid, block, 0, stream, a);
+    } else if (state_bf16) {
+        if (in_bf16)
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, uint16_t, false>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, float, false>), grid, block, 0, stream, a);
     } else {
         if (in_bf16)
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, uint16_t>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, uint16_t, false>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, float>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, float, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

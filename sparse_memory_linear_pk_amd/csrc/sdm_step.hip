@@ -108,24 +108,22 @@ __global__ __launch_bounds__(kWaves * 64) void step_address_kernel(StepArgs a)
 struct StepScanArgs {
     const int32_t* idx;  // [2][B*H][W]
     const float* wt;     // [2][B*H][W]
-    const float* alpha;  // [rows]
-    const float* beta;   // [rows]
-    const void* v;       // [rows, d]
+    const float* alpha;  // [B*H]
+    const float* beta;   // [B*H]
+    const void* v;       // [B*H, d]
     void* mem;           // [B*H, N, d]
-    float* out;          // [rows, d]
+    float* out;          // [B*H, d]
     int B, H, d, W;
     long N;
 };
 
 // One token for the workgroup's 128 bytes of the rows of memory bh: lane
 // (g, e) of wave w holds the 16 bytes e of write and read positions 16w + g
-// and 16w + 8 + g, as in the staged scan.  row: the token's row of alpha,
-// beta, v and out.  widx/wwt, ridx/rwt: the token's W write and read slots and
-// weights (global memory or LDS).  logp, when not null, receives the W write
-// slots' values before the write ([W, d] of the state type).
+// and 16w + 8 + g, as in the staged scan.  widx/wwt, ridx/rwt: the token's W
+// write and read slots and weights (global memory or LDS).
 template <class ST, class VT>
-__device__ void step_scan_body(const StepScanArgs& a, int bh, long row, int chunk, const int32_t* widx,
-                               const float* wwt, const int32_t* ridx, const float* rwt, ST* logp)
+__device__ void step_scan_body(const StepScanArgs& a, int bh, int chunk, const int32_t* widx, const float* wwt,
+                               const int32_t* ridx, const float* rwt)
 {
     using C = Cell<ST>;
     using CT = typename C::CT;
@@ -163,13 +161,7 @@ __device__ void step_scan_body(const StepScanArgs& a, int bh, long row, int chun
         s_wslot[pos[0]] = ws[0];
         s_wslot[pos[1]] = ws[1];
     }
-    if (logp) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            if (pos[p] < W)
-                *reinterpret_cast<uint4*>(logp + (size_t)pos[p] * a.d + (size_t)chunk * SEG + (size_t)el * E) = wv[p];
-    }
-    const CT al = a.alpha[row], be = a.beta[row];
+    const CT al = a.alpha[bh], be = a.beta[bh];
     const CT w0 = ww[0], w1 = ww[1];
 
     // the prediction of the decayed write slots
@@ -186,7 +178,7 @@ __device__ void step_scan_body(const StepScanArgs& a, int bh, long row, int chun
     // v of this lane's elements
     float vv[E];
     {
-        const size_t e0 = (size_t)row * a.d + (size_t)chunk * SEG + (size_t)el * E;
+        const size_t e0 = (size_t)bh * a.d + (size_t)chunk * SEG + (size_t)el * E;
 #pragma unroll
         for (int q = 0; q < E; ++q) {
             if constexpr (sizeof(VT) == 2)
@@ -244,7 +236,7 @@ __device__ void step_scan_body(const StepScanArgs& a, int bh, long row, int chun
     if (wave == 0 && g == 0) {
         float o[E];
         sum_waves<E, float>(reinterpret_cast<const float4*>(s_ored), el, o);
-        float* dst = a.out + (size_t)row * a.d + (size_t)chunk * SEG + (size_t)el * E;
+        float* dst = a.out + (size_t)bh * a.d + (size_t)chunk * SEG + (size_t)el * E;
 #pragma unroll
         for (int q = 0; q < E; ++q)
             dst[q] = o[q];
@@ -257,28 +249,7 @@ __global__ __launch_bounds__(kWaves * 64) void step_scan_kernel(StepScanArgs a)
     const int nchunk = a.d / (128 / (int)sizeof(ST));
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const long wrow = (long)bh * a.W, rrow = ((long)a.B * a.H + bh) * a.W;
-    step_scan_body<ST, VT>(a, bh, bh, chunk, a.idx + wrow, a.wt + wrow, a.idx + rrow, a.wt + rrow, nullptr);
-}
-
-// The forward of T tokens as T consecutive steps of every memory, saving each
-// write slot's value before its write (the log a reverse pass restores from).
-// One workgroup per (memory, 128-byte column) walks the tokens in order; the
-// body ends at a workgroup barrier, which completes token t's stores before
-// token t + 1 loads.  Rows are (b, t, h) of the call, as in the forward.
-template <class ST, class VT>
-__global__ __launch_bounds__(kWaves * 64) void train_scan_kernel(StepScanArgs a, const int32_t* idx_w,
-                                                               const float* wt_w, const int32_t* idx_r,
-                                                               const float* wt_r, int T, ST* log)
-{
-    const int nchunk = a.d / (128 / (int)sizeof(ST));
-    const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
-    const int b = bh / a.H, h = bh % a.H;
-    for (int t = 0; t < T; ++t) {
-        const long row = ((long)b * T + t) * a.H + h;
-        const long o = row * a.W;
-        step_scan_body<ST, VT>(a, bh, row, chunk, idx_w + o, wt_w + o, idx_r + o, wt_r + o,
-                               log + (size_t)o * a.d);
-    }
+    step_scan_body<ST, VT>(a, bh, chunk, a.idx + wrow, a.wt + wrow, a.idx + rrow, a.wt + rrow);
 }
 
 // The whole step in one launch, for bf16 queries: every workgroup of memory bh
@@ -312,7 +283,7 @@ __global__ __launch_bounds__(kWaves * 64) void step_fused_kernel(StepArgs a, Ste
         pksel::select_from_lists<R>(a.S, a.k, a.W, a.n_pairs, s_pairs, lane, s_buf[wave], s_val[wave], s_sub[wave],
                                     s_idx[wave], s_wt[wave]);
     __syncthreads();
-    step_scan_body<ST, uint16_t>(c, bh, bh, chunk, s_idx[0], s_wt[0], s_idx[1], s_wt[1], nullptr);
+    step_scan_body<ST, uint16_t>(c, bh, chunk, s_idx[0], s_wt[0], s_idx[1], s_wt[1]);
 }
 
 template <int DH, bool BF16, int J>
@@ -405,36 +376,6 @@ hipError_t launch_sdm_step(const void* wq, const void* rq, const void* v, const 
             hipLaunchKernelGGL((step_scan_kernel<float, uint16_t>), grid, block, 0, stream, ca);
         else
             hipLaunchKernelGGL((step_scan_kernel<float, float>), grid, block, 0, stream, ca);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_sdm_train_scan(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
-                                 const void* v, const float* alpha, const float* beta, void* mem, float* out,
-                                 void* log, int B, int H, int T, int d, int W, long N, bool in_bf16, bool state_bf16,
-                                 hipStream_t stream)
-{
-    if (!step_supported(d, state_bf16) || W > 64 || B * H < 1 || T < 1)
-        return hipErrorInvalidValue;
-    StepScanArgs ca{nullptr, nullptr, alpha, beta, v, mem, out, B, H, d, W, N};
-    const int nchunk = d * (state_bf16 ? 2 : 4) / 128;
-    dim3 grid((unsigned)(B * H * nchunk)), block(kWaves * 64);
-    if (state_bf16) {
-        uint16_t* lg = static_cast<uint16_t*>(log);
-        if (in_bf16)
-            hipLaunchKernelGGL((train_scan_kernel<uint16_t, uint16_t>), grid, block, 0, stream, ca, idx_w, wt_w, idx_r,
-                               wt_r, T, lg);
-        else
-            hipLaunchKernelGGL((train_scan_kernel<uint16_t, float>), grid, block, 0, stream, ca, idx_w, wt_w, idx_r,
-                               wt_r, T, lg);
-    } else {
-        float* lg = static_cast<float*>(log);
-        if (in_bf16)
-            hipLaunchKernelGGL((train_scan_kernel<float, uint16_t>), grid, block, 0, stream, ca, idx_w, wt_w, idx_r,
-                               wt_r, T, lg);
-        else
-            hipLaunchKernelGGL((train_scan_kernel<float, float>), grid, block, 0, stream, ca, idx_w, wt_w, idx_r,
-                               wt_r, T, lg);
     }
     return hipGetLastError();
 }

@@ -44,6 +44,8 @@ CASES = {
     "ragged_tiles": _cfg(B=1, H=3, T=33, d=96, S=40, dk=96, k=7, W=24),
     "one_slot": _cfg(B=2, H=1, T=17, d=32, S=8, dk=32, k=1, W=1),
     "k_eq_W_64": _cfg(B=1, H=1, T=20, d=32, S=64, dk=32, k=64, W=64),
+    # long enough to scan in chunks (1024 tokens, then the rest): the log of every chunk
+    "chunked_T2600": _cfg(B=2, H=1, T=2600, d=32, S=16, dk=32, k=4, W=8),
 }
 
 
@@ -60,7 +62,7 @@ def _run_gpu(cfg, x, g, reps=1):
         layer.forward(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem_f, out_f)
         mem = dev["mem0"].clone()
         out = torch.empty_like(out_f)
-        log = torch.empty((cfg.B, cfg.T, cfg.H, cfg.W, cfg.d), **f32)
+        log = torch.empty((cfg.B, cfg.H, cfg.T, cfg.W, cfg.d), **f32)
         layer.forward_train(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem, out, log)
         torch.cuda.synchronize()
         res.update(out_f=to_host(out_f), mem_f=to_host(mem_f), out=to_host(out), mem_T=to_host(mem), log=to_host(log))
@@ -149,7 +151,7 @@ def test_backward_matches_the_gradient_oracle(name):
             mem = np.ascontiguousarray(x["mem0"][b, h][None, None]).copy()
             for t in range(cfg.T):
                 r = (b * cfg.T + t) * cfg.H + h
-                ref_log[b, t, h] = mem[0, 0, res["idx_w"][r]]
+                ref_log[b, h, t] = mem[0, 0, res["idx_w"][r]]
                 orc.scan(one, res["idx_w"][r:r + 1], res["wt_w"][r:r + 1], res["idx_r"][r:r + 1],
                          res["wt_r"][r:r + 1], x["v"][b, t, h][None, None, None], x["alpha"][b, t, h].reshape(1, 1, 1),
                          x["beta"][b, t, h].reshape(1, 1, 1), mem, threads=1)
@@ -199,4 +201,4 @@ def test_backward_rejects_a_bf16_state():
             layer.forward_train(t(cfg.B, cfg.T, cfg.H, cfg.dk), t(cfg.B, cfg.T, cfg.H, cfg.dk),
                                 t(cfg.B, cfg.T, cfg.H, cfg.d), t(cfg.B, cfg.T, cfg.H), t(cfg.B, cfg.T, cfg.H),
                                 t(cfg.H, 2, cfg.S, cfg.dk // 2), mem, t(cfg.B, cfg.T, cfg.H, cfg.d),
-                                t(cfg.B, cfg.T, cfg.H, cfg.W, cfg.d))
+                                t(cfg.B, cfg.H, cfg.T, cfg.W, cfg.d))
