@@ -96,7 +96,7 @@ typedef struct {
     long long n_step;  /* steps timed */
     double ms_train;     /* the logging scan of sdm_forward_train */
     double ms_bwd_scan;  /* the reverse walk of sdm_backward */
-    double ms_bwd_rows;  /* per-row reduction, softmax derivative, query gradients */
+    double ms_bwd_rows;  /* per-row work: conflict flags, reduction, softmax derivative, query gradients */
     double ms_bwd_sub;   /* sub-key gradients */
     long long n_train, n_bwd_scan, n_bwd_rows, n_bwd_sub;
 } sdm_timing;

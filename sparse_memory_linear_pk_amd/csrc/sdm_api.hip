@@ -167,6 +167,7 @@ struct sdm_ctx {
     float* part;
     float* ds;
     float* sub_part;
+    int32_t* conflict;
     int nsplit;
 };
 
@@ -383,6 +384,7 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->timing = false;
     h->bwd_block = nullptr;
     h->part = h->ds = h->sub_part = nullptr;
+    h->conflict = nullptr;
     h->nsplit = 0;
     memset(&h->totals, 0, sizeof h->totals);
     e = hipMalloc(&h->block, h->L.total);
@@ -629,7 +631,7 @@ sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* bytes)
     const size_t rows = (size_t)c.B * c.T * c.H;
     const int nsplit = sdm::grad_sub_splits(c.B, c.H, c.T, c.n_sub, c.dk / 2);
     *bytes = align_up(sdm::grad_part_floats(c.B, c.H, c.T, c.d, c.W) * 4) + align_up(2 * rows * 2 * c.n_sub * 4) +
-             align_up((size_t)nsplit * c.H * 2 * c.n_sub * (c.dk / 2) * 4);
+             align_up((size_t)nsplit * c.H * 2 * c.n_sub * (c.dk / 2) * 4) + align_up(rows * 4);
     return SDM_OK;
 }
 
@@ -670,6 +672,8 @@ sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void
         p += align_up(2 * rows * 2 * c.n_sub * 4);
         h->sub_part = (float*)p;
         h->nsplit = sdm::grad_sub_splits(c.B, c.H, c.T, c.n_sub, c.dk / 2);
+        p += align_up((size_t)h->nsplit * c.H * 2 * c.n_sub * (c.dk / 2) * 4);
+        h->conflict = (int32_t*)p;
     }
     // the forward's slots and weights, recomputed by the same kernels
     if ((s = run_address_all(h, wq, rq, subkeys, h->stream)) != SDM_OK)
@@ -706,8 +710,15 @@ sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void
     a.part = h->part;
     a.ds = h->ds;
     a.sub_part = h->sub_part;
+    a.conflict = h->conflict;
     a.nsplit = h->nsplit;
     hipError_t e;
+    {
+        Timer t(h, K_BWD_ROWS, h->stream);
+        e = sdm::launch_grad_conflicts(a, h->stream);
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "conflict flags launch");
     {
         Timer t(h, K_BWD_SCAN, h->stream);
         e = sdm::launch_grad_scan(a, h->stream);

@@ -16,7 +16,9 @@
 //          and M[n_i] is restored to M_old[n_i] from the forward's log.
 // The state gradient is independent per slot element, like the forward, so
 // grad_scan_kernel keeps the forward's decomposition: one workgroup per
-// (memory, 128-byte column) walks all tokens in reverse.  Its dot products over
+// (memory, 128-byte column) walks all tokens in reverse.  It loads token t-1's
+// slots while it works on token t; grad_conflict_kernel flags the tokens whose
+// slots meet the next token's, and only those load again after token t's stores.  Its dot products over
 // d (dr, dw, dalpha, dbeta) leave as per-column partial sums; grad_rows_kernel
 // adds them in column order, applies the softmax's derivative
 // dsigma_i = w_i (dw_i - sum_k w_k dw_k) and sends dsigma to the query halves
@@ -83,58 +85,101 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
     const bool live[2] = {pos[0] < W, pos[1] < W};
     const int e0 = col * 32 + el * E; // this lane's first element of the row
 
-    // Everything of a token that does not depend on the state (its slots and
-    // weights, the log of its write slots, dout, v and the gates) is fetched one
-    // token ahead, so that a token starts with its slot loads.
-    struct Meta {
+    // A token's slots are fetched two tokens ahead, its other state-independent
+    // inputs (weights, the log of its write slots, dout, v, the gates) and its
+    // slot rows one token ahead.  The rows are loaded before the next token's
+    // stores, which is correct unless the two tokens share a slot (the conflict
+    // flag): then they are loaded again once the next token's stores are
+    // visible.  Buffers alternate between even and odd steps (the loop is
+    // unrolled by two), so no value still in flight is ever copied: a copy would
+    // make the compiler wait for every memory operation issued before it,
+    // stores included.  Every load is issued on every path (a position past W
+    // or a token before 0 reads a valid entry whose value is then dropped): a
+    // load skipped on some path makes the compiler's count of loads in flight
+    // conservative at the join, and it then waits for the newest loads too.
+    struct Ids {
         int32_t ws[2], rs[2];
+    };
+    struct Meta {
         float ww[2], rw[2];
         uint4 wo[2];
         float go[E], vv[E];
         float al, be;
+        int conflict;
     };
-    auto fetch = [&](int t, Meta& m) __attribute__((always_inline)) {
+    struct Rows4 {
+        uint4 rv[2], rg[2], wg[2]; // read slots' memory and gradient, write slots' gradient
+    };
+    const int posc[2] = {min(pos[0], W - 1), min(pos[1], W - 1)}; // a valid position to read
+    auto fetch_ids = [&](int t, Ids& m) __attribute__((always_inline)) {
         const long row = ((long)b * a.T + t) * a.H + h;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            m.ws[p] = live[p] ? a.idx[0][row * W + pos[p]] : -1;
-            m.rs[p] = live[p] ? a.idx[1][row * W + pos[p]] : -1;
-            m.ww[p] = live[p] ? a.wt[0][row * W + pos[p]] : 0.f;
-            m.rw[p] = live[p] ? a.wt[1][row * W + pos[p]] : 0.f;
-            m.wo[p] = live[p] ? *reinterpret_cast<const uint4*>(a.log + (((size_t)bh * a.T + t) * W + pos[p]) * a.d + e0)
-                              : make_uint4(0u, 0u, 0u, 0u);
+            const int32_t w = a.idx[0][row * W + posc[p]], r = a.idx[1][row * W + posc[p]];
+            m.ws[p] = live[p] ? w : -1;
+            m.rs[p] = live[p] ? r : -1;
+        }
+    };
+    auto fetch_meta = [&](int t, Meta& m) __attribute__((always_inline)) {
+        const long row = ((long)b * a.T + t) * a.H + h;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            // raw values: a position past W is zeroed where it is used (a select here
+            // would wait for the load)
+            m.ww[p] = a.wt[0][row * W + posc[p]];
+            m.rw[p] = a.wt[1][row * W + posc[p]];
+            m.wo[p] = *reinterpret_cast<const uint4*>(a.log + (((size_t)bh * a.T + t) * W + posc[p]) * a.d + e0);
         }
         load4(a.dout + (size_t)row * a.d + e0, m.go);
         load4(static_cast<const VT*>(a.v) + (size_t)row * a.d + e0, m.vv);
         m.al = a.alpha[row];
         m.be = a.beta[row];
+        m.conflict = a.conflict[row];
     };
-    Meta cur;
-    fetch(a.T - 1, cur);
-
-    for (int t = a.T - 1; t >= 0; --t) {
-        const long row = ((long)b * a.T + t) * a.H + h;
-        const int32_t ws[2] = {cur.ws[0], cur.ws[1]}, rs[2] = {cur.rs[0], cur.rs[1]};
-        const float ww[2] = {cur.ww[0], cur.ww[1]}, rw[2] = {cur.rw[0], cur.rw[1]};
-        const uint4 wo[2] = {cur.wo[0], cur.wo[1]};
-        uint4 rv[2], rg[2], wg[2];
+    auto issue = [&](const Ids& m, Rows4& st) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            rv[p] = ld128(r_mem, live[p] ? (uint32_t)rs[p] * row_bytes + lane_off : kOOB);
-            rg[p] = ld128(r_g, live[p] ? (uint32_t)rs[p] * row_bytes + lane_off : kOOB);
-            wg[p] = ld128(r_g, live[p] ? (uint32_t)ws[p] * row_bytes + lane_off : kOOB);
+            st.rv[p] = ld128(r_mem, live[p] ? (uint32_t)m.rs[p] * row_bytes + lane_off : kOOB);
+            st.rg[p] = ld128(r_g, live[p] ? (uint32_t)m.rs[p] * row_bytes + lane_off : kOOB);
+            st.wg[p] = ld128(r_g, live[p] ? (uint32_t)m.ws[p] * row_bytes + lane_off : kOOB);
         }
+    };
+    // step t of parity X = (T-1-t) & 1 starts with: I[X] = slots of t, I[1-X] = slots of
+    // t-1, Mt[X] = the rest of t, St[X] = t's rows (in flight)
+    Ids I[2];
+    Meta Mt[2];
+    Rows4 St[2];
+    fetch_ids(a.T - 1, I[0]);
+    fetch_meta(a.T - 1, Mt[0]);
+    issue(I[0], St[0]);
+    fetch_ids(max(a.T - 2, 0), I[1]);
+
+    for (int tp = a.T - 1; tp >= 0; tp -= 2)
+      static_for<2>([&](auto pc) __attribute__((always_inline)) {
+        constexpr int X = decltype(pc)::value, Y = 1 - X; // this step's buffers, the next step's
+        const int t = tp - X;
+        if (t < 0)
+            return;
+        const Ids cur = I[X]; // fetched two steps ago
+        fetch_ids(max(t - 2, 0), I[X]);
+        issue(I[Y], St[Y]); // token t-1's rows (for t = 0, token 0's again, unused)
+        fetch_meta(max(t - 1, 0), Mt[Y]);
+        const long row = ((long)b * a.T + t) * a.H + h;
+        const int32_t ws[2] = {cur.ws[0], cur.ws[1]}, rs[2] = {cur.rs[0], cur.rs[1]};
+        const Meta& m = Mt[X];
+        const float ww[2] = {live[0] ? m.ww[0] : 0.f, live[1] ? m.ww[1] : 0.f};
+        const float rw[2] = {live[0] ? m.rw[0] : 0.f, live[1] ? m.rw[1] : 0.f};
+        const uint4 wo[2] = {m.wo[0], m.wo[1]}; // dead positions: zeroed when unpacked below
+        const Rows4& sc = St[X];
+        const uint4 rv[2] = {sc.rv[0], sc.rv[1]}, rg[2] = {sc.rg[0], sc.rg[1]}, wg[2] = {sc.wg[0], sc.wg[1]};
         float go[E], vv[E];
 #pragma unroll
         for (int q = 0; q < E; ++q) {
-            go[q] = cur.go[q];
-            vv[q] = cur.vv[q];
+            go[q] = m.go[q];
+            vv[q] = m.vv[q];
         }
-        const float al = cur.al, be = cur.be;
-        if (t > 0)
-            fetch(t - 1, cur);
+        const float al = m.al, be = m.be;
         float* part = a.part + ((size_t)row * ncol + col) * P;
-
         // the read: the memory holds its state after token t's write
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -164,15 +209,22 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
         float gw[2][E], x[2][E], old[2][E];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
+            // branch-free (every entry read, the tests combined bitwise): the short-circuit
+            // form of this select has been compiled wrongly here, keeping the candidate
+            // index on lanes that did not match
             int hit = -1;
+            const int32_t wsp = ws[p];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                hit = (ws[p] >= 0 && el * 8 + u < W && s_rslot[el * 8 + u] == ws[p]) ? el * 8 + u : hit;
+            for (int u = 0; u < 8; ++u) {
+                const int j = el * 8 + u;
+                const int32_t sv = s_rslot[j];
+                hit = ((j < W) & (sv == wsp) & (wsp >= 0)) ? j : hit;
+            }
 #pragma unroll
             for (int m = 1; m < 8; m <<= 1)
                 hit = max(hit, __shfl_xor(hit, m));
             Cell<float>::unpack(hit >= 0 ? s_g[hit * 8 + el] : wg[p], gw[p]);
-            Cell<float>::unpack(wo[p], old[p]);
+            Cell<float>::unpack(live[p] ? wo[p] : make_uint4(0u, 0u, 0u, 0u), old[p]);
 #pragma unroll
             for (int q = 0; q < E; ++q)
                 x[p][q] = al * old[p][q];
@@ -236,10 +288,43 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             o.w = be * dd[3];
             *reinterpret_cast<float4*>(a.dv + (size_t)row * a.d + e0) = o;
         }
-        __syncthreads();
+        __syncthreads(); // token t's stores are visible to the workgroup's loads from here on
         if (threadIdx.x == 0)
             part[2 * W] = (s_al[0] + s_al[1]) + (s_al[2] + s_al[3]);
+        if (t >= 1 && Mt[Y].conflict)
+            issue(I[Y], St[Y]);
+      });
+}
+
+// flag[row] of token u of memory (b, h): nonzero when a slot token u writes or
+// reads is also written or read by token u + 1 (zero for the last token).  One
+// wave per row: each of token u's slots is broadcast and compared with token
+// u + 1's, two per lane.
+__global__ __launch_bounds__(256) void grad_conflict_kernel(const int32_t* idx_w, const int32_t* idx_r,
+                                                            int32_t* flag, long R, int T, int H, int W)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long row = (long)blockIdx.x * 4 + wave;
+    if (row >= R)
+        return; // the whole wave
+    const int u = (int)((row / H) % T);
+    if (u == T - 1) {
+        if (lane == 0)
+            flag[row] = 0;
+        return;
     }
+    const long nrow = row + H; // (b, u + 1, h)
+    const bool live = lane < W;
+    const int32_t aw = live ? idx_w[row * W + lane] : -1, ar = live ? idx_r[row * W + lane] : -1;
+    const int32_t nw = live ? idx_w[nrow * W + lane] : -2, nr = live ? idx_r[nrow * W + lane] : -2;
+    bool hit = false;
+    for (int k = 0; k < W; ++k) {
+        const int32_t x = __shfl(aw, k), y = __shfl(ar, k);
+        hit = hit || nw == x || nr == x || nw == y || nr == y;
+    }
+    const bool any = __builtin_amdgcn_ballot_w64(hit) != 0u;
+    if (lane == 0)
+        flag[row] = any ? 1 : 0;
 }
 
 constexpr int kRowsPerBlock = 4;
@@ -415,6 +500,14 @@ int grad_sub_splits(int B, int H, int T, int S, int dh)
     n = n < by_rows ? n : by_rows;
     n = n < 64 ? n : 64;
     return (int)(n < 1 ? 1 : n);
+}
+
+hipError_t launch_grad_conflicts(const GradArgs& a, hipStream_t stream)
+{
+    const long R = (long)a.B * a.T * a.H;
+    hipLaunchKernelGGL(grad_conflict_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream, a.idx[0], a.idx[1],
+                       a.conflict, R, a.T, a.H, a.W);
+    return hipGetLastError();
 }
 
 hipError_t launch_grad_scan(const GradArgs& a, hipStream_t stream)

@@ -173,10 +173,12 @@ struct GradArgs {
     float* part;                         // workspace: [rows, d/32, 2W+2]
     float* ds;                           // workspace: [2, rows, 2, S]
     float* sub_part;                     // workspace: [nsplit, H, 2, S, dh]
+    int32_t* conflict;                   // workspace: [rows], token shares a slot with the next one
     int nsplit;
 };
 size_t grad_part_floats(int B, int H, int T, int d, int W);
 int grad_sub_splits(int B, int H, int T, int S, int dh);
+hipError_t launch_grad_conflicts(const GradArgs& a, hipStream_t stream);
 hipError_t launch_grad_scan(const GradArgs& a, hipStream_t stream);
 hipError_t launch_grad_rows(const GradArgs& a, hipStream_t stream);
 hipError_t launch_grad_subkeys(const GradArgs& a, hipStream_t stream);

@@ -215,10 +215,16 @@ __device__ void step_scan_body(const StepScanArgs& a, int bh, int chunk, const i
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             // the 8 lanes of a group search 8 write positions each
+            // branch-free: every entry read, the tests combined bitwise (a short-circuit
+            // select of this shape has been compiled wrongly elsewhere)
             int hit = -1;
+            const int32_t rsp = rs[p];
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-                hit = (rs[p] >= 0 && s_wslot[el * 8 + t] == rs[p] && el * 8 + t < W) ? el * 8 + t : hit;
+            for (int t = 0; t < 8; ++t) {
+                const int j = el * 8 + t;
+                const int32_t sv = s_wslot[j];
+                hit = ((j < W) & (sv == rsp) & (rsp >= 0)) ? j : hit;
+            }
 #pragma unroll
             for (int m = 1; m < 8; m <<= 1)
                 hit = max(hit, __shfl_xor(hit, m));
