@@ -174,7 +174,7 @@ def train_bench(args, cfg):
     import torch
 
     import sdm_inputs as gi
-    from sparse_memory_linear_pk_amd import SDM
+    from sparse_memory_linear_pk_amd import SDM, pattern_probe_mix
 
     if cfg.state_bf16:
         raise SystemExit("the backward pass is built for a float32 state; use the 1.4B-shaped workload")
@@ -223,6 +223,17 @@ def train_bench(args, cfg):
     for k, v in g.items():
         if not torch.isfinite(v).all():
             raise RuntimeError(f"non-finite {k}")
+    # the ceiling of the reverse scan's access pattern: 4 reads and 3 writes of random 128-byte
+    # segments per slot position and token, same geometry, no arithmetic (scrambles the memory)
+    del log_buf
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=11)
+    s0.record()
+    for r in range(2):
+        pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=12 + r)
+    s1.record()
+    torch.cuda.synchronize()
+    probe_ms = s0.elapsed_time(s1) / 2
     tokens = cfg.B * cfg.T
     wd4 = cfg.W * cfg.d * 4
     bwd_bytes = tokens * cfg.H * 7 * wd4     # reads M, G (read slots), G, log (write slots); writes G, G, M
@@ -247,7 +258,11 @@ def train_bench(args, cfg):
                    "seq_len": cfg.T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "grad_scan", "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
                      "peak": 8000.0, "unit": "GB/s", "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / 8000.0,
-                     "traffic": None, "bytes_per_launch": bwd_bytes, "ms_per_launch": bwd_ms},
+                     "traffic": None, "bytes_per_launch": bwd_bytes, "ms_per_launch": bwd_ms,
+                     "pattern_ceiling": {"achieved": bwd_bytes / (probe_ms * 1e-3) / 1e9, "unit": "GB/s",
+                                         "ms_per_launch": probe_ms, "frac": probe_ms / bwd_ms,
+                                         "what": "sdm_pattern_probe_mix 4:3: the reverse scan's random 128-byte "
+                                                 "segment reads and writes with no arithmetic; frac = scan / this"}},
         "kernels_ms_per_step": {"train_scan": fwd_ms, "train_scan_GBps": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
                                 "pk_score": tm["ms_score"] / steps, "pk_topk": tm["ms_select"] / steps,
                                 "grad_scan": bwd_ms, "grad_rows": tm["ms_bwd_rows"] / steps,

@@ -211,6 +211,15 @@ SDM_API sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t);
 SDM_API sdm_status sdm_pattern_probe(void* mem, int memories, long rows, int row_bytes, int T, int W,
                                      unsigned seed, void* hip_stream);
 
+/* The same with `reads` row segments read and the first `writes` of them stored
+ * back per slot position and token: 2:1 is sdm_pattern_probe; 4:3 is the
+ * reverse scan of sdm_backward (the read slot's memory and gradient, the write
+ * slot's gradient and logged value read; both gradients and the restored
+ * memory written), the ceiling of its access pattern.  (reads + writes) * W *
+ * row_bytes * T * memories bytes move per call.  Other mixes: SDM_ERR_INVALID_ARG. */
+SDM_API sdm_status sdm_pattern_probe_mix(void* mem, int memories, long rows, int row_bytes, int T, int W, int reads,
+                                         int writes, unsigned seed, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

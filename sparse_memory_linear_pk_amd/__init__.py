@@ -15,7 +15,7 @@ import ctypes as C
 
 from ._lib import (SDM_BF16, SDM_F32, Config, SDMError, Timing, check, declared_symbols, lib)
 
-__all__ = ["SDM", "SDMError", "declared_symbols", "lib", "pattern_probe"]
+__all__ = ["SDM", "SDMError", "declared_symbols", "lib", "pattern_probe", "pattern_probe_mix"]
 
 
 def _ptr(t):
@@ -190,3 +190,15 @@ def pattern_probe(mem, memories: int, rows: int, row_bytes: int, T: int, W: int,
     handle = stream if isinstance(stream, int) else stream.cuda_stream
     check(lib().sdm_pattern_probe(_ptr(mem), memories, rows, row_bytes, T, W, seed, C.c_void_p(handle)),
           "sdm_pattern_probe")
+
+
+def pattern_probe_mix(mem, memories: int, rows: int, row_bytes: int, T: int, W: int, reads: int, writes: int,
+                      seed: int = 0, stream=None):
+    """sdm_pattern_probe_mix: (reads + writes)*W*row_bytes*T*memories bytes of random 128-byte row
+    segments, reads:writes per slot position and token (2:1 or 4:3).  Scrambles mem."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    check(lib().sdm_pattern_probe_mix(_ptr(mem), memories, rows, row_bytes, T, W, reads, writes, seed,
+                                      C.c_void_p(handle)), "sdm_pattern_probe_mix")

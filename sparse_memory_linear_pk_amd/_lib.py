@@ -71,6 +71,8 @@ def lib() -> C.CDLL:
         "sdm_set_timing": ([h, C.c_int], C.c_int),
         "sdm_get_timing": ([h, C.POINTER(Timing)], C.c_int),
         "sdm_pattern_probe": ([vp, C.c_int, C.c_long, C.c_int, C.c_int, C.c_int, C.c_uint, vp], C.c_int),
+        "sdm_pattern_probe_mix": ([vp, C.c_int, C.c_long, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_uint, vp],
+                                  C.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)

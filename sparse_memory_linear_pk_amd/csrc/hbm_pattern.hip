@@ -11,6 +11,10 @@
 // barriers.  Its bandwidth is the ceiling that random 128-byte reads and writes
 // in a 2:1 mix reach on the device: the scan cannot beat it, so the scan's
 // achieved bandwidth is judged against it as well as against the HBM peak.
+// The reverse scan of the backward pass reads 4 segments per slot position and
+// token (the read slot's memory and gradient, the write slot's gradient, its
+// logged value) and writes 3 (both gradients and the restored memory): the same
+// kernel with 4 reads and 3 writes per position gives its ceiling.
 // Every loaded value feeds a stored value, so the compiler removes no load; the
 // memory's contents are scrambled.
 #include "sdm_internal.h"
@@ -56,13 +60,16 @@ template <int N, class F> __device__ __forceinline__ void unroll(F&& f)
 
 constexpr int kP = 3;                           // tokens of loads in flight
 constexpr int kZ = kP + 1;                      // register stages
-constexpr int kOps = 4 + 2;                     // per token and wave: 4 loads, 2 stores
-constexpr int kWait = (kP - 1) * kOps + 2;      // after a token's stores: the last kP - 1 tokens may be in flight
 constexpr uint32_t kPast = 0xFFFFFFF0u;         // an offset past every buffer: reads zero, drops the store
 
+// NR row sets read and the first NW of them written back, per slot position and token.
+template <int NR, int NW>
 __global__ __launch_bounds__(256) void hbm_pattern_kernel(char* mem, int T, int W, uint32_t rows, uint32_t row_bytes,
                                                           int nchunk, uint32_t seed)
 {
+    constexpr int kOps = 2 * NR + 2 * NW;           // per token and wave (two positions per lane)
+    constexpr int kWait = (kP - 1) * kOps + 2 * NW; // after a token's stores: the last kP - 1 tokens may be in flight
+    static_assert(NW <= NR && kWait <= 63, "vmcnt");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 3, el = lane & 7;
     const int m = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const uint32_t lane_off = (uint32_t)(chunk * 8 + el) * 16u;
@@ -74,36 +81,50 @@ __global__ __launch_bounds__(256) void hbm_pattern_kernel(char* mem, int T, int 
         const uint32_t row = mix((seed + (uint32_t)m * 7919u + (uint32_t)t * 131u + set) * 1024u + (uint32_t)p) % rows;
         return row * row_bytes + lane_off;
     };
-    uint4 wr[kZ][2], rd[kZ][2];
+    uint4 v[kZ][NR][2];
     for (int z = 0; z < kZ; ++z)
-        for (int q = 0; q < 2; ++q)
-            wr[z][q] = rd[z][q] = make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < NR; ++i)
+            for (int q = 0; q < 2; ++q)
+                v[z][i][q] = make_uint4(0u, 0u, 0u, 0u);
     const int blocks = (T + kP + 1 + kZ - 1) / kZ;
     for (int blk = 0; blk < blocks; ++blk) {
         unroll<kZ>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             const int s = -kP - 1 + blk * kZ + j; // token whose rows are in stage j
-            const uint4 k = xor4(rd[j][0], rd[j][1]);
-            st(r, offset(s, pos[0], 0u), xor4(wr[j][0], k));
-            st(r, offset(s, pos[1], 0u), xor4(wr[j][1], k));
+            uint4 k = make_uint4(0u, 0u, 0u, 0u);  // every loaded value feeds the stores
+#pragma unroll
+            for (int i = NW; i < NR; ++i)
+                k = xor4(k, xor4(v[j][i][0], v[j][i][1]));
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                st(r, offset(s, pos[0], (uint32_t)i), xor4(v[j][i][0], k));
+                st(r, offset(s, pos[1], (uint32_t)i), xor4(v[j][i][1], k));
+            }
             wait_vm<kWait>();
             const int u = s + kZ;
-            for (int q = 0; q < 2; ++q) {
-                wr[j][q] = ld(r, offset(u, pos[q], 0u));
-                rd[j][q] = ld(r, offset(u, pos[q], 1u));
-            }
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                for (int q = 0; q < 2; ++q)
+                    v[j][i][q] = ld(r, offset(u, pos[q], (uint32_t)i));
         });
     }
 }
 
 } // namespace
 
-hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, uint32_t seed,
-                              hipStream_t stream)
+hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, int reads, int writes,
+                              uint32_t seed, hipStream_t stream)
 {
     const int nchunk = row_bytes / 128;
-    hipLaunchKernelGGL(hbm_pattern_kernel, dim3((unsigned)(memories * nchunk)), dim3(256), 0, stream, (char*)mem, T,
-                       W, (uint32_t)rows, (uint32_t)row_bytes, nchunk, seed);
+    dim3 grid((unsigned)(memories * nchunk)), block(256);
+    if (reads == 2 && writes == 1)
+        hipLaunchKernelGGL((hbm_pattern_kernel<2, 1>), grid, block, 0, stream, (char*)mem, T, W, (uint32_t)rows,
+                           (uint32_t)row_bytes, nchunk, seed);
+    else if (reads == 4 && writes == 3)
+        hipLaunchKernelGGL((hbm_pattern_kernel<4, 3>), grid, block, 0, stream, (char*)mem, T, W, (uint32_t)rows,
+                           (uint32_t)row_bytes, nchunk, seed);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

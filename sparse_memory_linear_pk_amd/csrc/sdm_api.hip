@@ -787,8 +787,8 @@ sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t)
     return rc;
 }
 
-sdm_status sdm_pattern_probe(void* mem, int memories, long rows, int row_bytes, int T, int W, unsigned seed,
-                             void* hip_stream)
+sdm_status sdm_pattern_probe_mix(void* mem, int memories, long rows, int row_bytes, int T, int W, int reads,
+                                 int writes, unsigned seed, void* hip_stream)
 {
     if (!mem || ((uintptr_t)mem & 15u))
         return fail(SDM_ERR_INVALID_ARG, "sdm_pattern_probe: mem is NULL or not 16-byte aligned");
@@ -797,8 +797,17 @@ sdm_status sdm_pattern_probe(void* mem, int memories, long rows, int row_bytes, 
     if (row_bytes < 128 || row_bytes % 128 != 0 || (unsigned long long)rows * (unsigned)row_bytes >= (1ull << 32) - 16)
         return fail(SDM_ERR_INVALID_ARG, "sdm_pattern_probe: row_bytes=%d must be a multiple of 128 and one memory "
                     "below 4 GiB", row_bytes);
-    hipError_t e = sdm::launch_hbm_pattern(mem, memories, rows, row_bytes, T, W, seed, (hipStream_t)hip_stream);
+    if (!((reads == 2 && writes == 1) || (reads == 4 && writes == 3)))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_pattern_probe: reads:writes %d:%d; built for 2:1 and 4:3", reads, writes);
+    hipError_t e = sdm::launch_hbm_pattern(mem, memories, rows, row_bytes, T, W, reads, writes, seed,
+                                           (hipStream_t)hip_stream);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "hbm_pattern launch");
+}
+
+sdm_status sdm_pattern_probe(void* mem, int memories, long rows, int row_bytes, int T, int W, unsigned seed,
+                             void* hip_stream)
+{
+    return sdm_pattern_probe_mix(mem, memories, rows, row_bytes, T, W, 2, 1, seed, hip_stream);
 }
 
 } // extern "C"

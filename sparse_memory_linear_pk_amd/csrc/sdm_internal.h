@@ -184,8 +184,10 @@ hipError_t launch_grad_rows(const GradArgs& a, hipStream_t stream);
 hipError_t launch_grad_subkeys(const GradArgs& a, hipStream_t stream);
 
 // Measurement only: the scan's traffic pattern without arithmetic on `memories`
-// memories of `rows` rows of row_bytes (a multiple of 128) bytes.
-hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, uint32_t seed,
-                              hipStream_t stream);
+// memories of `rows` rows of row_bytes (a multiple of 128) bytes; reads:writes
+// segments per slot position and token, 2:1 (the forward scan) or 4:3 (the
+// reverse scan of the backward pass).
+hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, int reads, int writes,
+                              uint32_t seed, hipStream_t stream);
 
 } // namespace sdm

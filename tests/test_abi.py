@@ -9,7 +9,7 @@ from sparse_memory_linear_pk_amd._lib import Config, Timing, SDM_OK, SDM_ERR_INV
 
 EXPECTED = ["sdm_create", "sdm_forward", "sdm_destroy", "sdm_status_str", "sdm_last_error", "sdm_workspace_bytes",
             "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing",
-            "sdm_pattern_probe", "sdm_step", "sdm_forward_train", "sdm_backward_workspace_bytes", "sdm_backward"]
+            "sdm_pattern_probe", "sdm_step", "sdm_forward_train", "sdm_backward_workspace_bytes", "sdm_backward", "sdm_pattern_probe_mix"]
 
 
 def _cfg(**kw):
@@ -117,3 +117,10 @@ def test_backward_rejects_what_it_does_not_build(kw):
     n = C.c_size_t()
     assert L.sdm_backward_workspace_bytes(C.byref(_cfg(**kw)), C.byref(n)) == SDM_ERR_UNSUPPORTED
     assert b"sdm_backward" in L.sdm_last_error()
+
+
+@pytest.mark.parametrize("reads,writes", [(3, 1), (4, 4), (2, 2), (0, 0)])
+def test_pattern_probe_mix_rejects_unbuilt_mixes(reads, writes):
+    L = _lib.lib()
+    assert L.sdm_pattern_probe_mix(16, 4, 230400, 8192, 16, 64, reads, writes, 0, None) == SDM_ERR_INVALID_ARG
+    assert b"reads:writes" in L.sdm_last_error()
