@@ -38,6 +38,17 @@ def build(src: str = SRC, out: str = LIB, extra_flags=()) -> str:
     return out
 
 
+PROJ_SRC = os.path.join(HERE, "sdm_oracle_proj.c")
+PROJ_LIB = os.path.join(HERE, "liboracle_sdm_proj.so")
+
+
+def build_proj(src: str = PROJ_SRC, out: str = PROJ_LIB, extra_flags=()) -> str:
+    """Compile the projection oracle (with the forward oracle, for its bf16 rounding)."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-I", HERE, src, SRC, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def build_grad(src: str = GRAD_SRC, out: str = GRAD_LIB, fwd_src: str = SRC, extra_flags=()) -> str:
     """Compile the gradient oracle together with the forward it replays."""
     cmd = ["gcc", *CFLAGS, *extra_flags, "-I", HERE, src, fwd_src, "-o", out, "-lm"]
@@ -335,8 +346,70 @@ class GradOracle:
         return dq, dsub
 
 
+class ProjOracle:
+    """Handle on one build of the projection oracle (sdm_oracle_proj.c)."""
+
+    def __init__(self, path: str | None = None):
+        path = path or PROJ_LIB
+        if path == PROJ_LIB and (not os.path.exists(path) or os.path.getmtime(path) < max(
+                os.path.getmtime(PROJ_SRC), os.path.getmtime(SRC))):
+            build_proj()
+        if not os.path.exists(path):
+            raise FileNotFoundError(path)
+        self.path = path
+        L = C.CDLL(path)
+        vp = C.c_void_p
+        L.oracle_project.argtypes = [C.c_int] * 6 + [vp, vp, vp, C.c_long, C.c_long, vp, vp, vp, vp, vp]
+        L.oracle_project.restype = C.c_int
+        L.oracle_broadcast_memory.argtypes = [C.c_int, C.c_int, C.c_long, vp, vp]
+        L.oracle_broadcast_memory.restype = C.c_int
+        self.L = L
+
+    def project(self, B, T, H, D, dk, d, x, w, bias, threads=None):
+        """(wq, rq, v as bf16 bits, alpha, beta float32) for x [B,T,D] bf16 bits, w [H*C, D] bf16 bits,
+        bias [H, 2] float32."""
+        x = np.ascontiguousarray(x, np.uint16)
+        w = np.ascontiguousarray(w, np.uint16)
+        bias = np.ascontiguousarray(bias, np.float32)
+        wq = np.empty((B, T, H, dk), np.uint16)
+        rq = np.empty((B, T, H, dk), np.uint16)
+        v = np.empty((B, T, H, d), np.uint16)
+        al = np.empty((B, T, H), np.float32)
+        be = np.empty((B, T, H), np.float32)
+        R = B * T
+        threads = threads or default_threads()
+        step = max(1, -(-R // (threads * 4)))
+        spans = [(a, min(R, a + step)) for a in range(0, R, step)]
+
+        def fn(sp):
+            return self.L.oracle_project(B, T, H, D, dk, d, _ptr(x), _ptr(w), _ptr(bias), sp[0], sp[1], _ptr(wq),
+                                         _ptr(rq), _ptr(v), _ptr(al), _ptr(be))
+
+        with ThreadPoolExecutor(min(threads, len(spans))) as ex:
+            rcs = list(ex.map(fn, spans))
+        if any(rcs):
+            raise ValueError("oracle_project rejected its arguments")
+        return wq, rq, v, al, be
+
+    def broadcast_memory(self, B, m0):
+        m0 = np.ascontiguousarray(m0)
+        H = m0.shape[0]
+        mem = np.empty((B,) + m0.shape, m0.dtype)
+        if self.L.oracle_broadcast_memory(B, H, m0[0].nbytes, _ptr(m0), _ptr(mem)):
+            raise ValueError("oracle_broadcast_memory rejected its arguments")
+        return mem
+
+
 _default = None
 _default_grad = None
+_default_proj = None
+
+
+def get_proj() -> ProjOracle:
+    global _default_proj
+    if _default_proj is None:
+        _default_proj = ProjOracle()
+    return _default_proj
 
 
 def get_grad() -> GradOracle:
