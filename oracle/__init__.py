@@ -395,6 +395,7 @@ class ProjOracle:
         m0 = np.ascontiguousarray(m0)
         H = m0.shape[0]
         mem = np.empty((B,) + m0.shape, m0.dtype)
+        mem.view(np.uint8)[...] = 0xA5  # poison: nothing may survive from an earlier allocation
         if self.L.oracle_broadcast_memory(B, H, m0[0].nbytes, _ptr(m0), _ptr(mem)):
             raise ValueError("oracle_broadcast_memory rejected its arguments")
         return mem
