@@ -271,6 +271,68 @@ def train_bench(args, cfg):
     print(json.dumps(res))
 
 
+def project_bench(args, cfg):
+    """The input projections (sdm_project) of the workload's B*T tokens from a D = d wide embedding:
+    one MFMA product [B*T, D] x [D, H*(2dk+d+2)] with the bf16 / sigmoid epilogue."""
+    import numpy as np
+    import torch
+
+    import sdm_inputs as gi
+    from sparse_memory_linear_pk_amd import SDM
+
+    D = cfg.d
+    log(f"generating projection inputs for {cfg}, D={D}")
+    p = gi.make_projection_inputs(cfg, D)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    d = {k: dev(v) for k, v in p.items()}
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    wq = torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **bf)
+    rq = torch.empty_like(wq)
+    v = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **bf)
+    al = torch.empty((cfg.B, cfg.T, cfg.H), **f32)
+    be = torch.empty_like(al)
+    layer = SDM.from_config(cfg)
+    for _ in range(max(1, args.warmup)):
+        layer.project(D, d["x"], d["w"], d["gate_bias"], wq, rq, v, al, be)
+    torch.cuda.synchronize()
+    layer.set_timing(True)
+    reps = max(args.steps, 10)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        layer.project(D, d["x"], d["w"], d["gate_bias"], wq, rq, v, al, be)
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    tm = layer.timing()
+    layer.close()
+    ms = tm["ms_project"] / tm["n_project"]
+    C = 2 * cfg.dk + cfg.d + 2
+    flops = 2.0 * cfg.B * cfg.T * D * cfg.H * C
+    res = {
+        "metric": "SDM input projections tokens/sec (1 GPU), sdm_project",
+        "value": cfg.B * cfg.T * reps / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3 / reps,
+        "higher_is_better": True,
+        "dtype": "bf16",
+        "data": "synthetic (seeded embedding ~N(0,1), weights ~N(0,1/sqrt(D)))",
+        "config": {"workload": f"sdm-{cfg.name} projections: {cfg.B * cfg.T} tokens, D={D} -> H={cfg.H} x "
+                               f"(2*{cfg.dk} + {cfg.d} + 2) outputs"},
+        "roofline": {"bound": "mfma", "kernel": "project_kernel", "achieved": flops / (ms * 1e-3) / 1e12,
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / 2500.0,
+                     "traffic": None, "flops_per_launch": flops, "ms_per_launch": ms},
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +345,8 @@ def main():
                          "4 8B-shaped: bf16 state)")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode step (sdm_step, one token per sequence per call) instead of the forward")
+    ap.add_argument("--project", action="store_true",
+                    help="time the input projections (sdm_project) instead of the forward")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (sdm_forward_train + sdm_backward) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -314,6 +378,8 @@ def main():
         return decode_bench(args, cfg)
     if args.train:
         return train_bench(args, cfg)
+    if args.project:
+        return project_bench(args, cfg)
     log(f"generating inputs for {cfg}")
     t0 = time.perf_counter()
     x = gi.make_inputs(cfg)

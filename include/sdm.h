@@ -99,6 +99,8 @@ typedef struct {
     double ms_bwd_rows;  /* per-row work: conflict flags, reduction, softmax derivative, query gradients */
     double ms_bwd_sub;   /* sub-key gradients */
     long long n_train, n_bwd_scan, n_bwd_rows, n_bwd_sub;
+    double ms_project;   /* input projections (sdm_project) */
+    long long n_project;
 } sdm_timing;
 
 /* Supported shapes: 1 <= k <= min(S, 64); 1 <= W <= min(k*k, 64); S <= 1024;
@@ -167,6 +169,28 @@ SDM_API sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, co
                                 const float* beta, const void* subkeys, void* mem_inout, const void* log,
                                 const float* dout, float* dmem_inout, float* dwq, float* drq, float* dv,
                                 float* dalpha, float* dbeta, float* dsubkeys);
+
+/* The layer's input projections for the call's B*T tokens (SDM blog post,
+ * section "How does SDM work?", its "Write & Read" subsection: the token
+ * embedding projected to the write keys and, separately, to the read query;
+ * the value and the gates of the gated delta rule from the same embedding).
+ * Per token and head, with C = 2*dk + d + 2 output rows per head:
+ *   wq = x Wq^T, rq = x Wr^T, v = x Wv^T               (bf16, nearest even)
+ *   alpha = sigmoid(x wa + bias[h][0]), beta = sigmoid(x wb + bias[h][1])  (float32)
+ *   x         [B, T, D] bf16 (D a multiple of 8), the embedding
+ *   w         [H*C, D] bf16: head h's rows h*C + [0,dk) Wq, [dk,2dk) Wr,
+ *             [2dk, 2dk+d) Wv, 2dk+d wa, 2dk+d+1 wb (an output's D weights contiguous)
+ *   gate_bias [H, 2] float32
+ *   wq, rq    [B, T, H, dk] bf16; v [B, T, H, d] bf16; alpha, beta [B, T, H] float32:
+ *             exactly the inputs sdm_forward takes.
+ * One MFMA launch; float32 accumulation, one rounding per output.
+ * SDM_ERR_UNSUPPORTED unless in_dtype is bf16. */
+SDM_API sdm_status sdm_project(sdm_handle h, int D, const void* x, const void* w, const float* gate_bias, void* wq,
+                               void* rq, void* v, float* alpha, float* beta);
+
+/* A learned initial memory m0 [H, N, d] (state dtype) copied into each of the
+ * B sequences' memories mem_out [B, H, N, d], ready for sdm_forward. */
+SDM_API sdm_status sdm_broadcast_memory(sdm_handle h, const void* m0, void* mem_out);
 
 /* Free the workspace and the handle.  Waits for the handle's stream first. */
 SDM_API sdm_status sdm_destroy(sdm_handle h);

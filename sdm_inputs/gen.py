@@ -15,6 +15,7 @@ CHUNK = 1 << 22
 # tensor ids
 _WQ, _RQ, _V, _ALPHA, _BETA, _SUBKEYS, _MEM0, _CENTROIDS, _PICK_W, _PICK_R, _NOISE_W, _NOISE_R = range(1, 13)
 _DOUT, _DMEM = 13, 14
+_EMB, _PROJ_W, _GATE_B = 15, 16, 17
 
 
 @dataclasses.dataclass(frozen=True)
@@ -200,3 +201,15 @@ def make_upstream_grads(cfg: Config, seed: int = 0, dmem_std: float = 0.1, threa
     dmem [B, H, N, d] ~ N(0, dmem_std) (the gradient reaching the final memory), float32."""
     return {"dout": normal_f32((cfg.B, cfg.T, cfg.H, cfg.d), seed, _DOUT, 1.0, threads),
             "dmem": normal_f32((cfg.B, cfg.H, cfg.N, cfg.d), seed, _DMEM, dmem_std, threads)}
+
+
+def make_projection_inputs(cfg: Config, D: int, seed: int = 0, threads=None) -> dict:
+    """Seeded inputs of the input projections: embedding x [B, T, D] ~ N(0, 1), weights
+    w [H*(2dk+d+2), D] ~ N(0, 1/sqrt(D)) (both bf16 bits), gate biases [H, 2] float32: alpha's
+    N(4, 1), beta's N(0, 1) (the workloads' gate distributions when the projection adds N(0, 1))."""
+    C = 2 * cfg.dk + cfg.d + 2
+    x = normal_f32((cfg.B, cfg.T, D), seed, _EMB, 1.0, threads)
+    w = normal_f32((cfg.H * C, D), seed, _PROJ_W, 1.0 / float(np.sqrt(D)), threads)
+    gb = normal_f32((cfg.H, 2), seed, _GATE_B, 1.0, threads)
+    gb[:, 0] += np.float32(4.0)
+    return {"x": bf16_bits_from_f32(x), "w": bf16_bits_from_f32(w), "gate_bias": gb}

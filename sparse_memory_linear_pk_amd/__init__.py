@@ -112,6 +112,23 @@ class SDM:
                 self._t(dsubkeys, "dsubkeys", (H, 2, S, dk // 2), "f32")]
         check(lib().sdm_backward(self._h, *[_ptr(a) for a in args]), "sdm_backward")
 
+    def project(self, D, x, w, gate_bias, wq, rq, v, alpha, beta):
+        """Input projections: x [B, T, D] bf16, w [H*(2dk+d+2), D] bf16, gate_bias [H, 2] float32 ->
+        wq, rq [B, T, H, dk], v [B, T, H, d] (bf16), alpha, beta [B, T, H] (float32)."""
+        B, H, T, d, S, dk, k, W = self._dims()
+        C_ = 2 * dk + d + 2
+        args = [self._t(x, "x", (B, T, D), "in"), self._t(w, "w", (H * C_, D), "in"),
+                self._t(gate_bias, "gate_bias", (H, 2), "f32"), self._t(wq, "wq", (B, T, H, dk), "in"),
+                self._t(rq, "rq", (B, T, H, dk), "in"), self._t(v, "v", (B, T, H, d), "in"),
+                self._t(alpha, "alpha", (B, T, H), "f32"), self._t(beta, "beta", (B, T, H), "f32")]
+        check(lib().sdm_project(self._h, int(D), *[_ptr(a) for a in args]), "sdm_project")
+
+    def broadcast_memory(self, m0, mem):
+        """mem [B, H, N, d] = B copies of m0 [H, N, d] (state dtype)."""
+        B, H, T, d, S, dk, k, W = self._dims()
+        args = [self._t(m0, "m0", (H, S * S, d), "state"), self._t(mem, "mem", (B, H, S * S, d), "state")]
+        check(lib().sdm_broadcast_memory(self._h, *[_ptr(a) for a in args]), "sdm_broadcast_memory")
+
     def score(self, q, subkeys, scores):
         B, H, T, d, S, dk, k, W = self._dims()
         args = [self._t(q, "q", (B, T, H, dk), "in"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),

@@ -32,7 +32,8 @@ class Timing(C.Structure):
                 ("n_plan", C.c_longlong), ("n_scan", C.c_longlong), ("ms_step", C.c_double),
                 ("n_step", C.c_longlong), ("ms_train", C.c_double), ("ms_bwd_scan", C.c_double),
                 ("ms_bwd_rows", C.c_double), ("ms_bwd_sub", C.c_double), ("n_train", C.c_longlong),
-                ("n_bwd_scan", C.c_longlong), ("n_bwd_rows", C.c_longlong), ("n_bwd_sub", C.c_longlong)]
+                ("n_bwd_scan", C.c_longlong), ("n_bwd_rows", C.c_longlong), ("n_bwd_sub", C.c_longlong),
+                ("ms_project", C.c_double), ("n_project", C.c_longlong)]
 
 
 def declared_symbols(header: str = HEADER) -> list[str]:
@@ -60,6 +61,8 @@ def lib() -> C.CDLL:
         "sdm_forward_train": ([h, vp, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
         "sdm_backward_workspace_bytes": ([C.POINTER(Config), C.POINTER(C.c_size_t)], C.c_int),
         "sdm_backward": ([h] + [vp] * 16, C.c_int),
+        "sdm_project": ([h, C.c_int] + [vp] * 8, C.c_int),
+        "sdm_broadcast_memory": ([h, vp, vp], C.c_int),
         "sdm_destroy": ([h], C.c_int),
         "sdm_status_str": ([C.c_int], C.c_char_p),
         "sdm_last_error": ([], C.c_char_p),

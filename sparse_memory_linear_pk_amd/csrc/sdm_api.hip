@@ -29,7 +29,7 @@ sdm_status fail(sdm_status s, const char* fmt, ...)
 }
 
 enum Kind { K_SCORE = 0, K_SELECT = 1, K_PLAN = 2, K_SCAN = 3, K_STEP = 4, K_TRAIN = 5, K_BWD_SCAN = 6,
-            K_BWD_ROWS = 7, K_BWD_SUB = 8 };
+            K_BWD_ROWS = 7, K_BWD_SUB = 8, K_PROJ = 9 };
 
 struct TimedLaunch {
     Kind kind;
@@ -738,6 +738,43 @@ sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sub-key gradient launch");
 }
 
+sdm_status sdm_project(sdm_handle h, int D, const void* x, const void* w, const float* gate_bias, void* wq, void* rq,
+                       void* v, float* alpha, float* beta)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!x || !w || !gate_bias || !wq || !rq || !v || !alpha || !beta)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_project: NULL pointer");
+    if (!aligned16(x) || !aligned16(w) || !aligned4(gate_bias) || !aligned4(wq) || !aligned4(rq) || !aligned4(v) ||
+        !aligned4(alpha) || !aligned4(beta))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_project: misaligned pointer");
+    const sdm_config& c = h->cfg;
+    if (c.in_dtype != SDM_BF16)
+        return fail(SDM_ERR_UNSUPPORTED, "sdm_project: built for bf16 embeddings and weights");
+    if (D < 8 || D % 8 || D > (1 << 20))
+        return fail(SDM_ERR_UNSUPPORTED, "sdm_project: D=%d must be a multiple of 8 in [8, 2^20]", D);
+    Timer t(h, K_PROJ, h->stream);
+    hipError_t e = sdm::launch_project(x, w, gate_bias, wq, rq, v, alpha, beta, c.B * c.T, D, c.H, c.dk, c.d,
+                                       h->stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "projection launch");
+}
+
+sdm_status sdm_broadcast_memory(sdm_handle h, const void* m0, void* mem_out)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!m0 || !mem_out)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_broadcast_memory: NULL pointer");
+    if (!aligned16(m0) || !aligned16(mem_out))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_broadcast_memory: misaligned pointer");
+    const sdm_config& c = h->cfg;
+    const size_t bytes = (size_t)c.H * c.n_sub * c.n_sub * c.d * (c.state_dtype == SDM_BF16 ? 2 : 4);
+    hipError_t e = sdm::launch_broadcast(m0, mem_out, bytes, c.B, h->stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "broadcast launch");
+}
+
 sdm_status sdm_set_timing(sdm_handle h, int enable)
 {
     sdm_status s = check_handle(h);
@@ -778,6 +815,7 @@ sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t)
         case K_BWD_SCAN: h->totals.ms_bwd_scan += ms; h->totals.n_bwd_scan++; break;
         case K_BWD_ROWS: h->totals.ms_bwd_rows += ms; h->totals.n_bwd_rows++; break;
         case K_BWD_SUB: h->totals.ms_bwd_sub += ms; h->totals.n_bwd_sub++; break;
+        case K_PROJ: h->totals.ms_project += ms; h->totals.n_project++; break;
         }
         (void)hipEventDestroy(tl.start);
         (void)hipEventDestroy(tl.stop);

@@ -183,6 +183,13 @@ hipError_t launch_grad_scan(const GradArgs& a, hipStream_t stream);
 hipError_t launch_grad_rows(const GradArgs& a, hipStream_t stream);
 hipError_t launch_grad_subkeys(const GradArgs& a, hipStream_t stream);
 
+// Input projections y = x w^T (x [R, D], w [H*(2dk+d+2), D], bf16) with the
+// epilogue into wq, rq, v (bf16) and sigmoid gates alpha, beta (float32).
+hipError_t launch_project(const void* x, const void* w, const float* bias, void* wq, void* rq, void* v, float* alpha,
+                          float* beta, int R, int D, int H, int dk, int d, hipStream_t stream);
+// mem[b] = m0 for b < B (bytes_all_heads per sequence, a multiple of 16).
+hipError_t launch_broadcast(const void* m0, void* mem, size_t bytes_all_heads, int B, hipStream_t stream);
+
 // Measurement only: the scan's traffic pattern without arithmetic on `memories`
 // memories of `rows` rows of row_bytes (a multiple of 128) bytes; reads:writes
 // segments per slot position and token, 2:1 (the forward scan) or 4:3 (the
