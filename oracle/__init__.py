@@ -39,12 +39,13 @@ def build(src: str = SRC, out: str = LIB, extra_flags=()) -> str:
 
 
 PROJ_SRC = os.path.join(HERE, "sdm_oracle_proj.c")
+DIAG_SRC = os.path.join(HERE, "sdm_oracle_diag.c")
 PROJ_LIB = os.path.join(HERE, "liboracle_sdm_proj.so")
 
 
 def build_proj(src: str = PROJ_SRC, out: str = PROJ_LIB, extra_flags=()) -> str:
-    """Compile the projection oracle (with the forward oracle, for its bf16 rounding)."""
-    cmd = ["gcc", *CFLAGS, *extra_flags, "-I", HERE, src, SRC, "-o", out, "-lm"]
+    """Compile the projection and diagnostic oracle (with the forward oracle, for its bf16 rounding)."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-I", HERE, src, DIAG_SRC, SRC, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -347,12 +348,13 @@ class GradOracle:
 
 
 class ProjOracle:
-    """Handle on one build of the projection oracle (sdm_oracle_proj.c)."""
+    """Handle on one build of the projection oracle (sdm_oracle_proj.c) and the bucket-overlap
+    diagnostic oracle (sdm_oracle_diag.c)."""
 
     def __init__(self, path: str | None = None):
         path = path or PROJ_LIB
         if path == PROJ_LIB and (not os.path.exists(path) or os.path.getmtime(path) < max(
-                os.path.getmtime(PROJ_SRC), os.path.getmtime(SRC))):
+                os.path.getmtime(PROJ_SRC), os.path.getmtime(DIAG_SRC), os.path.getmtime(SRC))):
             build_proj()
         if not os.path.exists(path):
             raise FileNotFoundError(path)
@@ -363,7 +365,22 @@ class ProjOracle:
         L.oracle_project.restype = C.c_int
         L.oracle_broadcast_memory.argtypes = [C.c_int, C.c_int, C.c_long, vp, vp]
         L.oracle_broadcast_memory.restype = C.c_int
+        L.oracle_overlap.argtypes = [C.c_int] * 4 + [C.c_long, C.c_int] + [vp] * 4 + [C.c_int] + [vp] * 4
+        L.oracle_overlap.restype = C.c_int
         self.L = L
+
+    def overlap(self, B, T, H, W, N, K, idx_w, wt_w, idx_r, wt_r, queries):
+        """(write_cum [B,H,T,K], read [B,H,T,K], overlap [B,H,Q,T]) float32."""
+        arrs = [np.ascontiguousarray(idx_w, np.int32), np.ascontiguousarray(wt_w, np.float32),
+                np.ascontiguousarray(idx_r, np.int32), np.ascontiguousarray(wt_r, np.float32)]
+        q = np.ascontiguousarray(queries, np.int32)
+        wc = np.empty((B, H, T, K), np.float32)
+        rd = np.empty((B, H, T, K), np.float32)
+        ov = np.empty((B, H, max(q.size, 1), T), np.float32)
+        if self.L.oracle_overlap(B, T, H, W, N, K, *[_ptr(a) for a in arrs], q.size, _ptr(q) if q.size else None,
+                                 _ptr(wc), _ptr(rd), _ptr(ov)):
+            raise ValueError("oracle_overlap rejected its arguments")
+        return wc, rd, ov[:, :, :q.size]
 
     def project(self, B, T, H, D, dk, d, x, w, bias, threads=None):
         """(wq, rq, v as bf16 bits, alpha, beta float32) for x [B,T,D] bf16 bits, w [H*C, D] bf16 bits,

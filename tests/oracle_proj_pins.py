@@ -98,3 +98,49 @@ def pin_broadcast(p):
 
 
 PINS = [pin_worked_example, pin_identity_and_one_hot, pin_gate_closed_forms, pin_rounding_of_ties, pin_broadcast]
+
+
+# --- the write/read bucket-overlap diagnostic (sdm_oracle_diag.c) -----------------------------
+
+def pin_overlap_worked_example(p):
+    """T = 3 tokens, W = 2, N = 8 slots, K = 4 buckets (bucket = n // 2).
+    writes: t0 {1: .5, 6: .5}, t1 {2: .25, 3: .75}, t2 {6: 1, 0: 0};  reads: t0 {6: 1, 5: 0},
+    t1 {1: .5, 2: .5}, t2 {6: .5, 3: .5}.
+    cumulative write mass per bucket: t0 (.5, 0, 0, .5), t1 (.5, 1, 0, .5), t2 (.5, 1, 0, 1.5);
+    read mass (slot 5 of t0 carries weight 0): t0 (0, 0, 0, 1), t1 (.5, .5, 0, 0), t2 (0, .5, 0, .5).  Overlap for query 2: a=0 shares slot 6: .5*.5 = .25; a=1 shares slot 3:
+    .75*.5 = .375; a=2 shares slot 6: 1*.5 = .5.  Query 0: a=0 shares slot 6: .5*1 = .5; later tokens 0."""
+    idx_w = np.array([[1, 6], [2, 3], [6, 0]], np.int32)
+    wt_w = np.array([[.5, .5], [.25, .75], [1.0, 0.0]], np.float32)
+    idx_r = np.array([[6, 5], [1, 2], [6, 3]], np.int32)
+    wt_r = np.array([[1.0, 0.0], [.5, .5], [.5, .5]], np.float32)
+    wc, rd, ov = p.overlap(1, 3, 1, 2, 8, 4, idx_w, wt_w, idx_r, wt_r, [2, 0])
+    assert np.array_equal(wc[0, 0], np.array([[.5, 0, 0, .5], [.5, 1, 0, .5], [.5, 1, 0, 1.5]], np.float32))
+    assert np.array_equal(rd[0, 0], np.array([[0, 0, 0, 1], [.5, .5, 0, 0], [0, .5, 0, .5]], np.float32))
+    assert np.array_equal(ov[0, 0], np.array([[.25, .375, .5], [.5, 0, 0]], np.float32))
+
+
+def pin_overlap_planted_needle(p):
+    """A read query equal to an earlier write query selects the same slots with the same weights (the
+    forward oracle's addressing), so their overlap is the sum of the squared weights; the total write
+    mass after t tokens is t + 1 and every token's read mass is 1 (softmax weights), up to rounding."""
+    import oracle as _o
+    from sdm_inputs import Config
+    cfg = Config(name="needle", B=1, H=2, T=40, d=8, S=16, dk=16, k=4, W=8, in_bf16=False, state_bf16=False)
+    rng = np.random.default_rng(7)
+    wq = rng.standard_normal((cfg.B, cfg.T, cfg.H, cfg.dk)).astype(np.float32)
+    rq = rng.standard_normal((cfg.B, cfg.T, cfg.H, cfg.dk)).astype(np.float32)
+    rq[:, 33] = wq[:, 5]
+    sub = (rng.standard_normal((cfg.H, 2, cfg.S, cfg.dk // 2)) * 0.5).astype(np.float32)
+    f = _o.get()
+    iw, ww, _ = f.address(cfg, wq, sub)
+    ir, wr, _ = f.address(cfg, rq, sub)
+    wc, rd, ov = p.overlap(cfg.B, cfg.T, cfg.H, cfg.W, cfg.N, cfg.S, iw, ww, ir, wr, [33])
+    for h in range(cfg.H):
+        w5 = ww[(0 * cfg.T + 5) * cfg.H + h].astype(np.float64)
+        assert ov[0, h, 0, 5] == np.float32(np.sum(w5 * w5))
+        assert np.all(ov[0, h, 0, 34:] == 0)
+        assert np.allclose(wc[0, h].sum(axis=1), np.arange(1, cfg.T + 1), rtol=0, atol=1e-5)
+        assert np.allclose(rd[0, h].sum(axis=1), 1.0, rtol=0, atol=1e-6)
+
+
+PINS += [pin_overlap_worked_example, pin_overlap_planted_needle]

@@ -22,6 +22,34 @@ MUTANTS = {
                           "for (int k = 0; k + 1 < D; ++k)\n        s += bf(xr[k]) * bf(wr[k]);"),
     "broadcast_one_copy": ("for (int b = 0; b < B; ++b)\n        memcpy(", "for (int b = 0; b < 1; ++b)\n        memcpy("),
 }
+DIAG_MUTANTS = {
+    "bucket_from_second_half": ("acc[(long)nw * K / N] += wt_w[r * W + i];", "acc[(long)(nw % K)] += wt_w[r * W + i];"),
+    "writes_not_cumulative": ("                for (int k = 0; k < K; ++k)\n                    cur[k] = 0.0;",
+                              "                for (int k = 0; k < K; ++k)\n                    cur[k] = acc[k] = 0.0;"),
+    "read_with_write_weights": ("cur[(long)nr * K / N] += wt_r[r * W + i];", "cur[(long)nr * K / N] += wt_w[r * W + i];"),
+    "own_token_excluded": ("if (a <= q) {", "if (a < q) {"),
+    "overlap_read_weight_dropped": ("s += (double)wt_w[ra * W + i] * wt_r[rq * W + j];", "s += (double)wt_w[ra * W + i];"),
+}
+
+
+def _build_diag(name, old, new):
+    src = open(oracle.DIAG_SRC).read()
+    assert src.count(old) == 1, f"mutant {name}: the text to change must occur exactly once"
+    d = os.path.join(oracle.HERE, "_build")
+    os.makedirs(d, exist_ok=True)
+    path = os.path.join(d, f"diag_mutant_{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    out = os.path.join(d, f"libdiag_mutant_{name}.so")
+    import subprocess
+    subprocess.run(["gcc", *oracle.CFLAGS, "-Wno-unused-variable", "-I", oracle.HERE, oracle.PROJ_SRC, path, oracle.SRC,
+                    "-o", out, "-lm"], check=True)
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(DIAG_MUTANTS))
+def test_diag_mutant_is_caught(name):
+    assert _caught(oracle.ProjOracle(_build_diag(name, *DIAG_MUTANTS[name]))), f"no pin catches {name!r}"
 
 
 def _build(name, old, new):
