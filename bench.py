@@ -333,6 +333,71 @@ def project_bench(args, cfg):
     print(json.dumps(res))
 
 
+def overlap_bench(args, cfg):
+    """The bucket-overlap diagnostic (sdm_overlap) on the long-context needle workload: the call's
+    addressing, then the bucket masses (K = S buckets) and the overlap of every token's writes with the
+    read of the query token T - 17."""
+    import numpy as np
+    import torch
+
+    import sdm_inputs as gi
+    from sparse_memory_linear_pk_amd import SDM
+
+    if cfg.query != "planted":
+        cfg = gi.config(3)
+    log(f"generating inputs for {cfg}")
+    x = gi.make_inputs(cfg, with_mem0=False)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    R = cfg.B * cfg.T * cfg.H
+    K = cfg.S
+    f32 = dict(dtype=torch.float32, device="cuda")
+    layer = SDM.from_config(cfg)
+    addr = {}
+    for s_, q in (("w", "wq"), ("r", "rq")):
+        idx = torch.empty((R, cfg.W), dtype=torch.int32, device="cuda")
+        wt = torch.empty((R, cfg.W), **f32)
+        layer.address(dev(x[q]), dev(x["subkeys"]), idx, wt)
+        addr[s_] = (idx, wt)
+    wc = torch.empty((cfg.B, cfg.H, cfg.T, K), **f32)
+    rd = torch.empty_like(wc)
+    qs = torch.tensor([cfg.T - 17], dtype=torch.int32, device="cuda")
+    ov = torch.empty((cfg.B, cfg.H, 1, cfg.T), **f32)
+    args_ = (addr["w"][0], addr["w"][1], addr["r"][0], addr["r"][1], K, wc, rd, qs, ov)
+    layer.overlap(*args_)
+    torch.cuda.synchronize()
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        layer.overlap(*args_)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    curve = ov[0, 0, 0].cpu().numpy()
+    layer.close()
+    res = {
+        "metric": "SDM write/read bucket-overlap diagnostic tokens/sec (1 GPU), sdm_overlap",
+        "value": cfg.B * cfg.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": 1,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "dtype": "f64 sums",
+        "data": "synthetic long-context needle: read query of token T-17 = write query of token 61",
+        "config": {"workload": f"sdm-{cfg.name} diagnostic: B={cfg.B} T={cfg.T} N={cfg.S}^2 W={cfg.W}, "
+                               f"{K} buckets, query token {cfg.T - 17}"},
+        "needle": {"query": cfg.T - 17, "peak_token": int(np.argmax(curve)), "peak": float(curve.max())},
+    }
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +410,8 @@ def main():
                          "4 8B-shaped: bf16 state)")
     ap.add_argument("--decode", action="store_true",
                     help="time the decode step (sdm_step, one token per sequence per call) instead of the forward")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time the write/read bucket-overlap diagnostic on the long-context needle workload")
     ap.add_argument("--project", action="store_true",
                     help="time the input projections (sdm_project) instead of the forward")
     ap.add_argument("--train", action="store_true",
@@ -380,6 +447,8 @@ def main():
         return train_bench(args, cfg)
     if args.project:
         return project_bench(args, cfg)
+    if args.overlap:
+        return overlap_bench(args, cfg)
     log(f"generating inputs for {cfg}")
     t0 = time.perf_counter()
     x = gi.make_inputs(cfg)

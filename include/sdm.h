@@ -192,6 +192,23 @@ SDM_API sdm_status sdm_project(sdm_handle h, int D, const void* x, const void* w
  * B sequences' memories mem_out [B, H, N, d], ready for sdm_forward. */
 SDM_API sdm_status sdm_broadcast_memory(sdm_handle h, const void* m0, void* mem_out);
 
+/* Diagnostic, not part of the layer: the write/read bucket overlap of the SDM
+ * blog post's needle-in-a-haystack figure (section "Memory Access Patterns on
+ * a Needle-in-a-Haystack Task"), from a call's addressing idx_w, wt_w, idx_r,
+ * wt_r [B*T*H, W] (as sdm_address gives them; row (b*T + t)*H + h).  Slot n
+ * falls in bucket n * buckets / N (a contiguous slot range; buckets = S gives
+ * the first sub-key).  Outputs, float32, overwritten:
+ *   write_cum [B, H, T, buckets]  write weight landed in each bucket by tokens 0..t
+ *   read      [B, H, T, buckets]  token t's read weight in each bucket
+ *   overlap   [B, H, n_queries, T]  for query token q = queries[i] (device
+ *             int32 array) and token a <= q: the sum over the slots token a
+ *             writes and token q reads of w_a * r_q; 0 for a > q and for a
+ *             query outside [0, T).
+ * Sums in double, each value rounded once. */
+SDM_API sdm_status sdm_overlap(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
+                               const float* wt_r, int buckets, float* write_cum, float* read, int n_queries,
+                               const int32_t* queries, float* overlap);
+
 /* Free the workspace and the handle.  Waits for the handle's stream first. */
 SDM_API sdm_status sdm_destroy(sdm_handle h);
 

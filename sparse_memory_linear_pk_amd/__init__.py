@@ -129,6 +129,22 @@ class SDM:
         args = [self._t(m0, "m0", (H, S * S, d), "state"), self._t(mem, "mem", (B, H, S * S, d), "state")]
         check(lib().sdm_broadcast_memory(self._h, *[_ptr(a) for a in args]), "sdm_broadcast_memory")
 
+    def overlap(self, idx_w, wt_w, idx_r, wt_r, buckets, write_cum, read, queries=None, overlap=None):
+        """Bucket-overlap diagnostic of a call's addressing (sdm_overlap): write_cum, read [B, H, T, buckets]
+        float32; for int32 query tokens [Q], overlap [B, H, Q, T] float32."""
+        B, H, T, d, S, dk, k, W = self._dims()
+        R = B * T * H
+        args = [self._t(idx_w, "idx_w", (R, W), "i32"), self._t(wt_w, "wt_w", (R, W), "f32"),
+                self._t(idx_r, "idx_r", (R, W), "i32"), self._t(wt_r, "wt_r", (R, W), "f32")]
+        outs = [self._t(write_cum, "write_cum", (B, H, T, buckets), "f32"),
+                self._t(read, "read", (B, H, T, buckets), "f32")]
+        Q = 0 if queries is None else int(queries.numel())
+        qs = [None, None]
+        if Q:
+            qs = [self._t(queries, "queries", (Q,), "i32"), self._t(overlap, "overlap", (B, H, Q, T), "f32")]
+        check(lib().sdm_overlap(self._h, *[_ptr(a) for a in args], int(buckets), *[_ptr(a) for a in outs], Q,
+                                *[None if a is None else _ptr(a) for a in qs]), "sdm_overlap")
+
     def score(self, q, subkeys, scores):
         B, H, T, d, S, dk, k, W = self._dims()
         args = [self._t(q, "q", (B, T, H, dk), "in"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),

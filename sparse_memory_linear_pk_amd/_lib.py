@@ -63,6 +63,7 @@ def lib() -> C.CDLL:
         "sdm_backward": ([h] + [vp] * 16, C.c_int),
         "sdm_project": ([h, C.c_int] + [vp] * 8, C.c_int),
         "sdm_broadcast_memory": ([h, vp, vp], C.c_int),
+        "sdm_overlap": ([h, vp, vp, vp, vp, C.c_int, vp, vp, C.c_int, vp, vp], C.c_int),
         "sdm_destroy": ([h], C.c_int),
         "sdm_status_str": ([C.c_int], C.c_char_p),
         "sdm_last_error": ([], C.c_char_p),

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsdm.so")
 SOURCES = ["sdm_scan.hip", "sdm_scan_staged.hip", "sdm_api.hip", "pk_score.hip", "pk_topk.hip", "hbm_pattern.hip", "sdm_step.hip",
-           "sdm_backward.hip", "sdm_project.hip"]
+           "sdm_backward.hip", "sdm_project.hip", "sdm_diag.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

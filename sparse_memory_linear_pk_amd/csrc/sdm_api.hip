@@ -775,6 +775,28 @@ sdm_status sdm_broadcast_memory(sdm_handle h, const void* m0, void* mem_out)
     return e == hipSuccess ? SDM_OK : hip_fail(e, "broadcast launch");
 }
 
+sdm_status sdm_overlap(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r,
+                       int buckets, float* write_cum, float* read, int n_queries, const int32_t* queries,
+                       float* overlap)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!idx_w || !wt_w || !idx_r || !wt_r || !write_cum || !read || (n_queries > 0 && (!queries || !overlap)))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_overlap: NULL pointer");
+    if (!aligned4(idx_w) || !aligned4(wt_w) || !aligned4(idx_r) || !aligned4(wt_r) || !aligned4(write_cum) ||
+        !aligned4(read) || (n_queries > 0 && (!aligned4(queries) || !aligned4(overlap))))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_overlap: misaligned pointer");
+    const sdm_config& c = h->cfg;
+    const long N = (long)c.n_sub * c.n_sub;
+    if (buckets < 1 || buckets > N || n_queries < 0 || n_queries > (1 << 20))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_overlap: buckets=%d must be in [1, N=%ld], n_queries=%d in [0, 2^20]",
+                    buckets, N, n_queries);
+    hipError_t e = sdm::launch_overlap(idx_w, wt_w, idx_r, wt_r, buckets, write_cum, read, n_queries, queries, overlap,
+                                       c.B, c.T, c.H, c.W, N, h->stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "overlap launch");
+}
+
 sdm_status sdm_set_timing(sdm_handle h, int enable)
 {
     sdm_status s = check_handle(h);

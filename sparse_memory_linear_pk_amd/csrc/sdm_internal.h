@@ -190,6 +190,11 @@ hipError_t launch_project(const void* x, const void* w, const float* bias, void*
 // mem[b] = m0 for b < B (bytes_all_heads per sequence, a multiple of 16).
 hipError_t launch_broadcast(const void* m0, void* mem, size_t bytes_all_heads, int B, hipStream_t stream);
 
+// The write/read bucket-overlap diagnostic of a call's addressing.
+hipError_t launch_overlap(const int32_t* idx_w, const float* wt_w, const int32_t* idx_r, const float* wt_r, int K,
+                          float* write_cum, float* read, int Q, const int32_t* queries, float* overlap, int B, int T,
+                          int H, int W, long N, hipStream_t stream);
+
 // Measurement only: the scan's traffic pattern without arithmetic on `memories`
 // memories of `rows` rows of row_bytes (a multiple of 128) bytes; reads:writes
 // segments per slot position and token, 2:1 (the forward scan) or 4:3 (the

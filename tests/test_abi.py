@@ -10,7 +10,7 @@ from sparse_memory_linear_pk_amd._lib import Config, Timing, SDM_OK, SDM_ERR_INV
 EXPECTED = ["sdm_create", "sdm_forward", "sdm_destroy", "sdm_status_str", "sdm_last_error", "sdm_workspace_bytes",
             "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing",
             "sdm_pattern_probe", "sdm_step", "sdm_forward_train", "sdm_backward_workspace_bytes", "sdm_backward", "sdm_pattern_probe_mix", "sdm_project",
-            "sdm_broadcast_memory"]
+            "sdm_broadcast_memory", "sdm_overlap"]
 
 
 def _cfg(**kw):
@@ -75,6 +75,7 @@ def test_null_arguments():
                  ("sdm_scan_with", 9), ("sdm_step", 8), ("sdm_forward_train", 9), ("sdm_backward", 16), ("sdm_broadcast_memory", 2)):
         assert getattr(L, f)(None, *([None] * n)) == SDM_ERR_INVALID_ARG, f
     assert L.sdm_project(None, 64, *([None] * 8)) == SDM_ERR_INVALID_ARG
+    assert L.sdm_overlap(None, None, None, None, None, 4, None, None, 0, None, None) == SDM_ERR_INVALID_ARG
     assert L.sdm_destroy(None) == SDM_ERR_INVALID_ARG
     assert L.sdm_set_timing(None, 1) == SDM_ERR_INVALID_ARG
     assert L.sdm_get_timing(None, C.byref(Timing())) == SDM_ERR_INVALID_ARG
