@@ -176,8 +176,6 @@ def train_bench(args, cfg):
     import sdm_inputs as gi
     from sparse_memory_linear_pk_amd import SDM, pattern_probe_mix
 
-    if cfg.state_bf16:
-        raise SystemExit("the backward pass is built for a float32 state; use the 1.4B-shaped workload")
     log(f"generating inputs for {cfg}")
     x = gi.make_inputs(cfg)
 
@@ -191,7 +189,8 @@ def train_bench(args, cfg):
     gen = torch.Generator(device="cuda").manual_seed(7)
     dout = torch.randn((cfg.B, cfg.T, cfg.H, cfg.d), generator=gen, **f32)
     out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32)
-    log_buf = torch.empty((cfg.B, cfg.H, cfg.T, cfg.W, cfg.d), **f32)
+    log_buf = torch.empty((cfg.B, cfg.H, cfg.T, cfg.W, cfg.d),
+                          dtype=torch.bfloat16 if cfg.state_bf16 else torch.float32, device="cuda")
     dmem = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), **f32)
     g = {"dwq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32), "drq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32),
          "dv": torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32), "dalpha": torch.empty((cfg.B, cfg.T, cfg.H), **f32),
@@ -223,21 +222,28 @@ def train_bench(args, cfg):
     for k, v in g.items():
         if not torch.isfinite(v).all():
             raise RuntimeError(f"non-finite {k}")
-    # the ceiling of the reverse scan's access pattern: 4 reads and 3 writes of random 128-byte
-    # segments per slot position and token, same geometry, no arithmetic (scrambles the memory)
+    # the ceiling of the reverse scan's access pattern (float32 state: every segment 128 bytes):
+    # 4 reads and 3 writes of random 128-byte segments per slot position and token, same geometry,
+    # no arithmetic (scrambles the memory).  A bf16 state mixes 128-byte memory segments with
+    # 256-byte gradient segments, which the probe does not model.
     del log_buf
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=11)
-    s0.record()
-    for r in range(2):
-        pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=12 + r)
-    s1.record()
-    torch.cuda.synchronize()
-    probe_ms = s0.elapsed_time(s1) / 2
+    probe_ms = None
+    if not cfg.state_bf16:
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=11)
+        s0.record()
+        for r in range(2):
+            pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=12 + r)
+        s1.record()
+        torch.cuda.synchronize()
+        probe_ms = s0.elapsed_time(s1) / 2
     tokens = cfg.B * cfg.T
-    wd4 = cfg.W * cfg.d * 4
-    bwd_bytes = tokens * cfg.H * 7 * wd4     # reads M, G (read slots), G, log (write slots); writes G, G, M
-    fwd_bytes = tokens * cfg.H * 4 * wd4     # 2W rows read, W written, W logged
+    s_ = 2 if cfg.state_bf16 else 4
+    wd = cfg.W * cfg.d
+    # reverse scan per token: reads M and G of the read slots, G and the log of the write slots;
+    # writes G of both and the restored M (state s_ bytes, gradient 4 bytes per element)
+    bwd_bytes = tokens * cfg.H * wd * (s_ + 4 + 4 + s_ + 4 + 4 + s_)
+    fwd_bytes = tokens * cfg.H * wd * s_ * 4  # 2W rows read, W written, W logged
     bwd_ms = tm["ms_bwd_scan"] / max(1, tm["n_bwd_scan"])
     fwd_ms = tm["ms_train"] / steps  # the forward's scan launches (one per chunk)
     res = {
@@ -251,7 +257,7 @@ def train_bench(args, cfg):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 state, f32 gradients" if cfg.state_bf16 else "f32",
         "data": "synthetic (seeded inputs as for the forward; upstream gradient of out ~N(0,1), none of the final memory)",
         "config": {"workload": f"sdm-{cfg.name} layer training step: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} "
                                f"N={cfg.S}^2 dk={cfg.dk} k={cfg.k} W={cfg.W}", "global_batch": cfg.B,
@@ -259,10 +265,11 @@ def train_bench(args, cfg):
         "roofline": {"bound": "hbm", "kernel": "grad_scan", "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
                      "peak": 8000.0, "unit": "GB/s", "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / 8000.0,
                      "traffic": None, "bytes_per_launch": bwd_bytes, "ms_per_launch": bwd_ms,
-                     "pattern_ceiling": {"achieved": bwd_bytes / (probe_ms * 1e-3) / 1e9, "unit": "GB/s",
-                                         "ms_per_launch": probe_ms, "frac": probe_ms / bwd_ms,
-                                         "what": "sdm_pattern_probe_mix 4:3: the reverse scan's random 128-byte "
-                                                 "segment reads and writes with no arithmetic; frac = scan / this"}},
+                     "pattern_ceiling": None if probe_ms is None else {
+                         "achieved": bwd_bytes / (probe_ms * 1e-3) / 1e9, "unit": "GB/s",
+                         "ms_per_launch": probe_ms, "frac": probe_ms / bwd_ms,
+                         "what": "sdm_pattern_probe_mix 4:3: the reverse scan's random 128-byte "
+                                 "segment reads and writes with no arithmetic; frac = scan / this"}},
         "kernels_ms_per_step": {"train_scan": fwd_ms, "train_scan_GBps": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
                                 "pk_score": tm["ms_score"] / steps, "pk_topk": tm["ms_select"] / steps,
                                 "grad_scan": bwd_ms, "grad_rows": tm["ms_bwd_rows"] / steps,

@@ -88,13 +88,13 @@ class SDM:
         check(lib().sdm_step(self._h, *[_ptr(a) for a in args]), "sdm_step")
 
     def forward_train(self, wq, rq, v, alpha, beta, subkeys, mem, out, log):
-        """sdm_forward, and every write slot's value before its write into log [B, H, T, W, d] float32."""
+        """sdm_forward, and every write slot's value before its write into log [B, H, T, W, d] (state dtype)."""
         B, H, T, d, S, dk, k, W = self._dims()
         args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
                 self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
                 self._t(beta, "beta", (B, T, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
                 self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, T, H, d), "f32"),
-                self._t(log, "log", (B, H, T, W, d), "f32")]
+                self._t(log, "log", (B, H, T, W, d), "state")]
         check(lib().sdm_forward_train(self._h, *[_ptr(a) for a in args]), "sdm_forward_train")
 
     def backward(self, wq, rq, v, alpha, beta, subkeys, mem, log, dout, dmem, dwq, drq, dv, dalpha, dbeta, dsubkeys):
@@ -104,7 +104,7 @@ class SDM:
         args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
                 self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
                 self._t(beta, "beta", (B, T, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
-                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(log, "log", (B, H, T, W, d), "f32"),
+                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(log, "log", (B, H, T, W, d), "state"),
                 self._t(dout, "dout", (B, T, H, d), "f32"), self._t(dmem, "dmem", (B, H, S * S, d), "f32"),
                 self._t(dwq, "dwq", (B, T, H, dk), "f32"), self._t(drq, "drq", (B, T, H, dk), "f32"),
                 self._t(dv, "dv", (B, T, H, d), "f32"), self._t(dalpha, "dalpha", (B, T, H), "f32"),

@@ -267,7 +267,7 @@ sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hi
     a.v = static_cast<const char*>(v) + first * (c.in_dtype == SDM_BF16 ? 2 : 4);
     a.mem = mem;
     a.out = out + first;
-    a.log = log ? static_cast<char*>(log) + (size_t)r.t0 * c.W * c.d * 4u : nullptr;
+    a.log = log ? static_cast<char*>(log) + (size_t)r.t0 * c.W * c.d * (c.state_dtype == SDM_BF16 ? 2u : 4u) : nullptr;
     a.B = c.B;
     a.T = r.Tc;
     a.Ts = c.T;
@@ -315,13 +315,13 @@ sdm_status forward_impl(sdm_ctx* h, const void* wq, const void* rq, const void* 
 
 sdm_status check_train_shape(const sdm_config& c, const char* who)
 {
-    if (c.state_dtype != SDM_F32)
-        return fail(SDM_ERR_UNSUPPORTED, "%s: the backward pass is built for a float32 state", who);
-    if (c.d % 32)
-        return fail(SDM_ERR_UNSUPPORTED, "%s: d=%d must be a multiple of 32 (128-byte slot columns)", who, c.d);
+    const int seg = c.state_dtype == SDM_BF16 ? 64 : 32;
+    if (c.d % seg)
+        return fail(SDM_ERR_UNSUPPORTED, "%s: d=%d must be a multiple of %d (128-byte slot columns)", who, c.d, seg);
+    const unsigned sb = c.state_dtype == SDM_BF16 ? 2u : 4u;
     const Chunking k = chunking_of(c);
     for (int ci = 0; ci < k.C(); ++ci)
-        if ((uint64_t)k.len(ci) * c.W * c.d * 4u >= (1ull << 32) - 16u)
+        if ((uint64_t)k.len(ci) * c.W * c.d * sb >= (1ull << 32) - 16u)
             return fail(SDM_ERR_UNSUPPORTED, "%s: one memory's log of a %d-token chunk exceeds 4 GiB", who, k.len(ci));
     return SDM_OK;
 }
@@ -630,7 +630,8 @@ sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* bytes)
     const sdm_config& c = *cfg;
     const size_t rows = (size_t)c.B * c.T * c.H;
     const int nsplit = sdm::grad_sub_splits(c.B, c.H, c.T, c.n_sub, c.dk / 2);
-    *bytes = align_up(sdm::grad_part_floats(c.B, c.H, c.T, c.d, c.W) * 4) + align_up(2 * rows * 2 * c.n_sub * 4) +
+    *bytes = align_up(sdm::grad_part_floats(c.B, c.H, c.T, c.d, c.W, c.state_dtype == SDM_BF16) * 4) +
+             align_up(2 * rows * 2 * c.n_sub * 4) +
              align_up((size_t)nsplit * c.H * 2 * c.n_sub * (c.dk / 2) * 4) + align_up(rows * 4);
     return SDM_OK;
 }
@@ -667,7 +668,7 @@ sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void
         }
         char* p = (char*)h->bwd_block;
         h->part = (float*)p;
-        p += align_up(sdm::grad_part_floats(c.B, c.H, c.T, c.d, c.W) * 4);
+        p += align_up(sdm::grad_part_floats(c.B, c.H, c.T, c.d, c.W, c.state_dtype == SDM_BF16) * 4);
         h->ds = (float*)p;
         p += align_up(2 * rows * 2 * c.n_sub * 4);
         h->sub_part = (float*)p;
@@ -687,9 +688,11 @@ sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void
     a.dh = c.dk / 2;
     a.W = c.W;
     a.in_bf16 = c.in_dtype == SDM_BF16;
-    a.mem = static_cast<float*>(mem_inout);
+    a.state_bf16 = c.state_dtype == SDM_BF16;
+    a.ncol = c.d * (a.state_bf16 ? 2 : 4) / 128;
+    a.mem = mem_inout;
     a.G = dmem_inout;
-    a.log = static_cast<const float*>(log);
+    a.log = log;
     for (int set = 0; set < 2; ++set) {
         a.idx[set] = h->idx[set];
         a.wt[set] = h->wt[set];

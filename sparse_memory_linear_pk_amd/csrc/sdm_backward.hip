@@ -1,4 +1,4 @@
-// The backward pass of the SDM layer (float32 state): reverse-mode
+// The backward pass of the SDM layer (float32 or bf16 state): reverse-mode
 // differentiation of the forward (SDM blog post, section "How does SDM
 // work?", its "Write & Read" subsection and the caption of the figure "The SDM
 // mechanism, end to end"), with the selected slots held fixed and the state
@@ -30,7 +30,6 @@ namespace sdm {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int E = 4; // float32 state: 4 values per lane, 32 per 128-byte column
 
 __device__ __forceinline__ void load4(const float* p, float (&x)[4])
 {
@@ -48,8 +47,55 @@ __device__ __forceinline__ void load4(const uint16_t* p, float (&x)[4])
     x[2] = bf16_lo(u.y);
     x[3] = bf16_hi(u.y);
 }
+__device__ __forceinline__ void load8(const float* p, float (&x)[8])
+{
+    const float4 u = *reinterpret_cast<const float4*>(p), w = *reinterpret_cast<const float4*>(p + 4);
+    x[0] = u.x;
+    x[1] = u.y;
+    x[2] = u.z;
+    x[3] = u.w;
+    x[4] = w.x;
+    x[5] = w.y;
+    x[6] = w.z;
+    x[7] = w.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8])
+{
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(q[i]);
+        x[2 * i + 1] = bf16_hi(q[i]);
+    }
+}
+template <int E, class T> __device__ __forceinline__ void loadE(const T* p, float (&x)[E])
+{
+    if constexpr (E == 4)
+        load4(p, x);
+    else
+        load8(p, x);
+}
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+
+// E float32 gradient values of a lane from / into GU 16-byte pieces
+template <int GU, int E> __device__ __forceinline__ void unpack_g(const uint4 (&u)[GU], float (&x)[E])
+{
+    static_assert(E == 4 * GU, "gradient pieces");
+#pragma unroll
+    for (int i = 0; i < GU; ++i) {
+        x[4 * i] = __uint_as_float(u[i].x);
+        x[4 * i + 1] = __uint_as_float(u[i].y);
+        x[4 * i + 2] = __uint_as_float(u[i].z);
+        x[4 * i + 3] = __uint_as_float(u[i].w);
+    }
+}
+template <int E> __device__ __forceinline__ uint4 pack_g(const float (&x)[E], int i)
+{
+    return make_uint4(__float_as_uint(x[4 * i]), __float_as_uint(x[4 * i + 1]), __float_as_uint(x[4 * i + 2]),
+                      __float_as_uint(x[4 * i + 3]));
+}
 
 // the sum over the 8 lanes of a lane group (lanes differing in bits 0..2), in a fixed tree
 __device__ __forceinline__ float sum8(float x)
@@ -60,30 +106,39 @@ __device__ __forceinline__ float sum8(float x)
     return x;
 }
 
-template <class VT>
+// ST: state element (float or bf16 bits); the gradient is float32 either way.
+// A workgroup owns 128 bytes of every memory row (E = 4 float32 or 8 bf16
+// values per lane) and the matching E float32 values per lane of the gradient
+// rows (16 or 32 bytes).
+template <class ST, class VT>
 __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint4 s_g[64 * 8]; // read slots' gradients after the read
+    constexpr int E = 16 / (int)sizeof(ST);
+    constexpr int GU = E / 4; // 16-byte gradient pieces per lane and position
+    __shared__ __attribute__((aligned(16))) uint4 s_g[64 * 8 * GU]; // read slots' gradients after the read
     __shared__ int32_t s_rslot[64];
     __shared__ __attribute__((aligned(16))) float s_y[kWaves * 8 * E];
     __shared__ __attribute__((aligned(16))) float s_d[kWaves * 8 * E];
     __shared__ float s_al[kWaves];
 
-    const int ncol = a.d / 32;
+    const int ncol = a.ncol; // d * sizeof(ST) / 128
     const int bh = blockIdx.x / ncol, col = blockIdx.x % ncol;
     const int b = bh / a.H, h = bh % a.H;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 3, el = lane & 7;
     const int W = a.W, P = 2 * a.W + 2;
     const long N = (long)a.S * a.S;
-    const uint32_t row_bytes = (uint32_t)a.d * 4u;
+    const uint32_t row_bytes = (uint32_t)a.d * (uint32_t)sizeof(ST), grow_bytes = (uint32_t)a.d * 4u;
     const uint32_t lane_off = (uint32_t)col * 128u + (uint32_t)el * 16u;
-    const size_t mem_off = (size_t)bh * N * a.d;
-    const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(a.mem + mem_off, (uint32_t)(N * row_bytes));
-    const __amdgpu_buffer_rsrc_t r_g = make_rsrc(a.G + mem_off, (uint32_t)(N * row_bytes));
+    const uint32_t glane_off = (uint32_t)col * (128u * GU) + (uint32_t)el * (16u * GU);
+    const size_t mem_el = (size_t)bh * N * a.d; // first element of memory bh
+    ST* const mem = static_cast<ST*>(a.mem);
+    const ST* const log = static_cast<const ST*>(a.log);
+    const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(mem + mem_el, (uint32_t)(N * row_bytes));
+    const __amdgpu_buffer_rsrc_t r_g = make_rsrc(a.G + mem_el, (uint32_t)(N * grow_bytes));
     const int pos[2] = {wave * 16 + g, wave * 16 + 8 + g};
     const bool live[2] = {pos[0] < W, pos[1] < W};
-    const int e0 = col * 32 + el * E; // this lane's first element of the row
+    const int e0 = col * (128 / (int)sizeof(ST)) + el * E; // this lane's first element of the row
 
     // A token's slots are fetched two tokens ahead, its other state-independent
     // inputs (weights, the log of its write slots, dout, v, the gates) and its
@@ -108,7 +163,7 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
         int conflict;
     };
     struct Rows4 {
-        uint4 rv[2], rg[2], wg[2]; // read slots' memory and gradient, write slots' gradient
+        uint4 rv[2], rg[2][GU], wg[2][GU]; // read slots' memory and gradient, write slots' gradient
     };
     const int posc[2] = {min(pos[0], W - 1), min(pos[1], W - 1)}; // a valid position to read
     auto fetch_ids = [&](int t, Ids& m) __attribute__((always_inline)) {
@@ -128,10 +183,10 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             // would wait for the load)
             m.ww[p] = a.wt[0][row * W + posc[p]];
             m.rw[p] = a.wt[1][row * W + posc[p]];
-            m.wo[p] = *reinterpret_cast<const uint4*>(a.log + (((size_t)bh * a.T + t) * W + posc[p]) * a.d + e0);
+            m.wo[p] = *reinterpret_cast<const uint4*>(log + (((size_t)bh * a.T + t) * W + posc[p]) * a.d + e0);
         }
-        load4(a.dout + (size_t)row * a.d + e0, m.go);
-        load4(static_cast<const VT*>(a.v) + (size_t)row * a.d + e0, m.vv);
+        loadE<E>(a.dout + (size_t)row * a.d + e0, m.go);
+        loadE<E>(static_cast<const VT*>(a.v) + (size_t)row * a.d + e0, m.vv);
         m.al = a.alpha[row];
         m.be = a.beta[row];
         m.conflict = a.conflict[row];
@@ -140,8 +195,11 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             st.rv[p] = ld128(r_mem, live[p] ? (uint32_t)m.rs[p] * row_bytes + lane_off : kOOB);
-            st.rg[p] = ld128(r_g, live[p] ? (uint32_t)m.rs[p] * row_bytes + lane_off : kOOB);
-            st.wg[p] = ld128(r_g, live[p] ? (uint32_t)m.ws[p] * row_bytes + lane_off : kOOB);
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                st.rg[p][u] = ld128(r_g, live[p] ? (uint32_t)m.rs[p] * grow_bytes + glane_off + 16u * u : kOOB);
+                st.wg[p][u] = ld128(r_g, live[p] ? (uint32_t)m.ws[p] * grow_bytes + glane_off + 16u * u : kOOB);
+            }
         }
     };
     // step t of parity X = (T-1-t) & 1 starts with: I[X] = slots of t, I[1-X] = slots of
@@ -171,7 +229,6 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
         const float rw[2] = {live[0] ? m.rw[0] : 0.f, live[1] ? m.rw[1] : 0.f};
         const uint4 wo[2] = {m.wo[0], m.wo[1]}; // dead positions: zeroed when unpacked below
         const Rows4& sc = St[X];
-        const uint4 rv[2] = {sc.rv[0], sc.rv[1]}, rg[2] = {sc.rg[0], sc.rg[1]}, wg[2] = {sc.wg[0], sc.wg[1]};
         float go[E], vv[E];
 #pragma unroll
         for (int q = 0; q < E; ++q) {
@@ -184,8 +241,8 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             float m[E], gr[E];
-            Cell<float>::unpack(rv[p], m);
-            Cell<float>::unpack(rg[p], gr);
+            Cell<ST>::unpack(sc.rv[p], m);
+            unpack_g<GU>(sc.rg[p], gr);
             float s = 0.f;
 #pragma unroll
             for (int q = 0; q < E; ++q) {
@@ -195,9 +252,12 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             s = sum8(s);
             if (el == 0 && live[p])
                 part[pos[p]] = s;
-            const uint4 pk = Cell<float>::pack(gr);
-            s_g[pos[p] * 8 + el] = pk;
-            st128(r_g, live[p] ? (uint32_t)rs[p] * row_bytes + lane_off : kOOB, pk);
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const uint4 pk = pack_g(gr, u);
+                s_g[(pos[p] * 8 + el) * GU + u] = pk;
+                st128(r_g, live[p] ? (uint32_t)rs[p] * grow_bytes + glane_off + 16u * u : kOOB, pk);
+            }
         }
         if (el == 0) {
             s_rslot[pos[0]] = rs[0];
@@ -223,8 +283,16 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
 #pragma unroll
             for (int m = 1; m < 8; m <<= 1)
                 hit = max(hit, __shfl_xor(hit, m));
-            Cell<float>::unpack(hit >= 0 ? s_g[hit * 8 + el] : wg[p], gw[p]);
-            Cell<float>::unpack(live[p] ? wo[p] : make_uint4(0u, 0u, 0u, 0u), old[p]);
+            if (hit >= 0) {
+                uint4 hv[GU];
+#pragma unroll
+                for (int u = 0; u < GU; ++u)
+                    hv[u] = s_g[(hit * 8 + el) * GU + u];
+                unpack_g<GU>(hv, gw[p]);
+            } else {
+                unpack_g<GU>(sc.wg[p], gw[p]);
+            }
+            Cell<ST>::unpack(live[p] ? wo[p] : make_uint4(0u, 0u, 0u, 0u), old[p]);
 #pragma unroll
             for (int q = 0; q < E; ++q)
                 x[p][q] = al * old[p][q];
@@ -264,9 +332,10 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             sw = sum8(sw);
             if (el == 0 && live[p])
                 part[W + pos[p]] = sw;
-            const uint32_t off = live[p] ? (uint32_t)ws[p] * row_bytes + lane_off : kOOB;
-            st128(r_g, off, Cell<float>::pack(ng));
-            st128(r_mem, off, wo[p]); // the slot's value before the token
+#pragma unroll
+            for (int u = 0; u < GU; ++u)
+                st128(r_g, live[p] ? (uint32_t)ws[p] * grow_bytes + glane_off + 16u * u : kOOB, pack_g(ng, u));
+            st128(r_mem, live[p] ? (uint32_t)ws[p] * row_bytes + lane_off : kOOB, wo[p]); // the slot before the token
         }
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1)
@@ -282,11 +351,14 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             sb = sum8(sb);
             if (el == 0)
                 part[2 * W + 1] = sb;
-            o.x = be * dd[0];
-            o.y = be * dd[1];
-            o.z = be * dd[2];
-            o.w = be * dd[3];
-            *reinterpret_cast<float4*>(a.dv + (size_t)row * a.d + e0) = o;
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                o.x = be * dd[4 * u];
+                o.y = be * dd[4 * u + 1];
+                o.z = be * dd[4 * u + 2];
+                o.w = be * dd[4 * u + 3];
+                *reinterpret_cast<float4*>(a.dv + (size_t)row * a.d + e0 + 4 * u) = o;
+            }
         }
         __syncthreads(); // token t's stores are visible to the workgroup's loads from here on
         if (threadIdx.x == 0)
@@ -339,7 +411,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void grad_rows_kernel(GradArgs 
     const long row = (long)blockIdx.x * kRowsPerBlock + wave;
     if (row >= R)
         return; // the whole wave; no block barriers below
-    const int W = a.W, P = 2 * a.W + 2, S = a.S, dh = a.dh, dk = 2 * a.dh, ncol = a.d / 32;
+    const int W = a.W, P = 2 * a.W + 2, S = a.S, dh = a.dh, dk = 2 * a.dh, ncol = a.ncol;
     const int h = (int)(row % a.H);
     float* my = s_dsrow + wave * S;
     const bool live = lane < W;
@@ -486,9 +558,9 @@ __global__ __launch_bounds__(256) void grad_subkey_sum_kernel(const float* part,
 
 } // namespace
 
-size_t grad_part_floats(int B, int H, int T, int d, int W)
+size_t grad_part_floats(int B, int H, int T, int d, int W, bool state_bf16)
 {
-    return (size_t)B * T * H * (size_t)(d / 32) * (size_t)(2 * W + 2);
+    return (size_t)B * T * H * (size_t)(d / (state_bf16 ? 64 : 32)) * (size_t)(2 * W + 2);
 }
 
 int grad_sub_splits(int B, int H, int T, int S, int dh)
@@ -512,13 +584,21 @@ hipError_t launch_grad_conflicts(const GradArgs& a, hipStream_t stream)
 
 hipError_t launch_grad_scan(const GradArgs& a, hipStream_t stream)
 {
-    if (a.d % 32 || a.W > 64 || a.W < 1)
+    const int seg = a.state_bf16 ? 64 : 32;
+    if (a.d % seg || a.ncol != a.d / seg || a.W > 64 || a.W < 1)
         return hipErrorInvalidValue;
-    dim3 grid((unsigned)(a.B * a.H * (a.d / 32))), block(kWaves * 64);
-    if (a.in_bf16)
-        hipLaunchKernelGGL((grad_scan_kernel<uint16_t>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((grad_scan_kernel<float>), grid, block, 0, stream, a);
+    dim3 grid((unsigned)(a.B * a.H * a.ncol)), block(kWaves * 64);
+    if (a.state_bf16) {
+        if (a.in_bf16)
+            hipLaunchKernelGGL((grad_scan_kernel<uint16_t, uint16_t>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((grad_scan_kernel<uint16_t, float>), grid, block, 0, stream, a);
+    } else {
+        if (a.in_bf16)
+            hipLaunchKernelGGL((grad_scan_kernel<float, uint16_t>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((grad_scan_kernel<float, float>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -150,13 +150,15 @@ hipError_t launch_sdm_step(const void* wq, const void* rq, const void* v, const 
                            const void* subkeys, void* mem, float* out, int32_t* idx, float* wt, int B, int H, int d,
                            int S, int dh, int k, int W, bool in_bf16, bool state_bf16, hipStream_t stream);
 
-// The backward pass (float32 state; d a multiple of 32).
+// The backward pass (float32 state with d a multiple of 32, or bf16 state with
+// d a multiple of 64: 128-byte memory columns; the gradient is float32).
 struct GradArgs {
     int B, H, T, d, S, dh, W;
-    bool in_bf16;
-    float* mem;                          // [B*H, N, d]: memory after the forward in, before it out
+    int ncol;                            // 128-byte memory columns per row: d * sizeof(state) / 128
+    bool in_bf16, state_bf16;
+    void* mem;                           // [B*H, N, d] state: memory after the forward in, before it out
     float* G;                            // [B*H, N, d]: dL/d(memory after) in, dL/d(memory before) out
-    const float* log;                    // [B*H, T, W, d]
+    const void* log;                     // [B*H, T, W, d] state
     const int32_t* idx[2];               // write, read slots [rows, W]
     const float* wt[2];                  // their weights
     const void* q[2];                    // wq, rq [rows, dk]
@@ -176,7 +178,7 @@ struct GradArgs {
     int32_t* conflict;                   // workspace: [rows], token shares a slot with the next one
     int nsplit;
 };
-size_t grad_part_floats(int B, int H, int T, int d, int W);
+size_t grad_part_floats(int B, int H, int T, int d, int W, bool state_bf16);
 int grad_sub_splits(int B, int H, int T, int S, int dh);
 hipError_t launch_grad_conflicts(const GradArgs& a, hipStream_t stream);
 hipError_t launch_grad_scan(const GradArgs& a, hipStream_t stream);

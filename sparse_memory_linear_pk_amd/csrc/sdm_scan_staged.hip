@@ -436,10 +436,15 @@ hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& p, bool sta
         return hipErrorInvalidValue;
     dim3 grid((unsigned)p.grid), block(kWaves * 64);
     if (a.log) {
-        // the log of a call: float32 state, and one memory's tokens of a chunk addressable by 32-bit offsets
-        if (state_bf16 || (uint64_t)a.T * a.W * a.d * 4u >= (1ull << 32) - 16u)
+        // the log of a call: one memory's tokens of a chunk addressable by 32-bit offsets
+        if ((uint64_t)a.T * a.W * a.d * (state_bf16 ? 2u : 4u) >= (1ull << 32) - 16u)
             return hipErrorInvalidValue;
-        if (in_bf16)
+        if (state_bf16) {
+            if (in_bf16)
+                hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, uint16_t, true>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, float, true>), grid, block, 0, stream, a);
+        } else if (in_bf16)
             hipLaunchKernelGGL((sdm_scan_staged_kernel<float, uint16_t, true>), grid, block, 0, stream, a);
         else
             hipLaunchKernelGGL((sdm_scan_staged_kernel<float, float, true>), grid, block, 0, stream, a);

@@ -113,9 +113,9 @@ def test_backward_workspace_for_the_1p4b_shape():
     assert n.value >= rows * 64 * 130 * 4 + 2 * rows * 2 * 480 * 4
 
 
-@pytest.mark.parametrize("kw", [dict(state_dtype=1, n_sub=240), dict(d=2040)])
+@pytest.mark.parametrize("kw", [dict(state_dtype=1, n_sub=240, d=2016), dict(d=2040)])
 def test_backward_rejects_what_it_does_not_build(kw):
-    """A bf16 state, and slot rows that are not whole 128-byte float32 columns."""
+    """Slot rows that are not whole 128-byte columns (64 bf16 or 32 float32 elements)."""
     L = _lib.lib()
     n = C.c_size_t()
     assert L.sdm_backward_workspace_bytes(C.byref(_cfg(**kw)), C.byref(n)) == SDM_ERR_UNSUPPORTED

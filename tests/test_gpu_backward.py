@@ -46,7 +46,14 @@ CASES = {
     "k_eq_W_64": _cfg(B=1, H=1, T=20, d=32, S=64, dk=32, k=64, W=64),
     # long enough to scan in chunks (1024 tokens, then the rest): the log of every chunk
     "chunked_T2600": _cfg(B=2, H=1, T=2600, d=32, S=16, dk=32, k=4, W=8),
+    # bf16 state (the 8B-shaped workload's): bf16 memory and log, float32 gradient
+    "bf16_state": _cfg(B=2, H=2, T=48, d=64, S=16, dk=32, k=4, W=8, in_bf16=True, state_bf16=True),
+    "bf16_state_8B_addressing_d128": gi.config(4, B=1, T=40, d=128),
 }
+
+
+def _bits(a):
+    return np.ascontiguousarray(a).view(np.uint8)
 
 
 def _run_gpu(cfg, x, g, reps=1):
@@ -62,7 +69,8 @@ def _run_gpu(cfg, x, g, reps=1):
         layer.forward(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem_f, out_f)
         mem = dev["mem0"].clone()
         out = torch.empty_like(out_f)
-        log = torch.empty((cfg.B, cfg.H, cfg.T, cfg.W, cfg.d), **f32)
+        log = torch.empty((cfg.B, cfg.H, cfg.T, cfg.W, cfg.d),
+                          dtype=torch.bfloat16 if cfg.state_bf16 else torch.float32, device="cuda")
         layer.forward_train(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem, out, log)
         torch.cuda.synchronize()
         res.update(out_f=to_host(out_f), mem_f=to_host(mem_f), out=to_host(out), mem_T=to_host(mem), log=to_host(log))
@@ -112,10 +120,10 @@ def test_backward_matches_the_gradient_oracle(name):
     run = res["runs"][0]
 
     # the training forward is the forward
-    assert np.array_equal(res["out"].view(np.uint32), res["out_f"].view(np.uint32))
-    assert np.array_equal(res["mem_T"].view(np.uint32), res["mem_f"].view(np.uint32))
+    assert np.array_equal(_bits(res["out"]), _bits(res["out_f"]))
+    assert np.array_equal(_bits(res["mem_T"]), _bits(res["mem_f"]))
     # the reverse walk restores the initial memory exactly
-    assert np.array_equal(run["mem0"].view(np.uint32), x["mem0"].view(np.uint32))
+    assert np.array_equal(_bits(run["mem0"]), _bits(x["mem0"]))
 
     for s_, q in (("w", x["wq"]), ("r", x["rq"])):
         ri, rw, rs = orc.address(cfg, q, x["subkeys"])
@@ -167,7 +175,7 @@ def test_backward_is_deterministic_and_repeatable():
     g = gi.make_upstream_grads(cfg)
     runs = _run_gpu(cfg, x, g, reps=2)["runs"]
     for k in runs[0]:
-        assert np.array_equal(runs[0][k].view(np.uint32), runs[1][k].view(np.uint32)), k
+        assert np.array_equal(_bits(runs[0][k]), _bits(runs[1][k])), k
 
 
 def test_backward_with_heavy_slot_reuse():
@@ -187,18 +195,19 @@ def test_backward_with_heavy_slot_reuse():
         e = rel_max_err(run[k], ref[k])
         say(f"[bwd reuse] {k} {e:.3g}")
         assert e <= TOL, k
-    assert np.array_equal(run["mem0"].view(np.uint32), x["mem0"].view(np.uint32))
+    assert np.array_equal(_bits(run["mem0"]), _bits(x["mem0"]))
 
 
-def test_backward_rejects_a_bf16_state():
+def test_backward_rejects_a_bf16_state_of_partial_columns():
+    """A bf16 state needs whole 128-byte columns of 64 elements: d = 96 is refused on the host."""
     import torch
     from sparse_memory_linear_pk_amd import SDM, SDMError
-    cfg = _cfg(state_bf16=True)
+    cfg = _cfg(state_bf16=True, d=96)
     with SDM.from_config(cfg) as layer:
         t = lambda *s: torch.zeros(s, dtype=torch.float32, device="cuda")
-        mem = torch.zeros((cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.bfloat16, device="cuda")
-        with pytest.raises(SDMError, match="float32 state"):
+        b = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(SDMError, match="multiple of 64"):
             layer.forward_train(t(cfg.B, cfg.T, cfg.H, cfg.dk), t(cfg.B, cfg.T, cfg.H, cfg.dk),
                                 t(cfg.B, cfg.T, cfg.H, cfg.d), t(cfg.B, cfg.T, cfg.H), t(cfg.B, cfg.T, cfg.H),
-                                t(cfg.H, 2, cfg.S, cfg.dk // 2), mem, t(cfg.B, cfg.T, cfg.H, cfg.d),
-                                t(cfg.B, cfg.H, cfg.T, cfg.W, cfg.d))
+                                t(cfg.H, 2, cfg.S, cfg.dk // 2), b(cfg.B, cfg.H, cfg.N, cfg.d),
+                                t(cfg.B, cfg.T, cfg.H, cfg.d), b(cfg.B, cfg.H, cfg.T, cfg.W, cfg.d))
