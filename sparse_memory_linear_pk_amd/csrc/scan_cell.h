@@ -67,6 +67,38 @@ template <> struct Cell<uint16_t> {
     }
 };
 
+// A lane's 8 bytes of a bf16 state in a 64-byte slot segment (4 values), for
+// memories too few to fill the device with 128-byte segments: the same
+// arithmetic and rounding as Cell<uint16_t>, held in the low half of a uint4.
+template <class ST> struct CellHalf;
+template <> struct CellHalf<uint16_t> {
+    static constexpr int E = 4;
+    using CT = double;
+    __device__ static void unpack(const uint4& u, float (&x)[4])
+    {
+        x[0] = bf16_lo(u.x);
+        x[1] = bf16_hi(u.x);
+        x[2] = bf16_lo(u.y);
+        x[3] = bf16_hi(u.y);
+    }
+    __device__ static uint4 pack(const double (&x)[4])
+    {
+        float f[4];
+        bool tie = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[q] = (float)x[q];
+            tie |= (__float_as_uint(f[q]) & 0xFFFFu) == 0x8000u;
+        }
+        if (__builtin_amdgcn_ballot_w64(tie) != 0u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                f[q] = settle_bf16_tie(x[q]);
+        }
+        return make_uint4(Cell<uint16_t>::pack2(f[0], f[1]), Cell<uint16_t>::pack2(f[2], f[3]), 0u, 0u);
+    }
+};
+
 // Totals over the 4 waves of the per-wave partials ([wave][el][E] values of
 // type X) of element lane el, in the same order in every lane.
 template <int E, class X>

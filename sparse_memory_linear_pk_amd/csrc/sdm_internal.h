@@ -104,6 +104,7 @@ struct ScanPlan {
     int grid;      // workgroups
     int lds;       // dynamic LDS bytes
     int Tp;        // staged: tokens per memory in the plan (T padded with sentinel tokens)
+    int seg_bytes; // staged: bytes of a slot row per workgroup, 128, or 64 (bf16 state, too few memories)
 };
 
 bool plan_scan(int B, int H, int T, int d, int W, long N, bool state_bf16, bool in_bf16, ScanPlan* plan);

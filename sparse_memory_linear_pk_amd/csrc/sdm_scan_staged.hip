@@ -13,7 +13,10 @@
 // the read sees the stored values and sums in float32.
 //
 // Work split.  A workgroup of 4 waves owns one (b, h) and 128 bytes of every
-// slot row (32 float32 or 64 bf16 elements) and walks all T tokens.  A token's
+// slot row (32 float32 or 64 bf16 elements) and walks all T tokens.  When the
+// memories are too few to fill the device that way (one long sequence), a
+// bf16 state is split into 64-byte segments instead (8 lanes x 8 bytes, 4
+// values per lane): twice the workgroups, half the arithmetic per token each.  A token's
 // 64 positions (the W selected slots, padded with sentinels) spread over the
 // waves, 16 each: lane (g, e) of wave w holds the 16 bytes e of positions
 // 16w + g and 16w + 8 + g (E = 4 or 8 elements).  Sums over positions are a
@@ -90,15 +93,35 @@ __device__ __forceinline__ void barrier_lds()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// A segment's 16 or 8 bytes of one lane (8 bytes: the low half of the uint4).
+template <int SEGB> __device__ __forceinline__ uint4 ldseg(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    if constexpr (SEGB == 128) {
+        return ld128(r, off);
+    } else {
+        const i32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_uint4((uint32_t)v[0], (uint32_t)v[1], 0u, 0u);
+    }
+}
+template <int SEGB> __device__ __forceinline__ void stseg(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v)
+{
+    if constexpr (SEGB == 128)
+        st128(r, off, v);
+    else
+        __builtin_amdgcn_raw_buffer_store_b64((i32x2_t){(int)v.x, (int)v.y}, r, off, 0, 0);
+}
+
 // ST: state element (float or bf16 bits), VT: v element (float or bf16 bits),
-// LOG: also store the write slots' values before the write to a.log.
-template <class ST, class VT, bool LOG>
+// LOG: also store the write slots' values before the write to a.log,
+// SEGB: bytes of every slot row the workgroup owns (128, or 64 for a bf16 state).
+template <class ST, class VT, bool LOG, int SEGB>
 __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
 {
-    using C = Cell<ST>;
+    static_assert(SEGB == 128 || (SEGB == 64 && sizeof(ST) == 2), "segment width");
+    using C = std::conditional_t<SEGB == 128, Cell<ST>, CellHalf<ST>>;
     using CT = typename C::CT;                       // type of the write arithmetic
     constexpr int E = C::E;                          // state elements per lane
-    constexpr int SEG = 128 / (int)sizeof(ST);       // state elements of a workgroup's segment
+    constexpr int SEG = SEGB / (int)sizeof(ST);      // state elements of a workgroup's segment
     constexpr int VB = E * (int)sizeof(VT);          // bytes of v per lane and token: 8, 16 or 32
     constexpr int NV = VB <= 16 ? 1 : 2;             // v loads per token
     constexpr int NO = E / 4;                        // out stores per token (16 bytes each)
@@ -120,7 +143,7 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const int b = bh / H;
     const uint32_t row_bytes = (uint32_t)d * (uint32_t)sizeof(ST);
-    const uint32_t lane_off = (uint32_t)chunk * 128u + (uint32_t)el * 16u;
+    const uint32_t lane_off = (uint32_t)chunk * SEGB + (uint32_t)el * (SEGB / 8);
     const uint32_t tok_elems = (uint32_t)T * H * d;
 
     const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * row_bytes,
@@ -321,10 +344,10 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         const uint32_t or0 = __umul24(u0.y & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
         const uint32_t or1 = __umul24(u1.y & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
         // a forwarded write slot is not loaded (top bit of y); a forwarded read slot is the sentinel
-        wset[S][0] = ld128(r_mem, (u0.y >> 31) ? kOOB : ow0);
-        wset[S][1] = ld128(r_mem, (u1.y >> 31) ? kOOB : ow1);
-        rset[S][0] = ld128(r_mem, or0);
-        rset[S][1] = ld128(r_mem, or1);
+        wset[S][0] = ldseg<SEGB>(r_mem, (u0.y >> 31) ? kOOB : ow0);
+        wset[S][1] = ldseg<SEGB>(r_mem, (u1.y >> 31) ? kOOB : ow1);
+        rset[S][0] = ldseg<SEGB>(r_mem, or0);
+        rset[S][1] = ldseg<SEGB>(r_mem, or1);
         soff[S][0] = (u0.x >> 31) ? kOOB : ow0;
         soff[S][1] = (u1.x >> 31) ? kOOB : ow1;
         if constexpr (VB == 8) {
@@ -409,18 +432,18 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
                 update(std::integral_constant<int, j1>{}, wset[j1 % ZS], b0, b1, __uint_as_float(hb.x),
                        __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1, ob0, ob1);
             }
-            st128(r_mem, soff[j0 % ZS][0], ya0);
-            st128(r_mem, soff[j0 % ZS][1], ya1);
-            st128(r_mem, soff[j1 % ZS][0], yb0);
-            st128(r_mem, soff[j1 % ZS][1], yb1);
+            stseg<SEGB>(r_mem, soff[j0 % ZS][0], ya0);
+            stseg<SEGB>(r_mem, soff[j0 % ZS][1], ya1);
+            stseg<SEGB>(r_mem, soff[j1 % ZS][0], yb0);
+            stseg<SEGB>(r_mem, soff[j1 % ZS][1], yb1);
             if constexpr (LOG) {
                 // tokens outside [0, T) and positions past W log nothing (offsets past the buffer)
                 const uint32_t la = (s >= 0 && s < T) ? (uint32_t)s * log_tok : kOOB;
                 const uint32_t lb = (s + 1 >= 0 && s + 1 < T) ? (uint32_t)(s + 1) * log_tok : kOOB;
-                st128(r_log, la == kOOB || lpos0 == kOOB ? kOOB : la + lpos0, oa0);
-                st128(r_log, la == kOOB || lpos1 == kOOB ? kOOB : la + lpos1, oa1);
-                st128(r_log, lb == kOOB || lpos0 == kOOB ? kOOB : lb + lpos0, ob0);
-                st128(r_log, lb == kOOB || lpos1 == kOOB ? kOOB : lb + lpos1, ob1);
+                stseg<SEGB>(r_log, la == kOOB || lpos0 == kOOB ? kOOB : la + lpos0, oa0);
+                stseg<SEGB>(r_log, la == kOOB || lpos1 == kOOB ? kOOB : la + lpos1, oa1);
+                stseg<SEGB>(r_log, lb == kOOB || lpos0 == kOOB ? kOOB : lb + lpos0, ob0);
+                stseg<SEGB>(r_log, lb == kOOB || lpos1 == kOOB ? kOOB : lb + lpos1, ob1);
             }
         });
     }
@@ -428,36 +451,38 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
 
 } // namespace
 
+namespace {
+template <class ST, class VT, int SEGB>
+void launch_typed_staged(const ScanArgs& a, dim3 grid, dim3 block, hipStream_t stream)
+{
+    if (a.log)
+        hipLaunchKernelGGL((sdm_scan_staged_kernel<ST, VT, true, SEGB>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((sdm_scan_staged_kernel<ST, VT, false, SEGB>), grid, block, 0, stream, a);
+}
+} // namespace
+
 hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& p, bool state_bf16, bool in_bf16,
                                   hipStream_t stream)
 {
-    const int seg = state_bf16 ? 64 : 32;
-    if (!p.staged || p.waves != kWaves || a.d % seg != 0 || a.W > kPos)
+    const int seg = p.seg_bytes / (state_bf16 ? 2 : 4);
+    if (!p.staged || p.waves != kWaves || a.d % seg != 0 || a.W > kPos ||
+        (p.seg_bytes != 128 && !(p.seg_bytes == 64 && state_bf16)))
+        return hipErrorInvalidValue;
+    // the log of a call: one memory's tokens of a chunk addressable by 32-bit offsets
+    if (a.log && (uint64_t)a.T * a.W * a.d * (state_bf16 ? 2u : 4u) >= (1ull << 32) - 16u)
         return hipErrorInvalidValue;
     dim3 grid((unsigned)p.grid), block(kWaves * 64);
-    if (a.log) {
-        // the log of a call: one memory's tokens of a chunk addressable by 32-bit offsets
-        if ((uint64_t)a.T * a.W * a.d * (state_bf16 ? 2u : 4u) >= (1ull << 32) - 16u)
-            return hipErrorInvalidValue;
-        if (state_bf16) {
-            if (in_bf16)
-                hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, uint16_t, true>), grid, block, 0, stream, a);
-            else
-                hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, float, true>), grid, block, 0, stream, a);
-        } else if (in_bf16)
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, uint16_t, true>), grid, block, 0, stream, a);
+    if (state_bf16) {
+        if (p.seg_bytes == 64)
+            in_bf16 ? launch_typed_staged<uint16_t, uint16_t, 64>(a, grid, block, stream)
+                    : launch_typed_staged<uint16_t, float, 64>(a, grid, block, stream);
         else
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, float, true>), grid, block, 0, stream, a);
-    } else if (state_bf16) {
-        if (in_bf16)
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, uint16_t, false>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<uint16_t, float, false>), grid, block, 0, stream, a);
+            in_bf16 ? launch_typed_staged<uint16_t, uint16_t, 128>(a, grid, block, stream)
+                    : launch_typed_staged<uint16_t, float, 128>(a, grid, block, stream);
     } else {
-        if (in_bf16)
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, uint16_t, false>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((sdm_scan_staged_kernel<float, float, false>), grid, block, 0, stream, a);
+        in_bf16 ? launch_typed_staged<float, uint16_t, 128>(a, grid, block, stream)
+                : launch_typed_staged<float, float, 128>(a, grid, block, stream);
     }
     return hipGetLastError();
 }
