@@ -52,22 +52,60 @@ __device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int 
     const int i = lane & 31, kg = lane >> 5;
     const int ctiles = (S + 31) / 32;
     const int dk = 2 * DH;
+    if constexpr (BF16) {
+        // The two queries' operands for both halves once, then the sub-key operands of G
+        // tiles at a time: one memory round trip per G tiles instead of per tile.  Each
+        // tile's MFMA sequence is unchanged.
+        constexpr int KSTEPS = DH / 16, G = 4;
+        bf16x8_t qv[2][KSTEPS];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint16_t* q = static_cast<const uint16_t*>(i == 0 ? a.wq : a.rq) + (long)bh * dk + half * DH + kg * 8;
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                qv[half][kk] = i < 2 ? *reinterpret_cast<const bf16x8_t*>(q + kk * 16) : bf16x8_t{};
+        }
+        const int ntask = 2 * ctiles;
+        for (int t0 = wave; t0 < ntask; t0 += kWaves * G) {
+            bf16x8_t bv[G][KSTEPS];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int task = t0 + g * kWaves;
+                const int half = task < ntask ? task / ctiles : 0, ct = task < ntask ? task % ctiles : 0;
+                const int s = ct * 32 + i;
+                const bool on = task < ntask && s < S;
+                const uint16_t* krow = static_cast<const uint16_t*>(a.subkeys) + ((long)h * 2 + half) * S * DH +
+                                       (long)(on ? s : 0) * DH + kg * 8;
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk) // a valid row either way; zeroed where used
+                    bv[g][kk] = *reinterpret_cast<const bf16x8_t*>(krow + kk * 16);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int task = t0 + g * kWaves;
+                if (task >= ntask)
+                    break; // wave-uniform
+                const int half = task / ctiles, ct = task % ctiles;
+                const int s = ct * 32 + i;
+                f32x16_t acc = {};
+#pragma unroll
+                for (int kk = 0; kk < KSTEPS; ++kk)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(half ? qv[1][kk] : qv[0][kk],
+                                                                  s < S ? bv[g][kk] : bf16x8_t{}, acc, 0, 0, 0);
+                // lane l < 32 holds column l of rows 0 (v = 0) and 1 (v = 1)
+                if (kg == 0 && s < S) {
+                    sc[(0 * 2 + half) * S + s] = acc[0];
+                    sc[(1 * 2 + half) * S + s] = acc[1];
+                }
+            }
+        }
+        return;
+    }
     for (int task = wave; task < 2 * ctiles; task += kWaves) {
         const int half = task / ctiles, ct = task % ctiles;
         const int s = ct * 32 + i;
         f32x16_t acc = {};
-        if constexpr (BF16) {
-            constexpr int KSTEPS = DH / 16;
-            const uint16_t* q = static_cast<const uint16_t*>(i == 0 ? a.wq : a.rq) + (long)bh * dk + half * DH + kg * 8;
-            const uint16_t* table = static_cast<const uint16_t*>(a.subkeys) + ((long)h * 2 + half) * S * DH;
-            const uint16_t* krow = table + (long)(s < S ? s : 0) * DH + kg * 8;
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                const bf16x8_t av = i < 2 ? *reinterpret_cast<const bf16x8_t*>(q + kk * 16) : bf16x8_t{};
-                const bf16x8_t bv = s < S ? *reinterpret_cast<const bf16x8_t*>(krow + kk * 16) : bf16x8_t{};
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
-            }
-        } else {
+        {
             constexpr int KSTEPS = DH / 2;
             const float* q = static_cast<const float*>(i == 0 ? a.wq : a.rq) + (long)bh * dk + half * DH + kg;
             const float* table = static_cast<const float*>(a.subkeys) + ((long)h * 2 + half) * S * DH;
