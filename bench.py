@@ -73,16 +73,43 @@ def cpu_baseline(cfg, x, budget_s: float):
                       f"(addressing rows and slot elements split over threads)"}
 
 
-def load_traffic(kernel_signature: str):
+def load_traffic(kernel_signature: str, mem_stride: int):
     """HBM bytes the scan moves per forward, from the committed rocprofv3 counter
-    summary, if it was taken on the kernel as it is now."""
+    summary, if it was taken on the kernel as it is now and on the same memory
+    layout."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_signature") != kernel_signature:
+    if t.get("kernel_signature") != kernel_signature or t.get("mem_stride") != mem_stride:
         return None
     return t.get("bytes_per_forward")
+
+
+def state_rows(args, cfg) -> int:
+    """Elements from one slot row to the next in the state tensors: the library's
+    stride hint (rows padded to an odd number of 128-byte units, which spreads the
+    scan's row segments over the memory channels) unless --dense-rows."""
+    from sparse_memory_linear_pk_amd import SDM
+    return cfg.d if args.dense_rows else SDM.stride_hint(cfg.d, cfg.state_bf16)
+
+
+def with_rows(t, ms: int):
+    """The [..., :d] view of a copy of t whose rows are ms elements apart (t itself
+    when ms is its row length)."""
+    import torch
+    d = t.shape[-1]
+    if ms == d:
+        return t
+    full = torch.empty((*t.shape[:-1], ms), dtype=t.dtype, device=t.device)
+    full[..., :d].copy_(t)
+    return full[..., :d]
+
+
+def rows_note(cfg, ms: int) -> dict:
+    s = 2 if cfg.state_bf16 else 4
+    return {"stride_elements": ms, "row_bytes": cfg.d * s, "stride_bytes": ms * s,
+            "layout": "dense" if ms == cfg.d else "padded (sdm_mem_stride_hint)"}
 
 
 def kernel_signature() -> str:
@@ -114,9 +141,11 @@ def decode_bench(args, cfg):
         return torch.from_numpy(a).cuda()
 
     d = {k: dev(v) for k, v in x.items()}
+    ms = state_rows(args, c)
+    d["mem0"] = with_rows(d["mem0"], ms)
     tok = [{k: d[k][:, t].contiguous() for k in ("wq", "rq", "v", "alpha", "beta")} for t in range(c.T)]
     out = torch.empty((c.B, c.H, c.d), dtype=torch.float32, device="cuda")
-    layer = SDM.from_config(c)
+    layer = SDM.from_config(c, mem_stride=ms)
     for t in range(args.warmup):
         layer.step(tok[t]["wq"], tok[t]["rq"], tok[t]["v"], tok[t]["alpha"], tok[t]["beta"], d["subkeys"], d["mem0"], out)
     torch.cuda.synchronize()
@@ -129,7 +158,7 @@ def decode_bench(args, cfg):
     tm = layer.timing()
     layer.close()
     # the same tokens through a one-token forward
-    one = SDM.from_config(c.replace(T=1))
+    one = SDM.from_config(c.replace(T=1), mem_stride=ms)
     o1 = torch.empty((c.B, 1, c.H, c.d), dtype=torch.float32, device="cuda")
     x1 = [{k: v.unsqueeze(1) for k, v in tk.items()} for tk in tok]
     for t in range(args.warmup):
@@ -156,7 +185,7 @@ def decode_bench(args, cfg):
         "dtype": "f32",
         "data": "synthetic (seeded), consecutive tokens of the workload's sequences",
         "config": {"workload": f"sdm-{c.name} decode: B={c.B} H={c.H} d={c.d} N={c.S}^2 dk={c.dk} k={c.k} W={c.W}, "
-                               f"one token per sequence per step"},
+                               f"one token per sequence per step", "state_rows": rows_note(c, ms)},
         "step_device_us": dev_ms * 1e3,
         "step_state_bytes": step_bytes,
         "step_device_GBps": step_bytes / (dev_ms * 1e-3) / 1e9,
@@ -185,17 +214,19 @@ def train_bench(args, cfg):
         return torch.from_numpy(a).cuda()
 
     d = {k: dev(v) for k, v in x.items()}
+    ms = state_rows(args, cfg)
+    d["mem0"] = with_rows(d["mem0"], ms)
     f32 = dict(dtype=torch.float32, device="cuda")
     gen = torch.Generator(device="cuda").manual_seed(7)
     dout = torch.randn((cfg.B, cfg.T, cfg.H, cfg.d), generator=gen, **f32)
     out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32)
     log_buf = torch.empty((cfg.B, cfg.H, cfg.T, cfg.W, cfg.d),
                           dtype=torch.bfloat16 if cfg.state_bf16 else torch.float32, device="cuda")
-    dmem = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), **f32)
+    dmem = torch.empty((cfg.B, cfg.H, cfg.N, ms), **f32)[..., :cfg.d]
     g = {"dwq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32), "drq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32),
          "dv": torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32), "dalpha": torch.empty((cfg.B, cfg.T, cfg.H), **f32),
          "dbeta": torch.empty((cfg.B, cfg.T, cfg.H), **f32), "dsub": torch.empty((cfg.H, 2, cfg.S, cfg.dh), **f32)}
-    layer = SDM.from_config(cfg)
+    layer = SDM.from_config(cfg, mem_stride=ms)
     mem_check = d["mem0"][0, 0, :4096].clone()
 
     def step():
@@ -230,10 +261,11 @@ def train_bench(args, cfg):
     probe_ms = None
     if not cfg.state_bf16:
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=11)
+        pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=11, row_stride=ms * 4)
         s0.record()
         for r in range(2):
-            pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=12 + r)
+            pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * 4, cfg.T, cfg.W, 4, 3, seed=12 + r,
+                              row_stride=ms * 4)
         s1.record()
         torch.cuda.synchronize()
         probe_ms = s0.elapsed_time(s1) / 2
@@ -261,7 +293,7 @@ def train_bench(args, cfg):
         "data": "synthetic (seeded inputs as for the forward; upstream gradient of out ~N(0,1), none of the final memory)",
         "config": {"workload": f"sdm-{cfg.name} layer training step: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} "
                                f"N={cfg.S}^2 dk={cfg.dk} k={cfg.k} W={cfg.W}", "global_batch": cfg.B,
-                   "seq_len": cfg.T, "parallelism": "single GPU"},
+                   "seq_len": cfg.T, "parallelism": "single GPU", "state_rows": rows_note(cfg, ms)},
         "roofline": {"bound": "hbm", "kernel": "grad_scan", "achieved": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
                      "peak": 8000.0, "unit": "GB/s", "frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / 8000.0,
                      "traffic": None, "bytes_per_launch": bwd_bytes, "ms_per_launch": bwd_ms,
@@ -423,6 +455,9 @@ def main():
                     help="time the input projections (sdm_project) instead of the forward")
     ap.add_argument("--train", action="store_true",
                     help="time a training step (sdm_forward_train + sdm_backward) instead of the forward")
+    ap.add_argument("--dense-rows", action="store_true",
+                    help="keep the memory's slot rows dense (d elements apart) instead of the library's padded "
+                         "stride hint")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 4 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -435,7 +470,7 @@ def main():
     import torch
 
     import sdm_inputs as gi
-    from sparse_memory_linear_pk_amd import SDM, pattern_probe
+    from sparse_memory_linear_pk_amd import SDM, pattern_probe_mix
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -467,8 +502,10 @@ def main():
         return torch.from_numpy(a).cuda()
 
     d = {k: dev(v) for k, v in x.items()}
+    ms = state_rows(args, cfg)
+    d["mem0"] = with_rows(d["mem0"], ms)
     out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), dtype=torch.float32, device="cuda")
-    layer = SDM.from_config(cfg)
+    layer = SDM.from_config(cfg, mem_stride=ms)
 
     def step():
         layer.forward(d["wq"], d["rq"], d["v"], d["alpha"], d["beta"], d["subkeys"], d["mem0"], out)
@@ -509,7 +546,8 @@ def main():
     for i in range(4):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        pattern_probe(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * s_bytes, cfg.T, cfg.W, seed=i)
+        pattern_probe_mix(d["mem0"], cfg.B * cfg.H, cfg.N, cfg.d * s_bytes, cfg.T, cfg.W, 2, 1, seed=i,
+                          row_stride=ms * s_bytes)
         e1.record()
         torch.cuda.synchronize()
         if i:
@@ -527,7 +565,7 @@ def main():
     nbytes = scan_bytes_per_step(cfg)
     achieved = nbytes / (scan_ms * 1e-3) / 1e9
     sig = kernel_signature()
-    traffic = load_traffic(sig) if args.workload == WORKLOAD else None
+    traffic = load_traffic(sig, ms) if args.workload == WORKLOAD else None
     score_tflops = score_flops_per_step(cfg) / (score_alone_ms * 1e-3) / 1e12
     peak_mfma = BF16_MFMA_PEAK_TFLOPS if cfg.in_bf16 else F32_MFMA_PEAK_TFLOPS
 
@@ -548,7 +586,8 @@ def main():
         "config": {"workload": f"sdm-{cfg.name} layer: B={cfg.B} H={cfg.H} T={cfg.T} d={cfg.d} N={cfg.S}^2 "
                                f"dk={cfg.dk} k={cfg.k} W={cfg.W}, {'bf16' if cfg.in_bf16 else 'float32'} inputs, "
                                f"{'bf16' if cfg.state_bf16 else 'float32'} state",
-                   "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU"},
+                   "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "single GPU",
+                   "state_rows": rows_note(cfg, ms)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic / scan_launches,
@@ -557,8 +596,9 @@ def main():
                      "pattern_ceiling": {"achieved": nbytes / (pattern_ms * 1e-3) / 1e9, "unit": "GB/s",
                                          "ms_per_launch": pattern_ms,
                                          "frac": (nbytes / (scan_ms * 1e-3)) / (nbytes / (pattern_ms * 1e-3)),
-                                         "what": "sdm_pattern_probe: the scan's random 128-byte segment reads "
-                                                 "and writes (2:1) with no arithmetic; frac = scan / this"}},
+                                         "what": "sdm_pattern_probe_mix 2:1: the scan's random 128-byte segment "
+                                                 "reads and writes with no arithmetic, on rows as far apart as "
+                                                 "the memory's; frac = scan / this"}},
         "kernels_ms_per_step": {"pk_score": per_step["score"], "pk_topk": per_step["select"],
                                 "sdm_plan": per_step["plan"], "sdm_scan": scan_ms,
                                 "note": "device time of each kernel in the forward; after the first chunk, "

@@ -30,7 +30,11 @@
  *   subkeys   [H, 2, S, dk/2]  in_dtype, table 0 then table 1 per head
  *   mem_inout [B, H, N, d]     state_dtype, slot-major: slot n's d values are
  *                              contiguous; read as the initial memory and
- *                              overwritten with the memory after token T-1
+ *                              overwritten with the memory after token T-1.
+ *                              Consecutive slot rows are mem_stride elements
+ *                              apart (sdm_config; d when it is 0): the tensor
+ *                              is [B, H, N, mem_stride] with elements d and up
+ *                              of each row never read or written
  *   out       [B, T, H, d]     float32
  *   idx, wt   [B*T*H, W]       int32 slot ids / float32 weights, best first
  *   scores    [B*T*H, 2, S]    float32 half scores
@@ -52,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SDM_ABI_VERSION 1
+#define SDM_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define SDM_API __attribute__((visibility("default")))
@@ -83,6 +87,11 @@ typedef struct {
     int W;      /* slots selected per token, for the write and for the read */
     sdm_dtype in_dtype;    /* wq, rq, v, subkeys */
     sdm_dtype state_dtype; /* mem_inout */
+    int mem_stride;        /* elements from one slot row to the next in every state tensor
+                              (mem_inout; dmem_inout of sdm_backward, in float32 elements; m0 and
+                              mem_out of sdm_broadcast_memory): 0 for dense rows (d), else at least
+                              d with mem_stride * sizeof(state) a multiple of 16 bytes; see
+                              sdm_mem_stride_hint */
 } sdm_config;
 
 /* Accumulated device time per kernel (milliseconds) since timing was enabled. */
@@ -104,8 +113,19 @@ typedef struct {
 } sdm_timing;
 
 /* Supported shapes: 1 <= k <= min(S, 64); 1 <= W <= min(k*k, 64); S <= 1024;
- * dk/2 a multiple of 16 and at most 256; d a multiple of 8; N*d*sizeof(state)
- * below 2^32 bytes per memory. */
+ * dk/2 a multiple of 16 and at most 256; d a multiple of 8;
+ * N*mem_stride*sizeof(state) below 2^32 bytes per memory. */
+
+/* A slot-row stride (elements, for sdm_config.mem_stride) that the scans run
+ * faster on: a dense row of 2m 128-byte units padded to 2m + 1 (d itself when
+ * the row is an odd number of units, is not a multiple of 128 bytes or is
+ * under 1 KB).  The scan reads and writes one 128-byte segment of each selected
+ * row per workgroup; with rows a multiple of 256 bytes apart the same segment
+ * of every row falls on a subset of the memory channels.  Measured on MI355X
+ * with the scan's access pattern (random rows, two segments read per segment
+ * written): 8192-byte rows 4.5 TB/s dense, 5.1 TB/s 8320 bytes apart.  The
+ * padding costs (stride - d) / d more memory.  Returns 0 for a NULL cfg. */
+SDM_API int sdm_mem_stride_hint(const sdm_config* cfg);
 
 /* Validate cfg, allocate the device workspace and bind the HIP stream
  * (a hipStream_t, NULL for the default stream).  *out receives the handle.
@@ -131,12 +151,13 @@ SDM_API sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const 
 
 /* Training forward: exactly sdm_forward's memory and outputs (the same
  * launches; the scan also stores), and the bits of every write slot before its
- * write, saved to log [B, H, T, W, d] (float32; entry ((b*H + h)*T + t)*W + i
- * is write position i of token t, best first), which sdm_backward consumes.
- * The log holds B*H*T*W*d*4 bytes (17.2 GB for B=4, H=1, T=8192, W=64,
- * d=2048), owned by the caller.  SDM_ERR_UNSUPPORTED unless the state is
- * float32, d is a multiple of 32 and one memory's log of a scan chunk (up to
- * 3071 tokens) stays below 4 GiB.  (SDM blog post, section "How does SDM
+ * write, saved to log [B, H, T, W, d] (state dtype, dense rows; entry
+ * ((b*H + h)*T + t)*W + i is write position i of token t, best first), which
+ * sdm_backward consumes.  The log holds B*H*T*W*d*sizeof(state) bytes (17.2 GB
+ * for B=4, H=1, T=8192, W=64, d=2048, float32), owned by the caller.
+ * SDM_ERR_UNSUPPORTED unless d * sizeof(state) is a multiple of 128 bytes, one
+ * memory's log of a scan chunk (up to 3071 tokens) stays below 4 GiB and one
+ * memory's float32 gradient (N * mem_stride * 4 bytes) below 4 GiB.  (SDM blog post, section "How does SDM
  * work?": the decay and delta-rule write whose inputs the log keeps.) */
 SDM_API sdm_status sdm_forward_train(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                                      const float* beta, const void* subkeys, void* mem_inout, float* out, void* log);
@@ -152,19 +173,19 @@ SDM_API sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* b
  * the selected slots are held fixed (top-k and top-W are piecewise constant),
  * and the rounding of stored values is passed straight through.
  * Inputs as given to sdm_forward_train (wq, rq, v, alpha, beta, subkeys), and:
- *   mem_inout  float32 [B, H, N, d]: the memory sdm_forward_train left; the
+ *   mem_inout  state [B, H, N, d]: the memory sdm_forward_train left; the
  *              reverse walk restores it, bit for bit, to the memory before it
  *   log        that call's log [B, H, T, W, d], read only
  *   dout       float32 [B, T, H, d]: dL/d(out)
- *   dmem_inout float32 [B, H, N, d]: in dL/d(final memory) (zeros if the
- *              loss does not use it), out dL/d(initial memory)
+ *   dmem_inout float32 [B, H, N, d], rows mem_stride float32 elements apart:
+ *              in dL/d(final memory) (zeros if the loss does not use it),
+ *              out dL/d(initial memory)
  * Outputs, float32, overwritten: dwq, drq [B, T, H, dk]; dv [B, T, H, d];
  * dalpha, dbeta [B, T, H]; dsubkeys [H, 2, S, dk/2].
  * The addressing of both query sets is recomputed by the forward's kernels, so
  * the slots are those the forward used.  Allocates its workspace on the first
  * call (sdm_backward_workspace_bytes).  Deterministic: every sum has a fixed
- * order.  SDM_ERR_UNSUPPORTED unless the state is float32 and d is a multiple
- * of 32. */
+ * order.  SDM_ERR_UNSUPPORTED for the shapes sdm_forward_train rejects. */
 SDM_API sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                                 const float* beta, const void* subkeys, void* mem_inout, const void* log,
                                 const float* dout, float* dmem_inout, float* dwq, float* drq, float* dv,
@@ -189,7 +210,8 @@ SDM_API sdm_status sdm_project(sdm_handle h, int D, const void* x, const void* w
                                void* rq, void* v, float* alpha, float* beta);
 
 /* A learned initial memory m0 [H, N, d] (state dtype) copied into each of the
- * B sequences' memories mem_out [B, H, N, d], ready for sdm_forward. */
+ * B sequences' memories mem_out [B, H, N, d], ready for sdm_forward.  Both
+ * have rows mem_stride elements apart; the copy includes the padding. */
 SDM_API sdm_status sdm_broadcast_memory(sdm_handle h, const void* m0, void* mem_out);
 
 /* Diagnostic, not part of the layer: the write/read bucket overlap of the SDM
@@ -256,10 +278,12 @@ SDM_API sdm_status sdm_pattern_probe(void* mem, int memories, long rows, int row
  * back per slot position and token: 2:1 is sdm_pattern_probe; 4:3 is the
  * reverse scan of sdm_backward (the read slot's memory and gradient, the write
  * slot's gradient and logged value read; both gradients and the restored
- * memory written), the ceiling of its access pattern.  (reads + writes) * W *
- * row_bytes * T * memories bytes move per call.  Other mixes: SDM_ERR_INVALID_ARG. */
-SDM_API sdm_status sdm_pattern_probe_mix(void* mem, int memories, long rows, int row_bytes, int T, int W, int reads,
-                                         int writes, unsigned seed, void* hip_stream);
+ * memory written), the ceiling of its access pattern.  Rows are row_stride
+ * bytes apart (0: row_bytes; else at least row_bytes, a multiple of 16), as a
+ * padded memory's are.  (reads + writes) * W * row_bytes * T * memories bytes
+ * move per call.  Other mixes: SDM_ERR_INVALID_ARG. */
+SDM_API sdm_status sdm_pattern_probe_mix(void* mem, int memories, long rows, int row_bytes, long row_stride, int T,
+                                         int W, int reads, int writes, unsigned seed, void* hip_stream);
 
 #ifdef __cplusplus
 }

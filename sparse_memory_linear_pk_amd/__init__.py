@@ -8,6 +8,11 @@ for device memory and the current HIP stream.
     layer = SDM(B=4, H=1, T=8192, d=2048, S=480, dk=256, k=32, W=64,
                 in_bf16=True, state_bf16=False)
     layer.forward(wq, rq, v, alpha, beta, subkeys, mem, out)   # mem updated in place
+
+State tensors ([.., N, d]: the memory, its gradient, a learned initial memory)
+may have slot rows mem_stride elements apart (SDM(..., mem_stride=...)): pass
+the [.., N, d] view of a [.., N, mem_stride] tensor, as layer.empty_state
+allocates it.  SDM.stride_hint gives a stride the scans run faster on.
 """
 from __future__ import annotations
 
@@ -28,11 +33,12 @@ def _ptr(t):
 class SDM:
     """One configured layer (the library handle) bound to a HIP stream."""
 
-    def __init__(self, B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False, stream=None):
+    def __init__(self, B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False, stream=None, mem_stride=0):
         self.shape = dict(B=B, H=H, T=T, d=d, S=S, dk=dk, k=k, W=W)
         self.in_bf16, self.state_bf16 = bool(in_bf16), bool(state_bf16)
+        self.mem_stride = int(mem_stride) or d  # elements from one slot row to the next in state tensors
         self._cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32,
-                           SDM_BF16 if state_bf16 else SDM_F32)
+                           SDM_BF16 if state_bf16 else SDM_F32, int(mem_stride))
         if stream is None:
             import torch
             stream = torch.cuda.current_stream()
@@ -48,8 +54,25 @@ class SDM:
         kw.update(overrides)
         return cls(stream=stream, **kw)
 
+    @staticmethod
+    def stride_hint(d: int, state_bf16: bool) -> int:
+        """sdm_mem_stride_hint: a slot-row stride (elements) the scans run faster on for rows of d values."""
+        cfg = Config(1, 1, 1, d, 1, 2, 1, 1, SDM_F32, SDM_BF16 if state_bf16 else SDM_F32, 0)
+        return int(lib().sdm_mem_stride_hint(C.byref(cfg)))
+
+    def empty_state(self, *lead, dtype=None, device="cuda"):
+        """An uninitialised state tensor [*lead, N, d] whose rows are this layer's mem_stride apart: the
+        [..., :d] view of a [*lead, N, mem_stride] allocation.  dtype defaults to the state dtype."""
+        import torch
+        if dtype is None:
+            dtype = torch.bfloat16 if self.state_bf16 else torch.float32
+        d, N = self.shape["d"], self.shape["S"] ** 2
+        return torch.empty((*lead, N, self.mem_stride), dtype=dtype, device=device)[..., :d]
+
     # ---- argument checks (shape, dtype, device, contiguity) ------------------
-    def _t(self, t, name, shape, dtype):
+    def _t(self, t, name, shape, dtype, rows=None):
+        """Checks a tensor argument; rows (a row stride in elements) allows a [.., N, d] state tensor
+        whose rows are that far apart, dense otherwise."""
         if isinstance(t, int):
             return t
         import torch
@@ -62,7 +85,15 @@ class SDM:
             raise ValueError(f"{name} has dtype {t.dtype}, expected {want}")
         if tuple(t.shape) != tuple(shape):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-        if not t.is_contiguous():
+        if rows is not None and rows != shape[-1]:
+            want_strides, acc = [], 1
+            for n in reversed(tuple(shape[:-1]) + (rows,)):
+                want_strides.append(acc)
+                acc *= n
+            if tuple(t.stride()) != tuple(reversed(want_strides)):
+                raise ValueError(f"{name} must be the [..., :{shape[-1]}] view of a contiguous "
+                                 f"{tuple(shape[:-1]) + (rows,)} tensor (strides {tuple(t.stride())})")
+        elif not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         return t
 
@@ -75,7 +106,8 @@ class SDM:
         args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
                 self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
                 self._t(beta, "beta", (B, T, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
-                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, T, H, d), "f32")]
+                self._t(mem, "mem", (B, H, S * S, d), "state", self.mem_stride),
+                self._t(out, "out", (B, T, H, d), "f32")]
         check(lib().sdm_forward(self._h, *[_ptr(a) for a in args]), "sdm_forward")
 
     def step(self, wq, rq, v, alpha, beta, subkeys, mem, out):
@@ -84,7 +116,7 @@ class SDM:
         args = [self._t(wq, "wq", (B, H, dk), "in"), self._t(rq, "rq", (B, H, dk), "in"),
                 self._t(v, "v", (B, H, d), "in"), self._t(alpha, "alpha", (B, H), "f32"),
                 self._t(beta, "beta", (B, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
-                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, H, d), "f32")]
+                self._t(mem, "mem", (B, H, S * S, d), "state", self.mem_stride), self._t(out, "out", (B, H, d), "f32")]
         check(lib().sdm_step(self._h, *[_ptr(a) for a in args]), "sdm_step")
 
     def forward_train(self, wq, rq, v, alpha, beta, subkeys, mem, out, log):
@@ -93,7 +125,8 @@ class SDM:
         args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
                 self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
                 self._t(beta, "beta", (B, T, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
-                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(out, "out", (B, T, H, d), "f32"),
+                self._t(mem, "mem", (B, H, S * S, d), "state", self.mem_stride),
+                self._t(out, "out", (B, T, H, d), "f32"),
                 self._t(log, "log", (B, H, T, W, d), "state")]
         check(lib().sdm_forward_train(self._h, *[_ptr(a) for a in args]), "sdm_forward_train")
 
@@ -104,8 +137,10 @@ class SDM:
         args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
                 self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
                 self._t(beta, "beta", (B, T, H), "f32"), self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
-                self._t(mem, "mem", (B, H, S * S, d), "state"), self._t(log, "log", (B, H, T, W, d), "state"),
-                self._t(dout, "dout", (B, T, H, d), "f32"), self._t(dmem, "dmem", (B, H, S * S, d), "f32"),
+                self._t(mem, "mem", (B, H, S * S, d), "state", self.mem_stride),
+                self._t(log, "log", (B, H, T, W, d), "state"),
+                self._t(dout, "dout", (B, T, H, d), "f32"),
+                self._t(dmem, "dmem", (B, H, S * S, d), "f32", self.mem_stride),
                 self._t(dwq, "dwq", (B, T, H, dk), "f32"), self._t(drq, "drq", (B, T, H, dk), "f32"),
                 self._t(dv, "dv", (B, T, H, d), "f32"), self._t(dalpha, "dalpha", (B, T, H), "f32"),
                 self._t(dbeta, "dbeta", (B, T, H), "f32"),
@@ -126,7 +161,8 @@ class SDM:
     def broadcast_memory(self, m0, mem):
         """mem [B, H, N, d] = B copies of m0 [H, N, d] (state dtype)."""
         B, H, T, d, S, dk, k, W = self._dims()
-        args = [self._t(m0, "m0", (H, S * S, d), "state"), self._t(mem, "mem", (B, H, S * S, d), "state")]
+        args = [self._t(m0, "m0", (H, S * S, d), "state", self.mem_stride),
+                self._t(mem, "mem", (B, H, S * S, d), "state", self.mem_stride)]
         check(lib().sdm_broadcast_memory(self._h, *[_ptr(a) for a in args]), "sdm_broadcast_memory")
 
     def overlap(self, idx_w, wt_w, idx_r, wt_r, buckets, write_cum, read, queries=None, overlap=None):
@@ -169,7 +205,8 @@ class SDM:
         args = [self._t(idx_w, "idx_w", (R, W), "i32"), self._t(wt_w, "wt_w", (R, W), "f32"),
                 self._t(idx_r, "idx_r", (R, W), "i32"), self._t(wt_r, "wt_r", (R, W), "f32"),
                 self._t(v, "v", (B, T, H, d), "in"), self._t(alpha, "alpha", (B, T, H), "f32"),
-                self._t(beta, "beta", (B, T, H), "f32"), self._t(mem, "mem", (B, H, S * S, d), "state"),
+                self._t(beta, "beta", (B, T, H), "f32"),
+                self._t(mem, "mem", (B, H, S * S, d), "state", self.mem_stride),
                 self._t(out, "out", (B, T, H, d), "f32")]
         check(lib().sdm_scan_with(self._h, *[_ptr(a) for a in args]), "sdm_scan_with")
 
@@ -183,15 +220,17 @@ class SDM:
         return {f: getattr(t, f) for f, _ in Timing._fields_}
 
     @staticmethod
-    def workspace_bytes(B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False) -> int:
-        cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32, SDM_BF16 if state_bf16 else SDM_F32)
+    def workspace_bytes(B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False, mem_stride=0) -> int:
+        cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32, SDM_BF16 if state_bf16 else SDM_F32,
+                     int(mem_stride))
         n = C.c_size_t()
         check(lib().sdm_workspace_bytes(C.byref(cfg), C.byref(n)), "sdm_workspace_bytes")
         return n.value
 
     @staticmethod
-    def backward_workspace_bytes(B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False) -> int:
-        cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32, SDM_BF16 if state_bf16 else SDM_F32)
+    def backward_workspace_bytes(B, H, T, d, S, dk, k, W, in_bf16=False, state_bf16=False, mem_stride=0) -> int:
+        cfg = Config(B, H, T, d, S, dk, k, W, SDM_BF16 if in_bf16 else SDM_F32, SDM_BF16 if state_bf16 else SDM_F32,
+                     int(mem_stride))
         n = C.c_size_t()
         check(lib().sdm_backward_workspace_bytes(C.byref(cfg), C.byref(n)), "sdm_backward_workspace_bytes")
         return n.value
@@ -226,12 +265,13 @@ def pattern_probe(mem, memories: int, rows: int, row_bytes: int, T: int, W: int,
 
 
 def pattern_probe_mix(mem, memories: int, rows: int, row_bytes: int, T: int, W: int, reads: int, writes: int,
-                      seed: int = 0, stream=None):
+                      seed: int = 0, stream=None, row_stride: int = 0):
     """sdm_pattern_probe_mix: (reads + writes)*W*row_bytes*T*memories bytes of random 128-byte row
-    segments, reads:writes per slot position and token (2:1 or 4:3).  Scrambles mem."""
+    segments, reads:writes per slot position and token (2:1 or 4:3), rows row_stride bytes apart
+    (0: row_bytes).  Scrambles mem."""
     if stream is None:
         import torch
         stream = torch.cuda.current_stream()
     handle = stream if isinstance(stream, int) else stream.cuda_stream
-    check(lib().sdm_pattern_probe_mix(_ptr(mem), memories, rows, row_bytes, T, W, reads, writes, seed,
+    check(lib().sdm_pattern_probe_mix(_ptr(mem), memories, rows, row_bytes, row_stride, T, W, reads, writes, seed,
                                       C.c_void_p(handle)), "sdm_pattern_probe_mix")

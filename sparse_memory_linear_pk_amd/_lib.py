@@ -23,7 +23,8 @@ class SDMError(RuntimeError):
 
 class Config(C.Structure):
     _fields_ = [("B", C.c_int), ("H", C.c_int), ("T", C.c_int), ("d", C.c_int), ("n_sub", C.c_int),
-                ("dk", C.c_int), ("k", C.c_int), ("W", C.c_int), ("in_dtype", C.c_int), ("state_dtype", C.c_int)]
+                ("dk", C.c_int), ("k", C.c_int), ("W", C.c_int), ("in_dtype", C.c_int), ("state_dtype", C.c_int),
+                ("mem_stride", C.c_int)]
 
 
 class Timing(C.Structure):
@@ -75,8 +76,9 @@ def lib() -> C.CDLL:
         "sdm_set_timing": ([h, C.c_int], C.c_int),
         "sdm_get_timing": ([h, C.POINTER(Timing)], C.c_int),
         "sdm_pattern_probe": ([vp, C.c_int, C.c_long, C.c_int, C.c_int, C.c_int, C.c_uint, vp], C.c_int),
-        "sdm_pattern_probe_mix": ([vp, C.c_int, C.c_long, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_uint, vp],
-                                  C.c_int),
+        "sdm_pattern_probe_mix": ([vp, C.c_int, C.c_long, C.c_int, C.c_long, C.c_int, C.c_int, C.c_int, C.c_int,
+                                   C.c_uint, vp], C.c_int),
+        "sdm_mem_stride_hint": ([C.POINTER(Config)], C.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)

@@ -64,7 +64,7 @@ constexpr uint32_t kPast = 0xFFFFFFF0u;         // an offset past every buffer: 
 
 // NR row sets read and the first NW of them written back, per slot position and token.
 template <int NR, int NW>
-__global__ __launch_bounds__(256) void hbm_pattern_kernel(char* mem, int T, int W, uint32_t rows, uint32_t row_bytes,
+__global__ __launch_bounds__(256) void hbm_pattern_kernel(char* mem, int T, int W, uint32_t rows, uint32_t row_stride,
                                                           int nchunk, uint32_t seed)
 {
     constexpr int kOps = 2 * NR + 2 * NW;           // per token and wave (two positions per lane)
@@ -73,13 +73,13 @@ __global__ __launch_bounds__(256) void hbm_pattern_kernel(char* mem, int T, int 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 3, el = lane & 7;
     const int m = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const uint32_t lane_off = (uint32_t)(chunk * 8 + el) * 16u;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(mem + (size_t)m * rows * row_bytes, rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(mem + (size_t)m * rows * row_stride, rows * row_stride);
     const int pos[2] = {wave * 16 + g, wave * 16 + 8 + g};
     auto offset = [&](int t, int p, uint32_t set) -> uint32_t {
         if (t < 0 || t >= T || p >= W)
             return kPast;
         const uint32_t row = mix((seed + (uint32_t)m * 7919u + (uint32_t)t * 131u + set) * 1024u + (uint32_t)p) % rows;
-        return row * row_bytes + lane_off;
+        return row * row_stride + lane_off;
     };
     uint4 v[kZ][NR][2];
     for (int z = 0; z < kZ; ++z)
@@ -112,17 +112,17 @@ __global__ __launch_bounds__(256) void hbm_pattern_kernel(char* mem, int T, int 
 
 } // namespace
 
-hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, int reads, int writes,
-                              uint32_t seed, hipStream_t stream)
+hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, long row_stride, int T, int W,
+                              int reads, int writes, uint32_t seed, hipStream_t stream)
 {
     const int nchunk = row_bytes / 128;
     dim3 grid((unsigned)(memories * nchunk)), block(256);
     if (reads == 2 && writes == 1)
         hipLaunchKernelGGL((hbm_pattern_kernel<2, 1>), grid, block, 0, stream, (char*)mem, T, W, (uint32_t)rows,
-                           (uint32_t)row_bytes, nchunk, seed);
+                           (uint32_t)row_stride, nchunk, seed);
     else if (reads == 4 && writes == 3)
         hipLaunchKernelGGL((hbm_pattern_kernel<4, 3>), grid, block, 0, stream, (char*)mem, T, W, (uint32_t)rows,
-                           (uint32_t)row_bytes, nchunk, seed);
+                           (uint32_t)row_stride, nchunk, seed);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

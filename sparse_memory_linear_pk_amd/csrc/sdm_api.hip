@@ -90,6 +90,9 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
     return L;
 }
 
+// Elements from one slot row of a memory to the next in the state tensors.
+int mem_stride_of(const sdm_config& c) { return c.mem_stride ? c.mem_stride : c.d; }
+
 sdm_status check_config(const sdm_config* c, std::vector<sdm::ScanPlan>* plans)
 {
     if (!c)
@@ -120,7 +123,11 @@ sdm_status check_config(const sdm_config* c, std::vector<sdm::ScanPlan>* plans)
     if (c->d % 8)
         return fail(SDM_ERR_UNSUPPORTED, "d=%d must be a multiple of 8", c->d);
     const size_t s = c->state_dtype == SDM_BF16 ? 2 : 4;
-    const size_t mem_bytes = (size_t)c->n_sub * c->n_sub * c->d * s;
+    if (c->mem_stride != 0 && (c->mem_stride < c->d || (c->mem_stride * s) % 16 != 0))
+        return fail(SDM_ERR_INVALID_ARG, "mem_stride=%d: 0 (dense rows), or at least d=%d with rows a multiple of 16 "
+                    "bytes", c->mem_stride, c->d);
+    const int ms = mem_stride_of(*c);
+    const size_t mem_bytes = (size_t)c->n_sub * c->n_sub * ms * s;
     if (mem_bytes >= (1ull << 32))
         return fail(SDM_ERR_UNSUPPORTED, "one memory is %zu bytes; at most 2^32 - 1", mem_bytes);
     if ((long)c->H * c->n_sub * 2 * 4 * 128 >= (1l << 31))
@@ -131,8 +138,8 @@ sdm_status check_config(const sdm_config* c, std::vector<sdm::ScanPlan>* plans)
     const long N = (long)c->n_sub * c->n_sub;
     plans->assign(k.C(), sdm::ScanPlan{});
     for (int ci = 0; ci < k.C(); ++ci)
-        if (!sdm::plan_scan(c->B, c->H, k.len(ci), c->d, c->W, N, c->state_dtype == SDM_BF16, c->in_dtype == SDM_BF16,
-                            &(*plans)[ci]))
+        if (!sdm::plan_scan(c->B, c->H, k.len(ci), c->d, ms, c->W, N, c->state_dtype == SDM_BF16,
+                            c->in_dtype == SDM_BF16, &(*plans)[ci]))
             return fail(SDM_ERR_UNSUPPORTED, "no scan layout for d=%d W=%d", c->d, c->W);
     return SDM_OK;
 }
@@ -276,6 +283,7 @@ sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hi
     a.W = c.W;
     a.Tp = p.Tp;
     a.N = (long)c.n_sub * c.n_sub;
+    a.ms = mem_stride_of(c);
     Timer t(h, kind, st);
     hipError_t e = sdm::launch_sdm_scan(a, p, c.state_dtype == SDM_BF16, c.in_dtype == SDM_BF16, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan launch");
@@ -319,6 +327,11 @@ sdm_status check_train_shape(const sdm_config& c, const char* who)
     if (c.d % seg)
         return fail(SDM_ERR_UNSUPPORTED, "%s: d=%d must be a multiple of %d (128-byte slot columns)", who, c.d, seg);
     const unsigned sb = c.state_dtype == SDM_BF16 ? 2u : 4u;
+    // the float32 gradient of one memory (rows of mem_stride elements) is addressed with 32-bit offsets
+    const uint64_t grad_bytes = (uint64_t)c.n_sub * c.n_sub * mem_stride_of(c) * 4u;
+    if (grad_bytes >= (1ull << 32))
+        return fail(SDM_ERR_UNSUPPORTED, "%s: one memory's float32 gradient is %llu bytes; at most 2^32 - 1", who,
+                    (unsigned long long)grad_bytes);
     const Chunking k = chunking_of(c);
     for (int ci = 0; ci < k.C(); ++ci)
         if ((uint64_t)k.len(ci) * c.W * c.d * sb >= (1ull << 32) - 16u)
@@ -343,6 +356,17 @@ const char* sdm_status_str(sdm_status s)
 }
 
 const char* sdm_last_error(void) { return g_err; }
+
+int sdm_mem_stride_hint(const sdm_config* cfg)
+{
+    if (!cfg)
+        return 0;
+    const int s = cfg->state_dtype == SDM_BF16 ? 2 : 4;
+    if ((cfg->d * s) % 128 || cfg->d * s < 1024)
+        return cfg->d;
+    const int units = cfg->d * s / 128; // 128-byte units of a dense row
+    return (units | 1) * 128 / s;
+}
 
 sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes)
 {
@@ -595,7 +619,7 @@ sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v,
     // entries of the forward's addressing workspace
     Timer t(h, K_STEP, h->stream);
     hipError_t e = sdm::launch_sdm_step(wq, rq, v, alpha, beta, subkeys, mem_inout, out, h->idx[0], h->wt[0], c.B,
-                                        c.H, c.d, c.n_sub, c.dk / 2, c.k, c.W, c.in_dtype == SDM_BF16,
+                                        c.H, c.d, mem_stride_of(c), c.n_sub, c.dk / 2, c.k, c.W, c.in_dtype == SDM_BF16,
                                         c.state_dtype == SDM_BF16, h->stream);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_step launch");
 }
@@ -684,6 +708,7 @@ sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void
     a.H = c.H;
     a.T = c.T;
     a.d = c.d;
+    a.ms = mem_stride_of(c);
     a.S = c.n_sub;
     a.dh = c.dk / 2;
     a.W = c.W;
@@ -773,7 +798,8 @@ sdm_status sdm_broadcast_memory(sdm_handle h, const void* m0, void* mem_out)
     if (!aligned16(m0) || !aligned16(mem_out))
         return fail(SDM_ERR_INVALID_ARG, "sdm_broadcast_memory: misaligned pointer");
     const sdm_config& c = h->cfg;
-    const size_t bytes = (size_t)c.H * c.n_sub * c.n_sub * c.d * (c.state_dtype == SDM_BF16 ? 2 : 4);
+    // rows of mem_stride elements in both (the padding is copied along)
+    const size_t bytes = (size_t)c.H * c.n_sub * c.n_sub * mem_stride_of(c) * (c.state_dtype == SDM_BF16 ? 2 : 4);
     hipError_t e = sdm::launch_broadcast(m0, mem_out, bytes, c.B, h->stream);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "broadcast launch");
 }
@@ -850,19 +876,22 @@ sdm_status sdm_get_timing(sdm_handle h, sdm_timing* t)
     return rc;
 }
 
-sdm_status sdm_pattern_probe_mix(void* mem, int memories, long rows, int row_bytes, int T, int W, int reads,
-                                 int writes, unsigned seed, void* hip_stream)
+sdm_status sdm_pattern_probe_mix(void* mem, int memories, long rows, int row_bytes, long row_stride, int T, int W,
+                                 int reads, int writes, unsigned seed, void* hip_stream)
 {
     if (!mem || ((uintptr_t)mem & 15u))
         return fail(SDM_ERR_INVALID_ARG, "sdm_pattern_probe: mem is NULL or not 16-byte aligned");
     if (memories < 1 || rows < 1 || T < 1 || W < 1 || W > 64)
         return fail(SDM_ERR_INVALID_ARG, "sdm_pattern_probe: memories=%d rows=%ld T=%d W=%d", memories, rows, T, W);
-    if (row_bytes < 128 || row_bytes % 128 != 0 || (unsigned long long)rows * (unsigned)row_bytes >= (1ull << 32) - 16)
-        return fail(SDM_ERR_INVALID_ARG, "sdm_pattern_probe: row_bytes=%d must be a multiple of 128 and one memory "
-                    "below 4 GiB", row_bytes);
+    if (row_stride == 0)
+        row_stride = row_bytes;
+    if (row_bytes < 128 || row_bytes % 128 != 0 || row_stride < row_bytes || row_stride % 16 != 0 ||
+        (unsigned long long)rows * (unsigned long long)row_stride >= (1ull << 32) - 16)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_pattern_probe: row_bytes=%d must be a multiple of 128, row_stride=%ld "
+                    "at least row_bytes and a multiple of 16, and one memory below 4 GiB", row_bytes, row_stride);
     if (!((reads == 2 && writes == 1) || (reads == 4 && writes == 3)))
         return fail(SDM_ERR_INVALID_ARG, "sdm_pattern_probe: reads:writes %d:%d; built for 2:1 and 4:3", reads, writes);
-    hipError_t e = sdm::launch_hbm_pattern(mem, memories, rows, row_bytes, T, W, reads, writes, seed,
+    hipError_t e = sdm::launch_hbm_pattern(mem, memories, rows, row_bytes, row_stride, T, W, reads, writes, seed,
                                            (hipStream_t)hip_stream);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "hbm_pattern launch");
 }
@@ -870,7 +899,7 @@ sdm_status sdm_pattern_probe_mix(void* mem, int memories, long rows, int row_byt
 sdm_status sdm_pattern_probe(void* mem, int memories, long rows, int row_bytes, int T, int W, unsigned seed,
                              void* hip_stream)
 {
-    return sdm_pattern_probe_mix(mem, memories, rows, row_bytes, T, W, 2, 1, seed, hip_stream);
+    return sdm_pattern_probe_mix(mem, memories, rows, row_bytes, 0, T, W, 2, 1, seed, hip_stream);
 }
 
 } // extern "C"

@@ -128,10 +128,11 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
     const int g = lane >> 3, el = lane & 7;
     const int W = a.W, P = 2 * a.W + 2;
     const long N = (long)a.S * a.S;
-    const uint32_t row_bytes = (uint32_t)a.d * (uint32_t)sizeof(ST), grow_bytes = (uint32_t)a.d * 4u;
+    // slot row to slot row in the memory and in the gradient (ms elements of each)
+    const uint32_t row_bytes = (uint32_t)a.ms * (uint32_t)sizeof(ST), grow_bytes = (uint32_t)a.ms * 4u;
     const uint32_t lane_off = (uint32_t)col * 128u + (uint32_t)el * 16u;
     const uint32_t glane_off = (uint32_t)col * (128u * GU) + (uint32_t)el * (16u * GU);
-    const size_t mem_el = (size_t)bh * N * a.d; // first element of memory bh
+    const size_t mem_el = (size_t)bh * N * a.ms; // first element of memory bh
     ST* const mem = static_cast<ST*>(a.mem);
     const ST* const log = static_cast<const ST*>(a.log);
     const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(mem + mem_el, (uint32_t)(N * row_bytes));
@@ -585,7 +586,10 @@ hipError_t launch_grad_conflicts(const GradArgs& a, hipStream_t stream)
 hipError_t launch_grad_scan(const GradArgs& a, hipStream_t stream)
 {
     const int seg = a.state_bf16 ? 64 : 32;
-    if (a.d % seg || a.ncol != a.d / seg || a.W > 64 || a.W < 1)
+    if (a.d % seg || a.ncol != a.d / seg || a.W > 64 || a.W < 1 || a.ms < a.d || a.ms % 4)
+        return hipErrorInvalidValue;
+    // one memory's rows of the memory and of the float32 gradient are addressed with 32-bit offsets
+    if ((uint64_t)a.S * a.S * a.ms * 4u >= (1ull << 32))
         return hipErrorInvalidValue;
     dim3 grid((unsigned)(a.B * a.H * a.ncol)), block(kWaves * 64);
     if (a.state_bf16) {

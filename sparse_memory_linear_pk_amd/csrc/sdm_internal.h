@@ -107,7 +107,8 @@ struct ScanPlan {
     int seg_bytes; // staged: bytes of a slot row per workgroup, 128, or 64 (bf16 state, too few memories)
 };
 
-bool plan_scan(int B, int H, int T, int d, int W, long N, bool state_bf16, bool in_bf16, ScanPlan* plan);
+// ms: elements from one slot row of a memory to the next (>= d).
+bool plan_scan(int B, int H, int T, int d, int ms, int W, long N, bool state_bf16, bool in_bf16, ScanPlan* plan);
 
 // The plan of a forward: per (b, h, t, position) a 16-byte record with the write
 // and read slot ids, their weights, where a slot written too recently to be read
@@ -135,6 +136,7 @@ struct ScanArgs {
     void* log;          // null, or the write slots' values before each write: memory (b, h) at
                         // log + (b*H + h)*Ts*W*d, token t of the chunk at + t*W*d (staged form only)
     int B, T, Ts, H, d, W, Tp;
+    int ms;             // state elements from one slot row to the next (>= d): memory (b, h) at mem + (b*H + h)*N*ms
     long N;
 };
 
@@ -144,21 +146,22 @@ hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& plan, bool 
                                   hipStream_t stream);
 
 // One token over a persistent memory (sdm_step): tensors [B, H, ...] of the
-// token; idx/wt: workspace of 2*B*H*W entries each.  Needs d * sizeof(state) a
-// multiple of 128 bytes.
+// token; idx/wt: workspace of 2*B*H*W entries each; slot rows ms elements apart.
+// Needs d * sizeof(state) a multiple of 128 bytes.
 bool step_supported(int d, bool state_bf16);
 hipError_t launch_sdm_step(const void* wq, const void* rq, const void* v, const float* alpha, const float* beta,
                            const void* subkeys, void* mem, float* out, int32_t* idx, float* wt, int B, int H, int d,
-                           int S, int dh, int k, int W, bool in_bf16, bool state_bf16, hipStream_t stream);
+                           int ms, int S, int dh, int k, int W, bool in_bf16, bool state_bf16, hipStream_t stream);
 
 // The backward pass (float32 state with d a multiple of 32, or bf16 state with
 // d a multiple of 64: 128-byte memory columns; the gradient is float32).
 struct GradArgs {
     int B, H, T, d, S, dh, W;
+    int ms;                              // elements from one slot row to the next in mem and G (>= d)
     int ncol;                            // 128-byte memory columns per row: d * sizeof(state) / 128
     bool in_bf16, state_bf16;
-    void* mem;                           // [B*H, N, d] state: memory after the forward in, before it out
-    float* G;                            // [B*H, N, d]: dL/d(memory after) in, dL/d(memory before) out
+    void* mem;                           // [B*H, N, ms] state: memory after the forward in, before it out
+    float* G;                            // [B*H, N, ms]: dL/d(memory after) in, dL/d(memory before) out
     const void* log;                     // [B*H, T, W, d] state
     const int32_t* idx[2];               // write, read slots [rows, W]
     const float* wt[2];                  // their weights
@@ -199,10 +202,10 @@ hipError_t launch_overlap(const int32_t* idx_w, const float* wt_w, const int32_t
                           int H, int W, long N, hipStream_t stream);
 
 // Measurement only: the scan's traffic pattern without arithmetic on `memories`
-// memories of `rows` rows of row_bytes (a multiple of 128) bytes; reads:writes
-// segments per slot position and token, 2:1 (the forward scan) or 4:3 (the
-// reverse scan of the backward pass).
-hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, int T, int W, int reads, int writes,
-                              uint32_t seed, hipStream_t stream);
+// memories of `rows` rows of row_bytes (a multiple of 128) bytes, consecutive
+// rows row_stride bytes apart; reads:writes segments per slot position and
+// token, 2:1 (the forward scan) or 4:3 (the reverse scan of the backward pass).
+hipError_t launch_hbm_pattern(void* mem, int memories, long rows, int row_bytes, long row_stride, int T, int W,
+                              int reads, int writes, uint32_t seed, hipStream_t stream);
 
 } // namespace sdm

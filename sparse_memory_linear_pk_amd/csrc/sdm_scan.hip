@@ -397,7 +397,7 @@ __global__ __launch_bounds__(RW == 2 ? 256 : 64) void sdm_scan_kernel(ScanArgs a
     const int nchunk = d / DC;
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const int b = bh / H, h = bh % H;
-    const uint32_t row_bytes = (uint32_t)d * (uint32_t)sizeof(ST);
+    const uint32_t row_bytes = (uint32_t)a.ms * (uint32_t)sizeof(ST); // slot row to slot row in memory
     const uint32_t lane_off = (uint32_t)(chunk * DC + el * VEC) * (uint32_t)sizeof(ST);
 
     const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * row_bytes,
@@ -676,13 +676,15 @@ hipError_t launch_typed(const ScanArgs& a, const ScanPlan& p, hipStream_t stream
 
 } // namespace
 
-bool plan_scan(int B, int H, int T, int d, int W, long N, bool state_bf16, bool in_bf16, ScanPlan* plan)
+bool plan_scan(int B, int H, int T, int d, int ms, int W, long N, bool state_bf16, bool in_bf16, ScanPlan* plan)
 {
     const long units = (long)B * H;
     const uint64_t v_bytes = in_bf16 ? 2 : 4;
     const uint64_t s_bytes = state_bf16 ? 2 : 4;
+    if (ms < d || (ms * s_bytes) % 16 || (uint64_t)N * ms * s_bytes >= (1ull << 32))
+        return false;
     if ((d * s_bytes) % 128 == 0 && W <= staged::kPos && N < (1l << staged::kSlotBits) &&
-        (uint64_t)(N + 1) * d * s_bytes <= (1ull << 32) && ((uint64_t)T * H + 1) * d * 4 <= (1ull << 32) &&
+        (uint64_t)(N + 1) * ms * s_bytes <= (1ull << 32) && ((uint64_t)T * H + 1) * d * 4 <= (1ull << 32) &&
         ((uint64_t)T * H + 1) * d * v_bytes <= (1ull << 32)) {
         plan->staged = true;
         plan->lps = 8;

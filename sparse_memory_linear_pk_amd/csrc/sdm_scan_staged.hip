@@ -142,12 +142,13 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     const int nchunk = d / SEG;
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     const int b = bh / H;
-    const uint32_t row_bytes = (uint32_t)d * (uint32_t)sizeof(ST);
+    const uint32_t row_bytes = (uint32_t)d * (uint32_t)sizeof(ST);      // a log row
+    const uint32_t mem_row = (uint32_t)a.ms * (uint32_t)sizeof(ST);     // slot row to slot row in memory
     const uint32_t lane_off = (uint32_t)chunk * SEGB + (uint32_t)el * (SEGB / 8);
     const uint32_t tok_elems = (uint32_t)T * H * d;
 
-    const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * row_bytes,
-                                                   N * row_bytes);
+    const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * mem_row,
+                                                   N * mem_row);
     const __amdgpu_buffer_rsrc_t r_plan = make_rsrc(a.plan + (size_t)bh * a.Tp * kRecs,
                                                     (uint32_t)a.Tp * kRecs * 16u);
     const size_t tok0 = (size_t)b * a.Ts * H;
@@ -339,10 +340,10 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         constexpr int S = decltype(sc)::value;
         uint4 u0, u1, hu;
         records(zc, u0, u1, hu);
-        const uint32_t ow0 = __umul24(u0.x & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
-        const uint32_t ow1 = __umul24(u1.x & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
-        const uint32_t or0 = __umul24(u0.y & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
-        const uint32_t or1 = __umul24(u1.y & ((1u << kSlotBits) - 1u), row_bytes) + lane_off;
+        const uint32_t ow0 = __umul24(u0.x & ((1u << kSlotBits) - 1u), mem_row) + lane_off;
+        const uint32_t ow1 = __umul24(u1.x & ((1u << kSlotBits) - 1u), mem_row) + lane_off;
+        const uint32_t or0 = __umul24(u0.y & ((1u << kSlotBits) - 1u), mem_row) + lane_off;
+        const uint32_t or1 = __umul24(u1.y & ((1u << kSlotBits) - 1u), mem_row) + lane_off;
         // a forwarded write slot is not loaded (top bit of y); a forwarded read slot is the sentinel
         wset[S][0] = ldseg<SEGB>(r_mem, (u0.y >> 31) ? kOOB : ow0);
         wset[S][1] = ldseg<SEGB>(r_mem, (u1.y >> 31) ? kOOB : ow1);

@@ -149,10 +149,11 @@ struct StepScanArgs {
     const float* alpha;  // [B*H]
     const float* beta;   // [B*H]
     const void* v;       // [B*H, d]
-    void* mem;           // [B*H, N, d]
+    void* mem;           // [B*H, N, ms]
     float* out;          // [B*H, d]
     int B, H, d, W;
     long N;
+    int ms;              // elements from one slot row to the next
 };
 
 // One token for the workgroup's 128 bytes of the rows of memory bh: lane
@@ -176,7 +177,7 @@ __device__ void step_scan_body(const StepScanArgs& a, int bh, int chunk, const i
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 3, el = lane & 7;
     const int W = a.W;
-    const uint32_t row_bytes = (uint32_t)a.d * (uint32_t)sizeof(ST);
+    const uint32_t row_bytes = (uint32_t)a.ms * (uint32_t)sizeof(ST); // slot row to slot row
     const uint32_t lane_off = (uint32_t)chunk * 128u + (uint32_t)el * 16u;
     const __amdgpu_buffer_rsrc_t r_mem =
         make_rsrc(static_cast<const char*>(a.mem) + (size_t)bh * a.N * row_bytes, (uint32_t)a.N * row_bytes);
@@ -384,14 +385,15 @@ bool step_supported(int d, bool state_bf16) { return (d * (state_bf16 ? 2 : 4)) 
 
 hipError_t launch_sdm_step(const void* wq, const void* rq, const void* v, const float* alpha, const float* beta,
                            const void* subkeys, void* mem, float* out, int32_t* idx, float* wt, int B, int H, int d,
-                           int S, int dh, int k, int W, bool in_bf16, bool state_bf16, hipStream_t stream)
+                           int ms, int S, int dh, int k, int W, bool in_bf16, bool state_bf16, hipStream_t stream)
 {
-    if (!step_supported(d, state_bf16) || S > 1024 || k > 64 || W > 64)
+    if (!step_supported(d, state_bf16) || S > 1024 || k > 64 || W > 64 || ms < d ||
+        (uint64_t)S * S * ms * (state_bf16 ? 2 : 4) >= (1ull << 32))
         return hipErrorInvalidValue;
     StepArgs sa{wq, rq, subkeys, idx, wt, B, H, S, k, W, pksel::pair_count(k, W)};
     if (sa.n_pairs > pksel::kPairsMax)
         return hipErrorInvalidValue;
-    StepScanArgs ca{idx, wt, alpha, beta, v, mem, out, B, H, d, W, (long)S * S};
+    StepScanArgs ca{idx, wt, alpha, beta, v, mem, out, B, H, d, W, (long)S * S, ms};
     const int nchunk = d * (state_bf16 ? 2 : 4) / 128;
     dim3 grid((unsigned)(B * H * nchunk)), block(kWaves * 64);
     // one launch for the workload shapes (bf16 queries, 128-wide halves) when

@@ -9,8 +9,8 @@ from sparse_memory_linear_pk_amd._lib import Config, Timing, SDM_OK, SDM_ERR_INV
 
 EXPECTED = ["sdm_create", "sdm_forward", "sdm_destroy", "sdm_status_str", "sdm_last_error", "sdm_workspace_bytes",
             "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing",
-            "sdm_pattern_probe", "sdm_step", "sdm_forward_train", "sdm_backward_workspace_bytes", "sdm_backward", "sdm_pattern_probe_mix", "sdm_project",
-            "sdm_broadcast_memory", "sdm_overlap"]
+            "sdm_pattern_probe", "sdm_step", "sdm_forward_train", "sdm_backward_workspace_bytes", "sdm_backward",
+            "sdm_pattern_probe_mix", "sdm_project", "sdm_broadcast_memory", "sdm_overlap", "sdm_mem_stride_hint"]
 
 
 def _cfg(**kw):
@@ -56,6 +56,10 @@ def test_workspace_bytes_for_the_1p4b_shape():
     (dict(n_sub=1025), SDM_ERR_UNSUPPORTED),
     (dict(d=2044), SDM_ERR_UNSUPPORTED),
     (dict(n_sub=640, d=3840, state_dtype=0), SDM_ERR_UNSUPPORTED),  # 6.3 GB per memory in float32
+    (dict(mem_stride=2047), SDM_ERR_INVALID_ARG),                   # rows closer than d
+    (dict(mem_stride=2050), SDM_ERR_INVALID_ARG),                   # rows not 16 bytes apart
+    (dict(mem_stride=4700), SDM_ERR_UNSUPPORTED),                   # 4.3 GB per memory with the padding
+    (dict(state_dtype=1, n_sub=640, d=3840, mem_stride=6000), SDM_ERR_UNSUPPORTED),  # 4.9 GB of bf16
 ])
 def test_bad_configs_are_rejected_on_the_host(kw, status):
     L = _lib.lib()
@@ -103,6 +107,27 @@ def test_pattern_probe_rejects_bad_arguments_on_the_host(mem, memories, rows, ro
     assert L.sdm_last_error().startswith(b"sdm_pattern_probe")
 
 
+@pytest.mark.parametrize("row_stride", [8191, 8200, 8192 * 3])  # closer than a row, not 16-byte, 5.7 GB
+def test_pattern_probe_rejects_bad_row_strides(row_stride):
+    L = _lib.lib()
+    assert L.sdm_pattern_probe_mix(16, 4, 230400, 8192, row_stride, 16, 64, 2, 1, 0, None) == SDM_ERR_INVALID_ARG
+    assert b"row_stride" in L.sdm_last_error()
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), 2080),                                  # 8192-byte rows -> 8320
+    (dict(state_dtype=1), 2112),                     # 4096 -> 4224
+    (dict(state_dtype=1, n_sub=640, d=3840), 3904),  # 7680 -> 7808
+    (dict(d=2080), 2080),                            # already an odd number of 128-byte units
+    (dict(d=128), 128),                              # under 1 KB: dense
+    (dict(d=2040), 2040),                            # not whole 128-byte units: dense
+])
+def test_mem_stride_hint(kw, want):
+    L = _lib.lib()
+    assert L.sdm_mem_stride_hint(C.byref(_cfg(**kw))) == want
+    assert L.sdm_mem_stride_hint(None) == 0
+
+
 def test_backward_workspace_for_the_1p4b_shape():
     """Column partials (2W+2 floats per row and 128-byte column), dense dsigma rows of both query
     sets, and the split sub-key sums."""
@@ -113,9 +138,12 @@ def test_backward_workspace_for_the_1p4b_shape():
     assert n.value >= rows * 64 * 130 * 4 + 2 * rows * 2 * 480 * 4
 
 
-@pytest.mark.parametrize("kw", [dict(state_dtype=1, n_sub=240, d=2016), dict(d=2040)])
+@pytest.mark.parametrize("kw", [dict(state_dtype=1, n_sub=240, d=2016), dict(d=2040),
+                                dict(state_dtype=1, n_sub=640, d=3840, T=2048),
+                                dict(state_dtype=1, n_sub=480, d=2048, mem_stride=4704)])
 def test_backward_rejects_what_it_does_not_build(kw):
-    """Slot rows that are not whole 128-byte columns (64 bf16 or 32 float32 elements)."""
+    """Slot rows that are not whole 128-byte columns (64 bf16 or 32 float32 elements), and a float32
+    gradient of 4 GiB or more per memory (the 8B shape's: 640^2 rows of 3840 float32 values)."""
     L = _lib.lib()
     n = C.c_size_t()
     assert L.sdm_backward_workspace_bytes(C.byref(_cfg(**kw)), C.byref(n)) == SDM_ERR_UNSUPPORTED
@@ -125,5 +153,5 @@ def test_backward_rejects_what_it_does_not_build(kw):
 @pytest.mark.parametrize("reads,writes", [(3, 1), (4, 4), (2, 2), (0, 0)])
 def test_pattern_probe_mix_rejects_unbuilt_mixes(reads, writes):
     L = _lib.lib()
-    assert L.sdm_pattern_probe_mix(16, 4, 230400, 8192, 16, 64, reads, writes, 0, None) == SDM_ERR_INVALID_ARG
+    assert L.sdm_pattern_probe_mix(16, 4, 230400, 8192, 0, 16, 64, reads, writes, 0, None) == SDM_ERR_INVALID_ARG
     assert b"reads:writes" in L.sdm_last_error()
