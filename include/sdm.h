@@ -155,16 +155,16 @@ SDM_API sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const 
  * ((b*H + h)*T + t)*W + i is write position i of token t, best first), which
  * sdm_backward consumes.  The log holds B*H*T*W*d*sizeof(state) bytes (17.2 GB
  * for B=4, H=1, T=8192, W=64, d=2048, float32), owned by the caller.
- * SDM_ERR_UNSUPPORTED unless d * sizeof(state) is a multiple of 128 bytes, one
- * memory's log of a scan chunk (up to 3071 tokens) stays below 4 GiB and one
- * memory's float32 gradient (N * mem_stride * 4 bytes) below 4 GiB.  (SDM blog post, section "How does SDM
+ * SDM_ERR_UNSUPPORTED unless d * sizeof(state) is a multiple of 128 bytes and
+ * one memory's log of a scan chunk (up to 3071 tokens) stays below 4 GiB.  (SDM blog post, section "How does SDM
  * work?": the decay and delta-rule write whose inputs the log keeps.) */
 SDM_API sdm_status sdm_forward_train(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                                      const float* beta, const void* subkeys, void* mem_inout, float* out, void* log);
 
 /* Device bytes sdm_backward allocates on its first call on a handle (kept
  * until sdm_destroy): per-column partial sums [B*T*H, d/32, 2W+2], dense
- * softmax-derivative rows [2, B*T*H, 2, S] and split sub-key sums, all float32. */
+ * softmax-derivative rows [2, B*T*H, 2, S] and split sub-key sums, all float32,
+ * one flag per row and an 8 KB sink. */
 SDM_API sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* bytes);
 
 /* Backward pass of sdm_forward_train, by reverse-mode differentiation of the

@@ -175,6 +175,7 @@ struct sdm_ctx {
     float* ds;
     float* sub_part;
     int32_t* conflict;
+    float* sink;
     int nsplit;
 };
 
@@ -327,11 +328,6 @@ sdm_status check_train_shape(const sdm_config& c, const char* who)
     if (c.d % seg)
         return fail(SDM_ERR_UNSUPPORTED, "%s: d=%d must be a multiple of %d (128-byte slot columns)", who, c.d, seg);
     const unsigned sb = c.state_dtype == SDM_BF16 ? 2u : 4u;
-    // the float32 gradient of one memory (rows of mem_stride elements) is addressed with 32-bit offsets
-    const uint64_t grad_bytes = (uint64_t)c.n_sub * c.n_sub * mem_stride_of(c) * 4u;
-    if (grad_bytes >= (1ull << 32))
-        return fail(SDM_ERR_UNSUPPORTED, "%s: one memory's float32 gradient is %llu bytes; at most 2^32 - 1", who,
-                    (unsigned long long)grad_bytes);
     const Chunking k = chunking_of(c);
     for (int ci = 0; ci < k.C(); ++ci)
         if ((uint64_t)k.len(ci) * c.W * c.d * sb >= (1ull << 32) - 16u)
@@ -407,7 +403,7 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->e_start = nullptr;
     h->timing = false;
     h->bwd_block = nullptr;
-    h->part = h->ds = h->sub_part = nullptr;
+    h->part = h->ds = h->sub_part = h->sink = nullptr;
     h->conflict = nullptr;
     h->nsplit = 0;
     memset(&h->totals, 0, sizeof h->totals);
@@ -656,7 +652,8 @@ sdm_status sdm_backward_workspace_bytes(const sdm_config* cfg, size_t* bytes)
     const int nsplit = sdm::grad_sub_splits(c.B, c.H, c.T, c.n_sub, c.dk / 2);
     *bytes = align_up(sdm::grad_part_floats(c.B, c.H, c.T, c.d, c.W, c.state_dtype == SDM_BF16) * 4) +
              align_up(2 * rows * 2 * c.n_sub * 4) +
-             align_up((size_t)nsplit * c.H * 2 * c.n_sub * (c.dk / 2) * 4) + align_up(rows * 4);
+             align_up((size_t)nsplit * c.H * 2 * c.n_sub * (c.dk / 2) * 4) + align_up(rows * 4) +
+             align_up(sdm::kGradSinkBytes);
     return SDM_OK;
 }
 
@@ -699,6 +696,8 @@ sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void
         h->nsplit = sdm::grad_sub_splits(c.B, c.H, c.T, c.n_sub, c.dk / 2);
         p += align_up((size_t)h->nsplit * c.H * 2 * c.n_sub * (c.dk / 2) * 4);
         h->conflict = (int32_t*)p;
+        p += align_up(rows * 4);
+        h->sink = (float*)p;
     }
     // the forward's slots and weights, recomputed by the same kernels
     if ((s = run_address_all(h, wq, rq, subkeys, h->stream)) != SDM_OK)
@@ -739,6 +738,7 @@ sdm_status sdm_backward(sdm_handle h, const void* wq, const void* rq, const void
     a.ds = h->ds;
     a.sub_part = h->sub_part;
     a.conflict = h->conflict;
+    a.sink = h->sink;
     a.nsplit = h->nsplit;
     hipError_t e;
     {

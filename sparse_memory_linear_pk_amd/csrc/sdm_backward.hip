@@ -106,11 +106,25 @@ __device__ __forceinline__ float sum8(float x)
     return x;
 }
 
+// 16 gradient bytes at a 64-bit address (global memory instructions, one per access)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4_t global_u32x4;
+__device__ __forceinline__ uint4 gld(const float* p)
+{
+    return __builtin_bit_cast(uint4, *(const global_u32x4*)(p));
+}
+__device__ __forceinline__ void gst(float* p, const uint4& v) { *(global_u32x4*)(p) = __builtin_bit_cast(u32x4_t, v); }
+
 // ST: state element (float or bf16 bits); the gradient is float32 either way.
 // A workgroup owns 128 bytes of every memory row (E = 4 float32 or 8 bf16
 // values per lane) and the matching E float32 values per lane of the gradient
 // rows (16 or 32 bytes).
-template <class ST, class VT>
+// WIDE: one memory's gradient is 4 GiB or more (the 8B shape's float32 gradient
+// of a bf16 state, 6.3 GB), past what a buffer offset reaches: it is then read
+// and written with 64-bit addresses, and a position past W (whose slot is -1)
+// addresses the lane's own entry of a small workspace sink instead of a place
+// past the buffer, so every access is still issued on every path.
+template <class ST, class VT, bool WIDE>
 __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
 {
     constexpr int E = 16 / (int)sizeof(ST);
@@ -136,9 +150,24 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
     ST* const mem = static_cast<ST*>(a.mem);
     const ST* const log = static_cast<const ST*>(a.log);
     const __amdgpu_buffer_rsrc_t r_mem = make_rsrc(mem + mem_el, (uint32_t)(N * row_bytes));
-    const __amdgpu_buffer_rsrc_t r_g = make_rsrc(a.G + mem_el, (uint32_t)(N * grow_bytes));
+    const __amdgpu_buffer_rsrc_t r_g = make_rsrc(a.G + mem_el, WIDE ? 0u : (uint32_t)(N * grow_bytes));
     const int pos[2] = {wave * 16 + g, wave * 16 + 8 + g};
     const bool live[2] = {pos[0] < W, pos[1] < W};
+    float* const g_mem = a.G + mem_el + glane_off / 4u;       // this lane's gradient values of slot 0 (WIDE)
+    float* const g_sink = a.sink + threadIdx.x * (4u * GU);   // where a position past W goes (WIDE)
+    // gradient piece u of slot `slot` at position p: load and store
+    auto gload = [&](int p, int32_t slot, int u) __attribute__((always_inline)) -> uint4 {
+        if constexpr (WIDE)
+            return gld((live[p] ? g_mem + (size_t)(uint32_t)slot * a.ms : g_sink) + 4 * u);
+        else
+            return ld128(r_g, live[p] ? (uint32_t)slot * grow_bytes + glane_off + 16u * u : kOOB);
+    };
+    auto gstore = [&](int p, int32_t slot, int u, const uint4& v) __attribute__((always_inline)) {
+        if constexpr (WIDE)
+            gst((live[p] ? g_mem + (size_t)(uint32_t)slot * a.ms : g_sink) + 4 * u, v);
+        else
+            st128(r_g, live[p] ? (uint32_t)slot * grow_bytes + glane_off + 16u * u : kOOB, v);
+    };
     const int e0 = col * (128 / (int)sizeof(ST)) + el * E; // this lane's first element of the row
 
     // A token's slots are fetched two tokens ahead, its other state-independent
@@ -198,8 +227,8 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             st.rv[p] = ld128(r_mem, live[p] ? (uint32_t)m.rs[p] * row_bytes + lane_off : kOOB);
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
-                st.rg[p][u] = ld128(r_g, live[p] ? (uint32_t)m.rs[p] * grow_bytes + glane_off + 16u * u : kOOB);
-                st.wg[p][u] = ld128(r_g, live[p] ? (uint32_t)m.ws[p] * grow_bytes + glane_off + 16u * u : kOOB);
+                st.rg[p][u] = gload(p, m.rs[p], u);
+                st.wg[p][u] = gload(p, m.ws[p], u);
             }
         }
     };
@@ -257,7 +286,7 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             for (int u = 0; u < GU; ++u) {
                 const uint4 pk = pack_g(gr, u);
                 s_g[(pos[p] * 8 + el) * GU + u] = pk;
-                st128(r_g, live[p] ? (uint32_t)rs[p] * grow_bytes + glane_off + 16u * u : kOOB, pk);
+                gstore(p, rs[p], u, pk);
             }
         }
         if (el == 0) {
@@ -335,7 +364,7 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
                 part[W + pos[p]] = sw;
 #pragma unroll
             for (int u = 0; u < GU; ++u)
-                st128(r_g, live[p] ? (uint32_t)ws[p] * grow_bytes + glane_off + 16u * u : kOOB, pack_g(ng, u));
+                gstore(p, ws[p], u, pack_g(ng, u));
             st128(r_mem, live[p] ? (uint32_t)ws[p] * row_bytes + lane_off : kOOB, wo[p]); // the slot before the token
         }
 #pragma unroll
@@ -588,21 +617,34 @@ hipError_t launch_grad_scan(const GradArgs& a, hipStream_t stream)
     const int seg = a.state_bf16 ? 64 : 32;
     if (a.d % seg || a.ncol != a.d / seg || a.W > 64 || a.W < 1 || a.ms < a.d || a.ms % 4)
         return hipErrorInvalidValue;
-    // one memory's rows of the memory and of the float32 gradient are addressed with 32-bit offsets
-    if ((uint64_t)a.S * a.S * a.ms * 4u >= (1ull << 32))
+    // one memory's state rows are addressed with 32-bit buffer offsets; its float32
+    // gradient too unless it reaches 4 GiB (then 64-bit addresses and the sink)
+    const uint64_t N = (uint64_t)a.S * a.S;
+    if (N * a.ms * (a.state_bf16 ? 2u : 4u) >= (1ull << 32))
+        return hipErrorInvalidValue;
+    const bool wide = N * a.ms * 4u >= (1ull << 32);
+    if (wide && !a.sink)
         return hipErrorInvalidValue;
     dim3 grid((unsigned)(a.B * a.H * a.ncol)), block(kWaves * 64);
+#define SDM_GRAD_SCAN(ST, VT)                                                                                        \
+    do {                                                                                                             \
+        if (wide)                                                                                                    \
+            hipLaunchKernelGGL((grad_scan_kernel<ST, VT, true>), grid, block, 0, stream, a);                         \
+        else                                                                                                         \
+            hipLaunchKernelGGL((grad_scan_kernel<ST, VT, false>), grid, block, 0, stream, a);                        \
+    } while (0)
     if (a.state_bf16) {
         if (a.in_bf16)
-            hipLaunchKernelGGL((grad_scan_kernel<uint16_t, uint16_t>), grid, block, 0, stream, a);
+            SDM_GRAD_SCAN(uint16_t, uint16_t);
         else
-            hipLaunchKernelGGL((grad_scan_kernel<uint16_t, float>), grid, block, 0, stream, a);
+            SDM_GRAD_SCAN(uint16_t, float);
     } else {
         if (a.in_bf16)
-            hipLaunchKernelGGL((grad_scan_kernel<float, uint16_t>), grid, block, 0, stream, a);
+            SDM_GRAD_SCAN(float, uint16_t);
         else
-            hipLaunchKernelGGL((grad_scan_kernel<float, float>), grid, block, 0, stream, a);
+            SDM_GRAD_SCAN(float, float);
     }
+#undef SDM_GRAD_SCAN
     return hipGetLastError();
 }
 

@@ -180,8 +180,11 @@ struct GradArgs {
     float* ds;                           // workspace: [2, rows, 2, S]
     float* sub_part;                     // workspace: [nsplit, H, 2, S, dh]
     int32_t* conflict;                   // workspace: [rows], token shares a slot with the next one
+    float* sink;                         // workspace: kGradSinkBytes, where positions past W go when
+                                         // the gradient is addressed with 64-bit pointers
     int nsplit;
 };
+constexpr size_t kGradSinkBytes = 256 * 32; // a workgroup's lanes x 32 gradient bytes
 size_t grad_part_floats(int B, int H, int T, int d, int W, bool state_bf16);
 int grad_sub_splits(int B, int H, int T, int S, int dh);
 hipError_t launch_grad_conflicts(const GradArgs& a, hipStream_t stream);

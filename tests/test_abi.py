@@ -138,16 +138,23 @@ def test_backward_workspace_for_the_1p4b_shape():
     assert n.value >= rows * 64 * 130 * 4 + 2 * rows * 2 * 480 * 4
 
 
-@pytest.mark.parametrize("kw", [dict(state_dtype=1, n_sub=240, d=2016), dict(d=2040),
-                                dict(state_dtype=1, n_sub=640, d=3840, T=2048),
-                                dict(state_dtype=1, n_sub=480, d=2048, mem_stride=4704)])
+@pytest.mark.parametrize("kw", [dict(state_dtype=1, n_sub=240, d=2016), dict(d=2040)])
 def test_backward_rejects_what_it_does_not_build(kw):
-    """Slot rows that are not whole 128-byte columns (64 bf16 or 32 float32 elements), and a float32
-    gradient of 4 GiB or more per memory (the 8B shape's: 640^2 rows of 3840 float32 values)."""
+    """Slot rows that are not whole 128-byte columns (64 bf16 or 32 float32 elements)."""
     L = _lib.lib()
     n = C.c_size_t()
     assert L.sdm_backward_workspace_bytes(C.byref(_cfg(**kw)), C.byref(n)) == SDM_ERR_UNSUPPORTED
     assert b"sdm_backward" in L.sdm_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(state_dtype=1, n_sub=640, d=3840, T=2048, B=8),
+                                dict(state_dtype=1, n_sub=640, d=3840, T=2048, B=8, mem_stride=3904)])
+def test_backward_takes_a_gradient_past_4_gib(kw):
+    """The 8B shape: its float32 memory gradient is 6.3 GB per memory (640^2 rows of 3840 values), which
+    the reverse scan addresses with 64-bit pointers."""
+    L = _lib.lib()
+    n = C.c_size_t()
+    assert L.sdm_backward_workspace_bytes(C.byref(_cfg(**kw)), C.byref(n)) == SDM_OK
 
 
 @pytest.mark.parametrize("reads,writes", [(3, 1), (4, 4), (2, 2), (0, 0)])

@@ -211,3 +211,64 @@ def test_backward_rejects_a_bf16_state_of_partial_columns():
                                 t(cfg.B, cfg.T, cfg.H, cfg.d), t(cfg.B, cfg.T, cfg.H), t(cfg.B, cfg.T, cfg.H),
                                 t(cfg.H, 2, cfg.S, cfg.dk // 2), b(cfg.B, cfg.H, cfg.N, cfg.d),
                                 t(cfg.B, cfg.T, cfg.H, cfg.d), b(cfg.B, cfg.H, cfg.T, cfg.W, cfg.d))
+
+
+@pytest.mark.timeout(600)
+def test_backward_with_a_gradient_past_4_gib():
+    """The 8B shape (N = 640^2, d = 3840, bf16 state, rows padded to 3904): the float32 memory gradient
+    is 6.4 GB per memory, past what a 32-bit buffer offset reaches, so the reverse scan addresses it with
+    64-bit pointers.  The memory gradient, the restored memory and dv are per-element given the slots and
+    weights, so the gradient oracle checks them on column slices (d = 64: the first and the last 64
+    columns, every one of the 409,600 slots), driven by the GPU's slots."""
+    import torch
+    from sparse_memory_linear_pk_amd import SDM
+    cfg = gi.config(4, B=1, T=16)
+    ms = SDM.stride_hint(cfg.d, True)
+    assert cfg.S ** 2 * ms * 4 >= 2 ** 32
+    go = oracle.get_grad()
+    x = gi.make_inputs(cfg)
+    g = gi.make_upstream_grads(cfg)
+    say(f"[bwd wide] {cfg} mem_stride {ms}")
+    dev = {k: to_dev(v) for k, v in x.items()}
+    f32 = dict(dtype=torch.float32, device="cuda")
+    R = cfg.B * cfg.T * cfg.H
+    with SDM.from_config(cfg, mem_stride=ms) as layer:
+        mem = layer.empty_state(cfg.B, cfg.H)
+        mem.copy_(dev["mem0"])
+        dmem = layer.empty_state(cfg.B, cfg.H, dtype=torch.float32)
+        dmem.copy_(to_dev(g["dmem"]))
+        out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32)
+        log = torch.empty((cfg.B, cfg.H, cfg.T, cfg.W, cfg.d), dtype=torch.bfloat16, device="cuda")
+        layer.forward_train(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem, out, log)
+        idx = {}
+        for s_, q in (("w", "wq"), ("r", "rq")):
+            i_ = torch.empty((R, cfg.W), dtype=torch.int32, device="cuda")
+            w_ = torch.empty((R, cfg.W), **f32)
+            layer.address(dev[q], dev["subkeys"], i_, w_)
+            idx[s_] = (to_host(i_), to_host(w_))
+        outs = {"dwq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32),
+                "drq": torch.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32),
+                "dv": torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32),
+                "dalpha": torch.empty((cfg.B, cfg.T, cfg.H), **f32),
+                "dbeta": torch.empty((cfg.B, cfg.T, cfg.H), **f32),
+                "dsub": torch.empty((cfg.H, 2, cfg.S, cfg.dk // 2), **f32)}
+        layer.backward(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem, log,
+                       to_dev(g["dout"]), dmem, outs["dwq"], outs["drq"], outs["dv"], outs["dalpha"], outs["dbeta"],
+                       outs["dsub"])
+        torch.cuda.synchronize()
+        # the reverse walk restores the initial memory exactly
+        assert torch.equal(mem.view(torch.int16), dev["mem0"].view(torch.int16))
+        hi = int((idx["w"][0] >= 2 ** 32 // (ms * 4)).sum())
+        say(f"[bwd wide] write slots past the first 4 GiB of the gradient: {hi} of {idx['w'][0].size}")
+        assert hi > 0
+        for c0 in (0, cfg.d - 64):
+            sl = slice(c0, c0 + 64)
+            cs = cfg.replace(d=64)
+            ref = go.scan_grad(cs, idx["w"][0], idx["w"][1], idx["r"][0], idx["r"][1],
+                               np.ascontiguousarray(x["v"][..., sl]), x["alpha"], x["beta"],
+                               np.ascontiguousarray(x["mem0"][..., sl]), np.ascontiguousarray(g["dout"][..., sl]),
+                               np.ascontiguousarray(g["dmem"][..., sl]).astype(np.float64))
+            e_g = rel_max_err(to_host(dmem[..., sl]), ref["dmem0"])
+            e_v = rel_max_err(to_host(outs["dv"][..., sl]), ref["dv"])
+            say(f"[bwd wide] columns {c0}..{c0 + 63}: dmem0 {e_g:.3g}, dv {e_v:.3g}")
+            assert e_g <= TOL and e_v <= TOL
