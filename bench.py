@@ -106,6 +106,29 @@ def with_rows(t, ms: int):
     return full[..., :d]
 
 
+def copy_bandwidth() -> dict:
+    """Bytes read plus bytes written per second by plain device copies of 2 GiB between the halves of a
+    4 GiB scratch tensor: the runtime's copy (torch copy_) and an elementwise kernel (torch mul by 1 into
+    the other half); the faster is the measured stand-in for the HBM peak."""
+    import torch
+    flat = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    a, b = flat[:1 << 29], flat[1 << 29:]
+    a.fill_(1.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("runtime copy", lambda: b.copy_(a)), ("elementwise kernel", lambda: torch.mul(a, 1.0, out=b))):
+        fn()
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = 5 * 2 * (2 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del flat
+    best = max(res, key=res.get)
+    return {"achieved": res[best], "kernel": best, "all": res}
+
+
 def rows_note(cfg, ms: int) -> dict:
     s = 2 if cfg.state_bf16 else 4
     return {"stride_elements": ms, "row_bytes": cfg.d * s, "stride_bytes": ms * s,
@@ -554,6 +577,7 @@ def main():
             pat.append(e0.elapsed_time(e1))
     pattern_ms = sum(pat) / len(pat)
     layer.close()
+    copy = copy_bandwidth()
 
     sec = t1 - t0
     tokens = cfg.B * cfg.T * args.steps
@@ -598,7 +622,12 @@ def main():
                                          "frac": (nbytes / (scan_ms * 1e-3)) / (nbytes / (pattern_ms * 1e-3)),
                                          "what": "sdm_pattern_probe_mix 2:1: the scan's random 128-byte segment "
                                                  "reads and writes with no arithmetic, on rows as far apart as "
-                                                 "the memory's; frac = scan / this"}},
+                                                 "the memory's; frac = scan / this"},
+                     "copy_peak": {"achieved": copy["achieved"], "unit": "GB/s", "frac": achieved / copy["achieved"],
+                                   "kernel": copy["kernel"], "all": copy["all"],
+                                   "what": "the faster of two plain 2 GiB device copies (bytes read + written "
+                                           "per second), the measured stand-in for the HBM peak; "
+                                           "frac = scan / this"}},
         "kernels_ms_per_step": {"pk_score": per_step["score"], "pk_topk": per_step["select"],
                                 "sdm_plan": per_step["plan"], "sdm_scan": scan_ms,
                                 "note": "device time of each kernel in the forward; after the first chunk, "
