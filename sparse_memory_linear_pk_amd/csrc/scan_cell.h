@@ -99,6 +99,36 @@ template <> struct CellHalf<uint16_t> {
     }
 };
 
+// A lane's 4 bytes of a bf16 state in a 32-byte slot segment (2 values), for a
+// single long sequence: twice the workgroups of 64-byte segments again, the same
+// arithmetic and rounding, held in the low word of a uint4.
+template <class ST> struct CellQuarter;
+template <> struct CellQuarter<uint16_t> {
+    static constexpr int E = 2;
+    using CT = double;
+    __device__ static void unpack(const uint4& u, float (&x)[2])
+    {
+        x[0] = bf16_lo(u.x);
+        x[1] = bf16_hi(u.x);
+    }
+    __device__ static uint4 pack(const double (&x)[2])
+    {
+        float f[2];
+        bool tie = false;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            f[q] = (float)x[q];
+            tie |= (__float_as_uint(f[q]) & 0xFFFFu) == 0x8000u;
+        }
+        if (__builtin_amdgcn_ballot_w64(tie) != 0u) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                f[q] = settle_bf16_tie(x[q]);
+        }
+        return make_uint4(Cell<uint16_t>::pack2(f[0], f[1]), 0u, 0u, 0u);
+    }
+};
+
 // Totals over the 4 waves of the per-wave partials ([wave][el][E] values of
 // type X) of element lane el, in the same order in every lane.
 template <int E, class X>
@@ -116,11 +146,17 @@ template <int E, class X>
 __device__ __forceinline__ void reduce_to_part(const X (&v)[E], float4* part, int wave, int el, int lane)
 {
     X* p = reinterpret_cast<X*>(part);
+    if constexpr (E == 2) {
+        // rows 0 and 2 end with the total of value 0, rows 1 and 3 with value 1's
+        const X t = reduce2_to_rows(v[0], v[1]);
+        p[(wave * 8 + el) * E + ((lane >> 4) & 1)] = t;
+    } else {
 #pragma unroll
-    for (int c = 0; c < E / 4; ++c) {
-        // row r (lanes 16r .. 16r+15) ends with the total of value 4c + r
-        const X t = reduce4_to_rows(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
-        p[(wave * 8 + el) * E + 4 * c + (lane >> 4)] = t;
+        for (int c = 0; c < E / 4; ++c) {
+            // row r (lanes 16r .. 16r+15) ends with the total of value 4c + r
+            const X t = reduce4_to_rows(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+            p[(wave * 8 + el) * E + 4 * c + (lane >> 4)] = t;
+        }
     }
 }
 

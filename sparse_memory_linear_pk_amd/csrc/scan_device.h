@@ -118,6 +118,20 @@ __device__ __forceinline__ float reduce4_to_rows(float v0, float v1, float v2, f
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Two values through the same tree: row r ends with the total of value r & 1 (the
+// last level pairs each row's partial with itself two rows away, which is the
+// tree's last addition for that value; addition is commutative, so every total
+// is the one reduce4_to_rows gives).
+__device__ __forceinline__ float reduce2_to_rows(float v0, float v1)
+{
+    v0 = bfly<8>(v0);
+    v1 = bfly<8>(v1);
+    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+    const float t01 = __uint_as_float(s01[0]) + __uint_as_float(s01[1]); // rows 0,2: v0; rows 1,3: v1
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(t01), __float_as_uint(t01), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // The float whose nearest-even bf16 rounding is that of the double x (one
 // rounding of x to bf16).  x rounds to float
 // first; that can only go wrong when the float lands exactly on a bf16 tie while
@@ -152,6 +166,17 @@ __device__ __forceinline__ void swap_rows_d(double a, double b, bool rows32, dou
     }
     x = __longlong_as_double((long long)(((uint64_t)xh << 32) | xl));
     y = __longlong_as_double((long long)(((uint64_t)yh << 32) | yl));
+}
+
+__device__ __forceinline__ double reduce2_to_rows(double v0, double v1)
+{
+    v0 = bfly<8>(v0);
+    v1 = bfly<8>(v1);
+    double a, b;
+    swap_rows_d(v0, v1, false, a, b);
+    const double t01 = a + b; // rows 0,2: v0; rows 1,3: v1
+    swap_rows_d(t01, t01, true, a, b);
+    return a + b;
 }
 
 __device__ __forceinline__ double reduce4_to_rows(double v0, double v1, double v2, double v3)

@@ -691,8 +691,10 @@ bool plan_scan(int B, int H, int T, int d, int ms, int W, long N, bool state_bf1
         plan->rw = 2;
         plan->waves = 4;
         plan->lookahead = staged::kP;
-        // 64-byte segments (4 bf16 values per lane) when 128-byte ones leave most CUs idle
-        plan->seg_bytes = (state_bf16 && units * (d * s_bytes / 128) < 128) ? 64 : 128;
+        // 64-byte (4 bf16 values per lane) or 32-byte segments (2 values) when 128-byte
+        // ones leave most CUs idle
+        const long cols = units * (d * s_bytes / 128);
+        plan->seg_bytes = !state_bf16 || cols >= 128 ? 128 : cols >= 64 ? 64 : 32;
         plan->grid = (int)(units * (d * s_bytes / plan->seg_bytes));
         plan->lds = 0;
         // pairs run from S0 to the pair after the one holding T-1; each loads the

@@ -15,11 +15,11 @@
 // Work split.  A workgroup of 4 waves owns one (b, h) and 128 bytes of every
 // slot row (32 float32 or 64 bf16 elements) and walks all T tokens.  When the
 // memories are too few to fill the device that way (one long sequence), a
-// bf16 state is split into 64-byte segments instead (8 lanes x 8 bytes, 4
-// values per lane): twice the workgroups, half the arithmetic per token each.  A token's
-// 64 positions (the W selected slots, padded with sentinels) spread over the
-// waves, 16 each: lane (g, e) of wave w holds the 16 bytes e of positions
-// 16w + g and 16w + 8 + g (E = 4 or 8 elements).  Sums over positions are a
+// bf16 state is split into 64-byte segments (8 lanes x 8 bytes, 4 values per
+// lane) or 32-byte ones (8 lanes x 4 bytes, 2 values): more workgroups, less
+// arithmetic per token each.  A token's 64 positions (the W selected slots,
+// padded with sentinels) spread over the waves, 16 each: lane (g, e) of wave w
+// holds the bytes e of positions 16w + g and 16w + 8 + g (E = 2, 4 or 8 elements).  Sums over positions are a
 // transposing reduction inside the wave and one LDS exchange across the waves.
 //
 // Pipeline.  Tokens go in pairs.  At the start of pair k: the read of pair k-1
@@ -93,38 +93,42 @@ __device__ __forceinline__ void barrier_lds()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// A segment's 16 or 8 bytes of one lane (8 bytes: the low half of the uint4).
+// A segment's 16, 8 or 4 bytes of one lane (held in the low part of the uint4).
 template <int SEGB> __device__ __forceinline__ uint4 ldseg(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     if constexpr (SEGB == 128) {
         return ld128(r, off);
-    } else {
+    } else if constexpr (SEGB == 64) {
         const i32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
         return make_uint4((uint32_t)v[0], (uint32_t)v[1], 0u, 0u);
+    } else {
+        return make_uint4((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0), 0u, 0u, 0u);
     }
 }
 template <int SEGB> __device__ __forceinline__ void stseg(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v)
 {
     if constexpr (SEGB == 128)
         st128(r, off, v);
-    else
+    else if constexpr (SEGB == 64)
         __builtin_amdgcn_raw_buffer_store_b64((i32x2_t){(int)v.x, (int)v.y}, r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b32((int)v.x, r, off, 0, 0);
 }
 
 // ST: state element (float or bf16 bits), VT: v element (float or bf16 bits),
 // LOG: also store the write slots' values before the write to a.log,
-// SEGB: bytes of every slot row the workgroup owns (128, or 64 for a bf16 state).
+// SEGB: bytes of every slot row the workgroup owns (128, or 64 or 32 for a bf16 state).
 template <class ST, class VT, bool LOG, int SEGB>
 __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
 {
-    static_assert(SEGB == 128 || (SEGB == 64 && sizeof(ST) == 2), "segment width");
-    using C = std::conditional_t<SEGB == 128, Cell<ST>, CellHalf<ST>>;
+    static_assert(SEGB == 128 || ((SEGB == 64 || SEGB == 32) && sizeof(ST) == 2), "segment width");
+    using C = std::conditional_t<SEGB == 128, Cell<ST>, std::conditional_t<SEGB == 64, CellHalf<ST>, CellQuarter<ST>>>;
     using CT = typename C::CT;                       // type of the write arithmetic
     constexpr int E = C::E;                          // state elements per lane
     constexpr int SEG = SEGB / (int)sizeof(ST);      // state elements of a workgroup's segment
-    constexpr int VB = E * (int)sizeof(VT);          // bytes of v per lane and token: 8, 16 or 32
+    constexpr int VB = E * (int)sizeof(VT);          // bytes of v per lane and token: 4, 8, 16 or 32
     constexpr int NV = VB <= 16 ? 1 : 2;             // v loads per token
-    constexpr int NO = E / 4;                        // out stores per token (16 bytes each)
+    constexpr int NO = E >= 4 ? E / 4 : 1;           // out stores per token (16 bytes each, or one of 8)
     constexpr int ZS = kStages, ZR = kRecSlots, ZL = 4;
     // Vector-memory operations of a pair, in issue order: at its start the loads
     // (per token of pair k+2 4 slot loads and NV of v; the records of pair k+4),
@@ -294,11 +298,9 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                vv[4 * i] = __uint_as_float(u[i].x);
-                vv[4 * i + 1] = __uint_as_float(u[i].y);
-                vv[4 * i + 2] = __uint_as_float(u[i].z);
-                vv[4 * i + 3] = __uint_as_float(u[i].w);
+            for (int q = 0; q < E; ++q) {
+                const uint4& w = u[q / 4];
+                vv[q] = __uint_as_float(q % 4 == 0 ? w.x : q % 4 == 1 ? w.y : q % 4 == 2 ? w.z : w.w);
             }
         }
         float m0[E], m1[E];
@@ -351,7 +353,9 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
         rset[S][1] = ldseg<SEGB>(r_mem, or1);
         soff[S][0] = (u0.x >> 31) ? kOOB : ow0;
         soff[S][1] = (u1.x >> 31) ? kOOB : ow1;
-        if constexpr (VB == 8) {
+        if constexpr (VB == 4) {
+            vr[S][0] = make_uint4((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r_v, hu.z + v_lane, 0, 0), 0u, 0u, 0u);
+        } else if constexpr (VB == 8) {
             const i32x2_t w2 = __builtin_amdgcn_raw_buffer_load_b64(r_v, hu.z + v_lane, 0, 0);
             vr[S][0] = make_uint4((uint32_t)w2[0], (uint32_t)w2[1], 0u, 0u);
         } else {
@@ -377,11 +381,16 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
             sum_waves<E, float>(ored, el, o);
             off = g == 0 ? (hd.w & ~kDepFlag) + o_lane : kOOB;
         }
+        if constexpr (E == 2) {
+            __builtin_amdgcn_raw_buffer_store_b64((i32x2_t){(int)__float_as_uint(o[0]), (int)__float_as_uint(o[1])},
+                                                  r_out, off, 0, 0);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NO; ++i)
-            st128(r_out, off == kOOB ? kOOB : off + 16u * i,
-                  make_uint4(__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]), __float_as_uint(o[4 * i + 2]),
-                             __float_as_uint(o[4 * i + 3])));
+            for (int i = 0; i < NO; ++i)
+                st128(r_out, off == kOOB ? kOOB : off + 16u * i,
+                      make_uint4(__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]),
+                                 __float_as_uint(o[4 * i + 2]), __float_as_uint(o[4 * i + 3])));
+        }
     };
 
     // Pair (s, s+1), s = S0 + ZR*blk + j0: record and ring slots j0, j0+1, register
@@ -468,14 +477,17 @@ hipError_t launch_sdm_scan_staged(const ScanArgs& a, const ScanPlan& p, bool sta
 {
     const int seg = p.seg_bytes / (state_bf16 ? 2 : 4);
     if (!p.staged || p.waves != kWaves || a.d % seg != 0 || a.W > kPos ||
-        (p.seg_bytes != 128 && !(p.seg_bytes == 64 && state_bf16)))
+        (p.seg_bytes != 128 && !((p.seg_bytes == 64 || p.seg_bytes == 32) && state_bf16)))
         return hipErrorInvalidValue;
     // the log of a call: one memory's tokens of a chunk addressable by 32-bit offsets
     if (a.log && (uint64_t)a.T * a.W * a.d * (state_bf16 ? 2u : 4u) >= (1ull << 32) - 16u)
         return hipErrorInvalidValue;
     dim3 grid((unsigned)p.grid), block(kWaves * 64);
     if (state_bf16) {
-        if (p.seg_bytes == 64)
+        if (p.seg_bytes == 32)
+            in_bf16 ? launch_typed_staged<uint16_t, uint16_t, 32>(a, grid, block, stream)
+                    : launch_typed_staged<uint16_t, float, 32>(a, grid, block, stream);
+        else if (p.seg_bytes == 64)
             in_bf16 ? launch_typed_staged<uint16_t, uint16_t, 64>(a, grid, block, stream)
                     : launch_typed_staged<uint16_t, float, 64>(a, grid, block, stream);
         else
