@@ -37,8 +37,11 @@ def _edge(**kw):
 # (config, padded row stride in elements, runs the oracle)
 CASES = {
     "f32_staged": (_edge(), 288, True),                                    # 1024-byte rows -> 1152
-    "bf16_state_32B_segments": (_edge(d=128, in_bf16=True, state_bf16=True), 192, True),    # 8 columns
-    "bf16_state_64B_segments": (_edge(B=1, H=1, T=24, d=4096, in_bf16=True, state_bf16=True), 4160, True),
+    # a bf16 state over few 128-byte columns scans in narrower segments: under 64 columns in 32-byte
+    # ones, 64 to 127 in 64-byte ones
+    "bf16_state_8_columns": (_edge(d=128, in_bf16=True, state_bf16=True), 192, True),
+    "bf16_state_64_columns": (_edge(B=1, H=1, T=24, d=4096, in_bf16=True, state_bf16=True), 4160, True),
+    "bf16_state_120_columns": (_edge(B=2, H=1, T=24, d=3840, in_bf16=True, state_bf16=True), 3904, True),
     "f32_register_ring": (_edge(d=40, T=24), 44, True),                     # 160-byte rows: not staged
     "1.4B_shape": (gi.config(2, T=24, B=1), 2080, False),                  # 8192-byte rows -> 8320
     "8B_shape_bf16": (gi.config(4, T=16, B=1), 3904, False),               # 7680 -> 7808
