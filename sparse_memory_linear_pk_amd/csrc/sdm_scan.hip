@@ -703,6 +703,9 @@ bool plan_scan(int B, int H, int T, int d, int ms, int W, long N, bool state_bf1
         plan->Tp = staged::kS0 + blocks * staged::kRecSlots + 8;
         return true;
     }
+    // the register-ring kernel addresses one sequence's v and out rows of a chunk with 32-bit offsets
+    if (((uint64_t)T * H + 1) * d * 4 > (1ull << 32))
+        return false;
     const int vec = state_bf16 ? 8 : 4;
     const int ct = state_bf16 ? 8 : 4; // bytes of the write path's arithmetic type
     int lps = 8;

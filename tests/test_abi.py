@@ -60,6 +60,9 @@ def test_workspace_bytes_for_the_1p4b_shape():
     (dict(mem_stride=2050), SDM_ERR_INVALID_ARG),                   # rows not 16 bytes apart
     (dict(mem_stride=4700), SDM_ERR_UNSUPPORTED),                   # 4.3 GB per memory with the padding
     (dict(state_dtype=1, n_sub=640, d=3840, mem_stride=6000), SDM_ERR_UNSUPPORTED),  # 4.9 GB of bf16
+    # rows of 8200 float32 values (the register-ring scan) over 64 heads: one sequence's v of a
+    # 2048-token chunk is 4.3 GB, past a 32-bit buffer offset
+    (dict(H=64, T=2048, d=8200, n_sub=64, dk=32, k=4, W=8), SDM_ERR_UNSUPPORTED),
 ])
 def test_bad_configs_are_rejected_on_the_host(kw, status):
     L = _lib.lib()
