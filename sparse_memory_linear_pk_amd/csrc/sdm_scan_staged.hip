@@ -242,10 +242,12 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     };
 
     // Write, first half: this lane's share of the prediction of the decayed
-    // slots, summed over the wave into red.
-    auto partials = [&](const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float4* red)
-        __attribute__((always_inline)) {
-        float m0[E], m1[E];
+    // slots, summed over the wave into red; the slots' values are left in m0, m1
+    // for the second half (no ring entry they come from changes in between: a
+    // pair overwrites the entries of tokens 11 and 12 back, a slot forwards from
+    // at most 7 back).
+    auto partials = [&](const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float4* red,
+                        float (&m0)[E], float (&m1)[E]) __attribute__((always_inline)) {
         slot_values(ws, r0.x, r1.x, m0, m1);
         const CT w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z), al = alpha;
         CT acc[E];
@@ -271,12 +273,12 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     };
 
     // Write, second half (after the barrier that publishes red): the delta-rule
-    // update of this lane's slots (the decayed values formed again, exactly as
-    // above), stored into the ring entry of the token in ring slot J; with LOG,
-    // the slots' bits before the update in o0, o1.
+    // update of this lane's slots (values m0, m1 from the first half, decayed
+    // exactly as there), stored into the ring entry of the token in ring slot J;
+    // with LOG, the slots' bits before the update in o0, o1.
     auto update = [&](auto jc, const uint4 (&ws)[2], const uint4& r0, const uint4& r1, float alpha, float beta,
-                      const uint4 (&vraw)[NV], const float4* red, uint4& p0, uint4& p1, uint4& o0, uint4& o1)
-        __attribute__((always_inline)) {
+                      const uint4 (&vraw)[NV], const float4* red, const float (&m0)[E], const float (&m1)[E],
+                      uint4& p0, uint4& p1, uint4& o0, uint4& o1) __attribute__((always_inline)) {
         constexpr int J = decltype(jc)::value;
         CT vh[E];
         sum_waves<E, CT>(red, el, vh);
@@ -303,8 +305,6 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
                 vv[q] = __uint_as_float(q % 4 == 0 ? w.x : q % 4 == 1 ? w.y : q % 4 == 2 ? w.z : w.w);
             }
         }
-        float m0[E], m1[E];
-        slot_values(ws, r0.x, r1.x, m0, m1);
         if constexpr (LOG)
             old_bits(ws, r0.x, r1.x, o0, o1);
         const CT w0 = __uint_as_float(r0.z), w1 = __uint_as_float(r1.z), al = alpha, be = beta;
@@ -424,23 +424,24 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
             records(std::integral_constant<int, j0>{}, a0, a1, ha);
             records(std::integral_constant<int, j1>{}, b0, b1, hb);
             uint4 ya0, ya1, yb0, yb1, oa0, oa1, ob0, ob1;
-            partials(wset[j0 % ZS], a0, a1, __uint_as_float(ha.x), g_red);
-            partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), g_red + kPartU4);
+            float ma0[E], ma1[E], mb0[E], mb1[E];
+            partials(wset[j0 % ZS], a0, a1, __uint_as_float(ha.x), g_red, ma0, ma1);
+            partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), g_red + kPartU4, mb0, mb1);
             barrier_lds();
             store_out(std::integral_constant<int, p0>{}, g_ored, 0);
             store_out(std::integral_constant<int, p1>{}, g_ored + kPartU4, 1);
             update(std::integral_constant<int, j0>{}, wset[j0 % ZS], a0, a1, __uint_as_float(ha.x),
-                   __uint_as_float(ha.y), vr[j0 % ZS], g_red, ya0, ya1, oa0, oa1);
+                   __uint_as_float(ha.y), vr[j0 % ZS], g_red, ma0, ma1, ya0, ya1, oa0, oa1);
             update(std::integral_constant<int, j1>{}, wset[j1 % ZS], b0, b1, __uint_as_float(hb.x),
-                   __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1, ob0, ob1);
+                   __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, mb0, mb1, yb0, yb1, ob0, ob1);
             if (__builtin_amdgcn_readfirstlane(hb.w) & kDepFlag) {
                 // token s+1 writes a slot token s writes: redo its write now that
                 // token s's values are in the ring
                 barrier_lds();
-                partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), g_red + kPartU4);
+                partials(wset[j1 % ZS], b0, b1, __uint_as_float(hb.x), g_red + kPartU4, mb0, mb1);
                 barrier_lds();
                 update(std::integral_constant<int, j1>{}, wset[j1 % ZS], b0, b1, __uint_as_float(hb.x),
-                       __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, yb0, yb1, ob0, ob1);
+                       __uint_as_float(hb.y), vr[j1 % ZS], g_red + kPartU4, mb0, mb1, yb0, yb1, ob0, ob1);
             }
             stseg<SEGB>(r_mem, soff[j0 % ZS][0], ya0);
             stseg<SEGB>(r_mem, soff[j0 % ZS][1], ya1);
