@@ -55,22 +55,28 @@ def cpu_baseline(cfg, x, budget_s: float):
     o = oracle.get()
     threads = oracle.default_threads()
 
-    def run(nb, tn):
+    def run(nb, tn, nthreads):
         c = cfg.replace(B=nb, T=tn)
         sl = {k: np.ascontiguousarray(x[k][:nb, :tn]) for k in ("wq", "rq", "v", "alpha", "beta")}
         mem = np.ascontiguousarray(x["mem0"][:nb])
         t0 = time.perf_counter()
-        o.forward(c, sl["wq"], sl["rq"], sl["v"], sl["alpha"], sl["beta"], x["subkeys"], mem, threads=threads)
+        o.forward(c, sl["wq"], sl["rq"], sl["v"], sl["alpha"], sl["beta"], x["subkeys"], mem, threads=nthreads)
         return time.perf_counter() - t0
 
-    per_tok = run(1, 256) / 256
+    per_tok = run(1, 256, threads) / 256
     nb = int(max(1, min(cfg.B, budget_s // max(per_tok * cfg.T, 1e-9))))
     tn = cfg.T if nb > 1 or per_tok * cfg.T <= budget_s else int(max(256, budget_s / per_tok))
-    dt = run(nb, tn)
+    dt = run(nb, tn, threads)
+    # one thread, on the first tokens of sequence 0 (about a third of the budget)
+    per_tok1 = run(1, 128, 1) / 128
+    tn1 = int(min(cfg.T, max(128, (budget_s / 3) / per_tok1)))
+    dt1 = run(1, tn1, 1)
     return {"value": nb * tn / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"sequences 0..{nb - 1} of {cfg.B}, tokens 0..{tn - 1} of {cfg.T}, full d and N "
                       f"({nb * tn} of {cfg.B * cfg.T} tokens); {dt:.1f} s wall with {threads} threads "
-                      f"(addressing rows and slot elements split over threads)"}
+                      f"(addressing rows and slot elements split over threads)",
+            "single_thread": {"value": tn1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"sequence 0, tokens 0..{tn1 - 1}, full d and N; {dt1:.1f} s wall"}}
 
 
 def load_traffic(kernel_signature: str, mem_stride: int):
