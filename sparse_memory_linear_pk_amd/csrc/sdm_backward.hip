@@ -293,7 +293,11 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             s_rslot[pos[0]] = rs[0];
             s_rslot[pos[1]] = rs[1];
         }
-        __syncthreads();
+        // a token that reads one of its own write slots (flag bit 1, the same for the whole
+        // workgroup) waits for every wave's read gradients in LDS; the others skip the wait
+        const bool intra = (__builtin_amdgcn_readfirstlane(m.conflict) & 2) != 0;
+        if (intra)
+            __syncthreads();
 
         // the write: a write slot also read by this token takes its gradient after the read
         float gw[2][E], x[2][E], old[2][E];
@@ -304,15 +308,17 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
             // index on lanes that did not match
             int hit = -1;
             const int32_t wsp = ws[p];
+            if (intra) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = el * 8 + u;
-                const int32_t sv = s_rslot[j];
-                hit = ((j < W) & (sv == wsp) & (wsp >= 0)) ? j : hit;
+                for (int u = 0; u < 8; ++u) {
+                    const int j = el * 8 + u;
+                    const int32_t sv = s_rslot[j];
+                    hit = ((j < W) & (sv == wsp) & (wsp >= 0)) ? j : hit;
+                }
+#pragma unroll
+                for (int m = 1; m < 8; m <<= 1)
+                    hit = max(hit, __shfl_xor(hit, m));
             }
-#pragma unroll
-            for (int m = 1; m < 8; m <<= 1)
-                hit = max(hit, __shfl_xor(hit, m));
             if (hit >= 0) {
                 uint4 hv[GU];
 #pragma unroll
@@ -393,15 +399,15 @@ __global__ __launch_bounds__(kWaves * 64) void grad_scan_kernel(GradArgs a)
         __syncthreads(); // token t's stores are visible to the workgroup's loads from here on
         if (threadIdx.x == 0)
             part[2 * W] = (s_al[0] + s_al[1]) + (s_al[2] + s_al[3]);
-        if (t >= 1 && Mt[Y].conflict)
+        if (t >= 1 && (Mt[Y].conflict & 1))
             issue(I[Y], St[Y]);
       });
 }
 
-// flag[row] of token u of memory (b, h): nonzero when a slot token u writes or
-// reads is also written or read by token u + 1 (zero for the last token).  One
-// wave per row: each of token u's slots is broadcast and compared with token
-// u + 1's, two per lane.
+// flag[row] of token u of memory (b, h): bit 0 when a slot token u writes or
+// reads is also written or read by token u + 1 (never for the last token), bit 1
+// when token u reads one of the slots it writes.  One wave per row: each of token
+// u's slots is broadcast and compared with token u + 1's and with u's own.
 __global__ __launch_bounds__(256) void grad_conflict_kernel(const int32_t* idx_w, const int32_t* idx_r,
                                                             int32_t* flag, long R, int T, int H, int W)
 {
@@ -410,23 +416,22 @@ __global__ __launch_bounds__(256) void grad_conflict_kernel(const int32_t* idx_w
     if (row >= R)
         return; // the whole wave
     const int u = (int)((row / H) % T);
-    if (u == T - 1) {
-        if (lane == 0)
-            flag[row] = 0;
-        return;
-    }
-    const long nrow = row + H; // (b, u + 1, h)
+    const bool last = u == T - 1;
+    const long nrow = last ? row : row + H; // (b, u + 1, h)
     const bool live = lane < W;
     const int32_t aw = live ? idx_w[row * W + lane] : -1, ar = live ? idx_r[row * W + lane] : -1;
-    const int32_t nw = live ? idx_w[nrow * W + lane] : -2, nr = live ? idx_r[nrow * W + lane] : -2;
-    bool hit = false;
+    const int32_t nw = live && !last ? idx_w[nrow * W + lane] : -2;
+    const int32_t nr = live && !last ? idx_r[nrow * W + lane] : -2;
+    bool hit = false, own = false;
     for (int k = 0; k < W; ++k) {
         const int32_t x = __shfl(aw, k), y = __shfl(ar, k);
         hit = hit || nw == x || nr == x || nw == y || nr == y;
+        own = own || (live && aw == y);
     }
     const bool any = __builtin_amdgcn_ballot_w64(hit) != 0u;
+    const bool any_own = __builtin_amdgcn_ballot_w64(own) != 0u;
     if (lane == 0)
-        flag[row] = any ? 1 : 0;
+        flag[row] = (any ? 1 : 0) | (any_own ? 2 : 0);
 }
 
 constexpr int kRowsPerBlock = 4;
