@@ -532,7 +532,10 @@ def main():
 
     d = {k: dev(v) for k, v in x.items()}
     ms = state_rows(args, cfg)
-    d["mem0"] = with_rows(d["mem0"], ms)
+    dense_mem = d["mem0"]
+    d["mem0"] = with_rows(dense_mem, ms)
+    if ms == cfg.d:
+        dense_mem = None
     out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), dtype=torch.float32, device="cuda")
     layer = SDM.from_config(cfg, mem_stride=ms)
 
@@ -554,6 +557,23 @@ def main():
     tm = layer.timing()
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
+
+    # The same forwards on dense slot rows (d elements apart), for comparison with the
+    # padded layout the headline uses.
+    dense = None
+    if dense_mem is not None:
+        with SDM.from_config(cfg) as dl:
+            dn = min(args.steps, 10)
+            dl.forward(d["wq"], d["rq"], d["v"], d["alpha"], d["beta"], d["subkeys"], dense_mem, out)
+            torch.cuda.synchronize()
+            t2 = time.perf_counter()
+            for _ in range(dn):
+                dl.forward(d["wq"], d["rq"], d["v"], d["alpha"], d["beta"], d["subkeys"], dense_mem, out)
+            torch.cuda.synchronize()
+            dsec = time.perf_counter() - t2
+        dense = {"value": cfg.B * cfg.T * dn / dsec, "unit": "tokens/s", "ms_per_step": dsec * 1e3 / dn, "steps": dn,
+                 "what": "the same forward with the memory's slot rows dense (d elements apart)"}
+        del dense_mem
 
     # Sub-key scoring on its own (in the forward it shares the GPU with the scan):
     # both query sets through the scoring seam, timed the same way.
@@ -644,6 +664,8 @@ def main():
                              "shares the GPU with the scan, so kernels_ms_per_step shows it longer"},
         "kernel_signature": sig,
     }
+    if dense is not None:
+        res["dense_rows"] = dense
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
