@@ -144,7 +144,15 @@ __global__ __launch_bounds__(256) void sdm_scan_staged_kernel(ScanArgs a)
     const int T = a.T, H = a.H, d = a.d;
     const uint32_t N = (uint32_t)a.N;
     const int nchunk = d / SEG;
-    const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    // Workgroups go to the 8 XCDs in turn (blockIdx mod 8).  Narrow segments share a
+    // 128-byte line with their neighbours: each XCD then takes a contiguous run of
+    // segments, so that the workgroups reading one line share one L2.
+    int lin = blockIdx.x;
+    if constexpr (SEGB < 128) {
+        if (gridDim.x % 8 == 0)
+            lin = (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8);
+    }
+    const int bh = lin / nchunk, chunk = lin % nchunk;
     const int b = bh / H;
     const uint32_t row_bytes = (uint32_t)d * (uint32_t)sizeof(ST);      // a log row
     const uint32_t mem_row = (uint32_t)a.ms * (uint32_t)sizeof(ST);     // slot row to slot row in memory
