@@ -145,6 +145,9 @@ EDGES = {
     "W64_k64": _edge(S=64, k=64, W=64, T=10, d=16),
     "mixed_state_f32_in_bf16": _edge(in_bf16=True, state_bf16=False, T=12),
     "mixed_state_bf16_in_f32": _edge(in_bf16=False, state_bf16=True, d=32, T=12),
+    # 32-byte segments, 4 per memory, 24 workgroups: renumbered into 8 runs of 3, so the runs cross from
+    # one memory to the next (T13_bf16, 4 workgroups, keeps the plain numbering)
+    "bf16_segments_runs_cross_memories": _edge(B=3, H=2, d=64, T=19, in_bf16=True, state_bf16=True),
 }
 
 
