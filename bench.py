@@ -491,7 +491,7 @@ def main():
                     help="run only a plain 4 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 

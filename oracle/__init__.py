@@ -281,7 +281,7 @@ class GradOracle:
         self.L = L
 
     def scan_forward(self, cfg, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem):
-        """The forward scan of this build's own copy of the forward oracle (mem updated in place,
+        """The forward scan of this library's own copy of the forward oracle (mem updated in place,
         any state kind including float64).  Returns out [B,T,H,d] f32."""
         cs = _cfg_struct(cfg)
         arrs = [np.ascontiguousarray(a) for a in (idx_w, wt_w, idx_r, wt_r, v, alpha, beta)]
