@@ -155,6 +155,7 @@ struct sdm_ctx {
     hipStream_t stream;  // the caller's: scans run here
     hipStream_t aux;     // addressing and plans of a chunked forward (default priority)
     hipEvent_t e_start;  // the caller's stream reached the forward
+    hipEvent_t e_read;   // the first chunk's read set is selected (on the caller's stream)
     std::vector<hipEvent_t> e_plan; // chunk c's plan is written
     int device;
     Chunking ck;
@@ -401,6 +402,7 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->L = layout_of(*cfg, h->ck, plans);
     h->aux = nullptr;
     h->e_start = nullptr;
+    h->e_read = nullptr;
     h->timing = false;
     h->bwd_block = nullptr;
     h->part = h->ds = h->sub_part = h->sink = nullptr;
@@ -429,6 +431,8 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
         e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
         if (e == hipSuccess)
             e = hipEventCreateWithFlags(&h->e_start, hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&h->e_read, hipEventDisableTiming);
         h->e_plan.assign(h->ck.C(), nullptr);
         for (int ci = 0; ci < h->ck.C() && e == hipSuccess; ++ci)
             e = hipEventCreateWithFlags(&h->e_plan[ci], hipEventDisableTiming);
@@ -438,6 +442,8 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
                     (void)hipEventDestroy(ev);
             if (h->e_start)
                 (void)hipEventDestroy(h->e_start);
+            if (h->e_read)
+                (void)hipEventDestroy(h->e_read);
             if (h->aux)
                 (void)hipStreamDestroy(h->aux);
             (void)hipFree(h->block);
@@ -462,6 +468,7 @@ sdm_status sdm_destroy(sdm_handle h)
         for (hipEvent_t ev : h->e_plan)
             (void)hipEventDestroy(ev);
         (void)hipEventDestroy(h->e_start);
+        (void)hipEventDestroy(h->e_read);
         (void)hipStreamDestroy(h->aux);
     }
     for (auto& tl : h->pending) {
@@ -571,14 +578,43 @@ sdm_status forward_impl(sdm_ctx* h, const void* wq, const void* rq, const void* 
     // order, after whatever the caller's stream holds before this call (its
     // inputs, and earlier calls' scans of the plans about to be rewritten); the
     // scan of chunk c waits for its plan on the caller's stream, so chunk c + 1's
-    // addressing runs while chunk c scans.
-    hipError_t e = hipEventRecord(h->e_start, h->stream);
+    // addressing runs while chunk c scans.  The first chunk, whose preparation
+    // nothing hides, has its read set scored and selected on the caller's stream
+    // beside the write set on aux.  Score rows are indexed by token, so the read
+    // set's scores go one first-chunk length further on, into rows of the second
+    // chunk (every chunk after the first is at least as long), which aux scores
+    // only after the first plan, and that plan waits for the read set.
+    const sdm_config& c = h->cfg;
+    const sdm::Rows r0 = chunk_rows(h, 0);
+    hipError_t e = hipSuccess;
+    if (c.in_dtype == SDM_BF16) {
+        Timer t(h, K_SCORE, h->stream);
+        e = sdm::launch_pk_subkey_frag(subkeys, h->frag, c.H, c.n_sub, c.dk / 2, h->stream);
+    }
+    if (e == hipSuccess)
+        e = hipEventRecord(h->e_start, h->stream);
     if (e == hipSuccess)
         e = hipStreamWaitEvent(h->aux, h->e_start, 0);
     if (e != hipSuccess)
         return hip_fail(e, "stream ordering");
+    float* scores_r0 = h->scores + (size_t)h->ck.len(0) * c.H * 2 * c.n_sub;
+    s = run_score(h, wq, subkeys, h->scores, r0, h->aux, false);
+    if (s == SDM_OK)
+        s = run_select(h, h->scores, h->idx[0], h->wt[0], r0, h->aux);
+    if (s == SDM_OK)
+        s = run_score(h, rq, subkeys, scores_r0, r0, h->stream, false);
+    if (s == SDM_OK)
+        s = run_select(h, scores_r0, h->idx[1], h->wt[1], r0, h->stream);
+    if (s != SDM_OK)
+        return s;
+    e = hipEventRecord(h->e_read, h->stream);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(h->aux, h->e_read, 0);
+    if (e != hipSuccess)
+        return hip_fail(e, "stream ordering");
     for (int ci = 0; ci < h->ck.C(); ++ci) {
-        s = run_chunk_front(h, ci, wq, rq, alpha, beta, subkeys, h->aux);
+        s = ci == 0 ? run_plan(h, 0, h->idx[0], h->wt[0], h->idx[1], h->wt[1], alpha, beta, h->aux)
+                    : run_chunk_front(h, ci, wq, rq, alpha, beta, subkeys, h->aux);
         if (s != SDM_OK)
             return s;
         e = hipEventRecord(h->e_plan[ci], h->aux);
