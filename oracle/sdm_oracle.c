@@ -265,9 +265,10 @@ int oracle_address(const oracle_cfg* c, const void* q, const void* subkeys, long
  *   M[n_i] = store(x_i + w_i * delta)  delta-rule write
  *   out   = sum_j r_j M[m_j]           read of the stored values, after the write
  * This is the gated delta rule with the key taken as the sparse weight vector
- * and the decay confined to the selected slots ("first decayed, then written
- * with the delta rule", section "How does SDM work?"; "decay, then delta v",
- * figure caption).  Slots not selected are left as they are. */
+ * and the decay confined to the selected slots: the SDM blog post's section
+ * "How does SDM work?" and the caption of its figure "The SDM mechanism, end
+ * to end" order the write as a decay of the chosen slots followed by a
+ * delta-rule update toward v.  Slots not selected are left as they are. */
 int oracle_scan(const oracle_cfg* c, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
                 const float* wt_r, const void* v, const float* alpha, const float* beta, void* mem,
                 float* out, int b, int h, int e0, int e1)

@@ -24,8 +24,8 @@ Layouts (row-major, innermost last):
   subkeys  [H, 2, S, dk/2] in_dtype
   mem0     [B, H, N, d]    state dtype, N = S*S, slot-major
 """
-from .gen import (CONFIGS, Config, config, make_inputs, make_mem0, make_upstream_grads, make_projection_inputs, bf16_bits_from_f32,
+from .gen import (CONFIGS, Config, config, make_inputs, make_mem0, make_mem0_seqs, make_upstream_grads, make_projection_inputs, bf16_bits_from_f32,
                   f32_from_bf16_bits, normal_f32)
 
-__all__ = ["CONFIGS", "Config", "config", "make_inputs", "make_mem0", "make_upstream_grads", "make_projection_inputs", "bf16_bits_from_f32",
+__all__ = ["CONFIGS", "Config", "config", "make_inputs", "make_mem0", "make_mem0_seqs", "make_upstream_grads", "make_projection_inputs", "bf16_bits_from_f32",
            "f32_from_bf16_bits", "normal_f32"]

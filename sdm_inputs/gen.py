@@ -174,6 +174,32 @@ def make_mem0(cfg: Config, seed: int = 0, threads=None) -> np.ndarray:
     return out.reshape(shape)
 
 
+def make_mem0_seqs(cfg: Config, b0: int, b1: int, seed: int = 0, threads=None) -> np.ndarray:
+    """Sequences b0 .. b1-1 of make_mem0(cfg, seed), [b1-b0, H, N, d], bit for bit, without
+    drawing the others (the seeded chunks that cover them are drawn, each from its start)."""
+    shape = (b1 - b0, cfg.H, cfg.N, cfg.d)
+    per_seq = cfg.H * cfg.N * cfg.d
+    dtype = np.uint16 if cfg.state_bf16 else np.float32
+    if cfg.m0_std == 0.0:
+        return np.zeros(shape, dtype)
+    lo, hi = b0 * per_seq, b1 * per_seq
+    out = np.empty(hi - lo, dtype)
+    c0, c1 = lo // CHUNK, (hi - 1) // CHUNK
+    std = np.float32(cfg.m0_std)
+
+    def fill(c):
+        a, b = max(lo, c * CHUNK), min(hi, (c + 1) * CHUNK)
+        x = np.empty(b - c * CHUNK, np.float32)
+        _gen(seed, _MEM0, c).standard_normal(out=x, dtype=np.float32)
+        x = x[a - c * CHUNK:]
+        x *= std
+        out[a - lo:b - lo] = bf16_bits_from_f32(x) if cfg.state_bf16 else x
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        list(ex.map(fill, range(c0, c1 + 1)))
+    return out.reshape(shape)
+
+
 def make_inputs(cfg: Config, seed: int = 0, threads=None, with_mem0: bool = True) -> dict:
     """All layer inputs for one configuration, as numpy arrays (see package docstring)."""
     wq, rq = _queries(cfg, seed, threads)

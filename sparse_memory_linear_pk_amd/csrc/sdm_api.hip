@@ -69,7 +69,7 @@ Chunking chunking_of(const sdm_config& c)
 }
 
 struct Layout {
-    size_t scores, idx, wt, plan, frag, total;
+    size_t scores, idx, wt, plan, frag, step, total;
     std::vector<size_t> plan_off; // byte offset of each chunk's plan
 };
 
@@ -86,7 +86,10 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
         L.plan += align_up(sdm::plan_bytes(plans[ci], c.B, c.H, k.len(ci), c.W));
     }
     L.frag = align_up(sdm::pk_score_frag_bytes(c.H, c.n_sub, c.dk / 2));
-    L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag;
+    // sdm_step's slot ids and weights, write then read set: 2*B*H*W of each,
+    // apart from the forward's buffers (which hold B*T*H*W and T may be 1)
+    L.step = align_up(2 * (size_t)c.B * c.H * c.W * sizeof(int32_t));
+    L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag + 2 * L.step;
     return L;
 }
 
@@ -167,6 +170,8 @@ struct sdm_ctx {
     float* wt[2];
     uint4* plan_buf;
     void* frag;
+    int32_t* step_idx;   // [2][B*H][W] (sdm_step)
+    float* step_wt;      // [2][B*H][W]
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
@@ -411,9 +416,10 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     memset(&h->totals, 0, sizeof h->totals);
     e = hipMalloc(&h->block, h->L.total);
     if (e != hipSuccess) {
+        const size_t total = h->L.total;
         delete h;
         (void)hipGetLastError();
-        return fail(SDM_ERR_OOM, "workspace of %zu bytes: %s", h->L.total, hipGetErrorString(e));
+        return fail(SDM_ERR_OOM, "workspace of %zu bytes: %s", total, hipGetErrorString(e));
     }
     char* p = (char*)h->block;
     h->scores = (float*)p;
@@ -427,6 +433,10 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->plan_buf = (uint4*)p;
     p += h->L.plan;
     h->frag = p;
+    p += h->L.frag;
+    h->step_idx = (int32_t*)p;
+    p += h->L.step;
+    h->step_wt = (float*)p;
     if (h->ck.C() > 1) {
         e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
         if (e == hipSuccess)
@@ -647,10 +657,10 @@ sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v,
     const sdm_config& c = h->cfg;
     if (!sdm::step_supported(c.d, c.state_dtype == SDM_BF16))
         return fail(SDM_ERR_UNSUPPORTED, "sdm_step: d=%d: a slot row must be a multiple of 128 bytes", c.d);
-    // the slot ids and weights of both query sets go to the first 2*B*H*W
-    // entries of the forward's addressing workspace
+    // the slot ids and weights of both query sets (two-launch path) go to the
+    // step's own 2*B*H*W entries of the workspace
     Timer t(h, K_STEP, h->stream);
-    hipError_t e = sdm::launch_sdm_step(wq, rq, v, alpha, beta, subkeys, mem_inout, out, h->idx[0], h->wt[0], c.B,
+    hipError_t e = sdm::launch_sdm_step(wq, rq, v, alpha, beta, subkeys, mem_inout, out, h->step_idx, h->step_wt, c.B,
                                         c.H, c.d, mem_stride_of(c), c.n_sub, c.dk / 2, c.k, c.W, c.in_dtype == SDM_BF16,
                                         c.state_dtype == SDM_BF16, h->stream);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_step launch");

@@ -467,6 +467,70 @@ def pin_planted_query(o):
     assert np.array_equal(iw, ir) and np.array_equal(ww, wr) and np.array_equal(sw, sr)
 
 
+def pin_address_from_scores(o):
+    """Selection from given scores, row by row: against candidate enumeration and
+    a float64 softmax written here (indices exact, weights within one float32
+    unit), on rows with ties planted, and bit for bit against the oracle's own
+    addressing from queries when handed the oracle's scores of those queries.
+    The staged GPU checks lean on this routine; it must address every row."""
+    cfg = _cfg(B=3, H=2, T=7, d=4, S=13, dk=8, k=4, W=10)
+    R = cfg.B * cfg.T * cfg.H
+    rng = np.random.default_rng(91)
+    sc = rng.standard_normal((R, 2, cfg.S)).astype(F32)
+    sc[3, 0, 5] = sc[3, 0, 9]                        # a tie inside one half
+    sc[7, 1] = np.round(sc[7, 1] * 2) / 2            # quantised half: many ties
+    sc[11] = 0.25                                    # every score equal
+    sc[12, 0, 2], sc[12, 1, 0] = 1.5, 1.0            # two pairs with the same sum
+    sc[12, 0, 3], sc[12, 1, 4] = 1.0, 1.5
+    idx, wt, sig = o.address_from_scores(cfg, sc, threads=3)
+    for r in range(R):
+        n, s = brute_select_candidates(sc[r, 0], sc[r, 1], cfg.k, cfg.W)
+        assert np.array_equal(idx[r], n), f"row {r}: slots {idx[r]} != {n}"
+        assert np.array_equal(sig[r], s), f"row {r}: sums differ"
+        u = np.abs(wt[r].view(np.int32).astype(np.int64) - softmax_f32(s).view(np.int32).astype(np.int64))
+        assert u.max() <= 1, f"row {r}: weights differ by {u.max()} units"
+    x = _rand_inputs(cfg, 92)
+    for q in (x["wq"], x["rq"]):
+        ai, aw, asg = o.address(cfg, q, x["subkeys"], threads=1)
+        fi, fw, fsg = o.address_from_scores(cfg, o.scores(cfg, q, x["subkeys"], threads=1), threads=1)
+        assert np.array_equal(ai, fi) and np.array_equal(aw.view(np.uint32), fw.view(np.uint32))
+        assert np.array_equal(asg.view(np.uint32), fsg.view(np.uint32))
+
+
+def pin_threads_bitwise(o):
+    """The driver's split of the work over threads changes no bit: row spans of
+    the scores and addressing, and the scan's slot-element slices (the element
+    offset inside the C scan), against one thread over everything; the scores
+    also against float64 dot products written here."""
+    cfg = _cfg(B=2, H=2, T=23, d=37, S=9, dk=6, k=3, W=7)
+    x = _rand_inputs(cfg, 93)
+    R = cfg.B * cfg.T * cfg.H
+    s1 = o.scores(cfg, x["wq"], x["subkeys"], threads=1)
+    s16 = o.scores(cfg, x["wq"], x["subkeys"], threads=16)
+    assert np.array_equal(s1.view(np.uint32), s16.view(np.uint32))
+    assert np.array_equal(s16, np_scores(cfg, x["wq"], x["subkeys"]))
+    a1 = o.address(cfg, x["wq"], x["subkeys"], threads=1)
+    a16 = o.address(cfg, x["wq"], x["subkeys"], threads=16)
+    f16 = o.address_from_scores(cfg, s16, threads=16)
+    sub = o.address(cfg, x["wq"], x["subkeys"], rows=np.arange(R)[::-1], threads=16)
+    for u, w in zip(a1, a16):
+        assert np.array_equal(u.view(np.uint32), w.view(np.uint32))
+    for u, w in zip(a1, f16):
+        assert np.array_equal(u.view(np.uint32), w.view(np.uint32))
+    for u, w in zip(a1, sub):
+        assert np.array_equal(u[::-1].view(np.uint32), w.view(np.uint32))
+    ar = o.address(cfg, x["rq"], x["subkeys"], threads=1)
+    runs = []
+    for threads, e_split in ((1, 1), (16, None), (16, 5), (4, cfg.d)):
+        mem = x["mem0"].copy()
+        out = o.scan(cfg, a1[0], a1[1], ar[0], ar[1], x["v"], x["alpha"], x["beta"], mem, threads=threads,
+                     e_split=e_split)
+        runs.append((out, mem))
+    for out, mem in runs[1:]:
+        assert np.array_equal(out.view(np.uint32), runs[0][0].view(np.uint32))
+        assert np.array_equal(mem.view(np.uint32), runs[0][1].view(np.uint32))
+
+
 PINS = [
     pin_bf16_bits,
     pin_worked_example,
@@ -483,4 +547,6 @@ PINS = [
     pin_permute_d,
     pin_power_of_two_scaling,
     pin_planted_query,
+    pin_address_from_scores,
+    pin_threads_bitwise,
 ]

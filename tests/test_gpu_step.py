@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import sdm_inputs as gi
-from parity import compare_index_sets, rel_max_err, scan_tol, to_dev, to_host
+from parity import check_scan, compare_index_sets, plain_err, rel_max_err, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -99,9 +99,8 @@ def test_steps_match_the_oracle(name):
             say(f"[step oracle {name}] {s_}: rows differing {differ} (excused {exc})")
     mem = x["mem0"].copy()
     out = orc.scan(cfg, addr["w"][0], addr["w"][1], addr["r"][0], addr["r"][1], x["v"], x["alpha"], x["beta"], mem)
-    eo, em = rel_max_err(out_s, out), rel_max_err(mem_s, mem)
-    say(f"[step oracle {name}] out {eo:.3g}, mem {em:.3g} (tol {scan_tol(cfg)})")
-    assert eo <= scan_tol(cfg) and em <= scan_tol(cfg)
+    check_scan(cfg, 4, f"step oracle {name}", {"out": (plain_err(out_s, out), rel_max_err(out_s, out)),
+                                                "mem": (plain_err(mem_s, mem), rel_max_err(mem_s, mem))}, say)
 
 
 def test_step_rejects_an_unsupported_width():
@@ -113,3 +112,29 @@ def test_step_rejects_an_unsupported_width():
         with pytest.raises(SDMError):
             layer.step(z(1, 1, 32), z(1, 1, 32), z(1, 1, 24), z(1, 1), z(1, 1), z(1, 2, 16, 16),
                        z(1, 1, 256, 24), z(1, 1, 24))
+
+
+def test_steps_on_a_one_token_handle_equal_forward_bitwise():
+    """A handle made with T = 1 (the natural one for decode), float32 queries
+    (the two-launch path, whose addressing passes 2*B*H*W slot ids and weights
+    through the workspace) and B*H*W a multiple of 64: the step's ids and weights
+    must not share memory, however few rows the forward's buffers hold."""
+    import torch
+    from sparse_memory_linear_pk_amd import SDM
+    cfg = _edge(T=6, B=2, H=2, d=64, S=64, k=8, W=64)
+    x = gi.make_inputs(cfg)
+    dev = {k: to_dev(v) for k, v in x.items()}
+    with SDM.from_config(cfg) as layer:
+        mem_f = dev["mem0"].clone()
+        out_f = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), dtype=torch.float32, device="cuda")
+        layer.forward(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem_f, out_f)
+        torch.cuda.synchronize()
+    with SDM.from_config(cfg, T=1) as layer:
+        mem_s = dev["mem0"].clone()
+        o = torch.empty((cfg.B, cfg.H, cfg.d), dtype=torch.float32, device="cuda")
+        for t in range(cfg.T):
+            tok = {k: dev[k][:, t].contiguous() for k in ("wq", "rq", "v", "alpha", "beta")}
+            layer.step(tok["wq"], tok["rq"], tok["v"], tok["alpha"], tok["beta"], dev["subkeys"], mem_s, o)
+            torch.cuda.synchronize()
+            assert torch.equal(o, out_f[:, t]), f"token {t}: step output differs from the forward"
+    assert torch.equal(mem_s, mem_f)

@@ -79,3 +79,15 @@ def test_bf16_conversion():
     x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -2.5, np.inf, 0.0], np.float32)
     assert gi.bf16_bits_from_f32(x).tolist() == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x7F80, 0x0000]
     assert gi.f32_from_bf16_bits(np.array([0x3F80, 0xC020], np.uint16)).tolist() == [1.0, -2.5]
+
+
+def test_initial_memory_by_sequence_equals_the_whole():
+    """make_mem0_seqs draws the same bits as make_mem0 for any sequence range,
+    also where a sequence starts or ends inside a seeded chunk."""
+    for cfg in (gi.config(1, T=8, B=5, H=3, S=100, d=72),                      # float32, ragged chunks
+                gi.config(4, T=8, B=3, S=90, d=3840 // 8),                     # bf16
+                gi.config(0, T=8, B=3)):                                       # zero memory
+        whole = gi.make_mem0(cfg)
+        for b0, b1 in ((0, 1), (1, 3), (2, cfg.B), (0, cfg.B)):
+            part = gi.make_mem0_seqs(cfg, b0, b1, threads=3)
+            assert part.dtype == whole.dtype and np.array_equal(part, whole[b0:b1]), (cfg.name, b0, b1)

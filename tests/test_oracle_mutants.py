@@ -38,6 +38,15 @@ MUTANTS = {
     "state_rounding_skipped": ("((float*)mem)[i] = (float)x;", "((float*)mem)[i] = (float)(x + x * 0x1p-20);"),
     "score_rounded_twice": ("acc += qj * kj;", "acc = (float)(acc + qj * kj);"),
     "head_ignored_in_subkeys": ("int h = (int)(r % c->H);\n        for (int half", "int h = 0;\n        for (int half"),
+    # selection from given scores: the second half read from the first half's row
+    "scores_second_half_misplaced": ("const float* s2 = scores + (o * 2 + 1) * S;",
+                                     "const float* s2 = scores + (o * 2 + 0) * S;"),
+    # selection from given scores: a row's output written at the previous row's place
+    "scores_rows_shifted": ("oracle_select(s1, s2, S, c->k, W, idx + o * W, sig)",
+                            "oracle_select(s1, s2, S, c->k, W, idx + (o ? o - 1 : o) * W, sig)"),
+    # the scan's element slice: v read from the slice's first element instead of its own
+    "scan_slice_offset_dropped_for_v": ("(load_in(v, r * d + e0 + e, c->in_bf16) - vhat)",
+                                        "(load_in(v, r * d + e, c->in_bf16) - vhat)"),
 }
 
 
