@@ -71,7 +71,11 @@ def cpu_baseline(cfg, x, budget_s: float):
     per_tok1 = run(1, 128, 1) / 128
     tn1 = int(min(cfg.T, max(128, (budget_s / 3) / per_tok1)))
     dt1 = run(1, tn1, 1)
+    visible = len(os.sched_getaffinity(0))
     return {"value": nb * tn / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpus_visible": visible,
+            "threads_note": f"{threads} threads: the oracle driver uses min(16, visible CPUs), 16 being the host "
+                            f"CPU share of one GPU on this machine ({visible} visible)",
             "sample": f"sequences 0..{nb - 1} of {cfg.B}, tokens 0..{tn - 1} of {cfg.T}, full d and N "
                       f"({nb * tn} of {cfg.B * cfg.T} tokens); {dt:.1f} s wall with {threads} threads "
                       f"(addressing rows and slot elements split over threads)",
@@ -536,6 +540,23 @@ def main():
     d["mem0"] = with_rows(dense_mem, ms)
     if ms == cfg.d:
         dense_mem = None
+    else:
+        # the benchmarked layout against dense rows, bit for bit, on one forward from the same memory
+        # (the full-size parity tests compare both with the oracle)
+        log("checking the padded layout against dense rows on one forward")
+        mem_p, mem_d = with_rows(dense_mem, ms), dense_mem.clone()
+        out_p, out_d = (torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), dtype=torch.float32, device="cuda")
+                        for _ in range(2))
+        with SDM.from_config(cfg, mem_stride=ms) as pl, SDM.from_config(cfg) as dl:
+            pl.forward(d["wq"], d["rq"], d["v"], d["alpha"], d["beta"], d["subkeys"], mem_p, out_p)
+            dl.forward(d["wq"], d["rq"], d["v"], d["alpha"], d["beta"], d["subkeys"], mem_d, out_d)
+            torch.cuda.synchronize()
+        ity = torch.int16 if cfg.state_bf16 else torch.int32
+        padded_equals_dense = bool(torch.equal(out_p.view(torch.int32), out_d.view(torch.int32))) and all(
+            bool(torch.equal(mem_p[b].contiguous().view(ity), mem_d[b].view(ity))) for b in range(cfg.B))
+        del mem_p, mem_d, out_p, out_d
+        if not padded_equals_dense:
+            raise RuntimeError("the padded layout's forward differs from the dense one")
     out = torch.empty((cfg.B, cfg.T, cfg.H, cfg.d), dtype=torch.float32, device="cuda")
     layer = SDM.from_config(cfg, mem_stride=ms)
 
@@ -665,6 +686,7 @@ def main():
         "kernel_signature": sig,
     }
     if dense is not None:
+        dense["bitwise_equal_to_padded"] = padded_equals_dense
         res["dense_rows"] = dense
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")

@@ -12,8 +12,11 @@ Addressing never reads the memory, so parity splits into exact stages:
   4. scan: the oracle's scan driven by the GPU's own indices and weights against
      the GPU's out and final memory: max |got - ref| / RMS(ref) <= tol, each
      tensor with its own RMS, tol = 1e-4 (float32 state) or 2e-2 (bf16 state);
-  5. end-to-end, when stage 3 excused no row: the GPU forward against the
-     oracle's forward (its own addressing).  The same plain figure for a
+  5. end-to-end: the GPU forward against the oracle's scan on the oracle's own
+     addressing, where a row that stage 3 excused takes the GPU's slots
+     weighted by the oracle's sums for them (resolve_near_ties: either choice
+     is correct there, and the scan cannot compare two different slot sets
+     element by element).  The same plain figure for a
      float32 state.  With a bf16 state the two sides' weights differ in their
      last float32 bits (float32 MFMA scores against double ones), which moves
      some stored values across a bf16 rounding boundary: one bf16 unit of a
@@ -146,6 +149,28 @@ def compare_index_sets(o, cfg, gpu_idx, ref_idx, ref_sig, ref_scores, rows=None)
     return differ, excused
 
 
+def differing_rows(gpu_idx, ref_idx) -> np.ndarray:
+    """Rows whose slot sets differ."""
+    return np.nonzero(~np.all(np.sort(gpu_idx, axis=1) == np.sort(ref_idx, axis=1), axis=1))[0]
+
+
+def resolve_near_ties(o, cfg, gpu_idx, ref_idx, ref_wt, ref_scores):
+    """The oracle's addressing, except that rows which chose differently across a
+    near-tie (stage 3 excused them) take the GPU's slots, weighted by a softmax
+    of the oracle's own sums for those slots: an end-to-end reference that
+    agrees with the GPU wherever the pages leave the choice open.  Returns
+    (idx, wt, number of rows taken from the GPU)."""
+    idx, wt = ref_idx.copy(), ref_wt.copy()
+    rows = differing_rows(gpu_idx, ref_idx)
+    S = cfg.S
+    for j in rows:
+        a, b = np.divmod(gpu_idx[j].astype(np.int64), S)
+        sig = (ref_scores[j, 0, a].astype(F32) + ref_scores[j, 1, b].astype(F32)).astype(F32)
+        idx[j] = gpu_idx[j]
+        wt[j] = o.softmax(sig)
+    return idx, wt, rows.size
+
+
 def _band(sorted_vals, k):
     """Score band around the k-th / (k+1)-th boundary, or None when the gap is wide."""
     if k >= sorted_vals.size:
@@ -189,14 +214,21 @@ class PlainAccum:
         self.maxabs, self.sumsq, self.n = 0.0, 0.0, 0
         self.rel = 0.0  # per-element figure of the parts (RMS floor per part)
 
-    def add(self, got: np.ndarray, ref: np.ndarray):
-        got = as_f32(got).astype(np.float64)
-        ref = as_f32(ref).astype(np.float64)
-        self.maxabs = max(self.maxabs, float(np.max(np.abs(got - ref))) if got.size else 0.0)
-        self.sumsq += float(np.sum(ref * ref))
-        self.n += ref.size
-        rms = max(np.sqrt(np.mean(ref ** 2)), 1e-30) if ref.size else 1.0
-        self.rel = max(self.rel, float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms))) if got.size else 0.0)
+    def add(self, got: np.ndarray, ref: np.ndarray, block: int = 1 << 24):
+        """Adds one part, in flat blocks of `block` elements (a full-size memory is billions of them)."""
+        g, r = got.reshape(-1), ref.reshape(-1)
+        n = r.size
+        rms_part = np.sqrt(sum(float(np.sum(as_f32(r[i:i + block]).astype(np.float64) ** 2))
+                               for i in range(0, n, block)) / max(n, 1))
+        rms_part = max(rms_part, 1e-30)
+        for i in range(0, n, block):
+            gb = as_f32(g[i:i + block]).astype(np.float64)
+            rb = as_f32(r[i:i + block]).astype(np.float64)
+            diff = np.abs(gb - rb)
+            self.maxabs = max(self.maxabs, float(diff.max()))
+            self.sumsq += float(np.sum(rb * rb))
+            self.rel = max(self.rel, float(np.max(diff / np.maximum(np.abs(rb), rms_part))))
+        self.n += n
 
     def value(self) -> float:
         return self.maxabs / max(np.sqrt(self.sumsq / max(self.n, 1)), 1e-30)

@@ -15,7 +15,7 @@ import pytest
 import oracle
 import sdm_inputs as gi
 from parity import (PlainAccum, check_scan, check_scores, check_selection_exact, compare_index_sets, plain_err,
-                    rel_max_err, score_error_bound, to_dev, to_host)
+                    rel_max_err, resolve_near_ties, score_error_bound, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,22 +85,22 @@ def full_parity(orc, cfg, x, g, label):
         ui, uw, _ = orc.address_from_scores(cfg, g[f"scores_{s}"])
         ulp = check_selection_exact(g[f"idx_{s}"], g[f"wt_{s}"], ui, uw)
         ri, rw, rs = orc.address(cfg, q, x["subkeys"])
-        ref_addr[s] = (ri, rw)
         differ, exc = compare_index_sets(orc, cfg, g[f"idx_{s}"], ri, rs, ref_scores)
+        ri, rw, taken = resolve_near_ties(orc, cfg, g[f"idx_{s}"], ri, rw, ref_scores)
+        ref_addr[s] = (ri, rw)
         excused_rows += exc
         say(f"[{label}] {s}: score err {err:.3g}, weight ulp {ulp}, rows differing {differ} (excused {exc})")
     mem = x["mem0"].copy()
     out = orc.scan(cfg, g["idx_w"], g["wt_w"], g["idx_r"], g["wt_r"], x["v"], x["alpha"], x["beta"], mem)
     check_scan(cfg, 4, label, {"out": (plain_err(g["out"], out), rel_max_err(g["out"], out)),
                                "mem": (plain_err(g["mem"], mem), rel_max_err(g["mem"], mem))}, say)
-    if excused_rows == 0:
-        mem = x["mem0"].copy()
-        out = orc.scan(cfg, ref_addr["w"][0], ref_addr["w"][1], ref_addr["r"][0], ref_addr["r"][1], x["v"],
-                       x["alpha"], x["beta"], mem)
-        check_scan(cfg, 5, label, {"out": (plain_err(g["out"], out), rel_max_err(g["out"], out)),
-                                   "mem": (plain_err(g["mem"], mem), rel_max_err(g["mem"], mem))}, say)
-    else:
-        say(f"[{label}] stage 5 not run: {excused_rows} rows chose differently across a near-tie")
+    mem = x["mem0"].copy()
+    out = orc.scan(cfg, ref_addr["w"][0], ref_addr["w"][1], ref_addr["r"][0], ref_addr["r"][1], x["v"],
+                   x["alpha"], x["beta"], mem)
+    if excused_rows:
+        say(f"[{label}] stage 5: {excused_rows} near-tie rows take the GPU's slots, weighted by the oracle's sums")
+    check_scan(cfg, 5, label, {"out": (plain_err(g["out"], out), rel_max_err(g["out"], out)),
+                               "mem": (plain_err(g["mem"], mem), rel_max_err(g["mem"], mem))}, say)
     return excused_rows
 
 
@@ -342,8 +342,9 @@ def full_size_parity(orc, T, cfg, label, padded=False):
         ulp = check_selection_exact(g[f"idx_{s_}"], g[f"wt_{s_}"], ui, uw)
         del ui, uw
         ri, rw, rs = orc.address_from_scores(cfg, ref_scores)
-        ref_addr[s_] = (ri, rw)
         differ, exc = compare_index_sets(orc, cfg, g[f"idx_{s_}"], ri, rs, ref_scores)
+        ri, rw, _ = resolve_near_ties(orc, cfg, g[f"idx_{s_}"], ri, rw, ref_scores)
+        ref_addr[s_] = (ri, rw)
         excused_rows += exc
         say(f"[{label}] {s_}: score err {err:.3g}, weight ulp {ulp}, rows differing {differ} (excused {exc}) "
             f"of {R}")
@@ -351,7 +352,8 @@ def full_size_parity(orc, T, cfg, label, padded=False):
 
     # stages 4 and 5, sequence by sequence
     acc = {k: PlainAccum() for k in ("out4", "mem4", "out5", "mem5")}
-    stage5 = excused_rows == 0
+    if excused_rows:
+        say(f"[{label}] stage 5: {excused_rows} near-tie rows take the GPU's slots, weighted by the oracle's sums")
     c1 = cfg.replace(B=1)
     per = cfg.T * cfg.H
     for b in range(cfg.B):
@@ -364,22 +366,18 @@ def full_size_parity(orc, T, cfg, label, padded=False):
                       xb["alpha"], xb["beta"], m)
         acc["out4"].add(g_out[b:b + 1], o4)
         acc["mem4"].add(gm, m)
-        if stage5:
-            m = m0
-            o5 = orc.scan(c1, ref_addr["w"][0][rows], ref_addr["w"][1][rows], ref_addr["r"][0][rows],
-                          ref_addr["r"][1][rows], xb["v"], xb["alpha"], xb["beta"], m)
-            acc["out5"].add(g_out[b:b + 1], o5)
-            acc["mem5"].add(gm, m)
-        say(f"[{label}] sequence {b}: out max/RMS {acc['out4'].value():.3g}, memory {acc['mem4'].value():.3g} "
-            f"(stage 4 so far)")
+        m = m0
+        o5 = orc.scan(c1, ref_addr["w"][0][rows], ref_addr["w"][1][rows], ref_addr["r"][0][rows],
+                      ref_addr["r"][1][rows], xb["v"], xb["alpha"], xb["beta"], m)
+        acc["out5"].add(g_out[b:b + 1], o5)
+        acc["mem5"].add(gm, m)
+        say(f"[{label}] sequence {b}: stage 4 so far out max/RMS {acc['out4'].value():.3g}, memory "
+            f"{acc['mem4'].value():.3g}; stage 5 out {acc['out5'].value():.3g}, memory {acc['mem5'].value():.3g}")
         del m0, m, gm
     check_scan(cfg, 4, label, {"out": (acc["out4"].value(), acc["out4"].rel),
                                "mem": (acc["mem4"].value(), acc["mem4"].rel)}, say)
-    if stage5:
-        check_scan(cfg, 5, label, {"out": (acc["out5"].value(), acc["out5"].rel),
-                                   "mem": (acc["mem5"].value(), acc["mem5"].rel)}, say)
-    else:
-        say(f"[{label}] stage 5 not run: {excused_rows} rows chose differently across a near-tie")
+    check_scan(cfg, 5, label, {"out": (acc["out5"].value(), acc["out5"].rel),
+                               "mem": (acc["mem5"].value(), acc["mem5"].rel)}, say)
     del mem, mem0
     T.cuda.empty_cache()
     return g
