@@ -149,6 +149,23 @@ SDM_API sdm_status sdm_forward(sdm_handle h, const void* wq, const void* rq, con
 SDM_API sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                             const float* beta, const void* subkeys, void* mem_inout, float* out);
 
+/* sdm_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * handle, no allocation and no library routine that allocates.  cfg, the
+ * stream (a hipStream_t, NULL for the default stream) and the token's tensors
+ * as for sdm_step on a handle made from cfg (cfg->T is not used); the result
+ * equals sdm_step's bit for bit.  Where sdm_step runs two launches (float32
+ * queries, or a shape outside its one-launch form) the slot ids and weights
+ * pass between them through a 1 MiB array in device memory that the library
+ * holds on each device until the process ends, so B*H*W may be at most 65536
+ * (SDM_ERR_UNSUPPORTED beyond; nothing launched).  The array holds no state
+ * between calls (every entry a call reads, the same call writes first), but
+ * calls that overlap on one device share it and race: issue them in order, on
+ * one stream or with events between streams.  Other errors as for sdm_step. */
+SDM_API sdm_status sdm_step_static(const sdm_config* cfg, void* hip_stream, const void* wq, const void* rq,
+                                   const void* v, const float* alpha, const float* beta, const void* subkeys,
+                                   void* mem_inout, float* out);
+
 /* Training forward: exactly sdm_forward's memory and outputs (the same
  * launches; the scan also stores), and the bits of every write slot before its
  * write, saved to log [B, H, T, W, d] (state dtype, dense rows; entry

@@ -59,6 +59,7 @@ def lib() -> C.CDLL:
         "sdm_create": ([C.POINTER(Config), vp, C.POINTER(C.c_void_p)], C.c_int),
         "sdm_forward": ([h, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
         "sdm_step": ([h, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
+        "sdm_step_static": ([C.POINTER(Config), vp, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
         "sdm_forward_train": ([h, vp, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
         "sdm_backward_workspace_bytes": ([C.POINTER(Config), C.POINTER(C.c_size_t)], C.c_int),
         "sdm_backward": ([h] + [vp] * 16, C.c_int),

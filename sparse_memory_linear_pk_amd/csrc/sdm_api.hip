@@ -8,9 +8,11 @@
 #include "sdm.h"
 #include "sdm_internal.h"
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -37,6 +39,16 @@ struct TimedLaunch {
 };
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// sdm_step_static's scratch: on the step's two-launch path, the slot ids then
+// (256-byte aligned) the weights of both query sets, 2*B*H*W of each.  One copy
+// per device, kept until the process ends; host code reaches it only through the
+// device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kStepScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kStepScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
 
 // A forward longer than kChunk tokens runs its scan in chunks: a first one of
 // kChunk / 2 tokens, then kChunk each, the last taking any remainder shorter
@@ -96,7 +108,8 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
 // Elements from one slot row of a memory to the next in the state tensors.
 int mem_stride_of(const sdm_config& c) { return c.mem_stride ? c.mem_stride : c.d; }
 
-sdm_status check_config(const sdm_config* c, std::vector<sdm::ScanPlan>* plans)
+// The shape checks that need no scan plan (and allocate nothing).
+sdm_status check_shape(const sdm_config* c)
 {
     if (!c)
         return fail(SDM_ERR_INVALID_ARG, "config is NULL");
@@ -137,8 +150,17 @@ sdm_status check_config(const sdm_config* c, std::vector<sdm::ScanPlan>* plans)
         return fail(SDM_ERR_UNSUPPORTED, "H*S=%ld: at most 2^21 - 1", (long)c->H * c->n_sub);
     if ((long)c->B * c->T * c->H > (1l << 31) / 64)
         return fail(SDM_ERR_UNSUPPORTED, "B*T*H=%ld rows is too many", (long)c->B * c->T * c->H);
+    return SDM_OK;
+}
+
+sdm_status check_config(const sdm_config* c, std::vector<sdm::ScanPlan>* plans)
+{
+    const sdm_status s = check_shape(c);
+    if (s != SDM_OK)
+        return s;
     const Chunking k = chunking_of(*c);
     const long N = (long)c->n_sub * c->n_sub;
+    const int ms = mem_stride_of(*c);
     plans->assign(k.C(), sdm::ScanPlan{});
     for (int ci = 0; ci < k.C(); ++ci)
         if (!sdm::plan_scan(c->B, c->H, k.len(ci), c->d, ms, c->W, N, c->state_dtype == SDM_BF16,
@@ -664,6 +686,68 @@ sdm_status sdm_step(sdm_handle h, const void* wq, const void* rq, const void* v,
                                         c.H, c.d, mem_stride_of(c), c.n_sub, c.dk / 2, c.k, c.W, c.in_dtype == SDM_BF16,
                                         c.state_dtype == SDM_BF16, h->stream);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_step launch");
+}
+
+} // extern "C"
+
+namespace {
+
+// The device address of `scratch` on the current device, resolved on the first
+// call on that device and kept.
+sdm_status step_scratch(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SDM_ERR_UNSUPPORTED, "sdm_step_static: device %d (at most %d devices)", dev, kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p)
+                return hip_fail(e, "hipGetSymbolAddress of the step scratch");
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return SDM_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+sdm_status sdm_step_static(const sdm_config* cfg, void* hip_stream, const void* wq, const void* rq, const void* v,
+                           const float* alpha, const float* beta, const void* subkeys, void* mem_inout, float* out)
+{
+    sdm_status s = check_shape(cfg);
+    if (s != SDM_OK)
+        return s;
+    if (!wq || !rq || !v || !alpha || !beta || !subkeys || !mem_inout || !out)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_step_static: NULL pointer");
+    if (!aligned16(wq) || !aligned16(rq) || !aligned16(v) || !aligned16(subkeys) || !aligned16(mem_inout) ||
+        !aligned16(out) || !aligned4(alpha) || !aligned4(beta))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_step_static: misaligned pointer");
+    const sdm_config& c = *cfg;
+    if (!sdm::step_supported(c.d, c.state_dtype == SDM_BF16))
+        return fail(SDM_ERR_UNSUPPORTED, "sdm_step_static: d=%d: a slot row must be a multiple of 128 bytes", c.d);
+    const size_t n = 2 * (size_t)c.B * c.H * c.W; // slot ids (and weights) of both query sets
+    if (2 * align_up(n * sizeof(int32_t)) > kStepScratchBytes)
+        return fail(SDM_ERR_UNSUPPORTED, "sdm_step_static: B*H*W=%zu exceeds the %zu-byte scratch (at most 65536)",
+                    n / 2, kStepScratchBytes);
+    void* base = nullptr;
+    if ((s = step_scratch(&base)) != SDM_OK)
+        return s;
+    int32_t* idx = static_cast<int32_t*>(base);
+    float* wt = reinterpret_cast<float*>(static_cast<char*>(base) + align_up(n * sizeof(int32_t)));
+    hipError_t e = sdm::launch_sdm_step(wq, rq, v, alpha, beta, subkeys, mem_inout, out, idx, wt, c.B, c.H, c.d,
+                                        mem_stride_of(c), c.n_sub, c.dk / 2, c.k, c.W, c.in_dtype == SDM_BF16,
+                                        c.state_dtype == SDM_BF16, (hipStream_t)hip_stream);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_step_static launch");
 }
 
 sdm_status sdm_forward_train(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,

@@ -10,7 +10,8 @@ from sparse_memory_linear_pk_amd._lib import Config, Timing, SDM_OK, SDM_ERR_INV
 EXPECTED = ["sdm_create", "sdm_forward", "sdm_destroy", "sdm_status_str", "sdm_last_error", "sdm_workspace_bytes",
             "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing",
             "sdm_pattern_probe", "sdm_step", "sdm_forward_train", "sdm_backward_workspace_bytes", "sdm_backward",
-            "sdm_pattern_probe_mix", "sdm_project", "sdm_broadcast_memory", "sdm_overlap", "sdm_mem_stride_hint"]
+            "sdm_pattern_probe_mix", "sdm_project", "sdm_broadcast_memory", "sdm_overlap", "sdm_mem_stride_hint",
+            "sdm_step_static"]
 
 
 def _cfg(**kw):
@@ -165,3 +166,17 @@ def test_pattern_probe_mix_rejects_unbuilt_mixes(reads, writes):
     L = _lib.lib()
     assert L.sdm_pattern_probe_mix(16, 4, 230400, 8192, 0, 16, 64, reads, writes, 0, None) == SDM_ERR_INVALID_ARG
     assert b"reads:writes" in L.sdm_last_error()
+
+
+def test_step_static_rejects_on_the_host():
+    """The allocation-free decode step checks its arguments before it touches a device: a missing
+    config or pointer, an unsupported row width, and more slot entries than its scratch holds."""
+    L = _lib.lib()
+    fake = [16] * 8  # aligned, never dereferenced: every case fails before any device call
+    assert L.sdm_step_static(None, None, *fake) == SDM_ERR_INVALID_ARG
+    small = dict(B=2, H=1, T=1, d=64, n_sub=32, dk=32, k=6, W=16, in_dtype=0, state_dtype=0)
+    assert L.sdm_step_static(C.byref(_cfg(**small)), None, *([None] * 8)) == SDM_ERR_INVALID_ARG
+    assert L.sdm_step_static(C.byref(_cfg(**dict(small, d=24))), None, *fake) == SDM_ERR_UNSUPPORTED
+    # B*H*W = 1025 * 64 > 65536
+    assert L.sdm_step_static(C.byref(_cfg(**dict(small, B=1025, W=64, k=8))), None, *fake) == SDM_ERR_UNSUPPORTED
+    assert b"scratch" in L.sdm_last_error()
