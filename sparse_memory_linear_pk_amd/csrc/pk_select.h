@@ -28,6 +28,23 @@
 // network on (sum, ~slot) and weighted by a softmax in double precision, so the
 // float32 weights are the correctly rounded values of the exact softmax of the
 // float32 sums, up to the rounding of exp.
+//
+// Exact scores (the forward's path, select_half with a Refine).  The scores from
+// the matrix cores are float32 sums; they only locate the candidates.  Every
+// score that can reach a half's top k is recomputed exactly: the dh products
+// (exact in double for bf16 and float32 inputs) summed in double in index
+// order and rounded once to float32, which is the definition the oracle
+// computes, operation for operation.  Which scores can reach the top k: if E
+// bounds |approximate - exact| for every score of the half, and beta is the
+// lower bound of step 1 (k scores have approximate values >= beta), the k-th
+// largest exact score is at least beta - E, so every member of the exact top k
+// has an approximate score >= beta - 2E, and every score below that is
+// strictly below the k-th exact one.  Those candidates (about the same 45 at
+// S = 480, k = 32) are made exact and sorted; more than 64 of them (heavy ties)
+// makes every score of the half exact and selects over all of them.  E is
+// 2 (dh + 2) 2^-24 sum_c |q_c| max |K|: the recursive-summation bound of a
+// dh-term float32 dot product in any order, plus the rounding of the exact one,
+// doubled.
 #pragma once
 
 #include "sdm_internal.h"
@@ -112,6 +129,157 @@ __device__ __forceinline__ void wave_sync_lds()
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Exact score of a query half against one sub-key row: products summed in
+// double in index order, rounded once to float32.
+template <bool BF16>
+__device__ inline float exact_score(const void* q_half, const void* krow, int dh)
+{
+    double acc = 0.0;
+    if constexpr (BF16) {
+        const uint4* qp = static_cast<const uint4*>(q_half);
+        const uint4* kp = static_cast<const uint4*>(krow);
+        for (int c = 0; c < dh / 8; ++c) {
+            const uint4 a = qp[c], b = kp[c];
+            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc = fma((double)bf16_lo(aw[w]), (double)bf16_lo(bw[w]), acc);
+                acc = fma((double)bf16_hi(aw[w]), (double)bf16_hi(bw[w]), acc);
+            }
+        }
+    } else {
+        const float4* qp = static_cast<const float4*>(q_half);
+        const float4* kp = static_cast<const float4*>(krow);
+        for (int c = 0; c < dh / 4; ++c) {
+            const float4 a = qp[c], b = kp[c];
+            acc = fma((double)a.x, (double)b.x, acc);
+            acc = fma((double)a.y, (double)b.y, acc);
+            acc = fma((double)a.z, (double)b.z, acc);
+            acc = fma((double)a.w, (double)b.w, acc);
+        }
+    }
+    return __double2float_rn(acc);
+}
+
+// What the exact path of one half needs: the row's query half, the half's
+// sub-key table [S, dh] and E, the bound on |approximate - exact| of its scores.
+struct Refine {
+    const void* q_half;
+    const void* table;
+    int dh;
+    float E;
+};
+
+// E for a query half: 2 (dh + 2) 2^-24 sum_c |q_c| kmax, kmax = max |K| over
+// the half's table; every lane returns it.
+template <bool BF16>
+__device__ inline float error_bound(const void* q_half, int dh, float kmax, int lane)
+{
+    float a = 0.f;
+    for (int c = lane; c < dh; c += 64)
+        a += BF16 ? fabsf(__uint_as_float((uint32_t)static_cast<const uint16_t*>(q_half)[c] << 16))
+                  : fabsf(static_cast<const float*>(q_half)[c]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        a += __shfl_xor(a, m);
+    // the float sums above lose at most a few parts in 2^24 of a: covered by the factor 2
+    return 2.f * (float)(dh + 2) * 0x1p-24f * a * kmax;
+}
+
+// The largest float32 no larger than x.
+__device__ inline float float_down(double x)
+{
+    float f = __double2float_rn(x);
+    if ((double)f > x) { // one float step down
+        const float z = f;
+        uint32_t u = __float_as_uint(f);
+        u = z > 0.f ? u - 1u : (z < 0.f ? u + 1u : 0x80000001u);
+        f = __uint_as_float(u);
+    }
+    return f;
+}
+
+// Top k of one half, sorted (score desc, index asc): lane r < k ends with the
+// r-th survivor as (key << 32) | ~index.  buf: 64 entries of wave scratch.
+// With ref, the scores that can reach the top k are made exact first (see the
+// header): the survivors and their keys are those of the exact scores.
+template <int J, bool BF16>
+__device__ inline uint64_t half_sorted_topk_exact(const float* __restrict__ s, int S, int k, int lane, uint64_t* buf,
+                                                  const Refine& ref)
+{
+    uint32_t key[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int idx = j * 64 + lane;
+        key[j] = idx < S ? ordered_key(s[idx]) : 0u;
+    }
+    uint32_t lane_max[1] = {0u};
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        lane_max[0] = key[j] > lane_max[0] ? key[j] : lane_max[0];
+    // with one key per lane every score is a candidate
+    uint32_t thr = 0u;
+    if (J > 1) {
+        const uint32_t bound = kth_largest<1>(lane_max, k, kBoundRounds);
+        const float beta = key_value(bound);
+        const double lo = (double)beta - 2.0 * (double)ref.E;
+        // a NaN bound (NaN scores) takes every score
+        thr = lo == lo ? ordered_key(float_down(lo)) : 0u;
+    }
+    int passing = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+        passing += __popcll(ballot(key[j] != 0u && key[j] >= thr));
+    const char* table = static_cast<const char*>(ref.table);
+    const size_t row_bytes = (size_t)ref.dh * (BF16 ? 2 : 4);
+    if (passing <= 64) {
+        int placed = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const bool sel = key[j] != 0u && key[j] >= thr;
+            const uint64_t sm = ballot(sel);
+            if (sel)
+                buf[placed + rank_below(sm)] = (uint64_t)(j * 64 + lane);
+            placed += __popcll(sm);
+        }
+        wave_sync_lds();
+        uint64_t x = 0ull;
+        if (lane < placed) {
+            const uint32_t sk = (uint32_t)buf[lane];
+            const float e = exact_score<BF16>(ref.q_half, table + sk * row_bytes, ref.dh);
+            x = ((uint64_t)ordered_key(e) << 32) | (uint64_t)(~sk);
+        }
+        wave_sync_lds();
+        return sort64_desc(x, lane);
+    }
+    // heavy ties: every score of the half exact, the k-th largest by a full radix select
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int idx = j * 64 + lane;
+        key[j] = idx < S ? ordered_key(exact_score<BF16>(ref.q_half, table + idx * row_bytes, ref.dh)) : 0u;
+    }
+    thr = kth_largest<J>(key, k);
+    const int need = k - count_above<J>(key, thr);
+    int tied = 0, placed = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const bool live = key[j] != 0u;
+        const uint64_t eq = ballot(live && key[j] == thr);
+        const bool take_tie = live && key[j] == thr && tied + rank_below(eq) < need;
+        tied += __popcll(eq);
+        const bool sel = live && (key[j] > thr || take_tie);
+        const uint64_t sm = ballot(sel);
+        const int p = placed + rank_below(sm);
+        if (sel && p < 64)
+            buf[p] = ((uint64_t)key[j] << 32) | (uint64_t)(~(uint32_t)(j * 64 + lane));
+        placed += __popcll(sm);
+    }
+    wave_sync_lds();
+    const uint64_t x = lane < placed ? buf[lane] : 0ull;
+    wave_sync_lds();
+    return sort64_desc(x, lane);
 }
 
 // Top k of one half, sorted (score desc, index asc): lane r < k ends with the
@@ -227,6 +395,17 @@ __device__ inline void select_half(const float* s, int S, int k, int lane, uint6
     sub[lane] = ~(uint32_t)x;
 }
 
+// The same with exact scores (the forward's path): the list holds the exact
+// top k and their exact scores.
+template <int J, bool BF16>
+__device__ inline void select_half_exact(const float* s, int S, int k, int lane, uint64_t* buf, float* val,
+                                         uint32_t* sub, const Refine& ref)
+{
+    const uint64_t x = half_sorted_topk_exact<J, BF16>(s, S, k, lane, buf, ref);
+    val[lane] = key_value((uint32_t)(x >> 32));
+    sub[lane] = ~(uint32_t)x;
+}
+
 // Step 2 by one wave, from both halves' sorted lists (val, sub: 2 x 64, in
 // LDS and visible to the wave): idx_row, wt_row receive the W slots and
 // weights, best first.  buf: 64 entries of the wave's LDS scratch.
@@ -247,6 +426,19 @@ __device__ inline void select_row(const float* s, int S, int k, int W, int n_pai
 #pragma unroll
     for (int h = 0; h < 2; ++h)
         select_half<J>(s + h * S, S, k, lane, buf, val[h], sub[h]);
+    wave_sync_lds();
+    select_from_lists<R>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
+}
+
+// select_row with exact scores: ref[h] for half h.
+template <int J, int R, bool BF16>
+__device__ inline void select_row_exact(const float* s, int S, int k, int W, int n_pairs, const uint16_t* s_pairs,
+                                        int lane, uint64_t* buf, float (*val)[64], uint32_t (*sub)[64],
+                                        int32_t* idx_row, float* wt_row, const Refine (&ref)[2])
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        select_half_exact<J, BF16>(s + h * S, S, k, lane, buf, val[h], sub[h], ref[h]);
     wave_sync_lds();
     select_from_lists<R>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
 }

@@ -1,7 +1,11 @@
 // pk_topk: the selection half of product-key addressing, for every row of a
 // call: per half the k best sub-keys, the W best of their outer sums, softmax
 // weights.  One wave64 per row runs pksel::select_row (pk_select.h has the
-// algorithm and the argument for its exactness).
+// algorithm and the argument for its exactness).  Given the queries and the
+// sub-key tables (the forward's path), the scores that can reach a half's top k
+// are first made exact (pksel::select_row_exact), so the slots and weights are
+// those of exactly rounded scores; given scores alone (the stage seam), the
+// scores are taken as they are.
 #include "pk_select.h"
 
 namespace sdm {
@@ -11,12 +15,22 @@ using namespace pksel;
 
 constexpr int kRowsPerBlock = 4; // one wave per row
 
-// J: sub-keys per lane per half (S <= 64*J); R: restricted candidates per lane.
-template <int J, int R>
+// What the exact path reads: the queries [B, Ts, H, dk], the sub-key tables
+// [H, 2, S, dh] and max |K| per table [H, 2].
+struct ExactIn {
+    const void* q;
+    const void* subkeys;
+    const float* kmax;
+    int dh;
+};
+
+// J: sub-keys per lane per half (S <= 64*J); R: restricted candidates per lane;
+// EX: 0 scores as given, 1 exact from bf16 inputs, 2 exact from float32 inputs.
+template <int J, int R, int EX>
 __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float* __restrict__ scores,
                                                                    int32_t* __restrict__ idx,
                                                                    float* __restrict__ wt, Rows rr, int S,
-                                                                   int k, int W, int n_pairs)
+                                                                   int k, int W, int n_pairs, ExactIn ex)
 {
     __shared__ uint64_t s_buf[kRowsPerBlock][64];       // compaction scratch, then the winners
     __shared__ float s_val[kRowsPerBlock][2][64];        // sorted half lists: scores
@@ -32,19 +46,59 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float
         return; // whole wave leaves; no block-level barriers below
     const long per_seq = (long)rr.Tc * rr.H;
     const long row = ((j / per_seq) * rr.Ts + rr.t0) * rr.H + j % per_seq; // row (b, t, h) of the call
-    select_row<J, R>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane, s_buf[wave], s_val[wave],
-                     s_sub[wave], idx + row * W, wt + row * W);
+    if constexpr (EX == 0) {
+        select_row<J, R>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane, s_buf[wave], s_val[wave],
+                         s_sub[wave], idx + row * W, wt + row * W);
+    } else {
+        constexpr bool BF16 = EX == 1;
+        const int h = (int)(row % rr.H), dh = ex.dh;
+        const size_t es = BF16 ? 2 : 4;
+        Refine ref[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            ref[half].q_half = static_cast<const char*>(ex.q) + ((size_t)row * 2 * dh + (size_t)half * dh) * es;
+            ref[half].table = static_cast<const char*>(ex.subkeys) + ((size_t)(h * 2 + half) * S * dh) * es;
+            ref[half].dh = dh;
+            ref[half].E = error_bound<BF16>(ref[half].q_half, dh, ex.kmax[h * 2 + half], lane);
+        }
+        select_row_exact<J, R, BF16>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane, s_buf[wave],
+                                     s_val[wave], s_sub[wave], idx + row * W, wt + row * W, ref);
+    }
 }
 
-template <int J>
+// max |K| of each sub-key table: one workgroup per (head, half).
+template <bool BF16>
+__global__ __launch_bounds__(256) void subkey_absmax_kernel(const void* __restrict__ subkeys, float* __restrict__ kmax,
+                                                            int S, int dh)
+{
+    __shared__ float s_red[4];
+    const long n = (long)S * dh;
+    const long base = (long)blockIdx.x * n;
+    float m = 0.f;
+    for (long e = threadIdx.x; e < n; e += blockDim.x) {
+        const float v = BF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(subkeys)[base + e] << 16)
+                             : static_cast<const float*>(subkeys)[base + e];
+        m = fmaxf(m, fabsf(v));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        m = fmaxf(m, __shfl_xor(m, o));
+    if ((threadIdx.x & 63) == 0)
+        s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        kmax[blockIdx.x] = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+}
+
+template <int J, int EX>
 hipError_t launch_j(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
-                    hipStream_t stream)
+                    const ExactIn& ex, hipStream_t stream)
 {
     dim3 grid((unsigned)((r.count() + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
 #define SDM_TOPK_R(Rv)                                                                                       \
     if (n_pairs <= 64 * Rv) {                                                                                \
-        hipLaunchKernelGGL((pk_topk_kernel<J, Rv>), grid, block, 0, stream, scores, idx, wt, r, S, k, W,    \
-                           n_pairs);                                                                         \
+        hipLaunchKernelGGL((pk_topk_kernel<J, Rv, EX>), grid, block, 0, stream, scores, idx, wt, r, S, k, W, \
+                           n_pairs, ex);                                                                     \
         return hipGetLastError();                                                                            \
     }
     SDM_TOPK_R(1)
@@ -55,29 +109,55 @@ hipError_t launch_j(const float* scores, int32_t* idx, float* wt, const Rows& r,
     return hipErrorInvalidValue;
 }
 
+template <int EX>
+hipError_t launch_ex(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
+                     const ExactIn& ex, hipStream_t stream)
+{
+    if (S <= 64)
+        return launch_j<1, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+    if (S <= 128)
+        return launch_j<2, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+    if (S <= 256)
+        return launch_j<4, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+    if (S <= 512)
+        return launch_j<8, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+    if (S <= 1024)
+        return launch_j<16, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+    return hipErrorInvalidValue;
+}
+
 } // namespace
 
+hipError_t launch_subkey_absmax(const void* subkeys, float* kmax, int H, int S, int dh, bool in_bf16,
+                                hipStream_t stream)
+{
+    if (in_bf16)
+        hipLaunchKernelGGL((subkey_absmax_kernel<true>), dim3((unsigned)(2 * H)), dim3(256), 0, stream, subkeys,
+                           kmax, S, dh);
+    else
+        hipLaunchKernelGGL((subkey_absmax_kernel<false>), dim3((unsigned)(2 * H)), dim3(256), 0, stream, subkeys,
+                           kmax, S, dh);
+    return hipGetLastError();
+}
+
 hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
+                          const void* q, const void* subkeys, const float* kmax, int dh, bool in_bf16,
                           hipStream_t stream)
 {
     if (r.count() <= 0)
         return hipSuccess;
     if (k < 1 || k > 64 || W < 1 || W > 64 || W > k * k || k > S)
         return hipErrorInvalidValue;
+    if (q && (!subkeys || !kmax || dh < 16 || dh % 16))
+        return hipErrorInvalidValue;
     const int n_pairs = pair_count(k, W);
     if (n_pairs > kPairsMax)
         return hipErrorInvalidValue;
-    if (S <= 64)
-        return launch_j<1>(scores, idx, wt, r, S, k, W, n_pairs, stream);
-    if (S <= 128)
-        return launch_j<2>(scores, idx, wt, r, S, k, W, n_pairs, stream);
-    if (S <= 256)
-        return launch_j<4>(scores, idx, wt, r, S, k, W, n_pairs, stream);
-    if (S <= 512)
-        return launch_j<8>(scores, idx, wt, r, S, k, W, n_pairs, stream);
-    if (S <= 1024)
-        return launch_j<16>(scores, idx, wt, r, S, k, W, n_pairs, stream);
-    return hipErrorInvalidValue;
+    const ExactIn ex{q, subkeys, kmax, dh};
+    if (!q)
+        return launch_ex<0>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+    return in_bf16 ? launch_ex<1>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream)
+                   : launch_ex<2>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
 }
 
 } // namespace sdm

@@ -81,7 +81,7 @@ Chunking chunking_of(const sdm_config& c)
 }
 
 struct Layout {
-    size_t scores, idx, wt, plan, frag, step, total;
+    size_t scores, idx, wt, plan, frag, kmax, step, total;
     std::vector<size_t> plan_off; // byte offset of each chunk's plan
 };
 
@@ -101,7 +101,8 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
     // sdm_step's slot ids and weights, write then read set: 2*B*H*W of each,
     // apart from the forward's buffers (which hold B*T*H*W and T may be 1)
     L.step = align_up(2 * (size_t)c.B * c.H * c.W * sizeof(int32_t));
-    L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag + 2 * L.step;
+    L.kmax = align_up(2 * (size_t)c.H * sizeof(float)); // max |K| per sub-key table
+    L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag + L.kmax + 2 * L.step;
     return L;
 }
 
@@ -194,6 +195,7 @@ struct sdm_ctx {
     void* frag;
     int32_t* step_idx;   // [2][B*H][W] (sdm_step)
     float* step_wt;      // [2][B*H][W]
+    float* kmax;         // [H][2]: max |K| of each sub-key table, for the exact scores of the selection
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
@@ -249,7 +251,21 @@ sdm::Rows chunk_rows(const sdm_ctx* h, int ci)
     return sdm::Rows{c.B, c.H, h->ck.len(ci), c.T, h->ck.t0(ci)};
 }
 
-// frag: rearrange the sub-key tables first (once per call that scores)
+// The per-call preparation of the sub-key tables: their MFMA operand order (bf16
+// inputs) and the largest magnitude of each table (the exact selection's bound).
+hipError_t prepare_subkeys(sdm_ctx* h, const void* subkeys, hipStream_t st)
+{
+    const sdm_config& c = h->cfg;
+    const bool bf16 = c.in_dtype == SDM_BF16;
+    hipError_t e = hipSuccess;
+    if (bf16)
+        e = sdm::launch_pk_subkey_frag(subkeys, h->frag, c.H, c.n_sub, c.dk / 2, st);
+    if (e == hipSuccess)
+        e = sdm::launch_subkey_absmax(subkeys, h->kmax, c.H, c.n_sub, c.dk / 2, bf16, st);
+    return e;
+}
+
+// frag: prepare the sub-key tables first (once per call that scores)
 sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, float* scores, const sdm::Rows& r,
                      hipStream_t st, bool frag)
 {
@@ -257,18 +273,23 @@ sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, float* scor
     const bool bf16 = c.in_dtype == SDM_BF16;
     Timer t(h, K_SCORE, st);
     hipError_t e = hipSuccess;
-    if (frag && bf16)
-        e = sdm::launch_pk_subkey_frag(subkeys, h->frag, c.H, c.n_sub, c.dk / 2, st);
+    if (frag)
+        e = prepare_subkeys(h, subkeys, st);
     if (e == hipSuccess)
         e = sdm::launch_pk_score(q, subkeys, h->frag, scores, r, c.n_sub, c.dk / 2, bf16, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_score launch");
 }
 
-sdm_status run_select(sdm_ctx* h, const float* scores, int32_t* idx, float* wt, const sdm::Rows& r, hipStream_t st)
+// q and subkeys given (the forward's path): the scores that can reach a half's
+// top k are made exact from them (h->kmax must be prepared); q null: the scores
+// are taken as given (the stage seam).
+sdm_status run_select(sdm_ctx* h, const float* scores, int32_t* idx, float* wt, const sdm::Rows& r, hipStream_t st,
+                      const void* q, const void* subkeys)
 {
     const sdm_config& c = h->cfg;
     Timer t(h, K_SELECT, st);
-    hipError_t e = sdm::launch_pk_topk(scores, idx, wt, r, c.n_sub, c.k, c.W, st);
+    hipError_t e = sdm::launch_pk_topk(scores, idx, wt, r, c.n_sub, c.k, c.W, q, subkeys, h->kmax, c.dk / 2,
+                                       c.in_dtype == SDM_BF16, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_topk launch");
 }
 
@@ -328,7 +349,7 @@ sdm_status run_chunk_front(sdm_ctx* h, int ci, const void* wq, const void* rq, c
     for (int set = 0; set < 2 && s == SDM_OK; ++set) {
         s = run_score(h, q[set], subkeys, h->scores, r, st, ci == 0 && set == 0);
         if (s == SDM_OK)
-            s = run_select(h, h->scores, h->idx[set], h->wt[set], r, st);
+            s = run_select(h, h->scores, h->idx[set], h->wt[set], r, st, q[set], subkeys);
     }
     return s == SDM_OK ? run_plan(h, ci, h->idx[0], h->wt[0], h->idx[1], h->wt[1], alpha, beta, st) : s;
 }
@@ -342,7 +363,7 @@ sdm_status run_address_all(sdm_ctx* h, const void* wq, const void* rq, const voi
     for (int set = 0; set < 2 && s == SDM_OK; ++set) {
         s = run_score(h, q[set], subkeys, h->scores, r, st, set == 0);
         if (s == SDM_OK)
-            s = run_select(h, h->scores, h->idx[set], h->wt[set], r, st);
+            s = run_select(h, h->scores, h->idx[set], h->wt[set], r, st, q[set], subkeys);
     }
     return s;
 }
@@ -456,6 +477,8 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     p += h->L.plan;
     h->frag = p;
     p += h->L.frag;
+    h->kmax = (float*)p;
+    p += h->L.kmax;
     h->step_idx = (int32_t*)p;
     p += h->L.step;
     h->step_wt = (float*)p;
@@ -542,7 +565,7 @@ sdm_status sdm_select(sdm_handle h, const float* scores, int32_t* idx, float* wt
         return fail(SDM_ERR_INVALID_ARG, "sdm_select: NULL pointer");
     if (!aligned4(scores) || !aligned4(idx) || !aligned4(wt))
         return fail(SDM_ERR_INVALID_ARG, "sdm_select: pointers must be 4-byte aligned");
-    return run_select(h, scores, idx, wt, all_rows(h->cfg), h->stream);
+    return run_select(h, scores, idx, wt, all_rows(h->cfg), h->stream, nullptr, nullptr);
 }
 
 sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t* idx, float* wt)
@@ -555,7 +578,7 @@ sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t
     if (!aligned16(q) || !aligned16(subkeys) || !aligned4(idx) || !aligned4(wt))
         return fail(SDM_ERR_INVALID_ARG, "sdm_address: misaligned pointer");
     s = run_score(h, q, subkeys, h->scores, all_rows(h->cfg), h->stream, true);
-    return s != SDM_OK ? s : run_select(h, h->scores, idx, wt, all_rows(h->cfg), h->stream);
+    return s != SDM_OK ? s : run_select(h, h->scores, idx, wt, all_rows(h->cfg), h->stream, q, subkeys);
 }
 
 sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
@@ -619,9 +642,9 @@ sdm_status forward_impl(sdm_ctx* h, const void* wq, const void* rq, const void* 
     const sdm_config& c = h->cfg;
     const sdm::Rows r0 = chunk_rows(h, 0);
     hipError_t e = hipSuccess;
-    if (c.in_dtype == SDM_BF16) {
+    {
         Timer t(h, K_SCORE, h->stream);
-        e = sdm::launch_pk_subkey_frag(subkeys, h->frag, c.H, c.n_sub, c.dk / 2, h->stream);
+        e = prepare_subkeys(h, subkeys, h->stream);
     }
     if (e == hipSuccess)
         e = hipEventRecord(h->e_start, h->stream);
@@ -632,11 +655,11 @@ sdm_status forward_impl(sdm_ctx* h, const void* wq, const void* rq, const void* 
     float* scores_r0 = h->scores + (size_t)h->ck.len(0) * c.H * 2 * c.n_sub;
     s = run_score(h, wq, subkeys, h->scores, r0, h->aux, false);
     if (s == SDM_OK)
-        s = run_select(h, h->scores, h->idx[0], h->wt[0], r0, h->aux);
+        s = run_select(h, h->scores, h->idx[0], h->wt[0], r0, h->aux, wq, subkeys);
     if (s == SDM_OK)
         s = run_score(h, rq, subkeys, scores_r0, r0, h->stream, false);
     if (s == SDM_OK)
-        s = run_select(h, scores_r0, h->idx[1], h->wt[1], r0, h->stream);
+        s = run_select(h, scores_r0, h->idx[1], h->wt[1], r0, h->stream, rq, subkeys);
     if (s != SDM_OK)
         return s;
     e = hipEventRecord(h->e_read, h->stream);

@@ -70,9 +70,16 @@ hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag,
                            int S, int dh, bool in_bf16, hipStream_t stream);
 
 // Per-half top-k, outer-sum top-W and softmax weights of the covered rows:
-// scores [B*Ts*H, 2, S] -> idx, wt [B*Ts*H, W].
+// scores [B*Ts*H, 2, S] -> idx, wt [B*Ts*H, W].  With q ([B, Ts, H, dk]),
+// subkeys and kmax (max |K| per table, [H, 2]) the scores that can reach a
+// half's top k are recomputed exactly first (double sums in index order, one
+// rounding); with q null the scores are taken as given.
 hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
+                          const void* q, const void* subkeys, const float* kmax, int dh, bool in_bf16,
                           hipStream_t stream);
+// kmax[h * 2 + half] = max |K| over sub-key table (h, half).
+hipError_t launch_subkey_absmax(const void* subkeys, float* kmax, int H, int S, int dh, bool in_bf16,
+                                hipStream_t stream);
 
 // Staged scan: constants shared by its plan and its kernel.
 // The kernel steps through tokens in pairs; the slot reads of a pair are issued

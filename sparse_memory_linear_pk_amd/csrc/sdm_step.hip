@@ -29,6 +29,20 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+
+// Running maxima of bf16 magnitudes, two per word (finite bf16 magnitudes order
+// as unsigned integers).
+__device__ __forceinline__ uint32_t absmax_bf16x8(uint32_t m, const bf16x8_t& v)
+{
+    const uint4 w = __builtin_bit_cast(uint4, v);
+    u16x2_t mm = __builtin_bit_cast(u16x2_t, m);
+    mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2_t, w.x & 0x7FFF7FFFu));
+    mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2_t, w.y & 0x7FFF7FFFu));
+    mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2_t, w.z & 0x7FFF7FFFu));
+    mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2_t, w.w & 0x7FFF7FFFu));
+    return __builtin_bit_cast(uint32_t, mm);
+}
 
 constexpr int kWaves = 4;
 
@@ -44,9 +58,11 @@ struct StepArgs {
 // Scores of the two queries of (b, h) against both sub-key tables, into
 // sc[query][half][S]: rows 0 (write) and 1 (read) of a 32-row MFMA tile whose
 // other rows are zero; the 32 columns are sub-keys.  Operands, instruction and
-// k-step order are pk_score's, so each score is the same float.
+// k-step order are pk_score's, so each score is the same float.  kmax[half]
+// receives this wave's share of max |K| of table `half` (every element of a
+// table is loaded by one lane of one wave); the caller reduces over the waves.
 template <int DH, bool BF16>
-__device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int wave)
+__device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int wave, float (&kmax)[2])
 {
     const int h = bh % a.H, S = a.S;
     const int i = lane & 31, kg = lane >> 5;
@@ -66,6 +82,7 @@ __device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int 
                 qv[half][kk] = i < 2 ? *reinterpret_cast<const bf16x8_t*>(q + kk * 16) : bf16x8_t{};
         }
         const int ntask = 2 * ctiles;
+        uint32_t km[2] = {0u, 0u};
         for (int t0 = wave; t0 < ntask; t0 += kWaves * G) {
             bf16x8_t bv[G][KSTEPS];
 #pragma unroll
@@ -79,6 +96,13 @@ __device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int 
 #pragma unroll
                 for (int kk = 0; kk < KSTEPS; ++kk) // a valid row either way; zeroed where used
                     bv[g][kk] = *reinterpret_cast<const bf16x8_t*>(krow + kk * 16);
+                if (on) { // rows past S repeat row 0, which another lane covers
+                    uint32_t m = 0u;
+#pragma unroll
+                    for (int kk = 0; kk < KSTEPS; ++kk)
+                        m = absmax_bf16x8(m, bv[g][kk]);
+                    km[half] = max(km[half], max(m & 0xFFFFu, m >> 16));
+                }
             }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -99,8 +123,11 @@ __device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int 
                 }
             }
         }
+        kmax[0] = __uint_as_float(km[0] << 16);
+        kmax[1] = __uint_as_float(km[1] << 16);
         return;
     }
+    kmax[0] = kmax[1] = 0.f;
     for (int task = wave; task < 2 * ctiles; task += kWaves) {
         const int half = task / ctiles, ct = task % ctiles;
         const int s = ct * 32 + i;
@@ -112,8 +139,11 @@ __device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int 
             const float* krow = table + (long)(s < S ? s : 0) * DH + kg;
             const float live = s < S ? 1.f : 0.f;
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk)
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(i < 2 ? q[kk * 2] : 0.f, krow[kk * 2] * live, acc, 0, 0, 0);
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                const float kv = krow[kk * 2] * live;
+                kmax[half] = fmaxf(kmax[half], fabsf(kv));
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(i < 2 ? q[kk * 2] : 0.f, kv, acc, 0, 0, 0);
+            }
         }
         // lane l < 32 holds column l of rows 0 (v = 0) and 1 (v = 1)
         if (kg == 0 && s < S) {
@@ -121,6 +151,41 @@ __device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int 
             sc[(1 * 2 + half) * S + s] = acc[1];
         }
     }
+}
+
+// Each wave's max |K| of both tables into s_km[wave][half] (visible after the
+// next barrier).
+__device__ __forceinline__ void publish_kmax(float (&km)[2], float (*s_km)[2], int lane, int wave)
+{
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        float m = km[half];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1)
+            m = fmaxf(m, __shfl_xor(m, o));
+        if (lane == 0)
+            s_km[wave][half] = m;
+    }
+}
+
+__device__ __forceinline__ float kmax_of(const float (*s_km)[2], int half)
+{
+    return fmaxf(fmaxf(s_km[0][half], s_km[1][half]), fmaxf(s_km[2][half], s_km[3][half]));
+}
+
+// The exact-score inputs of query half `half` of row bh (query 0 write, 1 read).
+template <int DH, bool BF16>
+__device__ __forceinline__ pksel::Refine step_refine(const StepArgs& a, int bh, int query, int half, float kmax,
+                                                     int lane)
+{
+    const size_t es = BF16 ? 2 : 4;
+    const int h = bh % a.H;
+    pksel::Refine r;
+    r.q_half = static_cast<const char*>(query ? a.rq : a.wq) + ((size_t)bh * 2 * DH + (size_t)half * DH) * es;
+    r.table = static_cast<const char*>(a.subkeys) + (size_t)(h * 2 + half) * a.S * DH * es;
+    r.dh = DH;
+    r.E = pksel::error_bound<BF16>(r.q_half, DH, kmax, lane);
+    return r;
 }
 
 template <int DH, bool BF16, int J, int R>
@@ -131,15 +196,20 @@ __global__ __launch_bounds__(kWaves * 64) void step_address_kernel(StepArgs a)
     __shared__ float s_val[2][2][64];
     __shared__ uint32_t s_sub[2][2][64];
     __shared__ uint16_t s_pairs[pksel::kPairsMax];
+    __shared__ float s_km[kWaves][2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bh = blockIdx.x;
     pksel::fill_pairs(s_pairs, a.k, a.W);
-    step_scores<DH, BF16>(a, bh, s_sc, lane, wave);
+    float km[2];
+    step_scores<DH, BF16>(a, bh, s_sc, lane, wave, km);
+    publish_kmax(km, s_km, lane, wave);
     __syncthreads();
     if (wave < 2) { // wave 0 selects the write slots, wave 1 the read slots
         const long o = ((long)wave * a.B * a.H + bh) * a.W;
-        pksel::select_row<J, R>(s_sc + wave * 2 * a.S, a.S, a.k, a.W, a.n_pairs, s_pairs, lane, s_buf[wave],
-                                s_val[wave], s_sub[wave], a.idx + o, a.wt + o);
+        const pksel::Refine ref[2] = {step_refine<DH, BF16>(a, bh, wave, 0, kmax_of(s_km, 0), lane),
+                                      step_refine<DH, BF16>(a, bh, wave, 1, kmax_of(s_km, 1), lane)};
+        pksel::select_row_exact<J, R, BF16>(s_sc + wave * 2 * a.S, a.S, a.k, a.W, a.n_pairs, s_pairs, lane,
+                                            s_buf[wave], s_val[wave], s_sub[wave], a.idx + o, a.wt + o, ref);
     }
 }
 
@@ -312,16 +382,20 @@ __global__ __launch_bounds__(kWaves * 64) void step_fused_kernel(StepArgs a, Ste
     __shared__ uint16_t s_pairs[pksel::kPairsMax];
     __shared__ int32_t s_idx[2][64];
     __shared__ float s_wt[2][64];
+    __shared__ float s_km[kWaves][2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nchunk = c.d / (128 / (int)sizeof(ST));
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
     pksel::fill_pairs(s_pairs, a.k, a.W);
-    step_scores<DH, true>(a, bh, s_sc, lane, wave);
+    float km[2];
+    step_scores<DH, true>(a, bh, s_sc, lane, wave, km);
+    publish_kmax(km, s_km, lane, wave);
     __syncthreads();
     {
         const int q = wave >> 1, half = wave & 1; // waves 0, 1: write query; 2, 3: read query
-        pksel::select_half<J>(s_sc + (q * 2 + half) * a.S, a.S, a.k, lane, s_buf[wave], s_val[q][half],
-                              s_sub[q][half]);
+        const pksel::Refine ref = step_refine<DH, true>(a, bh, q, half, kmax_of(s_km, half), lane);
+        pksel::select_half_exact<J, true>(s_sc + (q * 2 + half) * a.S, a.S, a.k, lane, s_buf[wave], s_val[q][half],
+                                          s_sub[q][half], ref);
     }
     __syncthreads();
     if (wave < 2)

@@ -15,7 +15,7 @@ import pytest
 import oracle
 import sdm_inputs as gi
 from parity import (PlainAccum, check_scan, check_scores, check_selection_exact, compare_index_sets, plain_err,
-                    rel_max_err, resolve_near_ties, score_error_bound, to_dev, to_host)
+                    rel_max_err, score_error_bound, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,46 +62,50 @@ def run_gpu(T, cfg, x, stages=True):
         if stages:
             mem2 = dev["mem0"].clone()
             out2 = T.empty_like(out)
-            layer.scan_with(res["idx_w"], res["wt_w"], res["idx_r"], res["wt_r"], dev["v"], dev["alpha"],
+            layer.scan_with(res["idx2_w"], res["wt2_w"], res["idx2_r"], res["wt2_r"], dev["v"], dev["alpha"],
                             dev["beta"], mem2, out2)
             res["mem2"], res["out2"] = mem2, out2
         T.cuda.synchronize()
     return {k: to_host(v) for k, v in res.items()}
 
 
+def check_exact_addressing(got_idx, got_wt, ref_idx, ref_wt, label, say_):
+    """The forward's addressing against the oracle's, from the same queries: the same slots in the
+    same order, weights within one float32 unit (the softmax's exp is a library routine on each side)."""
+    bad = np.nonzero((got_idx != ref_idx).any(axis=1))[0]
+    assert bad.size == 0, f"[{label}] {bad.size} rows address other slots than the oracle, first {bad[:5]}"
+    u = np.abs(got_wt.view(np.int32).astype(np.int64) - ref_wt.view(np.int32).astype(np.int64))
+    assert u.max() <= 1, f"[{label}] weights differ by {u.max()} units"
+    return int(u.max())
+
+
 def full_parity(orc, cfg, x, g, label):
     """Stages 1-5 on every row and element."""
     R = cfg.B * cfg.T * cfg.H
     rows = np.arange(R)
-    # the forward and the stage seams run the same kernels
-    for s in "wr":
-        assert np.array_equal(g[f"idx_{s}"], g[f"idx2_{s}"]) and np.array_equal(g[f"wt_{s}"], g[f"wt2_{s}"])
+    # the scan seam on the forward's addressing is the forward
     assert np.array_equal(g["out"], g["out2"]) and np.array_equal(g["mem"], g["mem2"])
-    excused_rows = 0
-    ref_addr = {}
     for s, q in (("w", x["wq"]), ("r", x["rq"])):
         ref_scores = orc.scores(cfg, q, x["subkeys"])
         err = check_scores(cfg, g[f"scores_{s}"], ref_scores, score_error_bound(cfg, q, x["subkeys"], rows))
         ui, uw, _ = orc.address_from_scores(cfg, g[f"scores_{s}"])
         ulp = check_selection_exact(g[f"idx_{s}"], g[f"wt_{s}"], ui, uw)
         ri, rw, rs = orc.address(cfg, q, x["subkeys"])
+        # the float32 scores alone choose as the oracle except across near-ties
         differ, exc = compare_index_sets(orc, cfg, g[f"idx_{s}"], ri, rs, ref_scores)
-        ri, rw, taken = resolve_near_ties(orc, cfg, g[f"idx_{s}"], ri, rw, ref_scores)
-        ref_addr[s] = (ri, rw)
-        excused_rows += exc
-        say(f"[{label}] {s}: score err {err:.3g}, weight ulp {ulp}, rows differing {differ} (excused {exc})")
+        # the forward's addressing makes the scores that matter exact: the oracle's slots and weights
+        ulp3 = check_exact_addressing(g[f"idx2_{s}"], g[f"wt2_{s}"], ri, rw, label, say)
+        say(f"[{label}] {s}: score err {err:.3g}, selection from the same scores exact (weight ulp {ulp}); "
+            f"float32 scores alone would choose differently on {differ} rows (near-ties: {exc}); "
+            f"forward addressing equals the oracle's (weight ulp {ulp3})")
     mem = x["mem0"].copy()
-    out = orc.scan(cfg, g["idx_w"], g["wt_w"], g["idx_r"], g["wt_r"], x["v"], x["alpha"], x["beta"], mem)
+    out = orc.scan(cfg, g["idx2_w"], g["wt2_w"], g["idx2_r"], g["wt2_r"], x["v"], x["alpha"], x["beta"], mem)
     check_scan(cfg, 4, label, {"out": (plain_err(g["out"], out), rel_max_err(g["out"], out)),
                                "mem": (plain_err(g["mem"], mem), rel_max_err(g["mem"], mem))}, say)
     mem = x["mem0"].copy()
-    out = orc.scan(cfg, ref_addr["w"][0], ref_addr["w"][1], ref_addr["r"][0], ref_addr["r"][1], x["v"],
-                   x["alpha"], x["beta"], mem)
-    if excused_rows:
-        say(f"[{label}] stage 5: {excused_rows} near-tie rows take the GPU's slots, weighted by the oracle's sums")
+    out = orc.forward(cfg, x["wq"], x["rq"], x["v"], x["alpha"], x["beta"], x["subkeys"], mem)[0]
     check_scan(cfg, 5, label, {"out": (plain_err(g["out"], out), rel_max_err(g["out"], out)),
                                "mem": (plain_err(g["mem"], mem), rel_max_err(g["mem"], mem))}, say)
-    return excused_rows
 
 
 REDUCED = {
@@ -304,6 +308,8 @@ def full_size_parity(orc, T, cfg, label, padded=False):
             layer.score(dev[s_ + "q"], dev["subkeys"], sc)
             layer.select(sc, idx, wt)
             g[f"scores_{s_}"], g[f"idx_{s_}"], g[f"wt_{s_}"] = to_host(sc), to_host(idx), to_host(wt)
+            layer.address(dev[s_ + "q"], dev["subkeys"], idx, wt)
+            g[f"idx2_{s_}"], g[f"wt2_{s_}"] = to_host(idx), to_host(wt)
             del sc
         layer.forward(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem, out)
         T.cuda.synchronize()
@@ -328,8 +334,6 @@ def full_size_parity(orc, T, cfg, label, padded=False):
     T.cuda.empty_cache()
 
     # stages 1-3 on every row
-    excused_rows = 0
-    ref_addr = {}
     for s_, q in (("w", x["wq"]), ("r", x["rq"])):
         say(f"[{label}] {s_}: oracle scores of {R} rows")
         ref_scores = orc.scores(cfg, q, x["subkeys"])
@@ -343,32 +347,28 @@ def full_size_parity(orc, T, cfg, label, padded=False):
         del ui, uw
         ri, rw, rs = orc.address_from_scores(cfg, ref_scores)
         differ, exc = compare_index_sets(orc, cfg, g[f"idx_{s_}"], ri, rs, ref_scores)
-        ri, rw, _ = resolve_near_ties(orc, cfg, g[f"idx_{s_}"], ri, rw, ref_scores)
-        ref_addr[s_] = (ri, rw)
-        excused_rows += exc
-        say(f"[{label}] {s_}: score err {err:.3g}, weight ulp {ulp}, rows differing {differ} (excused {exc}) "
-            f"of {R}")
-        del ref_scores, g[f"scores_{s_}"]
+        ulp3 = check_exact_addressing(g[f"idx2_{s_}"], g[f"wt2_{s_}"], ri, rw, label, say)
+        say(f"[{label}] {s_}: score err {err:.3g}, selection from the same scores exact (weight ulp {ulp}); "
+            f"float32 scores alone would choose differently on {differ} of {R} rows (near-ties: {exc}); "
+            f"forward addressing equals the oracle's on every row (weight ulp {ulp3})")
+        del ref_scores, g[f"scores_{s_}"], ri, rw, rs
 
-    # stages 4 and 5, sequence by sequence
+    # stages 4 and 5, sequence by sequence; the oracle addresses from the queries for stage 5
     acc = {k: PlainAccum() for k in ("out4", "mem4", "out5", "mem5")}
-    if excused_rows:
-        say(f"[{label}] stage 5: {excused_rows} near-tie rows take the GPU's slots, weighted by the oracle's sums")
     c1 = cfg.replace(B=1)
     per = cfg.T * cfg.H
     for b in range(cfg.B):
         rows = slice(b * per, (b + 1) * per)
-        xb = {k: np.ascontiguousarray(x[k][b:b + 1]) for k in ("v", "alpha", "beta")}
+        xb = {k: np.ascontiguousarray(x[k][b:b + 1]) for k in ("wq", "rq", "v", "alpha", "beta")}
         m0 = to_host(mem0[b:b + 1])
         gm = to_host(mem[b:b + 1])
         m = m0.copy()
-        o4 = orc.scan(c1, g["idx_w"][rows], g["wt_w"][rows], g["idx_r"][rows], g["wt_r"][rows], xb["v"],
+        o4 = orc.scan(c1, g["idx2_w"][rows], g["wt2_w"][rows], g["idx2_r"][rows], g["wt2_r"][rows], xb["v"],
                       xb["alpha"], xb["beta"], m)
         acc["out4"].add(g_out[b:b + 1], o4)
         acc["mem4"].add(gm, m)
         m = m0
-        o5 = orc.scan(c1, ref_addr["w"][0][rows], ref_addr["w"][1][rows], ref_addr["r"][0][rows],
-                      ref_addr["r"][1][rows], xb["v"], xb["alpha"], xb["beta"], m)
+        o5 = orc.forward(c1, xb["wq"], xb["rq"], xb["v"], xb["alpha"], xb["beta"], x["subkeys"], m)[0]
         acc["out5"].add(g_out[b:b + 1], o5)
         acc["mem5"].add(gm, m)
         say(f"[{label}] sequence {b}: stage 4 so far out max/RMS {acc['out4'].value():.3g}, memory "
@@ -398,8 +398,8 @@ def test_full_long_planted(orc, T):
     cfg = gi.config(3)
     g = full_size_parity(orc, T, cfg, "long")
     # the recurring query selects bit-identical slots and weights on the GPU
-    assert np.array_equal(g["idx_r"][cfg.T - 17], g["idx_w"][61])
-    assert np.array_equal(g["wt_r"][cfg.T - 17], g["wt_w"][61])
+    assert np.array_equal(g["idx2_r"][cfg.T - 17], g["idx2_w"][61])
+    assert np.array_equal(g["wt2_r"][cfg.T - 17], g["wt2_w"][61])
 
 
 @pytest.mark.timeout(1200)

@@ -3,7 +3,9 @@ oracle's selection of the very same scores: indices bit-exact, weights within
 one ulp.  The scores are built to hit every exact path of the kernel: heavy
 ties inside a half (more than 64 scores at the per-half bound), float sums that
 tie although their half scores differ (then slot order decides at the W-th
-sum), signed zeros, wide magnitudes, and the plain random case."""
+sum), signed zeros, wide magnitudes, and the plain random case.  Then the
+forward's addressing (sdm_address, which makes the scores that can reach a top
+k exact) from crafted queries and sub-keys against the oracle's addressing."""
 import numpy as np
 import pytest
 
@@ -69,3 +71,69 @@ def test_selection_of_crafted_scores_is_exact(S, k, W):
             torch.cuda.synchronize()
             ui, uw, _ = orc.address_from_scores(cfg, sc)
             check_selection_exact(idx.cpu().numpy(), wt.cpu().numpy(), ui, uw)
+
+
+# ---------------------------------------------------------------------------
+# the forward's addressing (sdm_address) from crafted queries and sub-keys
+# ---------------------------------------------------------------------------
+
+def _crafted_tables(S, dh, rng, kind):
+    """Sub-key tables [1, 2, S, dh] and the rows of the queries they are built for."""
+    K = (rng.standard_normal((1, 2, S, dh)) * 0.25).astype(np.float32)
+    if kind == "cancellation":
+        # row 0: 1 + 2^-25 - 1 (exactly 2^-25; a float32 sum in index order loses it), row 1: 2^-26,
+        # both above every other row for a query of ones; the other half the same, shifted by 2
+        for half in range(2):
+            K[0, half] = -1.0
+            K[0, half, 2 * half, :3] = [1.0, 2.0 ** -25, -1.0]
+            K[0, half, 2 * half, 3:] = 0.0
+            K[0, half, 2 * half + 1] = 0.0
+            K[0, half, 2 * half + 1, 0] = 2.0 ** -26
+    elif kind == "equal_rows":
+        # every sub-key of half 0 the same: more than 64 candidates tie, every score is made exact
+        K[0, 0] = K[0, 0, :1]
+    elif kind == "duplicate_rows":
+        K[0, 1, 1::2] = K[0, 1, ::2][: S // 2]
+    return K
+
+
+@pytest.mark.parametrize("in_bf16", [False, True])
+@pytest.mark.parametrize("kind,S,k,W", [("cancellation", 8, 1, 1), ("cancellation", 8, 2, 3), ("equal_rows", 100, 6, 20),
+                                         ("duplicate_rows", 48, 8, 30), ("random", 480, 32, 64)])
+def test_forward_addressing_equals_the_oracle(kind, S, k, W, in_bf16):
+    """sdm_address (the forward's addressing) against the oracle's addressing of the same queries:
+    the same slots, weights within one float32 unit, also where float32 sums order scores wrongly
+    (cancellation) and where more than 64 scores of a half tie (every score made exact)."""
+    import torch
+    from parity import to_dev, to_host
+    from sdm_inputs import bf16_bits_from_f32, f32_from_bf16_bits
+    from sparse_memory_linear_pk_amd import SDM
+    orc = oracle.get()
+    dh = 16 if kind == "cancellation" else 64
+    T = 40
+    cfg = gi.config(0).replace(B=1, H=1, T=T, d=8, S=S, dk=2 * dh, k=k, W=W, in_bf16=in_bf16)
+    rng = np.random.default_rng(7)
+    K = _crafted_tables(S, dh, rng, kind)
+    q = rng.standard_normal((1, T, 1, 2 * dh)).astype(np.float32)
+    if kind == "cancellation":
+        q[:, ::2] = 1.0
+        q[:, 1::4] = 2.0
+    if in_bf16:
+        K = bf16_bits_from_f32(K).reshape(K.shape)
+        q = bf16_bits_from_f32(q).reshape(q.shape)
+    with SDM.from_config(cfg) as layer:
+        idx = torch.empty((T, W), dtype=torch.int32, device="cuda")
+        wt = torch.empty((T, W), dtype=torch.float32, device="cuda")
+        layer.address(to_dev(q), to_dev(K), idx, wt)
+        sc = torch.empty((T, 2, S), dtype=torch.float32, device="cuda")
+        layer.score(to_dev(q), to_dev(K), sc)
+        torch.cuda.synchronize()
+    gi_, gw = to_host(idx), to_host(wt)
+    ri, rw, _ = orc.address(cfg, q, K)
+    fi, _, _ = orc.address_from_scores(cfg, to_host(sc))
+    print(f"[exact {kind} bf16={in_bf16}] rows where the float32 scores alone would select differently: "
+          f"{int((fi != ri).any(axis=1).sum())} of {T}", flush=True)
+    bad = np.nonzero((gi_ != ri).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ from the oracle, first {bad[:4]}"
+    u = np.abs(gw.view(np.int32).astype(np.int64) - rw.view(np.int32).astype(np.int64))
+    assert u.max() <= 1
