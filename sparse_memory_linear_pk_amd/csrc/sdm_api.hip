@@ -109,6 +109,19 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
 // Elements from one slot row of a memory to the next in the state tensors.
 int mem_stride_of(const sdm_config& c) { return c.mem_stride ? c.mem_stride : c.d; }
 
+// The integer a caller stored in a dtype field.  A C caller (or a binding) may
+// store any int there, and loading an enum object that holds a value outside its
+// enumerators is undefined in C++, so unchecked configs are read through this.
+static_assert(sizeof(sdm_dtype) == sizeof(int) && sizeof(sdm_status) == sizeof(int),
+              "sdm_dtype and sdm_status are int-sized in the C ABI");
+
+int dtype_bits(const sdm_dtype& f)
+{
+    int v;
+    memcpy(&v, &f, sizeof v);
+    return v;
+}
+
 // The shape checks that need no scan plan (and allocate nothing).
 sdm_status check_shape(const sdm_config* c)
 {
@@ -117,9 +130,9 @@ sdm_status check_shape(const sdm_config* c)
     if (c->B < 1 || c->H < 1 || c->T < 1 || c->d < 1 || c->n_sub < 1 || c->dk < 1 || c->k < 1 || c->W < 1)
         return fail(SDM_ERR_INVALID_ARG, "every size must be >= 1 (B=%d H=%d T=%d d=%d S=%d dk=%d k=%d W=%d)", c->B,
                     c->H, c->T, c->d, c->n_sub, c->dk, c->k, c->W);
-    if ((c->in_dtype != SDM_F32 && c->in_dtype != SDM_BF16) ||
-        (c->state_dtype != SDM_F32 && c->state_dtype != SDM_BF16))
-        return fail(SDM_ERR_INVALID_ARG, "unknown dtype");
+    const int in_dt = dtype_bits(c->in_dtype), st_dt = dtype_bits(c->state_dtype);
+    if ((in_dt != SDM_F32 && in_dt != SDM_BF16) || (st_dt != SDM_F32 && st_dt != SDM_BF16))
+        return fail(SDM_ERR_INVALID_ARG, "unknown dtype (in %d, state %d)", in_dt, st_dt);
     if (c->dk % 2)
         return fail(SDM_ERR_INVALID_ARG, "dk=%d must be even (two halves)", c->dk);
     if (c->k > c->n_sub)
@@ -390,7 +403,9 @@ extern "C" {
 
 const char* sdm_status_str(sdm_status s)
 {
-    switch (s) {
+    int code; // any int a C caller passed (an enum object out of its range may not be loaded in C++)
+    memcpy(&code, &s, sizeof code);
+    switch (code) {
     case SDM_OK: return "ok";
     case SDM_ERR_INVALID_ARG: return "invalid argument";
     case SDM_ERR_UNSUPPORTED: return "unsupported shape";
@@ -406,11 +421,12 @@ int sdm_mem_stride_hint(const sdm_config* cfg)
 {
     if (!cfg)
         return 0;
-    const int s = cfg->state_dtype == SDM_BF16 ? 2 : 4;
-    if ((cfg->d * s) % 128 || cfg->d * s < 1024)
+    const long s = dtype_bits(cfg->state_dtype) == SDM_BF16 ? 2 : 4;
+    const long row = (long)cfg->d * s; // bytes of a dense row (d is not validated here)
+    if (row % 128 || row < 1024 || row >= (1l << 30))
         return cfg->d;
-    const int units = cfg->d * s / 128; // 128-byte units of a dense row
-    return (units | 1) * 128 / s;
+    const long units = row / 128; // 128-byte units of a dense row
+    return (int)((units | 1) * 128 / s);
 }
 
 sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes)
