@@ -182,12 +182,15 @@ def decode_bench(args, cfg):
     for t in range(args.warmup):
         layer.step(tok[t]["wq"], tok[t]["rq"], tok[t]["v"], tok[t]["alpha"], tok[t]["beta"], d["subkeys"], d["mem0"], out)
     torch.cuda.synchronize()
-    layer.set_timing(True)
     t0 = time.perf_counter()
     for t in range(args.warmup, c.T):
         layer.step(tok[t]["wq"], tok[t]["rq"], tok[t]["v"], tok[t]["alpha"], tok[t]["beta"], d["subkeys"], d["mem0"], out)
     torch.cuda.synchronize()
     sec = time.perf_counter() - t0
+    # the device time of each step: the same tokens again with HIP events around the launches
+    layer.set_timing(True)
+    for t in range(args.warmup, c.T):
+        layer.step(tok[t]["wq"], tok[t]["rq"], tok[t]["v"], tok[t]["alpha"], tok[t]["beta"], d["subkeys"], d["mem0"], out)
     tm = layer.timing()
     layer.close()
     # the same tokens through a one-token forward
@@ -272,13 +275,16 @@ def train_bench(args, cfg):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    layer.set_timing(True)
     t0 = time.perf_counter()
     for i in range(steps):
         step()
         log(f"train step {i + 1}/{steps}")
     torch.cuda.synchronize()
     sec = time.perf_counter() - t0
+    # per-kernel device times: the same steps again with HIP events around every launch
+    layer.set_timing(True)
+    for i in range(steps):
+        step()
     tm = layer.timing()
     layer.close()
     if not torch.equal(d["mem0"][0, 0, :4096], mem_check):
@@ -373,13 +379,16 @@ def project_bench(args, cfg):
     for _ in range(max(1, args.warmup)):
         layer.project(D, d["x"], d["w"], d["gate_bias"], wq, rq, v, al, be)
     torch.cuda.synchronize()
-    layer.set_timing(True)
     reps = max(args.steps, 10)
     t0 = time.perf_counter()
     for _ in range(reps):
         layer.project(D, d["x"], d["w"], d["gate_bias"], wq, rq, v, al, be)
     torch.cuda.synchronize()
     sec = time.perf_counter() - t0
+    # the kernel's device time: the same calls again with HIP events around each launch
+    layer.set_timing(True)
+    for _ in range(reps):
+        layer.project(D, d["x"], d["w"], d["gate_bias"], wq, rq, v, al, be)
     tm = layer.timing()
     layer.close()
     ms = tm["ms_project"] / tm["n_project"]
@@ -566,8 +575,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    layer.set_timing(True)
-    torch.cuda.synchronize()
+    # the headline: K forwards with nothing recorded between the library's launches
     t0 = time.perf_counter()
     for i in range(args.steps):
         step()
@@ -575,9 +583,20 @@ def main():
             log(f"step {i + 1}/{args.steps}")
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    tm = layer.timing()
     if not torch.isfinite(out).all():
         raise RuntimeError("non-finite output")
+    # the same K forwards again with HIP events around every launch, on the stream it runs on: the
+    # device time of each kernel (the scan's per launch gives the roofline); the events themselves
+    # add about 10 us between dependent launches, so this region is not the headline
+    layer.set_timing(True)
+    torch.cuda.synchronize()
+    te0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    te1 = time.perf_counter()
+    tm = layer.timing()
+    layer.set_timing(False)
 
     # The same forwards on dense slot rows (d elements apart), for comparison with the
     # padded layout the headline uses.
@@ -631,6 +650,7 @@ def main():
     # device time per forward of each kernel (a forward scans in chunks: several
     # scan launches, with the next chunk's addressing and plan overlapping)
     per_step = {k: tm[f"ms_{k}"] / args.steps for k in ("score", "select", "plan", "scan")}
+    timed_ms_per_step = (te1 - te0) * 1e3 / args.steps
     scan_launches = tm["n_scan"] / args.steps
     scan_ms = per_step["scan"]
     nbytes = scan_bytes_per_step(cfg)
@@ -663,6 +683,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if traffic is None else traffic / scan_launches,
                      "kernel": "sdm_scan", "launches_per_step": scan_launches,
+                     "timing": "HIP events around each scan launch on the caller's stream, over a second run "
+                               "of the same steps right after the headline run",
                      "bytes_per_launch": nbytes / scan_launches, "ms_per_launch": scan_ms / scan_launches,
                      "pattern_ceiling": {"achieved": nbytes / (pattern_ms * 1e-3) / 1e9, "unit": "GB/s",
                                          "ms_per_launch": pattern_ms,
@@ -677,8 +699,11 @@ def main():
                                            "frac = scan / this"}},
         "kernels_ms_per_step": {"pk_score": per_step["score"], "pk_topk": per_step["select"],
                                 "sdm_plan": per_step["plan"], "sdm_scan": scan_ms,
-                                "note": "device time of each kernel in the forward; after the first chunk, "
-                                        "pk_score, pk_topk and sdm_plan run on a second stream under the scan"},
+                                "ms_per_step_with_events": timed_ms_per_step,
+                                "note": "device time of each kernel in the forward, from HIP events around every "
+                                        "launch over a second run of the same steps (the headline run records "
+                                        "none); after the first chunk, pk_score, pk_topk and sdm_plan run on a "
+                                        "second stream under the scan"},
         "pk_score": {"tflops": score_tflops, "peak_tflops": peak_mfma, "frac": score_tflops / peak_mfma,
                      "ms_per_step_alone": score_alone_ms,
                      "note": "both query sets scored alone; in the forward the scoring of the next chunk "

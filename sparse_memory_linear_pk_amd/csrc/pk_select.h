@@ -72,7 +72,7 @@ __device__ __forceinline__ float key_value(uint32_t k)
 // is a lower bound that still has `want` keys at or above it.  Items not in play
 // carry key 0, below every float's key.
 template <int J>
-__device__ inline uint32_t kth_largest(const uint32_t (&key)[J], int want, int rounds = 32)
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&key)[J], int want, int rounds = 32)
 {
     uint32_t thr = 0;
     for (int bit = 31; bit > 31 - rounds; --bit) {
@@ -88,7 +88,7 @@ __device__ inline uint32_t kth_largest(const uint32_t (&key)[J], int want, int r
 }
 
 template <int J>
-__device__ inline int count_above(const uint32_t (&key)[J], uint32_t thr)
+__device__ __forceinline__ int count_above(const uint32_t (&key)[J], uint32_t thr)
 {
     int cnt = 0;
 #pragma unroll
@@ -132,64 +132,83 @@ __device__ __forceinline__ void wave_sync_lds()
 }
 
 // Exact score of a query half against one sub-key row: products summed in
-// double in index order, rounded once to float32.
+// double in index order, rounded once to float32.  qd: the query half as
+// doubles in LDS (stage_query).  The row streams through a ring of three
+// 16-byte pieces, each loaded two pieces before its products, which keeps the
+// registers of the selection (and so the waves per SIMD that hide the latency
+// of its dependent steps) close to those of the selection from given scores.
 template <bool BF16>
-__device__ inline float exact_score(const void* q_half, const void* krow, int dh)
+__device__ __forceinline__ float exact_score(const double* __restrict__ qd, const void* krow, int dh)
 {
+    constexpr int EPP = BF16 ? 8 : 4; // elements per 16-byte piece
+    const uint4* kp = static_cast<const uint4*>(krow);
+    const int np = dh / EPP;          // at least 2 (dh >= 16)
     double acc = 0.0;
-    if constexpr (BF16) {
-        const uint4* qp = static_cast<const uint4*>(q_half);
-        const uint4* kp = static_cast<const uint4*>(krow);
-        for (int c = 0; c < dh / 8; ++c) {
-            const uint4 a = qp[c], b = kp[c];
-            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+    uint4 p0 = kp[0], p1 = kp[1];
+    for (int c = 0; c < np; ++c) {
+        const uint4 b = p0;
+        p0 = p1;
+        p1 = kp[min(c + 2, np - 1)]; // past the row: its last piece again, not used
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                acc = fma((double)bf16_lo(aw[w]), (double)bf16_lo(bw[w]), acc);
-                acc = fma((double)bf16_hi(aw[w]), (double)bf16_hi(bw[w]), acc);
+        for (int w = 0; w < 4; ++w) {
+            if constexpr (BF16) {
+                acc = fma(qd[c * EPP + 2 * w], (double)bf16_lo(bw[w]), acc);
+                acc = fma(qd[c * EPP + 2 * w + 1], (double)bf16_hi(bw[w]), acc);
+            } else {
+                acc = fma(qd[c * EPP + w], (double)__uint_as_float(bw[w]), acc);
             }
-        }
-    } else {
-        const float4* qp = static_cast<const float4*>(q_half);
-        const float4* kp = static_cast<const float4*>(krow);
-        for (int c = 0; c < dh / 4; ++c) {
-            const float4 a = qp[c], b = kp[c];
-            acc = fma((double)a.x, (double)b.x, acc);
-            acc = fma((double)a.y, (double)b.y, acc);
-            acc = fma((double)a.z, (double)b.z, acc);
-            acc = fma((double)a.w, (double)b.w, acc);
         }
     }
     return __double2float_rn(acc);
 }
 
-// What the exact path of one half needs: the row's query half, the half's
-// sub-key table [S, dh] and E, the bound on |approximate - exact| of its scores.
+// A query of dk elements (bf16 or float32) converted by one wave to doubles in
+// its LDS buffer qd (dk doubles).
+template <bool BF16>
+__device__ __forceinline__ void stage_query(const void* q, double* qd, int dk, int lane)
+{
+    for (int c = lane; c < dk; c += 64)
+        qd[c] = BF16 ? (double)__uint_as_float((uint32_t)static_cast<const uint16_t*>(q)[c] << 16)
+                     : (double)static_cast<const float*>(q)[c];
+    wave_sync_lds();
+}
+
+// What the exact path of one half needs: the row's query half as doubles (in
+// LDS), the half's sub-key table [S, dh] and E, the bound on |approximate -
+// exact| of its scores.
 struct Refine {
-    const void* q_half;
+    const double* qd;
     const void* table;
     int dh;
     float E;
 };
 
-// E for a query half: 2 (dh + 2) 2^-24 sum_c |q_c| kmax, kmax = max |K| over
-// the half's table; every lane returns it.
-template <bool BF16>
-__device__ inline float error_bound(const void* q_half, int dh, float kmax, int lane)
+// The largest of n partial maxima (n <= 64), on every lane.
+__device__ __forceinline__ float max_of_parts(const float* part, int n, int lane)
 {
-    float a = 0.f;
-    for (int c = lane; c < dh; c += 64)
-        a += BF16 ? fabsf(__uint_as_float((uint32_t)static_cast<const uint16_t*>(q_half)[c] << 16))
-                  : fabsf(static_cast<const float*>(q_half)[c]);
+    float m = lane < n ? part[lane] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        m = fmaxf(m, __shfl_xor(m, o));
+    return m;
+}
+
+// E for a query half (every lane returns it): 2 (dh + 2) 2^-24 sum_c |q_c|
+// kmax, kmax = max |K| over the half's table.
+__device__ __forceinline__ float half_bound(const Refine& r, float kmax, int lane)
+{
+    double a = 0.0;
+    for (int c = lane; c < r.dh; c += 64)
+        a += fabs(r.qd[c]);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1)
-        a += __shfl_xor(a, m);
-    // the float sums above lose at most a few parts in 2^24 of a: covered by the factor 2
-    return 2.f * (float)(dh + 2) * 0x1p-24f * a * kmax;
+        a += shfl_xor_f64(a, m);
+    return (float)(2.0 * (double)(r.dh + 2) * 0x1p-24 * a * (double)kmax);
 }
 
 // The largest float32 no larger than x.
-__device__ inline float float_down(double x)
+__device__ __forceinline__ float float_down(double x)
 {
     float f = __double2float_rn(x);
     if ((double)f > x) { // one float step down
@@ -206,8 +225,8 @@ __device__ inline float float_down(double x)
 // With ref, the scores that can reach the top k are made exact first (see the
 // header): the survivors and their keys are those of the exact scores.
 template <int J, bool BF16>
-__device__ inline uint64_t half_sorted_topk_exact(const float* __restrict__ s, int S, int k, int lane, uint64_t* buf,
-                                                  const Refine& ref)
+__device__ __forceinline__ uint64_t half_sorted_topk_exact(const float* __restrict__ s, int S, int k, int lane,
+                                                           uint64_t* buf, Refine ref)
 {
     uint32_t key[J];
 #pragma unroll
@@ -248,7 +267,9 @@ __device__ inline uint64_t half_sorted_topk_exact(const float* __restrict__ s, i
         uint64_t x = 0ull;
         if (lane < placed) {
             const uint32_t sk = (uint32_t)buf[lane];
-            const float e = exact_score<BF16>(ref.q_half, table + sk * row_bytes, ref.dh);
+            const void* krow = table + sk * row_bytes;
+            // rows of 256 bytes (bf16 halves of 128, float32 halves of 64) with every load up front
+            const float e = exact_score<BF16>(ref.qd, krow, ref.dh);
             x = ((uint64_t)ordered_key(e) << 32) | (uint64_t)(~sk);
         }
         wave_sync_lds();
@@ -258,7 +279,7 @@ __device__ inline uint64_t half_sorted_topk_exact(const float* __restrict__ s, i
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int idx = j * 64 + lane;
-        key[j] = idx < S ? ordered_key(exact_score<BF16>(ref.q_half, table + idx * row_bytes, ref.dh)) : 0u;
+        key[j] = idx < S ? ordered_key(exact_score<BF16>(ref.qd, table + idx * row_bytes, ref.dh)) : 0u;
     }
     thr = kth_largest<J>(key, k);
     const int need = k - count_above<J>(key, thr);
@@ -285,7 +306,7 @@ __device__ inline uint64_t half_sorted_topk_exact(const float* __restrict__ s, i
 // Top k of one half, sorted (score desc, index asc): lane r < k ends with the
 // r-th survivor as (key << 32) | ~index.  buf: 64 entries of wave scratch.
 template <int J>
-__device__ inline uint64_t half_sorted_topk(const float* __restrict__ s, int S, int k, int lane, uint64_t* buf)
+__device__ __forceinline__ uint64_t half_sorted_topk(const float* __restrict__ s, int S, int k, int lane, uint64_t* buf)
 {
     uint32_t key[J];
 #pragma unroll
@@ -334,7 +355,7 @@ __device__ inline uint64_t half_sorted_topk(const float* __restrict__ s, int S, 
 // The W best of M candidates per lane (key, slot), given thr, the W-th largest
 // key: ties at thr taken in slot order; the winners go to win[0..W) unsorted.
 template <int M>
-__device__ inline void select_w(const uint32_t (&key)[M], const uint32_t (&slot)[M], int W, uint32_t thr, uint64_t* win)
+__device__ __forceinline__ void select_w(const uint32_t (&key)[M], const uint32_t (&slot)[M], int W, uint32_t thr, uint64_t* win)
 {
     const int need = W - count_above<M>(key, thr);
     int n_eq = 0;
@@ -388,7 +409,7 @@ inline int pair_count(int k, int W)
 // Step 1 for one half by one wave: the half's sorted top k into val[lane] and
 // sub[lane] (scores and sub-key indices, 64 entries; lanes past k hold padding).
 template <int J>
-__device__ inline void select_half(const float* s, int S, int k, int lane, uint64_t* buf, float* val, uint32_t* sub)
+__device__ __forceinline__ void select_half(const float* s, int S, int k, int lane, uint64_t* buf, float* val, uint32_t* sub)
 {
     const uint64_t x = half_sorted_topk<J>(s, S, k, lane, buf);
     val[lane] = key_value((uint32_t)(x >> 32));
@@ -398,8 +419,8 @@ __device__ inline void select_half(const float* s, int S, int k, int lane, uint6
 // The same with exact scores (the forward's path): the list holds the exact
 // top k and their exact scores.
 template <int J, bool BF16>
-__device__ inline void select_half_exact(const float* s, int S, int k, int lane, uint64_t* buf, float* val,
-                                         uint32_t* sub, const Refine& ref)
+__device__ __forceinline__ void select_half_exact(const float* s, int S, int k, int lane, uint64_t* buf, float* val,
+                                                  uint32_t* sub, Refine ref)
 {
     const uint64_t x = half_sorted_topk_exact<J, BF16>(s, S, k, lane, buf, ref);
     val[lane] = key_value((uint32_t)(x >> 32));
@@ -410,7 +431,7 @@ __device__ inline void select_half_exact(const float* s, int S, int k, int lane,
 // LDS and visible to the wave): idx_row, wt_row receive the W slots and
 // weights, best first.  buf: 64 entries of the wave's LDS scratch.
 template <int R>
-__device__ inline void select_from_lists(int S, int k, int W, int n_pairs, const uint16_t* s_pairs, int lane,
+__device__ __forceinline__ void select_from_lists(int S, int k, int W, int n_pairs, const uint16_t* s_pairs, int lane,
                                          uint64_t* buf, const float (*val)[64], const uint32_t (*sub)[64],
                                          int32_t* idx_row, float* wt_row);
 
@@ -419,7 +440,7 @@ __device__ inline void select_from_lists(int S, int k, int W, int n_pairs, const
 // scratch (64 entries each, val and sub 2 x 64); idx_row, wt_row receive the W
 // slots and weights, best first.
 template <int J, int R>
-__device__ inline void select_row(const float* s, int S, int k, int W, int n_pairs, const uint16_t* s_pairs,
+__device__ __forceinline__ void select_row(const float* s, int S, int k, int W, int n_pairs, const uint16_t* s_pairs,
                                   int lane, uint64_t* buf, float (*val)[64], uint32_t (*sub)[64],
                                   int32_t* idx_row, float* wt_row)
 {
@@ -430,21 +451,21 @@ __device__ inline void select_row(const float* s, int S, int k, int W, int n_pai
     select_from_lists<R>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
 }
 
-// select_row with exact scores: ref[h] for half h.
+// select_row with exact scores: ref0, ref1 for halves 0 and 1.
 template <int J, int R, bool BF16>
-__device__ inline void select_row_exact(const float* s, int S, int k, int W, int n_pairs, const uint16_t* s_pairs,
-                                        int lane, uint64_t* buf, float (*val)[64], uint32_t (*sub)[64],
-                                        int32_t* idx_row, float* wt_row, const Refine (&ref)[2])
+__device__ __forceinline__ void select_row_exact(const float* s, int S, int k, int W, int n_pairs,
+                                                 const uint16_t* s_pairs, int lane, uint64_t* buf, float (*val)[64],
+                                                 uint32_t (*sub)[64], int32_t* idx_row, float* wt_row, Refine ref0,
+                                                 Refine ref1)
 {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-        select_half_exact<J, BF16>(s + h * S, S, k, lane, buf, val[h], sub[h], ref[h]);
+    select_half_exact<J, BF16>(s, S, k, lane, buf, val[0], sub[0], ref0);
+    select_half_exact<J, BF16>(s + S, S, k, lane, buf, val[1], sub[1], ref1);
     wave_sync_lds();
     select_from_lists<R>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
 }
 
 template <int R>
-__device__ inline void select_from_lists(int S, int k, int W, int n_pairs, const uint16_t* s_pairs, int lane,
+__device__ __forceinline__ void select_from_lists(int S, int k, int W, int n_pairs, const uint16_t* s_pairs, int lane,
                                          uint64_t* buf, const float (*val)[64], const uint32_t (*sub)[64],
                                          int32_t* idx_row, float* wt_row)
 {

@@ -16,7 +16,7 @@ using namespace pksel;
 constexpr int kRowsPerBlock = 4; // one wave per row
 
 // What the exact path reads: the queries [B, Ts, H, dk], the sub-key tables
-// [H, 2, S, dh] and max |K| per table [H, 2].
+// [H, 2, S, dh] and kAbsmaxParts partial maxima of |K| per table ([H, 2, parts]).
 struct ExactIn {
     const void* q;
     const void* subkeys;
@@ -36,6 +36,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float
     __shared__ float s_val[kRowsPerBlock][2][64];        // sorted half lists: scores
     __shared__ uint32_t s_sub[kRowsPerBlock][2][64];     // and sub-key indices
     __shared__ uint16_t s_pairs[kPairsMax];              // restricted candidates
+    __shared__ double s_qd[EX ? kRowsPerBlock : 1][EX ? 512 : 1]; // the row's query as doubles (exact path)
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     fill_pairs(s_pairs, k, W);
@@ -53,20 +54,18 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float
         constexpr bool BF16 = EX == 1;
         const int h = (int)(row % rr.H), dh = ex.dh;
         const size_t es = BF16 ? 2 : 4;
-        Refine ref[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            ref[half].q_half = static_cast<const char*>(ex.q) + ((size_t)row * 2 * dh + (size_t)half * dh) * es;
-            ref[half].table = static_cast<const char*>(ex.subkeys) + ((size_t)(h * 2 + half) * S * dh) * es;
-            ref[half].dh = dh;
-            ref[half].E = error_bound<BF16>(ref[half].q_half, dh, ex.kmax[h * 2 + half], lane);
-        }
+        stage_query<BF16>(static_cast<const char*>(ex.q) + (size_t)row * 2 * dh * es, s_qd[wave], 2 * dh, lane);
+        const char* tab = static_cast<const char*>(ex.subkeys) + (size_t)h * 2 * S * dh * es;
+        Refine r0{s_qd[wave], tab, dh, 0.f}, r1{s_qd[wave] + dh, tab + (size_t)S * dh * es, dh, 0.f};
+        r0.E = half_bound(r0, max_of_parts(ex.kmax + (h * 2 + 0) * kAbsmaxParts, kAbsmaxParts, lane), lane);
+        r1.E = half_bound(r1, max_of_parts(ex.kmax + (h * 2 + 1) * kAbsmaxParts, kAbsmaxParts, lane), lane);
         select_row_exact<J, R, BF16>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane, s_buf[wave],
-                                     s_val[wave], s_sub[wave], idx + row * W, wt + row * W, ref);
+                                     s_val[wave], s_sub[wave], idx + row * W, wt + row * W, r0, r1);
     }
 }
 
-// max |K| of each sub-key table: one workgroup per (head, half).
+// Partial maxima of |K|: workgroup (table, part) covers the part-th of
+// kAbsmaxParts equal slices of sub-key table (h, half) = blockIdx.x.
 template <bool BF16>
 __global__ __launch_bounds__(256) void subkey_absmax_kernel(const void* __restrict__ subkeys, float* __restrict__ kmax,
                                                             int S, int dh)
@@ -74,10 +73,11 @@ __global__ __launch_bounds__(256) void subkey_absmax_kernel(const void* __restri
     __shared__ float s_red[4];
     const long n = (long)S * dh;
     const long base = (long)blockIdx.x * n;
+    const long lo = n * blockIdx.y / kAbsmaxParts, hi = n * (blockIdx.y + 1) / kAbsmaxParts;
     float m = 0.f;
-    for (long e = threadIdx.x; e < n; e += blockDim.x) {
-        const float v = BF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(subkeys)[base + e] << 16)
-                             : static_cast<const float*>(subkeys)[base + e];
+    for (long i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+        const float v = BF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(subkeys)[base + i] << 16)
+                             : static_cast<const float*>(subkeys)[base + i];
         m = fmaxf(m, fabsf(v));
     }
 #pragma unroll
@@ -87,7 +87,8 @@ __global__ __launch_bounds__(256) void subkey_absmax_kernel(const void* __restri
         s_red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0)
-        kmax[blockIdx.x] = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+        kmax[(long)blockIdx.x * kAbsmaxParts + blockIdx.y] =
+            fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 }
 
 template <int J, int EX>
@@ -131,12 +132,11 @@ hipError_t launch_ex(const float* scores, int32_t* idx, float* wt, const Rows& r
 hipError_t launch_subkey_absmax(const void* subkeys, float* kmax, int H, int S, int dh, bool in_bf16,
                                 hipStream_t stream)
 {
+    const dim3 grid((unsigned)(2 * H), (unsigned)kAbsmaxParts);
     if (in_bf16)
-        hipLaunchKernelGGL((subkey_absmax_kernel<true>), dim3((unsigned)(2 * H)), dim3(256), 0, stream, subkeys,
-                           kmax, S, dh);
+        hipLaunchKernelGGL((subkey_absmax_kernel<true>), grid, dim3(256), 0, stream, subkeys, kmax, S, dh);
     else
-        hipLaunchKernelGGL((subkey_absmax_kernel<false>), dim3((unsigned)(2 * H)), dim3(256), 0, stream, subkeys,
-                           kmax, S, dh);
+        hipLaunchKernelGGL((subkey_absmax_kernel<false>), grid, dim3(256), 0, stream, subkeys, kmax, S, dh);
     return hipGetLastError();
 }
 

@@ -50,12 +50,12 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::mutex g_scratch_mu;
 
-// A forward longer than kChunk tokens runs its scan in chunks: a first one of
-// kChunk / 2 tokens, then kChunk each, the last taking any remainder shorter
-// than kChunk / 2.  The addressing and plan of chunk c + 1 run on a second
-// stream while chunk c scans (under a running scan they take about a third of
-// the scan's time per token), so only the first, short chunk's preparation is
-// exposed.
+// A forward longer than kChunk tokens runs its scan in chunks: two of kChunk /
+// 2 tokens, then kChunk each, the last taking any remainder shorter than
+// kChunk / 2.  The addressing and plan of chunk c + 1 run on a second stream
+// while chunk c scans; beside a running scan they take about 0.7 of the scan's
+// time per token, so a chunk may be at most about 1.4 times the one before it:
+// the second chunk is as short as the first, whose preparation nothing hides.
 constexpr int kChunk = 2048;
 
 struct Chunking {
@@ -76,7 +76,8 @@ Chunking chunking_of(const sdm_config& c)
         k.start.push_back(t);
         if (t == c.T)
             return k;
-        t += kChunk < c.T - t ? kChunk : c.T - t;
+        const int len = k.C() == 1 ? kChunk / 2 : kChunk; // the second chunk as long as the first
+        t += len < c.T - t ? len : c.T - t;
     }
 }
 
@@ -101,7 +102,7 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
     // sdm_step's slot ids and weights, write then read set: 2*B*H*W of each,
     // apart from the forward's buffers (which hold B*T*H*W and T may be 1)
     L.step = align_up(2 * (size_t)c.B * c.H * c.W * sizeof(int32_t));
-    L.kmax = align_up(2 * (size_t)c.H * sizeof(float)); // max |K| per sub-key table
+    L.kmax = align_up(2 * (size_t)c.H * sdm::kAbsmaxParts * sizeof(float)); // partial max |K| per sub-key table
     L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag + L.kmax + 2 * L.step;
     return L;
 }
@@ -192,9 +193,7 @@ struct sdm_ctx {
     uint32_t magic;
     sdm_config cfg;
     hipStream_t stream;  // the caller's: scans run here
-    hipStream_t aux;     // addressing and plans of a chunked forward (default priority)
-    hipEvent_t e_start;  // the caller's stream reached the forward
-    hipEvent_t e_read;   // the first chunk's read set is selected (on the caller's stream)
+    hipStream_t aux;     // addressing and plans of a chunked forward after its first chunk (default priority)
     std::vector<hipEvent_t> e_plan; // chunk c's plan is written
     int device;
     Chunking ck;
@@ -208,7 +207,7 @@ struct sdm_ctx {
     void* frag;
     int32_t* step_idx;   // [2][B*H][W] (sdm_step)
     float* step_wt;      // [2][B*H][W]
-    float* kmax;         // [H][2]: max |K| of each sub-key table, for the exact scores of the selection
+    float* kmax;         // [H][2][kAbsmaxParts]: partial max |K| of each sub-key table (the exact selection's bound)
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
@@ -465,8 +464,6 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->ck = chunking_of(*cfg);
     h->L = layout_of(*cfg, h->ck, plans);
     h->aux = nullptr;
-    h->e_start = nullptr;
-    h->e_read = nullptr;
     h->timing = false;
     h->bwd_block = nullptr;
     h->part = h->ds = h->sub_part = h->sink = nullptr;
@@ -500,10 +497,6 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     h->step_wt = (float*)p;
     if (h->ck.C() > 1) {
         e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
-        if (e == hipSuccess)
-            e = hipEventCreateWithFlags(&h->e_start, hipEventDisableTiming);
-        if (e == hipSuccess)
-            e = hipEventCreateWithFlags(&h->e_read, hipEventDisableTiming);
         h->e_plan.assign(h->ck.C(), nullptr);
         for (int ci = 0; ci < h->ck.C() && e == hipSuccess; ++ci)
             e = hipEventCreateWithFlags(&h->e_plan[ci], hipEventDisableTiming);
@@ -511,10 +504,6 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
             for (hipEvent_t ev : h->e_plan)
                 if (ev)
                     (void)hipEventDestroy(ev);
-            if (h->e_start)
-                (void)hipEventDestroy(h->e_start);
-            if (h->e_read)
-                (void)hipEventDestroy(h->e_read);
             if (h->aux)
                 (void)hipStreamDestroy(h->aux);
             (void)hipFree(h->block);
@@ -538,8 +527,6 @@ sdm_status sdm_destroy(sdm_handle h)
         e = e == hipSuccess ? ea : e;
         for (hipEvent_t ev : h->e_plan)
             (void)hipEventDestroy(ev);
-        (void)hipEventDestroy(h->e_start);
-        (void)hipEventDestroy(h->e_read);
         (void)hipStreamDestroy(h->aux);
     }
     for (auto& tl : h->pending) {
@@ -645,56 +632,32 @@ sdm_status forward_impl(sdm_ctx* h, const void* wq, const void* rq, const void* 
         s = run_chunk_front(h, 0, wq, rq, alpha, beta, subkeys, h->stream);
         return s == SDM_OK ? run_scan(h, 0, v, mem_inout, out, h->stream, log, kind) : s;
     }
-    // Chunked: the addressing and plan of every chunk go to the aux stream in
-    // order, after whatever the caller's stream holds before this call (its
-    // inputs, and earlier calls' scans of the plans about to be rewritten); the
-    // scan of chunk c waits for its plan on the caller's stream, so chunk c + 1's
-    // addressing runs while chunk c scans.  The first chunk, whose preparation
-    // nothing hides, has its read set scored and selected on the caller's stream
-    // beside the write set on aux.  Score rows are indexed by token, so the read
-    // set's scores go one first-chunk length further on, into rows of the second
-    // chunk (every chunk after the first is at least as long), which aux scores
-    // only after the first plan, and that plan waits for the read set.
-    const sdm_config& c = h->cfg;
-    const sdm::Rows r0 = chunk_rows(h, 0);
-    hipError_t e = hipSuccess;
-    {
-        Timer t(h, K_SCORE, h->stream);
-        e = prepare_subkeys(h, subkeys, h->stream);
-    }
-    if (e == hipSuccess)
-        e = hipEventRecord(h->e_start, h->stream);
-    if (e == hipSuccess)
-        e = hipStreamWaitEvent(h->aux, h->e_start, 0);
-    if (e != hipSuccess)
-        return hip_fail(e, "stream ordering");
-    float* scores_r0 = h->scores + (size_t)h->ck.len(0) * c.H * 2 * c.n_sub;
-    s = run_score(h, wq, subkeys, h->scores, r0, h->aux, false);
-    if (s == SDM_OK)
-        s = run_select(h, h->scores, h->idx[0], h->wt[0], r0, h->aux, wq, subkeys);
-    if (s == SDM_OK)
-        s = run_score(h, rq, subkeys, scores_r0, r0, h->stream, false);
-    if (s == SDM_OK)
-        s = run_select(h, scores_r0, h->idx[1], h->wt[1], r0, h->stream, rq, subkeys);
+    // Chunked: the first chunk, whose preparation nothing hides, is addressed and
+    // planned on the caller's stream (no wait between streams before its scan);
+    // the addressing and plan of every later chunk go, in order, to the aux
+    // stream, which starts after the first plan (so after everything the
+    // caller's stream held before this call: its inputs and earlier calls' scans
+    // of the plans about to be rewritten).  The scan of chunk c waits for its
+    // plan on the caller's stream, so chunk c + 1's addressing runs while chunk
+    // c scans.
+    s = run_chunk_front(h, 0, wq, rq, alpha, beta, subkeys, h->stream);
     if (s != SDM_OK)
         return s;
-    e = hipEventRecord(h->e_read, h->stream);
+    hipError_t e = hipEventRecord(h->e_plan[0], h->stream);
     if (e == hipSuccess)
-        e = hipStreamWaitEvent(h->aux, h->e_read, 0);
+        e = hipStreamWaitEvent(h->aux, h->e_plan[0], 0);
     if (e != hipSuccess)
         return hip_fail(e, "stream ordering");
-    for (int ci = 0; ci < h->ck.C(); ++ci) {
-        s = ci == 0 ? run_plan(h, 0, h->idx[0], h->wt[0], h->idx[1], h->wt[1], alpha, beta, h->aux)
-                    : run_chunk_front(h, ci, wq, rq, alpha, beta, subkeys, h->aux);
-        if (s != SDM_OK)
+    for (int ci = 1; ci < h->ck.C(); ++ci) {
+        if ((s = run_chunk_front(h, ci, wq, rq, alpha, beta, subkeys, h->aux)) != SDM_OK)
             return s;
-        e = hipEventRecord(h->e_plan[ci], h->aux);
-        if (e == hipSuccess)
-            e = hipStreamWaitEvent(h->stream, h->e_plan[ci], 0);
-        if (e != hipSuccess)
+        if ((e = hipEventRecord(h->e_plan[ci], h->aux)) != hipSuccess)
             return hip_fail(e, "stream ordering");
-        s = run_scan(h, ci, v, mem_inout, out, h->stream, log, kind);
-        if (s != SDM_OK)
+    }
+    for (int ci = 0; ci < h->ck.C(); ++ci) {
+        if (ci > 0 && (e = hipStreamWaitEvent(h->stream, h->e_plan[ci], 0)) != hipSuccess)
+            return hip_fail(e, "stream ordering");
+        if ((s = run_scan(h, ci, v, mem_inout, out, h->stream, log, kind)) != SDM_OK)
             return s;
     }
     return SDM_OK;

@@ -73,11 +73,15 @@ hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag,
 // scores [B*Ts*H, 2, S] -> idx, wt [B*Ts*H, W].  With q ([B, Ts, H, dk]),
 // subkeys and kmax (max |K| per table, [H, 2]) the scores that can reach a
 // half's top k are recomputed exactly first (double sums in index order, one
-// rounding); with q null the scores are taken as given.
+// rounding); with q null the scores are taken as given.  kmax: the partial
+// maxima of launch_subkey_absmax.
 hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
                           const void* q, const void* subkeys, const float* kmax, int dh, bool in_bf16,
                           hipStream_t stream);
-// kmax[h * 2 + half] = max |K| over sub-key table (h, half).
+// Partial maxima of |K| per sub-key table: kmax[(h * 2 + half) * kAbsmaxParts + p]
+// is the largest magnitude in the p-th of kAbsmaxParts slices of table (h, half);
+// the selection reduces the parts itself (no atomics, nothing to clear first).
+constexpr int kAbsmaxParts = 32;
 hipError_t launch_subkey_absmax(const void* subkeys, float* kmax, int H, int S, int dh, bool in_bf16,
                                 hipStream_t stream);
 

@@ -50,8 +50,8 @@ constexpr uint32_t kSlotMask = 0xFFFFFu;
 // plan
 // ---------------------------------------------------------------------------
 
-constexpr int kPlanTokens = 32;
-constexpr int kPlanThreads = 256;
+constexpr int kPlanTokens = 32;  // tokens per plan workgroup (at most; 16 when 32 leave CUs idle)
+constexpr int kPlanThreads = 512;
 constexpr int kFilterWords = 4096; // a 2^17-bit hashed filter of the slots written near a tile
 
 __device__ __forceinline__ uint32_t filter_bit(int n) { return ((uint32_t)n * 2654435761u) >> 15; }
@@ -79,6 +79,7 @@ struct PlanArgs {
     int Ts, t0;        // tokens per sequence of idx, wt, alpha, beta; the chunk's first token
     uint32_t N;        // slots per memory (the staged sentinel slot id)
     uint32_t v_bytes;  // bytes of one value element (staged header offsets)
+    int tile;          // tokens per workgroup, at most kPlanTokens
 };
 
 // For every token t and position i: the write slot's latest write by a token in
@@ -100,10 +101,10 @@ __global__ __launch_bounds__(kPlanThreads) void sdm_plan_kernel(PlanArgs a)
     extern __shared__ int32_t s_plan[];
     const int T = a.T, H = a.H, W = a.W;
     const int Tout = STAGED ? a.Tp : T; // tokens written per memory
-    const int tiles = (Tout + kPlanTokens - 1) / kPlanTokens;
+    const int tiles = (Tout + a.tile - 1) / a.tile;
     const int bh = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     const int b = bh / H, h = bh % H;
-    const int t0 = tile * kPlanTokens, t1 = min(Tout, t0 + kPlanTokens);
+    const int t0 = tile * a.tile, t1 = min(Tout, t0 + a.tile);
     const int lo = max(0, min(T, t0) - WIN), hi = min(T, t1 + P);
     const int span = max(0, hi - lo);
     int32_t* s_slot = s_plan;
@@ -761,7 +762,10 @@ hipError_t launch_sdm_plan(const ScanPlan& p, const int32_t* idx_w, const float*
     a.N = (uint32_t)N;
     a.v_bytes = in_bf16 ? 2u : 4u;
     const int P = p.staged ? staged::kP : kLookahead, WIN = p.staged ? staged::kWindow : 2 * kLookahead;
-    const int tiles = ((p.staged ? p.Tp : T) + kPlanTokens - 1) / kPlanTokens;
+    // 32 tokens a workgroup, or 16 when that leaves most CUs without one (short chunks)
+    const int Tout = p.staged ? p.Tp : T;
+    a.tile = (long)((Tout + kPlanTokens - 1) / kPlanTokens) * B * H < 512 ? kPlanTokens / 2 : kPlanTokens;
+    const int tiles = (Tout + a.tile - 1) / a.tile;
     const size_t lds = ((size_t)(kPlanTokens + WIN + P) * 64 * 2 + kFilterWords + kPlanTokens) * sizeof(int32_t);
     if (p.staged)
         hipLaunchKernelGGL((sdm_plan_kernel<staged::kP, staged::kWindow, true>), dim3((unsigned)(tiles * B * H)),

@@ -59,8 +59,9 @@ struct StepArgs {
 // sc[query][half][S]: rows 0 (write) and 1 (read) of a 32-row MFMA tile whose
 // other rows are zero; the 32 columns are sub-keys.  Operands, instruction and
 // k-step order are pk_score's, so each score is the same float.  kmax[half]
-// receives this wave's share of max |K| of table `half` (every element of a
-// table is loaded by one lane of one wave); the caller reduces over the waves.
+// receives this lane's share of max |K| of table `half` (every element of a
+// table is loaded by one lane of one wave); the caller reduces over the lanes
+// and waves.
 template <int DH, bool BF16>
 __device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int wave, float (&kmax)[2])
 {
@@ -155,7 +156,7 @@ __device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int 
 
 // Each wave's max |K| of both tables into s_km[wave][half] (visible after the
 // next barrier).
-__device__ __forceinline__ void publish_kmax(float (&km)[2], float (*s_km)[2], int lane, int wave)
+__device__ __forceinline__ void publish_kmax(const float (&km)[2], float (*s_km)[2], int lane, int wave)
 {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -173,18 +174,17 @@ __device__ __forceinline__ float kmax_of(const float (*s_km)[2], int half)
     return fmaxf(fmaxf(s_km[0][half], s_km[1][half]), fmaxf(s_km[2][half], s_km[3][half]));
 }
 
-// The exact-score inputs of query half `half` of row bh (query 0 write, 1 read).
+// The exact-score inputs of query half `half` of memory bh's table, the query
+// staged as doubles in qd (pksel::stage_query).
 template <int DH, bool BF16>
-__device__ __forceinline__ pksel::Refine step_refine(const StepArgs& a, int bh, int query, int half, float kmax,
-                                                     int lane)
+__device__ __forceinline__ pksel::Refine step_refine(const StepArgs& a, int bh, const double* qd, int half,
+                                                     const float (*s_km)[2], int lane)
 {
     const size_t es = BF16 ? 2 : 4;
     const int h = bh % a.H;
-    pksel::Refine r;
-    r.q_half = static_cast<const char*>(query ? a.rq : a.wq) + ((size_t)bh * 2 * DH + (size_t)half * DH) * es;
-    r.table = static_cast<const char*>(a.subkeys) + (size_t)(h * 2 + half) * a.S * DH * es;
-    r.dh = DH;
-    r.E = pksel::error_bound<BF16>(r.q_half, DH, kmax, lane);
+    pksel::Refine r{qd + half * DH, static_cast<const char*>(a.subkeys) + (size_t)(h * 2 + half) * a.S * DH * es, DH,
+                    0.f};
+    r.E = pksel::half_bound(r, kmax_of(s_km, half), lane);
     return r;
 }
 
@@ -197,6 +197,7 @@ __global__ __launch_bounds__(kWaves * 64) void step_address_kernel(StepArgs a)
     __shared__ uint32_t s_sub[2][2][64];
     __shared__ uint16_t s_pairs[pksel::kPairsMax];
     __shared__ float s_km[kWaves][2];
+    __shared__ double s_qd[2][2 * DH];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bh = blockIdx.x;
     pksel::fill_pairs(s_pairs, a.k, a.W);
@@ -206,10 +207,13 @@ __global__ __launch_bounds__(kWaves * 64) void step_address_kernel(StepArgs a)
     __syncthreads();
     if (wave < 2) { // wave 0 selects the write slots, wave 1 the read slots
         const long o = ((long)wave * a.B * a.H + bh) * a.W;
-        const pksel::Refine ref[2] = {step_refine<DH, BF16>(a, bh, wave, 0, kmax_of(s_km, 0), lane),
-                                      step_refine<DH, BF16>(a, bh, wave, 1, kmax_of(s_km, 1), lane)};
+        constexpr int es = BF16 ? 2 : 4;
+        pksel::stage_query<BF16>(static_cast<const char*>(wave ? a.rq : a.wq) + (size_t)bh * 2 * DH * es, s_qd[wave],
+                                 2 * DH, lane);
+        const pksel::Refine r0 = step_refine<DH, BF16>(a, bh, s_qd[wave], 0, s_km, lane);
+        const pksel::Refine r1 = step_refine<DH, BF16>(a, bh, s_qd[wave], 1, s_km, lane);
         pksel::select_row_exact<J, R, BF16>(s_sc + wave * 2 * a.S, a.S, a.k, a.W, a.n_pairs, s_pairs, lane,
-                                            s_buf[wave], s_val[wave], s_sub[wave], a.idx + o, a.wt + o, ref);
+                                            s_buf[wave], s_val[wave], s_sub[wave], a.idx + o, a.wt + o, r0, r1);
     }
 }
 
@@ -383,6 +387,7 @@ __global__ __launch_bounds__(kWaves * 64) void step_fused_kernel(StepArgs a, Ste
     __shared__ int32_t s_idx[2][64];
     __shared__ float s_wt[2][64];
     __shared__ float s_km[kWaves][2];
+    __shared__ double s_qd[kWaves][2 * DH];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nchunk = c.d / (128 / (int)sizeof(ST));
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
@@ -393,7 +398,9 @@ __global__ __launch_bounds__(kWaves * 64) void step_fused_kernel(StepArgs a, Ste
     __syncthreads();
     {
         const int q = wave >> 1, half = wave & 1; // waves 0, 1: write query; 2, 3: read query
-        const pksel::Refine ref = step_refine<DH, true>(a, bh, q, half, kmax_of(s_km, half), lane);
+        pksel::stage_query<true>(static_cast<const char*>(q ? a.rq : a.wq) + (size_t)bh * 2 * DH * 2, s_qd[wave],
+                                 2 * DH, lane);
+        const pksel::Refine ref = step_refine<DH, true>(a, bh, s_qd[wave], half, s_km, lane);
         pksel::select_half_exact<J, true>(s_sc + (q * 2 + half) * a.S, a.S, a.k, lane, s_buf[wave], s_val[q][half],
                                           s_sub[q][half], ref);
     }
