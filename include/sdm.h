@@ -263,7 +263,9 @@ SDM_API sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes);
 /* Stage seams (the same kernels sdm_forward runs), for staged checking.
  * sdm_score:     half scores of the B*T*H rows of q            -> scores
  * sdm_select:    top-k / outer-sum top-W / softmax of scores   -> idx, wt
- * sdm_address:   sdm_score then sdm_select, scores kept internal
+ * sdm_address:   the forward's addressing of the B*T*H rows of q -> idx, wt
+ *                (scores kept internal; the scores that can reach a half's
+ *                top k recomputed exactly, as sdm_forward does) 
  * sdm_scan_with: the scan driven by given write and read addressing */
 SDM_API sdm_status sdm_score(sdm_handle h, const void* q, const void* subkeys, float* scores);
 SDM_API sdm_status sdm_select(sdm_handle h, const float* scores, int32_t* idx, float* wt);

@@ -22,6 +22,17 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kWaves = 4;
+constexpr int kLinePitch = 72; // binary16 elements per row of a wave's transpose tile (64 and 16 bytes of pad)
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// the wave's LDS accesses done and visible to its lanes
+__device__ __forceinline__ void pksel_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // MFMA 32x32 operand layout used below (the same for A and B, so any ordering
 // of the reduction index inside a k-step cancels out): lane l supplies row or
@@ -53,12 +64,14 @@ __global__ __launch_bounds__(256) void pk_subkey_frag(const uint16_t* __restrict
 
 // A workgroup owns RB tiles of 32 rows of one head and half; each wave keeps
 // the RB query tiles in registers and walks every fourth 32-wide sub-key tile,
-// loading its operands once and using them for all RB row tiles.
-template <int DH, int RB>
+// loading its operands once and using them for all RB row tiles.  HALF: the
+// scores are stored as binary16 (rounded to nearest even), half the bytes.
+template <int DH, int RB, bool HALF>
 __global__ __launch_bounds__(kWaves * 64) void pk_score_bf16(const uint16_t* __restrict__ q,
                                                            const uint4* __restrict__ frag,
-                                                           float* __restrict__ scores, Rows r, int S)
+                                                           void* __restrict__ scores, Rows r, int S)
 {
+    constexpr uint32_t ES = HALF ? 2u : 4u; // bytes per stored score
     constexpr int KSTEPS = DH / 16;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 31, kg = lane >> 5;
@@ -92,16 +105,26 @@ __global__ __launch_bounds__(kWaves * 64) void pk_score_bf16(const uint16_t* __r
     // the last valid row's segment: a per-lane offset (sub-key column, row
     // group) plus a uniform one per row; rows past the chunk fall outside the
     // buffer and are dropped (the host keeps 128 rows below 2^31 bytes)
-    const uint32_t row_bytes = (uint32_t)(H * 2 * S) * 4u;
-    const __amdgpu_buffer_rsrc_t out = make_rsrc(scores + ((rr0 * H + h) * 2 + half) * (long)S,
-                                                 (uint32_t)(valid - 1) * row_bytes + (uint32_t)S * 4u);
+    const uint32_t row_bytes = (uint32_t)(H * 2 * S) * ES;
+    const __amdgpu_buffer_rsrc_t out =
+        make_rsrc(static_cast<char*>(scores) + (((rr0 * H + h) * 2 + half) * (long)S) * ES,
+                  (uint32_t)(valid - 1) * row_bytes + (uint32_t)S * ES);
+    // the next tile's operands load while this tile's products and stores go out
+    bf16x8_t bn[KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+        bn[kk] = wave < ctiles ? __builtin_bit_cast(bf16x8_t, fb[(wave * KSTEPS + kk) * 64]) : bf16x8_t{};
     for (int ct = wave; ct < ctiles; ct += kWaves) {
         bf16x8_t b[KSTEPS];
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
-            b[kk] = __builtin_bit_cast(bf16x8_t, fb[(ct * KSTEPS + kk) * 64]);
+            b[kk] = bn[kk];
+        const int cn = ct + kWaves < ctiles ? ct + kWaves : ct; // past the last tile: this one again, unused
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            bn[kk] = __builtin_bit_cast(bf16x8_t, fb[(cn * KSTEPS + kk) * 64]);
         const int s = ct * 32 + i;
-        const uint32_t lane_off = (uint32_t)(4 * kg) * row_bytes + (uint32_t)s * 4u;
+        const uint32_t lane_off = (uint32_t)(4 * kg) * row_bytes + (uint32_t)s * ES;
 #pragma unroll
         for (int t = 0; t < RB; ++t) {
             f32x16_t acc = {};
@@ -112,7 +135,11 @@ __global__ __launch_bounds__(kWaves * 64) void pk_score_bf16(const uint16_t* __r
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const uint32_t row_off = (uint32_t)(t * 32 + 8 * (v >> 2) + (v & 3)) * row_bytes;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v]), out, lane_off, row_off, 0);
+                    if constexpr (HALF)
+                        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)acc[v]), out,
+                                                              lane_off, row_off, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v]), out, lane_off, row_off, 0);
                 }
             }
         }
@@ -171,19 +198,110 @@ __global__ __launch_bounds__(kWaves * 64) void pk_score_f32(const float* __restr
     }
 }
 
+// Binary16 scores in whole cache lines, for S a multiple of 32: a row's two
+// halves are 4 S contiguous bytes, so with both halves of its rows in one
+// workgroup, tiles 2m and 2m + 1 of the row's 2 S / 32 column tiles (half
+// 0's, then half 1's) are exactly the row's m-th 128-byte line.  A workgroup
+// owns 64 rows (two 32-row tiles, both query halves in registers); each wave
+// walks every fourth line, passes the products through its LDS tile (32 rows x
+// 64 sub-keys) and stores each line with 8 lanes of 16 bytes, so every line is
+// written whole, once.
 template <int DH>
-hipError_t launch_dh(const void* q, const void* subkeys, const void* frag, float* scores, const Rows& r, int S,
-                     bool in_bf16, hipStream_t stream)
+__global__ __launch_bounds__(kWaves * 64) void pk_score_bf16_lines(const uint16_t* __restrict__ q,
+                                                                 const uint4* __restrict__ frag,
+                                                                 uint16_t* __restrict__ scores, Rows r, int S)
+{
+    constexpr int KSTEPS = DH / 16, RB = 2;
+    __shared__ uint16_t s_tile[kWaves][32 * kLinePitch];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = lane & 31, kg = lane >> 5;
+    uint16_t* tile = s_tile[wave];
+    const int H = r.H;
+    const int blocks = (r.Tc + 32 * RB - 1) / (32 * RB);
+    int bid = blockIdx.x;
+    const int blk = bid % blocks;
+    bid /= blocks;
+    const int b = bid % r.B, h = bid / r.B;
+    const int dk = 2 * DH;
+    const int tl0 = blk * RB * 32;
+    const int valid = min(RB * 32, r.Tc - tl0);
+    const long rr0 = (long)b * r.Ts + r.t0 + tl0;
+
+    bf16x8_t a[RB][2][KSTEPS];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) {
+        const int tl = t * 32 + i;
+        const uint16_t* qrow = q + ((rr0 + tl) * H + h) * dk + kg * 8;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk)
+                a[t][hf][kk] = tl < valid ? *reinterpret_cast<const bf16x8_t*>(qrow + hf * DH + kk * 16) : bf16x8_t{};
+    }
+    const int ctiles = S / 32, lines = ctiles; // 2 ctiles column tiles per row, two per line
+    const uint4* fb = frag + (long)h * 2 * ctiles * KSTEPS * 64 + lane; // tile c of the row: frag tile (h, c)
+    const uint32_t row_bytes = (uint32_t)(H * 4 * S);
+    const __amdgpu_buffer_rsrc_t out = make_rsrc(scores + (rr0 * H + h) * 2 * (long)S,
+                                                 (uint32_t)(valid - 1) * row_bytes + (uint32_t)S * 4u);
+    for (int m = wave; m < lines; m += kWaves) {
+        bf16x8_t b0[KSTEPS], b1[KSTEPS];
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            b0[kk] = __builtin_bit_cast(bf16x8_t, fb[((2 * m) * KSTEPS + kk) * 64]);
+            b1[kk] = __builtin_bit_cast(bf16x8_t, fb[((2 * m + 1) * KSTEPS + kk) * 64]);
+        }
+        const int hf0 = (2 * m) / ctiles, hf1 = (2 * m + 1) / ctiles; // query half of each tile
+#pragma unroll
+        for (int t = 0; t < RB; ++t) {
+            f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf0 ? a[t][1][kk] : a[t][0][kk], b0[kk], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf1 ? a[t][1][kk] : a[t][0][kk], b1[kk], acc1, 0, 0, 0);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = 8 * (v >> 2) + 4 * kg + (v & 3);
+                tile[row * kLinePitch + i] = __builtin_bit_cast(uint16_t, (_Float16)acc0[v]);
+                tile[row * kLinePitch + 32 + i] = __builtin_bit_cast(uint16_t, (_Float16)acc1[v]);
+            }
+            pksel_sync();
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int row = u * 8 + (lane >> 3), p8 = lane & 7;
+                const uint4 w = *reinterpret_cast<const uint4*>(tile + row * kLinePitch + p8 * 8);
+                const uint32_t off = (uint32_t)(t * 32 + row) * row_bytes + (uint32_t)m * 128u + (uint32_t)p8 * 16u;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, w), out, off, 0, 0);
+            }
+            pksel_sync(); // the next products overwrite the tile
+        }
+    }
+}
+
+template <int DH>
+hipError_t launch_dh(const void* q, const void* subkeys, const void* frag, void* scores, const Rows& r, int S,
+                     bool in_bf16, bool half_out, hipStream_t stream)
 {
     if (in_bf16) {
         constexpr int RB = DH <= 128 ? 4 : 2;
         const int blocks = (r.Tc + 32 * RB - 1) / (32 * RB);
-        hipLaunchKernelGGL((pk_score_bf16<DH, RB>), dim3((unsigned)(blocks * r.B * r.H * 2)), dim3(kWaves * 64), 0,
-                           stream, (const uint16_t*)q, (const uint4*)frag, scores, r, S);
+        const dim3 grid((unsigned)(blocks * r.B * r.H * 2));
+        if (half_out && S % 32 == 0) {
+            const int blocks2 = (r.Tc + 63) / 64;
+            hipLaunchKernelGGL(pk_score_bf16_lines<DH>, dim3((unsigned)(blocks2 * r.B * r.H)), dim3(kWaves * 64), 0,
+                               stream, (const uint16_t*)q, (const uint4*)frag, (uint16_t*)scores, r, S);
+        } else if (half_out)
+            hipLaunchKernelGGL((pk_score_bf16<DH, RB, true>), grid, dim3(kWaves * 64), 0, stream, (const uint16_t*)q,
+                               (const uint4*)frag, scores, r, S);
+        else
+            hipLaunchKernelGGL((pk_score_bf16<DH, RB, false>), grid, dim3(kWaves * 64), 0, stream, (const uint16_t*)q,
+                               (const uint4*)frag, scores, r, S);
     } else {
+        if (half_out)
+            return hipErrorInvalidValue;
         const int tiles = (r.Tc + 31) / 32;
         hipLaunchKernelGGL(pk_score_f32<DH>, dim3((unsigned)(tiles * r.B * r.H * 2)), dim3(kWaves * 64), 0, stream,
-                           (const float*)q, (const float*)subkeys, scores, r, S);
+                           (const float*)q, (const float*)subkeys, (float*)scores, r, S);
     }
     return hipGetLastError();
 }
@@ -200,20 +318,20 @@ hipError_t launch_pk_subkey_frag(const void* subkeys, void* frag, int H, int S, 
     return hipGetLastError();
 }
 
-hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag, float* scores, const Rows& r,
-                           int S, int dh, bool in_bf16, hipStream_t stream)
+hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag, void* scores, const Rows& r,
+                           int S, int dh, bool in_bf16, bool half_out, hipStream_t stream)
 {
     if (r.count() <= 0)
         return hipSuccess;
     switch (dh) {
-    case 16: return launch_dh<16>(q, subkeys, frag, scores, r, S, in_bf16, stream);
-    case 32: return launch_dh<32>(q, subkeys, frag, scores, r, S, in_bf16, stream);
-    case 48: return launch_dh<48>(q, subkeys, frag, scores, r, S, in_bf16, stream);
-    case 64: return launch_dh<64>(q, subkeys, frag, scores, r, S, in_bf16, stream);
-    case 96: return launch_dh<96>(q, subkeys, frag, scores, r, S, in_bf16, stream);
-    case 128: return launch_dh<128>(q, subkeys, frag, scores, r, S, in_bf16, stream);
-    case 192: return launch_dh<192>(q, subkeys, frag, scores, r, S, in_bf16, stream);
-    case 256: return launch_dh<256>(q, subkeys, frag, scores, r, S, in_bf16, stream);
+    case 16: return launch_dh<16>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
+    case 32: return launch_dh<32>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
+    case 48: return launch_dh<48>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
+    case 64: return launch_dh<64>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
+    case 96: return launch_dh<96>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
+    case 128: return launch_dh<128>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
+    case 192: return launch_dh<192>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
+    case 256: return launch_dh<256>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
     default: return hipErrorInvalidValue;
     }
 }

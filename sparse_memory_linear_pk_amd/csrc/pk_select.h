@@ -57,6 +57,14 @@ constexpr int kBoundRounds = 16;   // radix rounds of the per-half lower bound
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// A stored score as float: float32 as it is, or binary16 bits (the forward's
+// score buffer for bf16 inputs), which float holds exactly.
+__device__ __forceinline__ float score_at(const float* s, int i) { return s[i]; }
+__device__ __forceinline__ float score_at(const uint16_t* s, int i)
+{
+    return (float)__builtin_bit_cast(_Float16, s[i]);
+}
+
 __device__ __forceinline__ int rank_below(uint64_t m)
 {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -131,6 +139,34 @@ __device__ __forceinline__ void wave_sync_lds()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A counting form of the sort, for a wave that has its SIMD to itself (the
+// decode step): every lane compares its key with all 64 from LDS.  That is more
+// instructions than the bitonic network, but they are independent of one
+// another, where the network is a chain of 21 dependent exchanges that a lone
+// wave cannot hide.  The result is the same.
+// sort64_desc for keys that are distinct where nonzero (zeros are padding and
+// end up last): a key's place is the number of keys above it.  buf: 64
+// entries of wave scratch.
+__device__ __forceinline__ uint64_t sort64_desc_count(uint64_t x, int lane, uint64_t* buf)
+{
+    buf[lane] = x;
+    wave_sync_lds();
+    int gt = 0;
+#pragma unroll
+    for (int c = 0; c < 64; c += 2) {
+        const uint4 y = *reinterpret_cast<const uint4*>(buf + c);
+        gt += (int)((((uint64_t)y.y << 32) | y.x) > x) + (int)((((uint64_t)y.w << 32) | y.z) > x);
+    }
+    const int n = __popcll(ballot(x != 0ull));
+    wave_sync_lds();
+    if (x != 0ull)
+        buf[gt] = x;
+    wave_sync_lds();
+    const uint64_t r = lane < n ? buf[lane] : 0ull;
+    wave_sync_lds();
+    return r;
+}
+
 // Exact score of a query half against one sub-key row: products summed in
 // double in index order, rounded once to float32.  qd: the query half as
 // doubles in LDS (stage_query).  The row streams through a ring of three
@@ -194,17 +230,28 @@ __device__ __forceinline__ float max_of_parts(const float* part, int n, int lane
     return m;
 }
 
-// E for a query half (every lane returns it): 2 (dh + 2) 2^-24 sum_c |q_c|
-// kmax, kmax = max |K| over the half's table.
-__device__ __forceinline__ float half_bound(const Refine& r, float kmax, int lane)
+// sum_c |q_c| over a query half of dh doubles, on every lane.
+__device__ __forceinline__ double abs_sum(const double* qd, int dh, int lane)
 {
     double a = 0.0;
-    for (int c = lane; c < r.dh; c += 64)
-        a += fabs(r.qd[c]);
+    for (int c = lane; c < dh; c += 64)
+        a += fabs(qd[c]);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1)
         a += shfl_xor_f64(a, m);
-    return (float)(2.0 * (double)(r.dh + 2) * 0x1p-24 * a * (double)kmax);
+    return a;
+}
+
+// E for a query half: 2 (dh + 2) 2^-24 sum_c |q_c| kmax, kmax = max |K| over
+// the half's table.
+__device__ __forceinline__ float bound_from(double abs_q, int dh, float kmax)
+{
+    return (float)(2.0 * (double)(dh + 2) * 0x1p-24 * abs_q * (double)kmax);
+}
+
+__device__ __forceinline__ float half_bound(const Refine& r, float kmax, int lane)
+{
+    return bound_from(abs_sum(r.qd, r.dh, lane), r.dh, kmax);
 }
 
 // The largest float32 no larger than x.
@@ -220,19 +267,47 @@ __device__ __forceinline__ float float_down(double x)
     return f;
 }
 
+// Binary16 scores.  The float32 score s32 of a sub-key is stored rounded to
+// binary16, h = f16(s32), so |h - s| <= E0 + r |h| for the exact score s, with
+// E0 = E + 2^-24 (E bounds |s32 - s|; 2^-24 covers binary16's subnormal step)
+// and r = 2^-10 (binary16 rounds to 11 significant bits, and |s32| <= |h| /
+// (1 - 2^-11)).  If k stored scores are >= beta, each has s >= f(h) - E0 >=
+// f(beta) - E0 with f(x) = x - r |x| (increasing), so the k-th largest exact
+// score is at least L = f(beta) - E0.  A member of the exact top k then has
+// g(h) >= s - E0 >= L - E0 with g(x) = x + r |x| (increasing), i.e. h >=
+// g^-1(L - E0): every stored score below that is out.
+__device__ __forceinline__ double threshold_f16(float beta, float E)
+{
+    const double r = 0x1p-10, e0 = (double)E + 0x1p-24;
+    const double b = beta;
+    const double y = (b - r * fabs(b)) - 2.0 * e0;
+    return y >= 0.0 ? y / (1.0 + r) : y / (1.0 - r);
+}
+
+// E for the binary16 path: a half whose scores may leave binary16's range
+// (|s| could reach 65504) gets an infinite bound, which makes every score of
+// the half a candidate and every score exact.
+__device__ __forceinline__ float bound_f16(float E, int dh)
+{
+    const double a = (double)E / (2.0 * (double)(dh + 2) * 0x1p-24); // sum_c |q_c| max |K|
+    return a < 32768.0 ? E : __builtin_inff();
+}
+
 // Top k of one half, sorted (score desc, index asc): lane r < k ends with the
 // r-th survivor as (key << 32) | ~index.  buf: 64 entries of wave scratch.
 // With ref, the scores that can reach the top k are made exact first (see the
 // header): the survivors and their keys are those of the exact scores.
-template <int J, bool BF16>
-__device__ __forceinline__ uint64_t half_sorted_topk_exact(const float* __restrict__ s, int S, int k, int lane,
+// LAT: the counting sort (a wave alone on its SIMD).
+// SC: float (float32 scores) or uint16_t (binary16 scores; see threshold_f16).
+template <int J, bool BF16, bool LAT = false, class SC = float>
+__device__ __forceinline__ uint64_t half_sorted_topk_exact(const SC* __restrict__ s, int S, int k, int lane,
                                                            uint64_t* buf, Refine ref)
 {
     uint32_t key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int idx = j * 64 + lane;
-        key[j] = idx < S ? ordered_key(s[idx]) : 0u;
+        key[j] = idx < S ? ordered_key(score_at(s, idx)) : 0u;
     }
     uint32_t lane_max[1] = {0u};
 #pragma unroll
@@ -243,7 +318,7 @@ __device__ __forceinline__ uint64_t half_sorted_topk_exact(const float* __restri
     if (J > 1) {
         const uint32_t bound = kth_largest<1>(lane_max, k, kBoundRounds);
         const float beta = key_value(bound);
-        const double lo = (double)beta - 2.0 * (double)ref.E;
+        const double lo = sizeof(SC) == 2 ? threshold_f16(beta, ref.E) : (double)beta - 2.0 * (double)ref.E;
         // a NaN bound (NaN scores) takes every score
         thr = lo == lo ? ordered_key(float_down(lo)) : 0u;
     }
@@ -273,7 +348,7 @@ __device__ __forceinline__ uint64_t half_sorted_topk_exact(const float* __restri
             x = ((uint64_t)ordered_key(e) << 32) | (uint64_t)(~sk);
         }
         wave_sync_lds();
-        return sort64_desc(x, lane);
+        return LAT ? sort64_desc_count(x, lane, buf) : sort64_desc(x, lane);
     }
     // heavy ties: every score of the half exact, the k-th largest by a full radix select
 #pragma unroll
@@ -385,16 +460,22 @@ __device__ __forceinline__ void select_w(const uint32_t (&key)[M], const uint32_
 
 // Restricted candidate pairs of k-long sorted lists for W winners: row i of the
 // lists pairs with columns j < min(k, W / (i + 1)), listed row-major as
-// (i << 8 | j).  Filled by all threads of a block.
+// (i << 8 | j).  Written by the block's last wave (lane i: row i, from where
+// a prefix sum over the lanes' row lengths puts it); visible to the block after
+// a barrier.
 __device__ inline void fill_pairs(uint16_t* pairs, int k, int W)
 {
-    for (int i = threadIdx.x; i < k; i += blockDim.x) {
-        int off = 0;
-        for (int r = 0; r < i; ++r)
-            off += min(k, W / (r + 1));
-        const int len = min(k, W / (i + 1));
+    const int i = (int)threadIdx.x - ((int)blockDim.x - 64);
+    if (i >= 0) {
+        const int len = i < k ? min(k, W / (i + 1)) : 0;
+        int end = len;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(end, o);
+            end += i >= o ? t : 0;
+        }
         for (int j = 0; j < len; ++j)
-            pairs[off + j] = (uint16_t)((i << 8) | j);
+            pairs[end - len + j] = (uint16_t)((i << 8) | j);
     }
 }
 
@@ -418,19 +499,37 @@ __device__ __forceinline__ void select_half(const float* s, int S, int k, int la
 
 // The same with exact scores (the forward's path): the list holds the exact
 // top k and their exact scores.
-template <int J, bool BF16>
-__device__ __forceinline__ void select_half_exact(const float* s, int S, int k, int lane, uint64_t* buf, float* val,
+template <int J, bool BF16, bool LAT = false, class SC = float>
+__device__ __forceinline__ void select_half_exact(const SC* s, int S, int k, int lane, uint64_t* buf, float* val,
                                                   uint32_t* sub, Refine ref)
 {
-    const uint64_t x = half_sorted_topk_exact<J, BF16>(s, S, k, lane, buf, ref);
+    const uint64_t x = half_sorted_topk_exact<J, BF16, LAT, SC>(s, S, k, lane, buf, ref);
     val[lane] = key_value((uint32_t)(x >> 32));
     sub[lane] = ~(uint32_t)x;
 }
 
+// The W winners in lane order (lane 0 the best) as slots and weights: a softmax
+// over their sums in double, each weight rounded once to float32.
+__device__ __forceinline__ void emit_winners(uint64_t x, int W, int lane, int32_t* idx_row, float* wt_row)
+{
+    const float sig = key_value((uint32_t)(x >> 32));
+    const double mx = __shfl((double)sig, 0);
+    double e = lane < W ? exp((double)sig - mx) : 0.0;
+    double z = e;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+        z += shfl_xor_f64(z, m);
+    if (lane < W) {
+        idx_row[lane] = (int32_t)(~(uint32_t)x);
+        wt_row[lane] = (float)(e / z);
+    }
+}
+
 // Step 2 by one wave, from both halves' sorted lists (val, sub: 2 x 64, in
 // LDS and visible to the wave): idx_row, wt_row receive the W slots and
-// weights, best first.  buf: 64 entries of the wave's LDS scratch.
-template <int R>
+// weights, best first.  buf: 64 entries of the wave's LDS scratch.  LAT: the
+// counting sort.
+template <int R, bool LAT = false>
 __device__ __forceinline__ void select_from_lists(int S, int k, int W, int n_pairs, const uint16_t* s_pairs, int lane,
                                          uint64_t* buf, const float (*val)[64], const uint32_t (*sub)[64],
                                          int32_t* idx_row, float* wt_row);
@@ -452,19 +551,19 @@ __device__ __forceinline__ void select_row(const float* s, int S, int k, int W, 
 }
 
 // select_row with exact scores: ref0, ref1 for halves 0 and 1.
-template <int J, int R, bool BF16>
-__device__ __forceinline__ void select_row_exact(const float* s, int S, int k, int W, int n_pairs,
+template <int J, int R, bool BF16, bool LAT = false, class SC = float>
+__device__ __forceinline__ void select_row_exact(const SC* s, int S, int k, int W, int n_pairs,
                                                  const uint16_t* s_pairs, int lane, uint64_t* buf, float (*val)[64],
                                                  uint32_t (*sub)[64], int32_t* idx_row, float* wt_row, Refine ref0,
                                                  Refine ref1)
 {
-    select_half_exact<J, BF16>(s, S, k, lane, buf, val[0], sub[0], ref0);
-    select_half_exact<J, BF16>(s + S, S, k, lane, buf, val[1], sub[1], ref1);
+    select_half_exact<J, BF16, LAT, SC>(s, S, k, lane, buf, val[0], sub[0], ref0);
+    select_half_exact<J, BF16, LAT, SC>(s + S, S, k, lane, buf, val[1], sub[1], ref1);
     wave_sync_lds();
-    select_from_lists<R>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
+    select_from_lists<R, LAT>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
 }
 
-template <int R>
+template <int R, bool LAT>
 __device__ __forceinline__ void select_from_lists(int S, int k, int W, int n_pairs, const uint16_t* s_pairs, int lane,
                                          uint64_t* buf, const float (*val)[64], const uint32_t (*sub)[64],
                                          int32_t* idx_row, float* wt_row)
@@ -556,19 +655,8 @@ __device__ __forceinline__ void select_from_lists(int S, int k, int W, int n_pai
     wave_sync_lds();
 
     // sort the W winners, descending by (sum, ~slot)
-    const uint64_t x = sort64_desc(lane < W ? buf[lane] : 0ull, lane);
-    // softmax in double over the sorted sums; lane 0 holds the largest
-    const float sig = key_value((uint32_t)(x >> 32));
-    const double mx = __shfl((double)sig, 0);
-    double e = lane < W ? exp((double)sig - mx) : 0.0;
-    double z = e;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1)
-        z += shfl_xor_f64(z, m);
-    if (lane < W) {
-        idx_row[lane] = (int32_t)(~(uint32_t)x);
-        wt_row[lane] = (float)(e / z);
-    }
+    const uint64_t x = lane < W ? buf[lane] : 0ull;
+    emit_winners(LAT ? sort64_desc_count(x, lane, buf) : sort64_desc(x, lane), W, lane, idx_row, wt_row);
 }
 
 } // namespace pksel

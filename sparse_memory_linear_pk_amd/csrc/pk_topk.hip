@@ -4,9 +4,12 @@
 // algorithm and the argument for its exactness).  Given the queries and the
 // sub-key tables (the forward's path), the scores that can reach a half's top k
 // are first made exact (pksel::select_row_exact), so the slots and weights are
-// those of exactly rounded scores; given scores alone (the stage seam), the
-// scores are taken as they are.
+// those of exactly rounded scores; the stored scores only locate the
+// candidates, and for bf16 inputs they are binary16.  Given scores alone (the
+// stage seam), the float32 scores are taken as they are.
 #include "pk_select.h"
+
+#include <type_traits>
 
 namespace sdm {
 namespace {
@@ -25,9 +28,10 @@ struct ExactIn {
 };
 
 // J: sub-keys per lane per half (S <= 64*J); R: restricted candidates per lane;
-// EX: 0 scores as given, 1 exact from bf16 inputs, 2 exact from float32 inputs.
+// EX: 0 float32 scores as given, 1 exact from bf16 inputs (binary16 scores), 2
+// exact from float32 inputs (float32 scores).
 template <int J, int R, int EX>
-__global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float* __restrict__ scores,
+__global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const void* __restrict__ scores_v,
                                                                    int32_t* __restrict__ idx,
                                                                    float* __restrict__ wt, Rows rr, int S,
                                                                    int k, int W, int n_pairs, ExactIn ex)
@@ -48,6 +52,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float
     const long per_seq = (long)rr.Tc * rr.H;
     const long row = ((j / per_seq) * rr.Ts + rr.t0) * rr.H + j % per_seq; // row (b, t, h) of the call
     if constexpr (EX == 0) {
+        const float* scores = static_cast<const float*>(scores_v);
         select_row<J, R>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane, s_buf[wave], s_val[wave],
                          s_sub[wave], idx + row * W, wt + row * W);
     } else {
@@ -59,8 +64,15 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const float
         Refine r0{s_qd[wave], tab, dh, 0.f}, r1{s_qd[wave] + dh, tab + (size_t)S * dh * es, dh, 0.f};
         r0.E = half_bound(r0, max_of_parts(ex.kmax + (h * 2 + 0) * kAbsmaxParts, kAbsmaxParts, lane), lane);
         r1.E = half_bound(r1, max_of_parts(ex.kmax + (h * 2 + 1) * kAbsmaxParts, kAbsmaxParts, lane), lane);
-        select_row_exact<J, R, BF16>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane, s_buf[wave],
-                                     s_val[wave], s_sub[wave], idx + row * W, wt + row * W, r0, r1);
+        using SC = std::conditional_t<BF16, uint16_t, float>;
+        if constexpr (BF16) {
+            r0.E = bound_f16(r0.E, dh);
+            r1.E = bound_f16(r1.E, dh);
+        }
+        const SC* scores = static_cast<const SC*>(scores_v);
+        select_row_exact<J, R, BF16, false, SC>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane,
+                                                s_buf[wave], s_val[wave], s_sub[wave], idx + row * W, wt + row * W, r0,
+                                                r1);
     }
 }
 
@@ -92,7 +104,7 @@ __global__ __launch_bounds__(256) void subkey_absmax_kernel(const void* __restri
 }
 
 template <int J, int EX>
-hipError_t launch_j(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
+hipError_t launch_j(const void* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
                     const ExactIn& ex, hipStream_t stream)
 {
     dim3 grid((unsigned)((r.count() + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
@@ -111,7 +123,7 @@ hipError_t launch_j(const float* scores, int32_t* idx, float* wt, const Rows& r,
 }
 
 template <int EX>
-hipError_t launch_ex(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
+hipError_t launch_ex(const void* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
                      const ExactIn& ex, hipStream_t stream)
 {
     if (S <= 64)
@@ -140,7 +152,7 @@ hipError_t launch_subkey_absmax(const void* subkeys, float* kmax, int H, int S, 
     return hipGetLastError();
 }
 
-hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
+hipError_t launch_pk_topk(const void* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
                           const void* q, const void* subkeys, const float* kmax, int dh, bool in_bf16,
                           hipStream_t stream)
 {

@@ -90,7 +90,9 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
 {
     const size_t rows = (size_t)c.B * c.T * c.H;
     Layout L;
-    L.scores = align_up(rows * 2 * (size_t)c.n_sub * sizeof(float));
+    // the forward's scores: binary16 for bf16 inputs (they only locate the
+    // candidates of the exact selection), float32 otherwise
+    L.scores = align_up(rows * 2 * (size_t)c.n_sub * (c.in_dtype == SDM_BF16 ? 2u : 4u));
     L.idx = align_up(rows * (size_t)c.W * sizeof(int32_t));
     L.wt = align_up(rows * (size_t)c.W * sizeof(float));
     L.plan = 0;
@@ -200,7 +202,7 @@ struct sdm_ctx {
     std::vector<sdm::ScanPlan> plans; // scan layout of each chunk
     void* block;
     Layout L;
-    float* scores;
+    void* scores; // the forward's scores (binary16 for bf16 inputs)
     int32_t* idx[2];
     float* wt[2];
     uint4* plan_buf;
@@ -277,25 +279,29 @@ hipError_t prepare_subkeys(sdm_ctx* h, const void* subkeys, hipStream_t st)
     return e;
 }
 
-// frag: prepare the sub-key tables first (once per call that scores)
-sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, float* scores, const sdm::Rows& r,
-                     hipStream_t st, bool frag)
+// frag: prepare the sub-key tables first (once per call that scores).
+// exact: scores for the exact selection (run_select with q), stored as binary16
+// for bf16 inputs; otherwise float32 (the stage seam).
+sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, void* scores, const sdm::Rows& r,
+                     hipStream_t st, bool frag, bool exact = true)
 {
     const sdm_config& c = h->cfg;
     const bool bf16 = c.in_dtype == SDM_BF16;
-    Timer t(h, K_SCORE, st);
     hipError_t e = hipSuccess;
     if (frag)
         e = prepare_subkeys(h, subkeys, st);
-    if (e == hipSuccess)
-        e = sdm::launch_pk_score(q, subkeys, h->frag, scores, r, c.n_sub, c.dk / 2, bf16, st);
+    if (e == hipSuccess) {
+        Timer t(h, K_SCORE, st); // pk_score alone
+        e = sdm::launch_pk_score(q, subkeys, h->frag, scores, r, c.n_sub, c.dk / 2, bf16, exact && bf16, st);
+    }
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_score launch");
 }
 
 // q and subkeys given (the forward's path): the scores that can reach a half's
-// top k are made exact from them (h->kmax must be prepared); q null: the scores
-// are taken as given (the stage seam).
-sdm_status run_select(sdm_ctx* h, const float* scores, int32_t* idx, float* wt, const sdm::Rows& r, hipStream_t st,
+// top k are made exact from them (h->kmax must be prepared; the scores are
+// those of run_score with exact); q null: the float32 scores are taken as given
+// (the stage seam).
+sdm_status run_select(sdm_ctx* h, const void* scores, int32_t* idx, float* wt, const sdm::Rows& r, hipStream_t st,
                       const void* q, const void* subkeys)
 {
     const sdm_config& c = h->cfg;
@@ -478,7 +484,7 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
         return fail(SDM_ERR_OOM, "workspace of %zu bytes: %s", total, hipGetErrorString(e));
     }
     char* p = (char*)h->block;
-    h->scores = (float*)p;
+    h->scores = p;
     p += h->L.scores;
     for (int set = 0; set < 2; ++set) {
         h->idx[set] = (int32_t*)p;
@@ -556,7 +562,7 @@ sdm_status sdm_score(sdm_handle h, const void* q, const void* subkeys, float* sc
         return fail(SDM_ERR_INVALID_ARG, "sdm_score: NULL pointer");
     if (!aligned16(q) || !aligned16(subkeys) || !aligned4(scores))
         return fail(SDM_ERR_INVALID_ARG, "sdm_score: q and subkeys must be 16-byte aligned");
-    return run_score(h, q, subkeys, scores, all_rows(h->cfg), h->stream, true);
+    return run_score(h, q, subkeys, scores, all_rows(h->cfg), h->stream, true, false);
 }
 
 sdm_status sdm_select(sdm_handle h, const float* scores, int32_t* idx, float* wt)

@@ -64,18 +64,20 @@ size_t pk_score_frag_bytes(int H, int S, int dh);
 hipError_t launch_pk_subkey_frag(const void* subkeys, void* frag, int H, int S, int dh, hipStream_t stream);
 
 // Half scores of the rows of q ([B, Ts, H, dk]) against subkeys [H, 2, S, dh]
-// (float32 inputs) or frag (bf16 inputs): scores [B*Ts*H, 2, S] float32, only the
-// covered rows written.
-hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag, float* scores, const Rows& r,
-                           int S, int dh, bool in_bf16, hipStream_t stream);
+// (float32 inputs) or frag (bf16 inputs): scores [B*Ts*H, 2, S], only the
+// covered rows written, float32, or binary16 (half_out, bf16 inputs only: the
+// forward's candidates for the exact selection).
+hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag, void* scores, const Rows& r,
+                           int S, int dh, bool in_bf16, bool half_out, hipStream_t stream);
 
 // Per-half top-k, outer-sum top-W and softmax weights of the covered rows:
 // scores [B*Ts*H, 2, S] -> idx, wt [B*Ts*H, W].  With q ([B, Ts, H, dk]),
 // subkeys and kmax (max |K| per table, [H, 2]) the scores that can reach a
 // half's top k are recomputed exactly first (double sums in index order, one
-// rounding); with q null the scores are taken as given.  kmax: the partial
-// maxima of launch_subkey_absmax.
-hipError_t launch_pk_topk(const float* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
+// rounding) and the stored scores are binary16 for bf16 inputs, float32
+// otherwise; with q null the float32 scores are taken as given.  kmax: the
+// partial maxima of launch_subkey_absmax.
+hipError_t launch_pk_topk(const void* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
                           const void* q, const void* subkeys, const float* kmax, int dh, bool in_bf16,
                           hipStream_t stream);
 // Partial maxima of |K| per sub-key table: kmax[(h * 2 + half) * kAbsmaxParts + p]

@@ -10,10 +10,11 @@
 // rows.  Otherwise two launches sized for a single token:
 //
 //  1. step_address_kernel: one workgroup per (b, h) scores both queries of the
-//     token on the matrix cores, with the instruction, operand layout and
-//     reduction order of pk_score (so every score is bit-identical to it), and
-//     two of its waves select the write and the read slots with the selection
-//     of pk_topk (pk_select.h).
+//     token on the matrix cores and two of its waves select the write and the
+//     read slots with the selection of pk_topk (pk_select.h).  The float32
+//     scores only locate the candidates: the selection recomputes every score
+//     that can reach a half's top k exactly, so the slots and weights are those
+//     of the forward, whatever the order of the float32 sums.
 //  2. step_scan_kernel: one workgroup per (b, h, 128 bytes of the slot rows)
 //     loads the token's W write and W read segments at once, forms the
 //     prediction, updates and stores the write slots, and reads; a read slot
@@ -29,6 +30,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
 
 // Running maxima of bf16 magnitudes, two per word (finite bf16 magnitudes order
@@ -55,75 +57,171 @@ struct StepArgs {
     int B, H, S, k, W, n_pairs;
 };
 
-// Scores of the two queries of (b, h) against both sub-key tables, into
-// sc[query][half][S]: rows 0 (write) and 1 (read) of a 32-row MFMA tile whose
-// other rows are zero; the 32 columns are sub-keys.  Operands, instruction and
-// k-step order are pk_score's, so each score is the same float.  kmax[half]
-// receives this lane's share of max |K| of table `half` (every element of a
-// table is loaded by one lane of one wave); the caller reduces over the lanes
-// and waves.
+// Float32 scores of the two queries of (b, h) against both sub-key tables, into
+// sc[query][half][S], on the matrix cores (within the bound E of the exact
+// scores that the selection relies on, as for any order of the float32 sums).
+// kmax[half] receives this lane's share of max |K| of table `half` (every
+// element of a table is loaded by one lane of one wave); the caller reduces
+// over the lanes and waves.  float32: rows 0 (write) and 1 (read) of a 32-row
+// MFMA tile whose other rows are zero, the 32 columns sub-keys.
+//
+// bf16: a 32-column tile of sub-keys is 32 contiguous table rows.  Each wave
+// walks its tiles with D of them in flight, loaded in coalesced 16-byte pieces
+// (a kilobyte per load, through a buffer resource that ends with the tile's last
+// row, so pieces past the table read zeros) and passes each through its LDS
+// tile buffer (rows padded by 16 bytes, so that the operand reads hit distinct
+// banks) to read it back in MFMA operand order.  The A operand holds both
+// queries' halves for the whole walk: rows 0 and 1 the write and read queries'
+// first halves, rows 2 and 3 their second halves; a tile of table `half` keeps
+// rows 2 half and 2 half + 1.  Every wave issues the same loads in the same
+// order (tiles past its share read zeros), so the wait for a tile is a fixed
+// count.
+template <int DH> constexpr int step_tile_u4() { return 32 * (DH / 8 + 1); }
+
+// qd (optional, bf16): also stage query (wave >> 1) as doubles into qd and leave
+// the sum of |q| over its half `half_q` in *abs_q, while the first tiles load.
 template <int DH, bool BF16>
-__device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int wave, float (&kmax)[2])
+__device__ void step_scores(const StepArgs& a, int bh, float* sc, int lane, int wave, float (&kmax)[2], uint4* tile,
+                            double* qd = nullptr, int half_q = 0, double* abs_q = nullptr)
 {
     const int h = bh % a.H, S = a.S;
     const int i = lane & 31, kg = lane >> 5;
     const int ctiles = (S + 31) / 32;
     const int dk = 2 * DH;
     if constexpr (BF16) {
-        // The two queries' operands for both halves once, then the sub-key operands of G
-        // tiles at a time: one memory round trip per G tiles instead of per tile.  Each
-        // tile's MFMA sequence is unchanged.
-        constexpr int KSTEPS = DH / 16, G = 4;
-        bf16x8_t qv[2][KSTEPS];
+        constexpr int KSTEPS = DH / 16;
+        constexpr int RP = DH / 8;             // 16-byte pieces per table row
+        constexpr int PITCH = RP + 1;          // LDS row pitch in pieces
+        constexpr int NP = 32 * RP / 64;       // pieces per lane per tile
+        constexpr int D = NP <= 8 ? 4 : 2;     // tiles in flight: at most 32 pieces per lane
+        static_assert(32 * RP % 64 == 0, "whole pieces per lane");
+        // the raw query elements this lane stages, loaded first
+        constexpr int QE = (2 * DH + 63) / 64;
+        uint32_t qraw[QE];
+        if (qd) {
+            const __amdgpu_buffer_rsrc_t rq =
+                make_rsrc(static_cast<const uint16_t*>((wave >> 1) ? a.rq : a.wq) + (long)bh * dk, (uint32_t)dk * 2u);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const uint16_t* q = static_cast<const uint16_t*>(i == 0 ? a.wq : a.rq) + (long)bh * dk + half * DH + kg * 8;
+            for (int e = 0; e < QE; ++e)
+                qraw[e] = __builtin_amdgcn_raw_buffer_load_b16(rq, (uint32_t)(e * 64 + lane) * 2u, 0, 0);
+        }
+        // A operand: row r < 4 is half r >> 1 of query r & 1.  With half widths a
+        // multiple of 32, v_mfma_f32_16x16x32_bf16 (lane l: row or column l % 16,
+        // elements 8 (l / 16) .. + 8 of a 32-wide k-step; half the cycles of the
+        // 32-row form for the four rows in use), else v_mfma_f32_32x32x16_bf16
+        // (lane l: row or column l % 32, elements 8 (l / 32) .. + 8 of 16).
+        constexpr bool K32 = DH % 32 == 0;
+        constexpr int KS32 = K32 ? DH / 32 : 1;
+        const int c16 = lane & 15, g16 = lane >> 4;
+        bf16x8_t qv[K32 ? 1 : KSTEPS], qv32[KS32];
+        if constexpr (K32) {
+            const uint16_t* q = static_cast<const uint16_t*>((c16 & 1) ? a.rq : a.wq) + (long)bh * dk +
+                                (c16 >> 1) * DH + g16 * 8;
+#pragma unroll
+            for (int kk = 0; kk < KS32; ++kk)
+                qv32[kk] = c16 < 4 ? *reinterpret_cast<const bf16x8_t*>(q + kk * 32) : bf16x8_t{};
+        } else {
+            const uint16_t* q = static_cast<const uint16_t*>((i & 1) ? a.rq : a.wq) + (long)bh * dk + (i >> 1) * DH +
+                                kg * 8;
 #pragma unroll
             for (int kk = 0; kk < KSTEPS; ++kk)
-                qv[half][kk] = i < 2 ? *reinterpret_cast<const bf16x8_t*>(q + kk * 16) : bf16x8_t{};
+                qv[kk] = i < 4 ? *reinterpret_cast<const bf16x8_t*>(q + kk * 16) : bf16x8_t{};
         }
+        asm volatile("" ::: "memory"); // the query loads above go out before the tiles'
         const int ntask = 2 * ctiles;
-        uint32_t km[2] = {0u, 0u};
-        for (int t0 = wave; t0 < ntask; t0 += kWaves * G) {
-            bf16x8_t bv[G][KSTEPS];
+        const int M = (ntask + kWaves - 1) / kWaves; // tiles per wave, the same for every wave
+        const uint16_t* tab = static_cast<const uint16_t*>(a.subkeys) + (long)h * 2 * S * DH;
+        const int wv = __builtin_amdgcn_readfirstlane(wave); // uniform: the tile walk is scalar
+        // the wave's tiles are wv, wv + kWaves, ...: (half, ct) of the next one to issue
+        int is_half = 0, is_ct = wv;
+        auto issue = [&](uint4 (&dst)[NP]) __attribute__((always_inline)) {
+            const bool live = is_half < 2;
+            const int rows = live ? min(32, S - is_ct * 32) : 0; // rows of the tile inside its table
+            const __amdgpu_buffer_rsrc_t r =
+                make_rsrc(tab + ((long)(live ? is_half : 0) * S + (long)is_ct * 32) * DH, (uint32_t)(rows * DH * 2));
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int task = t0 + g * kWaves;
-                const int half = task < ntask ? task / ctiles : 0, ct = task < ntask ? task % ctiles : 0;
-                const int s = ct * 32 + i;
-                const bool on = task < ntask && s < S;
-                const uint16_t* krow = static_cast<const uint16_t*>(a.subkeys) + ((long)h * 2 + half) * S * DH +
-                                       (long)(on ? s : 0) * DH + kg * 8;
-#pragma unroll
-                for (int kk = 0; kk < KSTEPS; ++kk) // a valid row either way; zeroed where used
-                    bv[g][kk] = *reinterpret_cast<const bf16x8_t*>(krow + kk * 16);
-                if (on) { // rows past S repeat row 0, which another lane covers
-                    uint32_t m = 0u;
-#pragma unroll
-                    for (int kk = 0; kk < KSTEPS; ++kk)
-                        m = absmax_bf16x8(m, bv[g][kk]);
-                    km[half] = max(km[half], max(m & 0xFFFFu, m >> 16));
-                }
+            for (int u = 0; u < NP; ++u)
+                dst[u] = ld128(r, (uint32_t)(u * 64 + lane) * 16u);
+            is_ct += kWaves;
+            if (is_ct >= ctiles) { // wave-uniform
+                is_ct -= ctiles;
+                ++is_half;
             }
+        };
+        uint4 ring[D][NP];
+        static_for<D>([&](auto jc) __attribute__((always_inline)) { issue(ring[decltype(jc)::value]); });
+        if (qd) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int task = t0 + g * kWaves;
-                if (task >= ntask)
-                    break; // wave-uniform
-                const int half = task / ctiles, ct = task % ctiles;
-                const int s = ct * 32 + i;
-                f32x16_t acc = {};
-#pragma unroll
-                for (int kk = 0; kk < KSTEPS; ++kk)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(half ? qv[1][kk] : qv[0][kk],
-                                                                  s < S ? bv[g][kk] : bf16x8_t{}, acc, 0, 0, 0);
-                // lane l < 32 holds column l of rows 0 (v = 0) and 1 (v = 1)
-                if (kg == 0 && s < S) {
-                    sc[(0 * 2 + half) * S + s] = acc[0];
-                    sc[(1 * 2 + half) * S + s] = acc[1];
-                }
-            }
+            for (int e = 0; e < QE; ++e)
+                if (e * 64 + lane < dk)
+                    qd[e * 64 + lane] = (double)__uint_as_float(qraw[e] << 16);
+            pksel::wave_sync_lds();
+            *abs_q = pksel::abs_sum(qd + half_q * DH, DH, lane);
         }
+        uint32_t km[2] = {0u, 0u};
+        int half = 0, ct = wv; // the tile processed next
+        for (int mb = 0; mb < M; mb += D) {
+            static_for<D>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                if (half < 2) { // wave-uniform
+                    uint32_t mx = 0u;
+#pragma unroll
+                    for (int u = 0; u < NP; ++u) {
+                        const int p = u * 64 + lane;
+                        mx = absmax_bf16x8(mx, __builtin_bit_cast(bf16x8_t, ring[j][u]));
+                        tile[(p / RP) * PITCH + p % RP] = ring[j][u];
+                    }
+                    km[half] = max(km[half], max(mx & 0xFFFFu, mx >> 16));
+                    pksel::wave_sync_lds();
+                    if constexpr (K32) {
+                        // two 16-column halves of the tile, DH / 32 k-steps each
+                        bf16x8_t bv[2][KS32];
+#pragma unroll
+                        for (int st = 0; st < 2; ++st)
+#pragma unroll
+                            for (int kk = 0; kk < KS32; ++kk)
+                                bv[st][kk] = __builtin_bit_cast(bf16x8_t, tile[(st * 16 + c16) * PITCH + kk * 4 + g16]);
+                        pksel::wave_sync_lds(); // the next tile overwrites the buffer
+#pragma unroll
+                        for (int st = 0; st < 2; ++st) {
+                            f32x4_t acc = {};
+#pragma unroll
+                            for (int kk = 0; kk < KS32; ++kk)
+                                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv32[kk], bv[st][kk], acc, 0, 0, 0);
+                            // lane l < 16 holds column l of rows 0..3 (v = 0..3)
+                            const int s = ct * 32 + st * 16 + c16;
+                            if (g16 == 0 && s < S) {
+                                sc[(0 * 2 + half) * S + s] = half ? acc[2] : acc[0];
+                                sc[(1 * 2 + half) * S + s] = half ? acc[3] : acc[1];
+                            }
+                        }
+                    } else {
+                        bf16x8_t bv[KSTEPS];
+#pragma unroll
+                        for (int kk = 0; kk < KSTEPS; ++kk)
+                            bv[kk] = __builtin_bit_cast(bf16x8_t, tile[i * PITCH + kk * 2 + kg]);
+                        pksel::wave_sync_lds(); // the next tile overwrites the buffer
+                        f32x16_t acc = {};
+#pragma unroll
+                        for (int kk = 0; kk < KSTEPS; ++kk)
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qv[kk], bv[kk], acc, 0, 0, 0);
+                        // lane l < 32 holds column l of rows 0..3 (v = 0..3)
+                        const int s = ct * 32 + i;
+                        if (kg == 0 && s < S) {
+                            sc[(0 * 2 + half) * S + s] = half ? acc[2] : acc[0];
+                            sc[(1 * 2 + half) * S + s] = half ? acc[3] : acc[1];
+                        }
+                    }
+                    ct += kWaves;
+                    if (ct >= ctiles) {
+                        ct -= ctiles;
+                        ++half;
+                    }
+                }
+                issue(ring[j]);
+            });
+        }
+        wait_vmcnt<0>(); // the last tiles' loads (past the wave's share) land before the registers are reused
         kmax[0] = __uint_as_float(km[0] << 16);
         kmax[1] = __uint_as_float(km[1] << 16);
         return;
@@ -198,11 +296,12 @@ __global__ __launch_bounds__(kWaves * 64) void step_address_kernel(StepArgs a)
     __shared__ uint16_t s_pairs[pksel::kPairsMax];
     __shared__ float s_km[kWaves][2];
     __shared__ double s_qd[2][2 * DH];
+    __shared__ uint4 s_tile[kWaves][BF16 ? step_tile_u4<DH>() : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bh = blockIdx.x;
     pksel::fill_pairs(s_pairs, a.k, a.W);
     float km[2];
-    step_scores<DH, BF16>(a, bh, s_sc, lane, wave, km);
+    step_scores<DH, BF16>(a, bh, s_sc, lane, wave, km, s_tile[wave]);
     publish_kmax(km, s_km, lane, wave);
     __syncthreads();
     if (wave < 2) { // wave 0 selects the write slots, wave 1 the read slots
@@ -212,7 +311,7 @@ __global__ __launch_bounds__(kWaves * 64) void step_address_kernel(StepArgs a)
                                  2 * DH, lane);
         const pksel::Refine r0 = step_refine<DH, BF16>(a, bh, s_qd[wave], 0, s_km, lane);
         const pksel::Refine r1 = step_refine<DH, BF16>(a, bh, s_qd[wave], 1, s_km, lane);
-        pksel::select_row_exact<J, R, BF16>(s_sc + wave * 2 * a.S, a.S, a.k, a.W, a.n_pairs, s_pairs, lane,
+        pksel::select_row_exact<J, R, BF16, true>(s_sc + wave * 2 * a.S, a.S, a.k, a.W, a.n_pairs, s_pairs, lane,
                                             s_buf[wave], s_val[wave], s_sub[wave], a.idx + o, a.wt + o, r0, r1);
     }
 }
@@ -372,10 +471,11 @@ __global__ __launch_bounds__(kWaves * 64) void step_scan_kernel(StepScanArgs a)
 }
 
 // The whole step in one launch, for bf16 queries: every workgroup of memory bh
-// forms bh's addressing itself (the same scores and selection as
-// step_address_kernel, the four half selections on the four waves at once, the
-// two top-W selections on two of them), then scans its 128 bytes.  The
-// repeated addressing runs in parallel, so it adds no latency.
+// forms bh's addressing itself (the same selection as step_address_kernel, the
+// four half selections on the four waves at once, the two top-W selections on
+// two of them, with the counting sorts of a wave alone on its SIMD), then scans
+// its 128 bytes.  The repeated addressing runs in parallel, so it adds no
+// latency.
 template <int DH, int J, int R, class ST>
 __global__ __launch_bounds__(kWaves * 64) void step_fused_kernel(StepArgs a, StepScanArgs c)
 {
@@ -388,26 +488,31 @@ __global__ __launch_bounds__(kWaves * 64) void step_fused_kernel(StepArgs a, Ste
     __shared__ float s_wt[2][64];
     __shared__ float s_km[kWaves][2];
     __shared__ double s_qd[kWaves][2 * DH];
+    __shared__ uint4 s_tile[kWaves][step_tile_u4<DH>()];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nchunk = c.d / (128 / (int)sizeof(ST));
     const int bh = blockIdx.x / nchunk, chunk = blockIdx.x % nchunk;
+    const int q = wave >> 1, half = wave & 1; // waves 0, 1: write query; 2, 3: read query
     pksel::fill_pairs(s_pairs, a.k, a.W);
+    // the scores, with the wave's query staged as doubles and the sum of |q| over
+    // its half while the first sub-key tiles are in flight
     float km[2];
-    step_scores<DH, true>(a, bh, s_sc, lane, wave, km);
+    double abs_q;
+    step_scores<DH, true>(a, bh, s_sc, lane, wave, km, s_tile[wave], s_qd[wave], half, &abs_q);
     publish_kmax(km, s_km, lane, wave);
     __syncthreads();
     {
-        const int q = wave >> 1, half = wave & 1; // waves 0, 1: write query; 2, 3: read query
-        pksel::stage_query<true>(static_cast<const char*>(q ? a.rq : a.wq) + (size_t)bh * 2 * DH * 2, s_qd[wave],
-                                 2 * DH, lane);
-        const pksel::Refine ref = step_refine<DH, true>(a, bh, s_qd[wave], half, s_km, lane);
-        pksel::select_half_exact<J, true>(s_sc + (q * 2 + half) * a.S, a.S, a.k, lane, s_buf[wave], s_val[q][half],
-                                          s_sub[q][half], ref);
+        const int h = bh % a.H;
+        const pksel::Refine ref{s_qd[wave] + half * DH,
+                                static_cast<const char*>(a.subkeys) + (size_t)(h * 2 + half) * a.S * DH * 2, DH,
+                                pksel::bound_from(abs_q, DH, kmax_of(s_km, half))};
+        pksel::select_half_exact<J, true, true>(s_sc + (q * 2 + half) * a.S, a.S, a.k, lane, s_buf[wave],
+                                                s_val[q][half], s_sub[q][half], ref);
     }
     __syncthreads();
     if (wave < 2)
-        pksel::select_from_lists<R>(a.S, a.k, a.W, a.n_pairs, s_pairs, lane, s_buf[wave], s_val[wave], s_sub[wave],
-                                    s_idx[wave], s_wt[wave]);
+        pksel::select_from_lists<R, true>(a.S, a.k, a.W, a.n_pairs, s_pairs, lane, s_buf[wave], s_val[wave],
+                                          s_sub[wave], s_idx[wave], s_wt[wave]);
     __syncthreads();
     step_scan_body<ST, uint16_t>(c, bh, chunk, s_idx[0], s_wt[0], s_idx[1], s_wt[1]);
 }

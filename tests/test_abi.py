@@ -42,7 +42,11 @@ def test_workspace_bytes_for_the_1p4b_shape():
     n = C.c_size_t()
     assert L.sdm_workspace_bytes(C.byref(_cfg()), C.byref(n)) == SDM_OK
     rows = 4 * 8192
-    assert n.value >= rows * 2 * 480 * 4 + 2 * 3 * rows * 64 * 4
+    # bf16 inputs: the forward's half scores are binary16; slot ids and weights of both query sets
+    assert n.value >= rows * 2 * 480 * 2 + 2 * 2 * rows * 64 * 4
+    f32 = C.c_size_t()
+    assert L.sdm_workspace_bytes(C.byref(_cfg(in_dtype=0)), C.byref(f32)) == SDM_OK
+    assert f32.value - n.value >= rows * 2 * 480 * 2 - 4096  # float32 scores for float32 inputs
 
 
 @pytest.mark.parametrize("kw,status", [
