@@ -94,16 +94,26 @@ def _crafted_tables(S, dh, rng, kind):
         K[0, 0] = K[0, 0, :1]
     elif kind == "duplicate_rows":
         K[0, 1, 1::2] = K[0, 1, ::2][: S // 2]
+    elif kind == "near_binary16_limit":
+        # sum |q| max |K| just under the forward's binary16 limit: scores near 1000, where a binary16
+        # step is 0.5, far wider than the float32 error the threshold otherwise allows for
+        K *= 60.0
+    elif kind == "beyond_binary16":
+        # scores past binary16's range: every score of the half is made exact
+        K *= 300.0
     return K
 
 
 @pytest.mark.parametrize("in_bf16", [False, True])
 @pytest.mark.parametrize("kind,S,k,W", [("cancellation", 8, 1, 1), ("cancellation", 8, 2, 3), ("equal_rows", 100, 6, 20),
-                                         ("duplicate_rows", 48, 8, 30), ("random", 480, 32, 64)])
+                                         ("duplicate_rows", 48, 8, 30), ("random", 480, 32, 64),
+                                         ("near_binary16_limit", 480, 32, 64), ("beyond_binary16", 480, 32, 64)])
 def test_forward_addressing_equals_the_oracle(kind, S, k, W, in_bf16):
     """sdm_address (the forward's addressing) against the oracle's addressing of the same queries:
     the same slots, weights within one float32 unit, also where float32 sums order scores wrongly
-    (cancellation) and where more than 64 scores of a half tie (every score made exact)."""
+    (cancellation), where more than 64 scores of a half tie (every score made exact), and, for bf16
+    inputs (whose forward stores binary16 scores), with scores near binary16's range limit, where
+    its rounding step is wide, and beyond it."""
     import torch
     from parity import to_dev, to_host
     from sdm_inputs import bf16_bits_from_f32, f32_from_bf16_bits
@@ -118,6 +128,8 @@ def test_forward_addressing_equals_the_oracle(kind, S, k, W, in_bf16):
     if kind == "cancellation":
         q[:, ::2] = 1.0
         q[:, 1::4] = 2.0
+    if kind in ("near_binary16_limit", "beyond_binary16"):
+        q *= 8.0 if kind == "near_binary16_limit" else 100.0
     if in_bf16:
         K = bf16_bits_from_f32(K).reshape(K.shape)
         q = bf16_bits_from_f32(q).reshape(q.shape)
