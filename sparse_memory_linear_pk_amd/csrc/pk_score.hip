@@ -206,12 +206,17 @@ __global__ __launch_bounds__(kWaves * 64) void pk_score_f32(const float* __restr
 // walks every fourth line, passes the products through its LDS tile (32 rows x
 // 64 sub-keys) and stores each line with 8 lanes of 16 bytes, so every line is
 // written whole, once.
+// blockIdx.y picks the query set: (q0, scores0) or (q1, scores1).
 template <int DH>
-__global__ __launch_bounds__(kWaves * 64) void pk_score_bf16_lines(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kWaves * 64) void pk_score_bf16_lines(const uint16_t* __restrict__ q0,
+                                                                 const uint16_t* __restrict__ q1,
                                                                  const uint4* __restrict__ frag,
-                                                                 uint16_t* __restrict__ scores, Rows r, int S)
+                                                                 uint16_t* __restrict__ scores0,
+                                                                 uint16_t* __restrict__ scores1, Rows r, int S)
 {
     constexpr int KSTEPS = DH / 16, RB = 2;
+    const uint16_t* q = blockIdx.y ? q1 : q0;
+    uint16_t* scores = blockIdx.y ? scores1 : scores0;
     __shared__ uint16_t s_tile[kWaves][32 * kLinePitch];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 31, kg = lane >> 5;
@@ -289,7 +294,8 @@ hipError_t launch_dh(const void* q, const void* subkeys, const void* frag, void*
         if (half_out && S % 32 == 0) {
             const int blocks2 = (r.Tc + 63) / 64;
             hipLaunchKernelGGL(pk_score_bf16_lines<DH>, dim3((unsigned)(blocks2 * r.B * r.H)), dim3(kWaves * 64), 0,
-                               stream, (const uint16_t*)q, (const uint4*)frag, (uint16_t*)scores, r, S);
+                               stream, (const uint16_t*)q, (const uint16_t*)q, (const uint4*)frag, (uint16_t*)scores,
+                               (uint16_t*)scores, r, S);
         } else if (half_out)
             hipLaunchKernelGGL((pk_score_bf16<DH, RB, true>), grid, dim3(kWaves * 64), 0, stream, (const uint16_t*)q,
                                (const uint4*)frag, scores, r, S);
@@ -303,6 +309,17 @@ hipError_t launch_dh(const void* q, const void* subkeys, const void* frag, void*
         hipLaunchKernelGGL(pk_score_f32<DH>, dim3((unsigned)(tiles * r.B * r.H * 2)), dim3(kWaves * 64), 0, stream,
                            (const float*)q, (const float*)subkeys, (float*)scores, r, S);
     }
+    return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_pair_dh(const void* q0, const void* q1, const void* frag, void* s0, void* s1, const Rows& r, int S,
+                          hipStream_t stream)
+{
+    const int blocks2 = (r.Tc + 63) / 64;
+    hipLaunchKernelGGL(pk_score_bf16_lines<DH>, dim3((unsigned)(blocks2 * r.B * r.H), 2u), dim3(kWaves * 64), 0, stream,
+                       (const uint16_t*)q0, (const uint16_t*)q1, (const uint4*)frag, (uint16_t*)s0, (uint16_t*)s1, r,
+                       S);
     return hipGetLastError();
 }
 
@@ -334,6 +351,32 @@ hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag,
     case 256: return launch_dh<256>(q, subkeys, frag, scores, r, S, in_bf16, half_out, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+} // namespace sdm
+
+namespace sdm {
+
+hipError_t launch_pk_score_pair(const void* q0, const void* q1, const void* subkeys, const void* frag, void* s0,
+                                void* s1, const Rows& r, int S, int dh, bool in_bf16, hipStream_t stream)
+{
+    if (r.count() <= 0)
+        return hipSuccess;
+    if (in_bf16 && S % 32 == 0) { // the line kernel, both sets in one launch
+        switch (dh) {
+        case 16: return launch_pair_dh<16>(q0, q1, frag, s0, s1, r, S, stream);
+        case 32: return launch_pair_dh<32>(q0, q1, frag, s0, s1, r, S, stream);
+        case 48: return launch_pair_dh<48>(q0, q1, frag, s0, s1, r, S, stream);
+        case 64: return launch_pair_dh<64>(q0, q1, frag, s0, s1, r, S, stream);
+        case 96: return launch_pair_dh<96>(q0, q1, frag, s0, s1, r, S, stream);
+        case 128: return launch_pair_dh<128>(q0, q1, frag, s0, s1, r, S, stream);
+        case 192: return launch_pair_dh<192>(q0, q1, frag, s0, s1, r, S, stream);
+        case 256: return launch_pair_dh<256>(q0, q1, frag, s0, s1, r, S, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    const hipError_t e = launch_pk_score(q0, subkeys, frag, s0, r, S, dh, in_bf16, in_bf16, stream);
+    return e != hipSuccess ? e : launch_pk_score(q1, subkeys, frag, s1, r, S, dh, in_bf16, in_bf16, stream);
 }
 
 } // namespace sdm

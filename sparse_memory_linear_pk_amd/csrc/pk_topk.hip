@@ -27,15 +27,26 @@ struct ExactIn {
     int dh;
 };
 
+// The outputs of one query set; blockIdx.y picks set 0 or 1 (q0 is ExactIn::q).
+struct SetOut {
+    const void* scores;
+    int32_t* idx;
+    float* wt;
+    const void* q;
+};
+
 // J: sub-keys per lane per half (S <= 64*J); R: restricted candidates per lane;
 // EX: 0 float32 scores as given, 1 exact from bf16 inputs (binary16 scores), 2
 // exact from float32 inputs (float32 scores).
 template <int J, int R, int EX>
-__global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(const void* __restrict__ scores_v,
-                                                                   int32_t* __restrict__ idx,
-                                                                   float* __restrict__ wt, Rows rr, int S,
-                                                                   int k, int W, int n_pairs, ExactIn ex)
+__global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(SetOut s0, SetOut s1, Rows rr, int S, int k,
+                                                                   int W, int n_pairs, ExactIn ex)
 {
+    const SetOut& so = blockIdx.y ? s1 : s0;
+    const void* __restrict__ scores_v = so.scores;
+    int32_t* __restrict__ idx = so.idx;
+    float* __restrict__ wt = so.wt;
+    ex.q = so.q;
     __shared__ uint64_t s_buf[kRowsPerBlock][64];       // compaction scratch, then the winners
     __shared__ float s_val[kRowsPerBlock][2][64];        // sorted half lists: scores
     __shared__ uint32_t s_sub[kRowsPerBlock][2][64];     // and sub-key indices
@@ -104,15 +115,14 @@ __global__ __launch_bounds__(256) void subkey_absmax_kernel(const void* __restri
 }
 
 template <int J, int EX>
-hipError_t launch_j(const void* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
+hipError_t launch_j(const SetOut& s0, const SetOut& s1, int nsets, const Rows& r, int S, int k, int W, int n_pairs,
                     const ExactIn& ex, hipStream_t stream)
 {
-    dim3 grid((unsigned)((r.count() + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
-#define SDM_TOPK_R(Rv)                                                                                       \
-    if (n_pairs <= 64 * Rv) {                                                                                \
-        hipLaunchKernelGGL((pk_topk_kernel<J, Rv, EX>), grid, block, 0, stream, scores, idx, wt, r, S, k, W, \
-                           n_pairs, ex);                                                                     \
-        return hipGetLastError();                                                                            \
+    dim3 grid((unsigned)((r.count() + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)nsets), block(kRowsPerBlock * 64);
+#define SDM_TOPK_R(Rv)                                                                                        \
+    if (n_pairs <= 64 * Rv) {                                                                                 \
+        hipLaunchKernelGGL((pk_topk_kernel<J, Rv, EX>), grid, block, 0, stream, s0, s1, r, S, k, W, n_pairs, ex); \
+        return hipGetLastError();                                                                             \
     }
     SDM_TOPK_R(1)
     SDM_TOPK_R(2)
@@ -123,20 +133,41 @@ hipError_t launch_j(const void* scores, int32_t* idx, float* wt, const Rows& r, 
 }
 
 template <int EX>
-hipError_t launch_ex(const void* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W, int n_pairs,
+hipError_t launch_ex(const SetOut& s0, const SetOut& s1, int nsets, const Rows& r, int S, int k, int W, int n_pairs,
                      const ExactIn& ex, hipStream_t stream)
 {
     if (S <= 64)
-        return launch_j<1, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+        return launch_j<1, EX>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
     if (S <= 128)
-        return launch_j<2, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+        return launch_j<2, EX>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
     if (S <= 256)
-        return launch_j<4, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+        return launch_j<4, EX>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
     if (S <= 512)
-        return launch_j<8, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+        return launch_j<8, EX>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
     if (S <= 1024)
-        return launch_j<16, EX>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+        return launch_j<16, EX>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
     return hipErrorInvalidValue;
+}
+
+// Both query sets' selection in one launch (nsets 2) or one set (nsets 1, s1 unused).
+hipError_t launch_sets(const SetOut& s0, const SetOut& s1, int nsets, const Rows& r, int S, int k, int W,
+                       const void* subkeys, const float* kmax, int dh, bool in_bf16, hipStream_t stream)
+{
+    if (r.count() <= 0)
+        return hipSuccess;
+    if (k < 1 || k > 64 || W < 1 || W > 64 || W > k * k || k > S)
+        return hipErrorInvalidValue;
+    const bool exact = s0.q != nullptr;
+    if (exact && (!subkeys || !kmax || dh < 16 || dh % 16 || (nsets == 2 && !s1.q)))
+        return hipErrorInvalidValue;
+    const int n_pairs = pair_count(k, W);
+    if (n_pairs > kPairsMax)
+        return hipErrorInvalidValue;
+    const ExactIn ex{s0.q, subkeys, kmax, dh};
+    if (!exact)
+        return launch_ex<0>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
+    return in_bf16 ? launch_ex<1>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream)
+                   : launch_ex<2>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
 }
 
 } // namespace
@@ -156,20 +187,18 @@ hipError_t launch_pk_topk(const void* scores, int32_t* idx, float* wt, const Row
                           const void* q, const void* subkeys, const float* kmax, int dh, bool in_bf16,
                           hipStream_t stream)
 {
-    if (r.count() <= 0)
-        return hipSuccess;
-    if (k < 1 || k > 64 || W < 1 || W > 64 || W > k * k || k > S)
+    const SetOut s0{scores, idx, wt, q};
+    return launch_sets(s0, s0, 1, r, S, k, W, subkeys, kmax, dh, in_bf16, stream);
+}
+
+hipError_t launch_pk_topk_pair(const void* scores0, const void* scores1, int32_t* idx0, int32_t* idx1, float* wt0,
+                               float* wt1, const Rows& r, int S, int k, int W, const void* q0, const void* q1,
+                               const void* subkeys, const float* kmax, int dh, bool in_bf16, hipStream_t stream)
+{
+    if (!q0 || !q1)
         return hipErrorInvalidValue;
-    if (q && (!subkeys || !kmax || dh < 16 || dh % 16))
-        return hipErrorInvalidValue;
-    const int n_pairs = pair_count(k, W);
-    if (n_pairs > kPairsMax)
-        return hipErrorInvalidValue;
-    const ExactIn ex{q, subkeys, kmax, dh};
-    if (!q)
-        return launch_ex<0>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
-    return in_bf16 ? launch_ex<1>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream)
-                   : launch_ex<2>(scores, idx, wt, r, S, k, W, n_pairs, ex, stream);
+    const SetOut s0{scores0, idx0, wt0, q0}, s1{scores1, idx1, wt1, q1};
+    return launch_sets(s0, s1, 2, r, S, k, W, subkeys, kmax, dh, in_bf16, stream);
 }
 
 } // namespace sdm

@@ -105,7 +105,7 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
     // apart from the forward's buffers (which hold B*T*H*W and T may be 1)
     L.step = align_up(2 * (size_t)c.B * c.H * c.W * sizeof(int32_t));
     L.kmax = align_up(2 * (size_t)c.H * sdm::kAbsmaxParts * sizeof(float)); // partial max |K| per sub-key table
-    L.total = L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag + L.kmax + 2 * L.step;
+    L.total = 2 * L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag + L.kmax + 2 * L.step;
     return L;
 }
 
@@ -202,7 +202,7 @@ struct sdm_ctx {
     std::vector<sdm::ScanPlan> plans; // scan layout of each chunk
     void* block;
     Layout L;
-    void* scores; // the forward's scores (binary16 for bf16 inputs)
+    void* scores[2]; // the forward's scores of each query set (binary16 for bf16 inputs)
     int32_t* idx[2];
     float* wt[2];
     uint4* plan_buf;
@@ -357,33 +357,38 @@ sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hi
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan launch");
 }
 
+// Scores and exact selection of both query sets for rows r, one launch each.
+sdm_status run_address_pair(sdm_ctx* h, const sdm::Rows& r, const void* wq, const void* rq, const void* subkeys,
+                            hipStream_t st, bool prepare)
+{
+    const sdm_config& c = h->cfg;
+    const bool bf16 = c.in_dtype == SDM_BF16;
+    hipError_t e = prepare ? prepare_subkeys(h, subkeys, st) : hipSuccess;
+    if (e == hipSuccess) {
+        Timer t(h, K_SCORE, st);
+        e = sdm::launch_pk_score_pair(wq, rq, subkeys, h->frag, h->scores[0], h->scores[1], r, c.n_sub, c.dk / 2,
+                                      bf16, st);
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "pk_score launch");
+    Timer t(h, K_SELECT, st);
+    e = sdm::launch_pk_topk_pair(h->scores[0], h->scores[1], h->idx[0], h->idx[1], h->wt[0], h->wt[1], r, c.n_sub,
+                                 c.k, c.W, wq, rq, subkeys, h->kmax, c.dk / 2, bf16, st);
+    return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_topk launch");
+}
+
 // The addressing of both query sets for chunk ci, then its plan.
 sdm_status run_chunk_front(sdm_ctx* h, int ci, const void* wq, const void* rq, const float* alpha, const float* beta,
                            const void* subkeys, hipStream_t st)
 {
-    const sdm::Rows r = chunk_rows(h, ci);
-    const void* q[2] = {wq, rq};
-    sdm_status s = SDM_OK;
-    for (int set = 0; set < 2 && s == SDM_OK; ++set) {
-        s = run_score(h, q[set], subkeys, h->scores, r, st, ci == 0 && set == 0);
-        if (s == SDM_OK)
-            s = run_select(h, h->scores, h->idx[set], h->wt[set], r, st, q[set], subkeys);
-    }
+    const sdm_status s = run_address_pair(h, chunk_rows(h, ci), wq, rq, subkeys, st, ci == 0);
     return s == SDM_OK ? run_plan(h, ci, h->idx[0], h->wt[0], h->idx[1], h->wt[1], alpha, beta, st) : s;
 }
 
 // Scores and selection of both query sets for every row of the call, on st.
 sdm_status run_address_all(sdm_ctx* h, const void* wq, const void* rq, const void* subkeys, hipStream_t st)
 {
-    const sdm::Rows r = all_rows(h->cfg);
-    const void* q[2] = {wq, rq};
-    sdm_status s = SDM_OK;
-    for (int set = 0; set < 2 && s == SDM_OK; ++set) {
-        s = run_score(h, q[set], subkeys, h->scores, r, st, set == 0);
-        if (s == SDM_OK)
-            s = run_select(h, h->scores, h->idx[set], h->wt[set], r, st, q[set], subkeys);
-    }
-    return s;
+    return run_address_pair(h, all_rows(h->cfg), wq, rq, subkeys, st, true);
 }
 
 sdm_status forward_impl(sdm_ctx* h, const void* wq, const void* rq, const void* v, const float* alpha,
@@ -484,8 +489,10 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
         return fail(SDM_ERR_OOM, "workspace of %zu bytes: %s", total, hipGetErrorString(e));
     }
     char* p = (char*)h->block;
-    h->scores = p;
-    p += h->L.scores;
+    for (int set = 0; set < 2; ++set) {
+        h->scores[set] = p;
+        p += h->L.scores;
+    }
     for (int set = 0; set < 2; ++set) {
         h->idx[set] = (int32_t*)p;
         p += h->L.idx;
@@ -586,8 +593,8 @@ sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t
         return fail(SDM_ERR_INVALID_ARG, "sdm_address: NULL pointer");
     if (!aligned16(q) || !aligned16(subkeys) || !aligned4(idx) || !aligned4(wt))
         return fail(SDM_ERR_INVALID_ARG, "sdm_address: misaligned pointer");
-    s = run_score(h, q, subkeys, h->scores, all_rows(h->cfg), h->stream, true);
-    return s != SDM_OK ? s : run_select(h, h->scores, idx, wt, all_rows(h->cfg), h->stream, q, subkeys);
+    s = run_score(h, q, subkeys, h->scores[0], all_rows(h->cfg), h->stream, true);
+    return s != SDM_OK ? s : run_select(h, h->scores[0], idx, wt, all_rows(h->cfg), h->stream, q, subkeys);
 }
 
 sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,

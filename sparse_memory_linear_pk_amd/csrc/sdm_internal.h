@@ -70,6 +70,11 @@ hipError_t launch_pk_subkey_frag(const void* subkeys, void* frag, int H, int S, 
 hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag, void* scores, const Rows& r,
                            int S, int dh, bool in_bf16, bool half_out, hipStream_t stream);
 
+// Both query sets of the forward at once (q0 -> s0, q1 -> s1), scores stored as
+// for half_out = in_bf16: one launch for bf16 inputs with S a multiple of 32.
+hipError_t launch_pk_score_pair(const void* q0, const void* q1, const void* subkeys, const void* frag, void* s0,
+                                void* s1, const Rows& r, int S, int dh, bool in_bf16, hipStream_t stream);
+
 // Per-half top-k, outer-sum top-W and softmax weights of the covered rows:
 // scores [B*Ts*H, 2, S] -> idx, wt [B*Ts*H, W].  With q ([B, Ts, H, dk]),
 // subkeys and kmax (max |K| per table, [H, 2]) the scores that can reach a
@@ -80,6 +85,10 @@ hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag,
 hipError_t launch_pk_topk(const void* scores, int32_t* idx, float* wt, const Rows& r, int S, int k, int W,
                           const void* q, const void* subkeys, const float* kmax, int dh, bool in_bf16,
                           hipStream_t stream);
+// The exact selection of both query sets in one launch (q0, q1 required).
+hipError_t launch_pk_topk_pair(const void* scores0, const void* scores1, int32_t* idx0, int32_t* idx1, float* wt0,
+                               float* wt1, const Rows& r, int S, int k, int W, const void* q0, const void* q1,
+                               const void* subkeys, const float* kmax, int dh, bool in_bf16, hipStream_t stream);
 // Partial maxima of |K| per sub-key table: kmax[(h * 2 + half) * kAbsmaxParts + p]
 // is the largest magnitude in the p-th of kAbsmaxParts slices of table (h, half);
 // the selection reduces the parts itself (no atomics, nothing to clear first).
