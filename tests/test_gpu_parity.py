@@ -280,13 +280,12 @@ def test_permuted_elements_are_bitwise_permuted(T):
 # full workload sizes: every row and every element
 # ---------------------------------------------------------------------------
 
-def full_size_parity(orc, T, cfg, label, padded=False):
-    """Stages 1-5 at a full workload size.  The GPU runs the whole call (B
-    sequences, the library's chunked forward) as bench.py does; the oracle
-    checks every row's addressing, then scans sequence by sequence (memories
-    are independent), accumulating the whole tensors' figures.  padded: the
-    same forward also on slot rows padded to sdm_mem_stride_hint (bench.py's
-    layout), which must equal the dense one bit for bit."""
+def full_gpu_run(T, cfg, label, padded=False) -> dict:
+    """The GPU half of a full-size parity case.  The GPU runs the whole call (B
+    sequences, the library's chunked forward) as bench.py does, and the scoring
+    and selection seams and the forward's own addressing of both query sets.
+    padded: the same forward also on slot rows padded to sdm_mem_stride_hint
+    (bench.py's layout), which must equal the dense one bit for bit."""
     from sparse_memory_linear_pk_amd import SDM
     R = cfg.B * cfg.T * cfg.H
     say(f"[{label}] inputs {cfg}")
@@ -332,9 +331,16 @@ def full_size_parity(orc, T, cfg, label, padded=False):
     g_out = to_host(out)
     del out, dev
     T.cuda.empty_cache()
+    acc = {k: PlainAccum() for k in ("out4", "mem4", "out5", "mem5")}
+    return {"x": x, "g": g, "g_out": g_out, "mem": mem, "mem0": mem0, "acc": acc, "seqs_done": set()}
 
-    # stages 1-3 on every row
-    for s_, q in (("w", x["wq"]), ("r", x["rq"])):
+
+def full_addressing(orc, cfg, st, label, sets="wr"):
+    """Stages 1-3 on every row of the query sets named in `sets`."""
+    x, g = st["x"], st["g"]
+    R = cfg.B * cfg.T * cfg.H
+    for s_ in sets:
+        q = x[s_ + "q"]
         say(f"[{label}] {s_}: oracle scores of {R} rows")
         ref_scores = orc.scores(cfg, q, x["subkeys"])
         err = 0.0
@@ -353,32 +359,60 @@ def full_size_parity(orc, T, cfg, label, padded=False):
             f"forward addressing equals the oracle's on every row (weight ulp {ulp3})")
         del ref_scores, g[f"scores_{s_}"], ri, rw, rs
 
-    # stages 4 and 5, sequence by sequence; the oracle addresses from the queries for stage 5
-    acc = {k: PlainAccum() for k in ("out4", "mem4", "out5", "mem5")}
+
+def full_scan(orc, cfg, st, label, seqs):
+    """Stages 4 and 5 on the sequences `seqs` (memories are independent); the
+    oracle addresses from the queries for stage 5.  The whole tensors' figures
+    accumulate in st["acc"]; each sequence's own figures are asserted here."""
+    x, g, g_out, mem, mem0, acc = st["x"], st["g"], st["g_out"], st["mem"], st["mem0"], st["acc"]
     c1 = cfg.replace(B=1)
     per = cfg.T * cfg.H
-    for b in range(cfg.B):
+    for b in seqs:
         rows = slice(b * per, (b + 1) * per)
         xb = {k: np.ascontiguousarray(x[k][b:b + 1]) for k in ("wq", "rq", "v", "alpha", "beta")}
         m0 = to_host(mem0[b:b + 1])
         gm = to_host(mem[b:b + 1])
+        one = {k: PlainAccum() for k in acc}
         m = m0.copy()
         o4 = orc.scan(c1, g["idx2_w"][rows], g["wt2_w"][rows], g["idx2_r"][rows], g["wt2_r"][rows], xb["v"],
                       xb["alpha"], xb["beta"], m)
-        acc["out4"].add(g_out[b:b + 1], o4)
-        acc["mem4"].add(gm, m)
+        for a in (acc, one):
+            a["out4"].add(g_out[b:b + 1], o4)
+            a["mem4"].add(gm, m)
         m = m0
         o5 = orc.forward(c1, xb["wq"], xb["rq"], xb["v"], xb["alpha"], xb["beta"], x["subkeys"], m)[0]
-        acc["out5"].add(g_out[b:b + 1], o5)
-        acc["mem5"].add(gm, m)
-        say(f"[{label}] sequence {b}: stage 4 so far out max/RMS {acc['out4'].value():.3g}, memory "
-            f"{acc['mem4'].value():.3g}; stage 5 out {acc['out5'].value():.3g}, memory {acc['mem5'].value():.3g}")
+        for a in (acc, one):
+            a["out5"].add(g_out[b:b + 1], o5)
+            a["mem5"].add(gm, m)
+        say(f"[{label}] sequence {b}: stage 4 out max/RMS {one['out4'].value():.3g}, memory "
+            f"{one['mem4'].value():.3g}; stage 5 out {one['out5'].value():.3g}, memory {one['mem5'].value():.3g}")
+        for stage in (4, 5):
+            check_scan(cfg, stage, f"{label} sequence {b}",
+                       {"out": (one[f"out{stage}"].value(), one[f"out{stage}"].rel),
+                        "mem": (one[f"mem{stage}"].value(), one[f"mem{stage}"].rel)}, say)
+        st["seqs_done"].add(b)
         del m0, m, gm
-    check_scan(cfg, 4, label, {"out": (acc["out4"].value(), acc["out4"].rel),
-                               "mem": (acc["mem4"].value(), acc["mem4"].rel)}, say)
-    check_scan(cfg, 5, label, {"out": (acc["out5"].value(), acc["out5"].rel),
-                               "mem": (acc["mem5"].value(), acc["mem5"].rel)}, say)
-    del mem, mem0
+
+
+def full_scan_check(cfg, st, label):
+    """The whole tensors' figures of stages 4 and 5, once every sequence is in."""
+    assert st["seqs_done"] == set(range(cfg.B)), "every sequence's scan compared"
+    acc = st["acc"]
+    for stage in (4, 5):
+        check_scan(cfg, stage, label, {"out": (acc[f"out{stage}"].value(), acc[f"out{stage}"].rel),
+                                       "mem": (acc[f"mem{stage}"].value(), acc[f"mem{stage}"].rel)}, say)
+
+
+def full_size_parity(orc, T, cfg, label, padded=False):
+    """Stages 1-5 at a full workload size: the GPU run, then the oracle checks
+    every row's addressing and scans sequence by sequence, accumulating the
+    whole tensors' figures."""
+    st = full_gpu_run(T, cfg, label, padded)
+    full_addressing(orc, cfg, st, label)
+    full_scan(orc, cfg, st, label, range(cfg.B))
+    full_scan_check(cfg, st, label)
+    g = st["g"]
+    del st
     T.cuda.empty_cache()
     return g
 
@@ -402,6 +436,33 @@ def test_full_long_planted(orc, T):
     assert np.array_equal(g["wt2_r"][cfg.T - 17], g["wt2_w"][61])
 
 
-@pytest.mark.timeout(1200)
-def test_full_8b(orc, T):
-    full_size_parity(orc, T, gi.config(4), "8B")
+# The 8B-shaped workload in parts (its memories are 3.1 GB each): the GPU run
+# once for the module, then each query set's addressing and each sequence's scan
+# as a test of its own.
+@pytest.fixture(scope="module")
+def full8b(T):
+    st = full_gpu_run(T, gi.config(4), "8B")
+    yield st
+    st.clear()
+    T.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_full_8b_gpu_run(full8b):
+    assert np.isfinite(full8b["g_out"]).all()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("s_", ["w", "r"])
+def test_full_8b_addressing(orc, full8b, s_):
+    full_addressing(orc, gi.config(4), full8b, "8B", s_)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("b", range(gi.config(4).B))
+def test_full_8b_scan(orc, full8b, b):
+    full_scan(orc, gi.config(4), full8b, "8B", [b])
+
+
+def test_full_8b_whole_tensors(full8b):
+    full_scan_check(gi.config(4), full8b, "8B")
