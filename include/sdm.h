@@ -266,10 +266,16 @@ SDM_API sdm_status sdm_workspace_bytes(const sdm_config* cfg, size_t* bytes);
  * sdm_address:   the forward's addressing of the B*T*H rows of q -> idx, wt
  *                (scores kept internal; the scores that can reach a half's
  *                top k recomputed exactly, as sdm_forward does) 
+ * sdm_address_pair: both query sets at once, as sdm_forward launches them
+ *                (one scoring and one selection launch for wq and rq)
+ *                -> idx_w, wt_w and idx_r, wt_r; the same values as two
+ *                sdm_address calls
  * sdm_scan_with: the scan driven by given write and read addressing */
 SDM_API sdm_status sdm_score(sdm_handle h, const void* q, const void* subkeys, float* scores);
 SDM_API sdm_status sdm_select(sdm_handle h, const float* scores, int32_t* idx, float* wt);
 SDM_API sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t* idx, float* wt);
+SDM_API sdm_status sdm_address_pair(sdm_handle h, const void* wq, const void* rq, const void* subkeys,
+                                    int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r);
 SDM_API sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,
                          const float* wt_r, const void* v, const float* alpha, const float* beta,
                          void* mem_inout, float* out);

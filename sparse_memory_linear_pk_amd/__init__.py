@@ -199,6 +199,15 @@ class SDM:
                 self._t(idx, "idx", (B * T * H, W), "i32"), self._t(wt, "wt", (B * T * H, W), "f32")]
         check(lib().sdm_address(self._h, *[_ptr(a) for a in args]), "sdm_address")
 
+    def address_pair(self, wq, rq, subkeys, idx_w, wt_w, idx_r, wt_r):
+        B, H, T, d, S, dk, k, W = self._dims()
+        R = B * T * H
+        args = [self._t(wq, "wq", (B, T, H, dk), "in"), self._t(rq, "rq", (B, T, H, dk), "in"),
+                self._t(subkeys, "subkeys", (H, 2, S, dk // 2), "in"),
+                self._t(idx_w, "idx_w", (R, W), "i32"), self._t(wt_w, "wt_w", (R, W), "f32"),
+                self._t(idx_r, "idx_r", (R, W), "i32"), self._t(wt_r, "wt_r", (R, W), "f32")]
+        check(lib().sdm_address_pair(self._h, *[_ptr(a) for a in args]), "sdm_address_pair")
+
     def scan_with(self, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, mem, out):
         B, H, T, d, S, dk, k, W = self._dims()
         R = B * T * H

@@ -73,6 +73,7 @@ def lib() -> C.CDLL:
         "sdm_score": ([h, vp, vp, vp], C.c_int),
         "sdm_select": ([h, vp, vp, vp], C.c_int),
         "sdm_address": ([h, vp, vp, vp, vp], C.c_int),
+        "sdm_address_pair": ([h, vp, vp, vp, vp, vp, vp, vp], C.c_int),
         "sdm_scan_with": ([h, vp, vp, vp, vp, vp, vp, vp, vp, vp], C.c_int),
         "sdm_set_timing": ([h, C.c_int], C.c_int),
         "sdm_get_timing": ([h, C.POINTER(Timing)], C.c_int),

@@ -15,6 +15,8 @@
 // operands read straight from the table.
 #include "sdm_internal.h"
 
+#include <cmath>
+
 namespace sdm {
 namespace {
 
@@ -283,6 +285,255 @@ __global__ __launch_bounds__(kWaves * 64) void pk_score_bf16_lines(const uint16_
     }
 }
 
+// Scoring fused with the candidate search of the exact selection (bf16 inputs,
+// S a multiple of 32): the scores never leave the CUs.  The selection needs,
+// per row and half, a set of sub-keys that holds the half's exact top k; it
+// gets every sub-key whose float32 MFMA score reaches a threshold tau, as a
+// bitmask, and checks on its exact rescoring that tau was low enough (at least k
+// candidates exact-score at or above tau + E, E bounding |float32 - exact|);
+// the check failing, or more than 64 candidates, makes it rescore the whole
+// half.  So tau only steers the cost, never the result.  It is set from the
+// row's query and the table's statistics: the scores of a row against a table
+// have mean <q, mu> (mu the table's mean row) and, for a table with roughly
+// isotropic spread sigma per coordinate, standard deviation ~ sigma |q|, and
+// tau = <q, mu> + z sigma |q| with z the normal quantile that leaves about
+// cand_target(k) of S above it.
+//
+// MFMA roles are swapped against pk_score_bf16: the sub-key tile is the A
+// operand (32 sub-keys) and the queries the B operand (32 rows), so lane l
+// holds the scores of query row (l % 32) against sub-keys 8 (v / 4) + 4 (l /
+// 32) + (v % 4), v = 0..15, and compares them with its own row's tau.  A wave
+// owns 64 rows (two B groups) of one head and half; the two waves of a
+// workgroup (128 consecutive tokens of one sequence) share each sub-key tile
+// through LDS, double-buffered, with each tile's global loads issued two tiles
+// ahead.  The loop is software-pipelined: the products of tile c + 1 are issued
+// before the comparisons of tile c, into the other of two accumulator sets, so
+// the matrix cores and the vector ALUs work at once.  Registers (at most 256
+// per lane) and LDS (under 43 KB per workgroup) stay within what the scan
+// leaves free, so the next chunk's scoring runs beside the scan.  Record of
+// (half, row): S / 32 bit words, word c for sub-keys 32 c .. 32 c + 31 (bit p
+// < 16: lane group 0 with v = 15 - p; bit p >= 16: group 1 with v = 31 - p),
+// then tau's bits, then zeros, padded to cand_record_dwords(S) words; records
+// [2][B * Ts * H][RW].
+constexpr int kCandWaves = 2;
+constexpr int kCandRows = 64 * kCandWaves; // tokens per workgroup
+constexpr int kCandMaxRW = 36;             // record words for S <= 1120
+
+// The 16 comparisons of one MFMA result as bits, first score highest: bit set
+// where acc[v] < tau (the sign of acc[v] - tau; the complement marks the
+// candidates).
+__device__ __forceinline__ uint32_t below_bits(const f32x16_t& acc, float tau)
+{
+    uint32_t w = 0u;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+        w = __builtin_amdgcn_alignbit(w, __float_as_uint(acc[v] - tau), 31);
+    return w;
+}
+
+template <int DH>
+__global__ __launch_bounds__(kCandWaves * 64) void pk_score_cand(const uint16_t* __restrict__ q0,
+                                                               const uint16_t* __restrict__ q1,
+                                                               const uint4* __restrict__ frag,
+                                                               const float* __restrict__ kstat,
+                                                               uint32_t* __restrict__ rec0,
+                                                               uint32_t* __restrict__ rec1, Rows r, int S, float z)
+{
+    constexpr int NT = kCandWaves * 64;
+    constexpr int KSTEPS = DH / 16, TILE = KSTEPS * 64; // 16-byte operand pieces per sub-key tile
+    static_assert(TILE % NT == 0, "a tile loads in whole rounds of the workgroup");
+    constexpr int PER = TILE / NT;
+    __shared__ uint4 s_a[2][TILE];
+    __shared__ uint32_t s_rec[kCandWaves][64 * kCandMaxRW];
+    const uint16_t* __restrict__ q = blockIdx.y ? q1 : q0;
+    uint32_t* __restrict__ rec = blockIdx.y ? rec1 : rec0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kg = lane >> 5;
+    const int tblocks = (r.Tc + kCandRows - 1) / kCandRows;
+    int bid = blockIdx.x;
+    const int half = bid & 1;
+    bid >>= 1;
+    const int tb = bid % tblocks;
+    bid /= tblocks;
+    const int b = bid % r.B, h = bid / r.B;
+    const int H = r.H, ctiles = S / 32, RW = cand_record_dwords(S);
+    const int tw = tb * kCandRows + wave * 64; // the wave's first token in the chunk
+
+    // Sub-key tiles stream through two register sets, each tile's loads issued
+    // two tiles before its store to LDS (the tables come from the last-level
+    // cache or HBM, a latency of more than a tile's work).
+    const uint4* fb = frag + (long)(h * 2 + half) * ctiles * TILE;
+    typedef uint32_t pieces_t __attribute__((ext_vector_type(4 * PER))); // one vector value (an array ends up in scratch)
+    pieces_t R0, R1;
+    auto load_tile = [&](pieces_t& R, int c) {
+        c = c < ctiles ? c : ctiles - 1; // past the last tile: the last one again, unused
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const uint4 x = fb[(long)c * TILE + u * NT + threadIdx.x];
+            R[4 * u] = x.x;
+            R[4 * u + 1] = x.y;
+            R[4 * u + 2] = x.z;
+            R[4 * u + 3] = x.w;
+        }
+    };
+    auto store_tile = [&](const pieces_t& R, int buf) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            s_a[buf][u * NT + threadIdx.x] = make_uint4(R[4 * u], R[4 * u + 1], R[4 * u + 2], R[4 * u + 3]);
+    };
+    load_tile(R0, 0);
+
+    // B operands: group g, lane l -> token tw + 32 g + (l % 32), k-slice l / 32
+    bf16x8_t bq[2][KSTEPS];
+    float tau[2];
+    const float* st = kstat + (h * 2 + half) * (DH + 4); // mean row, then sigma
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int tl = tw + 32 * g + (lane & 31);
+        const long row = ((long)b * r.Ts + r.t0 + tl) * H + h;
+        const uint16_t* qrow = q + row * 2 * DH + half * DH + kg * 8;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk)
+            bq[g][kk] = tl < r.Tc ? *reinterpret_cast<const bf16x8_t*>(qrow + kk * 16) : bf16x8_t{};
+    }
+    store_tile(R0, 0);
+    load_tile(R1, 1);
+    load_tile(R0, 2);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        float sm = 0.f, sq = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            const float4 m0 = *reinterpret_cast<const float4*>(st + kk * 16 + kg * 8);
+            const float4 m1 = *reinterpret_cast<const float4*>(st + kk * 16 + kg * 8 + 4);
+            const float mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = (float)bq[g][kk][e];
+                sm = fmaf(x, mu[e], sm);
+                sq = fmaf(x, x, sq);
+            }
+        }
+        sm += __shfl_xor(sm, 32);
+        sq += __shfl_xor(sq, 32);
+        tau[g] = sm + z * st[DH] * sqrtf(sq);
+    }
+    __syncthreads(); // tile 0 in s_a[0]
+
+    // products of tile c in accumulator set c % 2 (no copies between the sets,
+    // so a step never waits for the products it has just issued)
+    f32x16_t A0 = {}, A1 = {}, B0 = {}, B1 = {};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s_a[0][kk * 64 + lane]);
+        A0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[0][kk], A0, 0, 0, 0);
+        A1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[1][kk], A1, 0, 0, 0);
+    }
+    uint32_t* my = s_rec[wave] + lane * RW;
+    // One tile: R holds tile ct + 1, which goes to LDS (into the buffer tile ct
+    // - 1 used) and is multiplied into (n0, n1); R then takes tile ct + 3; tile
+    // ct's products (c0, c1) are compared meanwhile.
+    auto step = [&](int ct, pieces_t& R, const f32x16_t& c0, const f32x16_t& c1, f32x16_t& n0, f32x16_t& n1) {
+        const int nb = (ct + 1) & 1;
+        store_tile(R, nb);
+        __syncthreads();
+        load_tile(R, ct + 3);
+        __builtin_amdgcn_sched_barrier(0); // the loads go out here, their wait stays at the store
+        const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, s_a[nb][lane]);
+        n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[0][0], f32x16_t{}, 0, 0, 0);
+        n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bq[1][0], f32x16_t{}, 0, 0, 0);
+#pragma unroll
+        for (int kk = 1; kk < KSTEPS; ++kk) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, s_a[nb][kk * 64 + lane]);
+            n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[0][kk], n0, 0, 0, 0);
+            n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[1][kk], n1, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0); // the products of tile ct + 1 go out before the comparisons of tile ct
+        const uint32_t w0 = ~below_bits(c0, tau[0]) & 0xFFFFu, w1 = ~below_bits(c1, tau[1]) & 0xFFFFu;
+        // lane l < 32 keeps row l of group 0 (its own bits and lane l + 32's),
+        // lane l >= 32 row l - 32 of group 1 (lane l - 32's bits and its own):
+        // v_permlane32_swap exchanges w0's upper lanes with w1's lower ones
+        const auto sw = __builtin_amdgcn_permlane32_swap(w0, w1, false, false);
+        my[ct] = sw[0] | (sw[1] << 16);
+    };
+    // the register set of tile c + 1 is (c + 1) % 2; the steps run to an even
+    // count with no branch between them (so the loads' waits stay counted),
+    // one past the last tile repeating it into a record word that is
+    // overwritten below (ctiles < RW)
+    for (int ct = 0; ct < ctiles; ct += 2) {
+        step(ct, R1, A0, A1, B0, B1);
+        step(ct + 1, R0, B0, B1, A0, A1);
+    }
+    // lane l's row: token tw + l
+    const int tl = tw + lane;
+    if (tl < r.Tc) {
+        my[ctiles] = __float_as_uint(lane < 32 ? tau[0] : tau[1]);
+        for (int c = ctiles + 1; c < RW; ++c)
+            my[c] = 0u;
+        const long rows_all = (long)r.B * r.Ts * H;
+        const long row = ((long)b * r.Ts + r.t0 + tl) * H + h;
+        uint4* dst = reinterpret_cast<uint4*>(rec + ((long)half * rows_all + row) * RW);
+        for (int c = 0; c < RW / 4; ++c)
+            dst[c] = make_uint4(my[4 * c], my[4 * c + 1], my[4 * c + 2], my[4 * c + 3]);
+    }
+}
+
+// The statistics the fused scoring sets its thresholds from, per table (h,
+// half) = blockIdx.x: the mean row mu (dh floats) and sigma, the root mean
+// square deviation from it over all S dh entries; [2 H][dh + 4].  Thread t sums
+// column t % dh over the rows t / dh, t / dh + 1024 / dh, ...; sums and squares
+// in float32 (the thresholds steer only the cost of the selection).
+constexpr int kStatThreads = 1024;
+
+__global__ __launch_bounds__(kStatThreads) void subkey_stats_kernel(const uint16_t* __restrict__ subkeys,
+                                                                    float* __restrict__ kstat, int S, int dh)
+{
+    __shared__ float s_sum[kStatThreads], s_sq[kStatThreads];
+    const uint16_t* tab = subkeys + (long)blockIdx.x * S * dh;
+    float* out = kstat + (long)blockIdx.x * (dh + 4);
+    const int t = threadIdx.x, phases = kStatThreads / dh, c = t % dh, p0 = t / dh;
+    float sum = 0.f, sq = 0.f;
+    if (p0 < phases) {
+#pragma unroll 4
+        for (int j = p0; j < S; j += phases) {
+            const float x = __uint_as_float((uint32_t)tab[(long)j * dh + c] << 16);
+            sum += x;
+            sq = fmaf(x, x, sq);
+        }
+    }
+    s_sum[t] = sum;
+    s_sq[t] = sq;
+    __syncthreads();
+    if (t < dh) {
+        float m = 0.f, m2 = 0.f;
+        for (int p = 0; p < phases; ++p) {
+            m += s_sum[p * dh + t];
+            m2 += s_sq[p * dh + t];
+        }
+        m /= (float)S;
+        out[t] = m;
+        s_sq[t] = fmaxf(m2 / (float)S - m * m, 0.f); // the column's variance
+    }
+    __syncthreads();
+    if (t == 0) {
+        float v = 0.f;
+        for (int i = 0; i < dh; ++i)
+            v += s_sq[i];
+        out[dh] = sqrtf(v / (float)dh);
+    }
+}
+
+template <int DH>
+hipError_t launch_cand_dh(const void* q0, const void* q1, const void* frag, const float* kstat, void* rec0,
+                          void* rec1, int nsets, const Rows& r, int S, float z, hipStream_t stream)
+{
+    const int tblocks = (r.Tc + kCandRows - 1) / kCandRows;
+    hipLaunchKernelGGL(pk_score_cand<DH>, dim3((unsigned)(tblocks * r.B * r.H * 2), (unsigned)nsets), dim3(64 * kCandWaves), 0,
+                       stream, (const uint16_t*)q0, (const uint16_t*)q1, (const uint4*)frag,
+                       kstat, (uint32_t*)rec0, (uint32_t*)rec1, r, S, z);
+    return hipGetLastError();
+}
+
 template <int DH>
 hipError_t launch_dh(const void* q, const void* subkeys, const void* frag, void* scores, const Rows& r, int S,
                      bool in_bf16, bool half_out, hipStream_t stream)
@@ -377,6 +628,54 @@ hipError_t launch_pk_score_pair(const void* q0, const void* q1, const void* subk
     }
     const hipError_t e = launch_pk_score(q0, subkeys, frag, s0, r, S, dh, in_bf16, in_bf16, stream);
     return e != hipSuccess ? e : launch_pk_score(q1, subkeys, frag, s1, r, S, dh, in_bf16, in_bf16, stream);
+}
+
+} // namespace sdm
+
+namespace sdm {
+
+bool pk_cand_path(int S, int dh, int k, bool in_bf16)
+{
+    return in_bf16 && S % 32 == 0 && S >= 128 && cand_record_dwords(S) <= kCandMaxRW && (dh == 64 || dh == 128) &&
+           k <= 48 && 2 * cand_target(k) <= S;
+}
+
+size_t subkey_stats_floats(int H, int dh) { return (size_t)2 * H * (dh + 4); }
+
+hipError_t launch_subkey_stats(const void* subkeys, float* kstat, int H, int S, int dh, hipStream_t stream)
+{
+    if (dh > kStatThreads)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(subkey_stats_kernel, dim3((unsigned)(2 * H)), dim3(kStatThreads), 0, stream,
+                       (const uint16_t*)subkeys, kstat, S, dh);
+    return hipGetLastError();
+}
+
+float cand_quantile(int S, int k)
+{
+    // z with P(N(0,1) > z) = cand_target(k) / S, by bisection on erfc
+    const double p = (double)cand_target(k) / (double)S;
+    double lo = -8.0, hi = 8.0;
+    for (int i = 0; i < 80; ++i) {
+        const double mid = 0.5 * (lo + hi);
+        if (0.5 * std::erfc(mid / std::sqrt(2.0)) > p)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return (float)(0.5 * (lo + hi));
+}
+
+hipError_t launch_pk_score_cand(const void* q0, const void* q1, const void* frag, const float* kstat, void* rec0,
+                                void* rec1, int nsets, const Rows& r, int S, int dh, int k, hipStream_t stream)
+{
+    if (r.count() <= 0)
+        return hipSuccess;
+    if (!pk_cand_path(S, dh, k, true) || nsets < 1 || nsets > 2)
+        return hipErrorInvalidValue;
+    const float z = cand_quantile(S, k);
+    return dh == 64 ? launch_cand_dh<64>(q0, q1, frag, kstat, rec0, rec1, nsets, r, S, z, stream)
+                    : launch_cand_dh<128>(q0, q1, frag, kstat, rec0, rec1, nsets, r, S, z, stream);
 }
 
 } // namespace sdm

@@ -293,6 +293,9 @@ __device__ __forceinline__ float bound_f16(float E, int dh)
     return a < 32768.0 ? E : __builtin_inff();
 }
 
+template <int J, bool BF16>
+__device__ __forceinline__ uint64_t half_all_exact(int S, int k, int lane, uint64_t* buf, Refine ref);
+
 // Top k of one half, sorted (score desc, index asc): lane r < k ends with the
 // r-th survivor as (key << 32) | ~index.  buf: 64 entries of wave scratch.
 // With ref, the scores that can reach the top k are made exact first (see the
@@ -351,12 +354,24 @@ __device__ __forceinline__ uint64_t half_sorted_topk_exact(const SC* __restrict_
         return LAT ? sort64_desc_count(x, lane, buf) : sort64_desc(x, lane);
     }
     // heavy ties: every score of the half exact, the k-th largest by a full radix select
+    return half_all_exact<J, BF16>(S, k, lane, buf, ref);
+}
+
+// Top k of one half with every score made exact, the k-th largest by a full
+// radix select, ties at it taken lowest index first; sorted as
+// half_sorted_topk_exact's result.
+template <int J, bool BF16>
+__device__ __forceinline__ uint64_t half_all_exact(int S, int k, int lane, uint64_t* buf, Refine ref)
+{
+    const char* table = static_cast<const char*>(ref.table);
+    const size_t row_bytes = (size_t)ref.dh * (BF16 ? 2 : 4);
+    uint32_t key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int idx = j * 64 + lane;
         key[j] = idx < S ? ordered_key(exact_score<BF16>(ref.qd, table + idx * row_bytes, ref.dh)) : 0u;
     }
-    thr = kth_largest<J>(key, k);
+    const uint32_t thr = kth_largest<J>(key, k);
     const int need = k - count_above<J>(key, thr);
     int tied = 0, placed = 0;
 #pragma unroll
@@ -377,6 +392,69 @@ __device__ __forceinline__ uint64_t half_sorted_topk_exact(const SC* __restrict_
     wave_sync_lds();
     return sort64_desc(x, lane);
 }
+
+// Sub-key of bit p of candidate word c (the fused scoring's record layout):
+// bits 0-15 from lane group 0, 16-31 from group 1, each group's first score in
+// its highest bit; within the 32-wide tile, score v of group g is sub-key
+// 8 (v / 4) + 4 g + (v % 4).
+__device__ __forceinline__ uint32_t cand_subkey(int c, int p)
+{
+    const int g = p >> 4, v = 15 - (p & 15);
+    return (uint32_t)(c * 32 + 8 * (v >> 2) + 4 * g + (v & 3));
+}
+
+// Top k of one half from a candidate record: the sub-keys whose float32 score
+// reached the record's threshold tau are made exact.  If at least k of them have
+// exact scores >= tau + E, the k-th largest exact score is at least tau + E, so
+// every sub-key that ties or beats it has a float32 score >= tau (E bounds the
+// difference) and is a candidate: the sorted candidates then start with the
+// exact top k.  Otherwise, or with more than 64 candidates, or an E too large to
+// rule out float32 overflow in the scores, every score of the half is made
+// exact.  rec: the record (S / 32 words, then tau); sorted as
+// half_sorted_topk_exact's result.
+template <int J, bool BF16>
+__device__ __forceinline__ uint64_t half_sorted_topk_cand(const uint32_t* __restrict__ rec, int S, int k, int lane,
+                                                          uint64_t* buf, Refine ref)
+{
+    const int nw = S / 32;
+    uint32_t bits = lane < nw ? rec[lane] : 0u;
+    const float tau = __uint_as_float(rec[nw]);
+    const int cnt = __popc(bits);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        incl += lane >= o ? t : 0;
+    }
+    const int total = __shfl(incl, 63);
+    if (total >= k && total <= 64 && ref.E < 1e30f) {
+        int pos = incl - cnt;
+        while (bits) {
+            const int p = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            buf[pos++] = (uint64_t)cand_subkey(lane, p);
+        }
+        wave_sync_lds();
+        const char* table = static_cast<const char*>(ref.table);
+        const size_t row_bytes = (size_t)ref.dh * (BF16 ? 2 : 4);
+        uint64_t x = 0ull;
+        float e = 0.f;
+        if (lane < total) {
+            const uint32_t sk = (uint32_t)buf[lane];
+            e = exact_score<BF16>(ref.qd, table + sk * row_bytes, ref.dh);
+            x = ((uint64_t)ordered_key(e) << 32) | (uint64_t)(~sk);
+        }
+        // tau + E in double, nudged up past its rounding (and past subnormal flushes)
+        double lim = (double)tau + (double)ref.E;
+        lim += fabs(lim) * 0x1p-50 + 0x1p-110;
+        const bool ok = __popcll(ballot(lane < total && (double)e >= lim)) >= k;
+        wave_sync_lds();
+        if (ok)
+            return sort64_desc(x, lane);
+    }
+    return half_all_exact<J, BF16>(S, k, lane, buf, ref);
+}
+
 
 // Top k of one half, sorted (score desc, index asc): lane r < k ends with the
 // r-th survivor as (key << 32) | ~index.  buf: 64 entries of wave scratch.
@@ -561,6 +639,25 @@ __device__ __forceinline__ void select_row_exact(const SC* s, int S, int k, int 
     select_half_exact<J, BF16, LAT, SC>(s + S, S, k, lane, buf, val[1], sub[1], ref1);
     wave_sync_lds();
     select_from_lists<R, LAT>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
+}
+
+// select_row_exact from candidate records (rec0, rec1 for halves 0 and 1).
+template <int J, int R, bool BF16>
+__device__ __forceinline__ void select_row_cand(const uint32_t* rec0, const uint32_t* rec1, int S, int k, int W,
+                                                int n_pairs, const uint16_t* s_pairs, int lane, uint64_t* buf,
+                                                float (*val)[64], uint32_t (*sub)[64], int32_t* idx_row,
+                                                float* wt_row, Refine ref0, Refine ref1)
+{
+    const uint32_t* rec[2] = {rec0, rec1};
+    const Refine ref[2] = {ref0, ref1};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const uint64_t x = half_sorted_topk_cand<J, BF16>(rec[hf], S, k, lane, buf, ref[hf]);
+        val[hf][lane] = key_value((uint32_t)(x >> 32));
+        sub[hf][lane] = ~(uint32_t)x;
+    }
+    wave_sync_lds();
+    select_from_lists<R, false>(S, k, W, n_pairs, s_pairs, lane, buf, val, sub, idx_row, wt_row);
 }
 
 template <int R, bool LAT>

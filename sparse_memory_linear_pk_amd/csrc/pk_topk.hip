@@ -37,7 +37,8 @@ struct SetOut {
 
 // J: sub-keys per lane per half (S <= 64*J); R: restricted candidates per lane;
 // EX: 0 float32 scores as given, 1 exact from bf16 inputs (binary16 scores), 2
-// exact from float32 inputs (float32 scores).
+// exact from float32 inputs (float32 scores), 3 exact from bf16 inputs and the
+// fused scoring's candidate records (in place of scores).
 template <int J, int R, int EX>
 __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(SetOut s0, SetOut s1, Rows rr, int S, int k,
                                                                    int W, int n_pairs, ExactIn ex)
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(SetOut s0, 
         select_row<J, R>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane, s_buf[wave], s_val[wave],
                          s_sub[wave], idx + row * W, wt + row * W);
     } else {
-        constexpr bool BF16 = EX == 1;
+        constexpr bool BF16 = EX == 1 || EX == 3;
         const int h = (int)(row % rr.H), dh = ex.dh;
         const size_t es = BF16 ? 2 : 4;
         stage_query<BF16>(static_cast<const char*>(ex.q) + (size_t)row * 2 * dh * es, s_qd[wave], 2 * dh, lane);
@@ -76,14 +77,21 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(SetOut s0, 
         r0.E = half_bound(r0, max_of_parts(ex.kmax + (h * 2 + 0) * kAbsmaxParts, kAbsmaxParts, lane), lane);
         r1.E = half_bound(r1, max_of_parts(ex.kmax + (h * 2 + 1) * kAbsmaxParts, kAbsmaxParts, lane), lane);
         using SC = std::conditional_t<BF16, uint16_t, float>;
-        if constexpr (BF16) {
+        if constexpr (EX == 1) {
             r0.E = bound_f16(r0.E, dh);
             r1.E = bound_f16(r1.E, dh);
         }
-        const SC* scores = static_cast<const SC*>(scores_v);
-        select_row_exact<J, R, BF16, false, SC>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane,
-                                                s_buf[wave], s_val[wave], s_sub[wave], idx + row * W, wt + row * W, r0,
-                                                r1);
+        if constexpr (EX == 3) {
+            const uint32_t* rec = static_cast<const uint32_t*>(scores_v);
+            const long rows_all = (long)rr.B * rr.Ts * rr.H, rw = cand_record_dwords(S);
+            select_row_cand<J, R, true>(rec + row * rw, rec + (rows_all + row) * rw, S, k, W, n_pairs, s_pairs, lane,
+                                        s_buf[wave], s_val[wave], s_sub[wave], idx + row * W, wt + row * W, r0, r1);
+        } else {
+            const SC* scores = static_cast<const SC*>(scores_v);
+            select_row_exact<J, R, BF16, false, SC>(scores + row * 2 * (long)S, S, k, W, n_pairs, s_pairs, lane,
+                                                    s_buf[wave], s_val[wave], s_sub[wave], idx + row * W,
+                                                    wt + row * W, r0, r1);
+        }
     }
 }
 
@@ -150,8 +158,10 @@ hipError_t launch_ex(const SetOut& s0, const SetOut& s1, int nsets, const Rows& 
 }
 
 // Both query sets' selection in one launch (nsets 2) or one set (nsets 1, s1 unused).
+// cand: the sets' scores are the fused scoring's candidate records (bf16 inputs).
 hipError_t launch_sets(const SetOut& s0, const SetOut& s1, int nsets, const Rows& r, int S, int k, int W,
-                       const void* subkeys, const float* kmax, int dh, bool in_bf16, hipStream_t stream)
+                       const void* subkeys, const float* kmax, int dh, bool in_bf16, hipStream_t stream,
+                       bool cand = false)
 {
     if (r.count() <= 0)
         return hipSuccess;
@@ -166,6 +176,9 @@ hipError_t launch_sets(const SetOut& s0, const SetOut& s1, int nsets, const Rows
     const ExactIn ex{s0.q, subkeys, kmax, dh};
     if (!exact)
         return launch_ex<0>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
+    if (cand)
+        return in_bf16 && pk_cand_path(S, dh, k, true) ? launch_ex<3>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream)
+                                                       : hipErrorInvalidValue;
     return in_bf16 ? launch_ex<1>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream)
                    : launch_ex<2>(s0, s1, nsets, r, S, k, W, n_pairs, ex, stream);
 }
@@ -199,6 +212,17 @@ hipError_t launch_pk_topk_pair(const void* scores0, const void* scores1, int32_t
         return hipErrorInvalidValue;
     const SetOut s0{scores0, idx0, wt0, q0}, s1{scores1, idx1, wt1, q1};
     return launch_sets(s0, s1, 2, r, S, k, W, subkeys, kmax, dh, in_bf16, stream);
+}
+
+hipError_t launch_pk_topk_cand(const void* rec0, const void* rec1, int32_t* idx0, int32_t* idx1, float* wt0,
+                               float* wt1, int nsets, const Rows& r, int S, int k, int W, const void* q0,
+                               const void* q1, const void* subkeys, const float* kmax, int dh, hipStream_t stream)
+{
+    if (!q0 || (nsets == 2 && !q1) || nsets < 1 || nsets > 2)
+        return hipErrorInvalidValue;
+    const SetOut s0{rec0, idx0, wt0, q0}, s1{nsets == 2 ? rec1 : rec0, nsets == 2 ? idx1 : idx0,
+                                              nsets == 2 ? wt1 : wt0, nsets == 2 ? q1 : q0};
+    return launch_sets(s0, s1, nsets, r, S, k, W, subkeys, kmax, dh, true, stream, true);
 }
 
 } // namespace sdm

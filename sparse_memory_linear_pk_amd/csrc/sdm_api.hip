@@ -82,7 +82,7 @@ Chunking chunking_of(const sdm_config& c)
 }
 
 struct Layout {
-    size_t scores, idx, wt, plan, frag, kmax, step, total;
+    size_t scores, idx, wt, plan, frag, kmax, kstat, step, total;
     std::vector<size_t> plan_off; // byte offset of each chunk's plan
 };
 
@@ -105,7 +105,9 @@ Layout layout_of(const sdm_config& c, const Chunking& k, const std::vector<sdm::
     // apart from the forward's buffers (which hold B*T*H*W and T may be 1)
     L.step = align_up(2 * (size_t)c.B * c.H * c.W * sizeof(int32_t));
     L.kmax = align_up(2 * (size_t)c.H * sdm::kAbsmaxParts * sizeof(float)); // partial max |K| per sub-key table
-    L.total = 2 * L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag + L.kmax + 2 * L.step;
+    // the tables' mean rows and spreads, for the fused scoring's thresholds
+    L.kstat = align_up(sdm::subkey_stats_floats(c.H, c.dk / 2) * sizeof(float));
+    L.total = 2 * L.scores + 2 * (L.idx + L.wt) + L.plan + L.frag + L.kmax + L.kstat + 2 * L.step;
     return L;
 }
 
@@ -210,6 +212,7 @@ struct sdm_ctx {
     int32_t* step_idx;   // [2][B*H][W] (sdm_step)
     float* step_wt;      // [2][B*H][W]
     float* kmax;         // [H][2][kAbsmaxParts]: partial max |K| of each sub-key table (the exact selection's bound)
+    float* kstat;        // [H][2][dh + 4]: mean row and spread of each table (the fused scoring's thresholds)
     bool timing;
     std::vector<TimedLaunch> pending;
     sdm_timing totals;
@@ -265,8 +268,12 @@ sdm::Rows chunk_rows(const sdm_ctx* h, int ci)
     return sdm::Rows{c.B, c.H, h->ck.len(ci), c.T, h->ck.t0(ci)};
 }
 
+// Whether the forward's addressing scores with the fused candidate search.
+bool cand_path(const sdm_config& c) { return sdm::pk_cand_path(c.n_sub, c.dk / 2, c.k, c.in_dtype == SDM_BF16); }
+
 // The per-call preparation of the sub-key tables: their MFMA operand order (bf16
-// inputs) and the largest magnitude of each table (the exact selection's bound).
+// inputs), the largest magnitude of each table (the exact selection's bound)
+// and, for the fused scoring, each table's mean row and spread.
 hipError_t prepare_subkeys(sdm_ctx* h, const void* subkeys, hipStream_t st)
 {
     const sdm_config& c = h->cfg;
@@ -276,6 +283,8 @@ hipError_t prepare_subkeys(sdm_ctx* h, const void* subkeys, hipStream_t st)
         e = sdm::launch_pk_subkey_frag(subkeys, h->frag, c.H, c.n_sub, c.dk / 2, st);
     if (e == hipSuccess)
         e = sdm::launch_subkey_absmax(subkeys, h->kmax, c.H, c.n_sub, c.dk / 2, bf16, st);
+    if (e == hipSuccess && cand_path(c))
+        e = sdm::launch_subkey_stats(subkeys, h->kstat, c.H, c.n_sub, c.dk / 2, st);
     return e;
 }
 
@@ -292,7 +301,9 @@ sdm_status run_score(sdm_ctx* h, const void* q, const void* subkeys, void* score
         e = prepare_subkeys(h, subkeys, st);
     if (e == hipSuccess) {
         Timer t(h, K_SCORE, st); // pk_score alone
-        e = sdm::launch_pk_score(q, subkeys, h->frag, scores, r, c.n_sub, c.dk / 2, bf16, exact && bf16, st);
+        e = exact && cand_path(c)
+                ? sdm::launch_pk_score_cand(q, q, h->frag, h->kstat, scores, scores, 1, r, c.n_sub, c.dk / 2, c.k, st)
+                : sdm::launch_pk_score(q, subkeys, h->frag, scores, r, c.n_sub, c.dk / 2, bf16, exact && bf16, st);
     }
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_score launch");
 }
@@ -306,8 +317,11 @@ sdm_status run_select(sdm_ctx* h, const void* scores, int32_t* idx, float* wt, c
 {
     const sdm_config& c = h->cfg;
     Timer t(h, K_SELECT, st);
-    hipError_t e = sdm::launch_pk_topk(scores, idx, wt, r, c.n_sub, c.k, c.W, q, subkeys, h->kmax, c.dk / 2,
-                                       c.in_dtype == SDM_BF16, st);
+    hipError_t e = q && cand_path(c)
+                       ? sdm::launch_pk_topk_cand(scores, scores, idx, idx, wt, wt, 1, r, c.n_sub, c.k, c.W, q, q,
+                                                  subkeys, h->kmax, c.dk / 2, st)
+                       : sdm::launch_pk_topk(scores, idx, wt, r, c.n_sub, c.k, c.W, q, subkeys, h->kmax, c.dk / 2,
+                                             c.in_dtype == SDM_BF16, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_topk launch");
 }
 
@@ -357,23 +371,33 @@ sdm_status run_scan(sdm_ctx* h, int ci, const void* v, void* mem, float* out, hi
     return e == hipSuccess ? SDM_OK : hip_fail(e, "sdm_scan launch");
 }
 
-// Scores and exact selection of both query sets for rows r, one launch each.
+// Scores and exact selection of both query sets for rows r, one launch each,
+// into h->idx and h->wt, or into idx/wt (both sets) when given.
 sdm_status run_address_pair(sdm_ctx* h, const sdm::Rows& r, const void* wq, const void* rq, const void* subkeys,
-                            hipStream_t st, bool prepare)
+                            hipStream_t st, bool prepare, int32_t* const* idx = nullptr, float* const* wt = nullptr)
 {
+    int32_t* io0 = idx ? idx[0] : h->idx[0];
+    int32_t* io1 = idx ? idx[1] : h->idx[1];
+    float* wo0 = wt ? wt[0] : h->wt[0];
+    float* wo1 = wt ? wt[1] : h->wt[1];
     const sdm_config& c = h->cfg;
     const bool bf16 = c.in_dtype == SDM_BF16;
     hipError_t e = prepare ? prepare_subkeys(h, subkeys, st) : hipSuccess;
+    const bool cand = cand_path(c);
     if (e == hipSuccess) {
         Timer t(h, K_SCORE, st);
-        e = sdm::launch_pk_score_pair(wq, rq, subkeys, h->frag, h->scores[0], h->scores[1], r, c.n_sub, c.dk / 2,
-                                      bf16, st);
+        e = cand ? sdm::launch_pk_score_cand(wq, rq, h->frag, h->kstat, h->scores[0], h->scores[1], 2, r, c.n_sub,
+                                             c.dk / 2, c.k, st)
+                 : sdm::launch_pk_score_pair(wq, rq, subkeys, h->frag, h->scores[0], h->scores[1], r, c.n_sub,
+                                             c.dk / 2, bf16, st);
     }
     if (e != hipSuccess)
         return hip_fail(e, "pk_score launch");
     Timer t(h, K_SELECT, st);
-    e = sdm::launch_pk_topk_pair(h->scores[0], h->scores[1], h->idx[0], h->idx[1], h->wt[0], h->wt[1], r, c.n_sub,
-                                 c.k, c.W, wq, rq, subkeys, h->kmax, c.dk / 2, bf16, st);
+    e = cand ? sdm::launch_pk_topk_cand(h->scores[0], h->scores[1], io0, io1, wo0, wo1, 2, r, c.n_sub, c.k, c.W, wq,
+                                        rq, subkeys, h->kmax, c.dk / 2, st)
+             : sdm::launch_pk_topk_pair(h->scores[0], h->scores[1], io0, io1, wo0, wo1, r, c.n_sub, c.k, c.W, wq, rq,
+                                        subkeys, h->kmax, c.dk / 2, bf16, st);
     return e == hipSuccess ? SDM_OK : hip_fail(e, "pk_topk launch");
 }
 
@@ -505,6 +529,8 @@ sdm_status sdm_create(const sdm_config* cfg, void* hip_stream, sdm_handle* out)
     p += h->L.frag;
     h->kmax = (float*)p;
     p += h->L.kmax;
+    h->kstat = (float*)p;
+    p += h->L.kstat;
     h->step_idx = (int32_t*)p;
     p += h->L.step;
     h->step_wt = (float*)p;
@@ -595,6 +621,22 @@ sdm_status sdm_address(sdm_handle h, const void* q, const void* subkeys, int32_t
         return fail(SDM_ERR_INVALID_ARG, "sdm_address: misaligned pointer");
     s = run_score(h, q, subkeys, h->scores[0], all_rows(h->cfg), h->stream, true);
     return s != SDM_OK ? s : run_select(h, h->scores[0], idx, wt, all_rows(h->cfg), h->stream, q, subkeys);
+}
+
+sdm_status sdm_address_pair(sdm_handle h, const void* wq, const void* rq, const void* subkeys, int32_t* idx_w,
+                            float* wt_w, int32_t* idx_r, float* wt_r)
+{
+    sdm_status s = check_handle(h);
+    if (s != SDM_OK)
+        return s;
+    if (!wq || !rq || !subkeys || !idx_w || !wt_w || !idx_r || !wt_r)
+        return fail(SDM_ERR_INVALID_ARG, "sdm_address_pair: NULL pointer");
+    if (!aligned16(wq) || !aligned16(rq) || !aligned16(subkeys) || !aligned4(idx_w) || !aligned4(wt_w) ||
+        !aligned4(idx_r) || !aligned4(wt_r))
+        return fail(SDM_ERR_INVALID_ARG, "sdm_address_pair: misaligned pointer");
+    int32_t* const idx[2] = {idx_w, idx_r};
+    float* const wt[2] = {wt_w, wt_r};
+    return run_address_pair(h, all_rows(h->cfg), wq, rq, subkeys, h->stream, true, idx, wt);
 }
 
 sdm_status sdm_scan_with(sdm_handle h, const int32_t* idx_w, const float* wt_w, const int32_t* idx_r,

@@ -75,6 +75,25 @@ hipError_t launch_pk_score(const void* q, const void* subkeys, const void* frag,
 hipError_t launch_pk_score_pair(const void* q0, const void* q1, const void* subkeys, const void* frag, void* s0,
                                 void* s1, const Rows& r, int S, int dh, bool in_bf16, hipStream_t stream);
 
+// Scoring fused with the exact selection's candidate search (bf16 inputs; see
+// pk_score.hip): per (half, row) a record of cand_record_dwords(S) words, the
+// bitmask of the sub-keys whose float32 score reached the record's threshold,
+// then the threshold; records [2][B * Ts * H][RW].  kstat: the tables' mean
+// rows and spreads (launch_subkey_stats, subkey_stats_floats(H, dh) floats).
+__host__ __device__ inline int cand_record_dwords(int S) { return (S / 32 + 1 + 3) & ~3; }
+// candidates per half the threshold aims at
+__host__ __device__ inline int cand_target(int k) { return (k + 64) / 2; }
+bool pk_cand_path(int S, int dh, int k, bool in_bf16);
+size_t subkey_stats_floats(int H, int dh);
+hipError_t launch_subkey_stats(const void* subkeys, float* kstat, int H, int S, int dh, hipStream_t stream);
+hipError_t launch_pk_score_cand(const void* q0, const void* q1, const void* frag, const float* kstat, void* rec0,
+                                void* rec1, int nsets, const Rows& r, int S, int dh, int k, hipStream_t stream);
+// The exact selection from candidate records (nsets query sets; q0, q1 the
+// queries the records were made from).
+hipError_t launch_pk_topk_cand(const void* rec0, const void* rec1, int32_t* idx0, int32_t* idx1, float* wt0,
+                               float* wt1, int nsets, const Rows& r, int S, int k, int W, const void* q0,
+                               const void* q1, const void* subkeys, const float* kmax, int dh, hipStream_t stream);
+
 // Per-half top-k, outer-sum top-W and softmax weights of the covered rows:
 // scores [B*Ts*H, 2, S] -> idx, wt [B*Ts*H, W].  With q ([B, Ts, H, dk]),
 // subkeys and kmax (max |K| per table, [H, 2]) the scores that can reach a

@@ -8,7 +8,7 @@ from sparse_memory_linear_pk_amd import _lib
 from sparse_memory_linear_pk_amd._lib import Config, Timing, SDM_OK, SDM_ERR_INVALID_ARG, SDM_ERR_UNSUPPORTED
 
 EXPECTED = ["sdm_create", "sdm_forward", "sdm_destroy", "sdm_status_str", "sdm_last_error", "sdm_workspace_bytes",
-            "sdm_score", "sdm_select", "sdm_address", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing",
+            "sdm_score", "sdm_select", "sdm_address", "sdm_address_pair", "sdm_scan_with", "sdm_set_timing", "sdm_get_timing",
             "sdm_pattern_probe", "sdm_step", "sdm_forward_train", "sdm_backward_workspace_bytes", "sdm_backward",
             "sdm_pattern_probe_mix", "sdm_project", "sdm_broadcast_memory", "sdm_overlap", "sdm_mem_stride_hint",
             "sdm_step_static"]
@@ -84,7 +84,8 @@ def test_null_arguments():
     assert L.sdm_workspace_bytes(None, None) == SDM_ERR_INVALID_ARG
     assert L.sdm_create(C.byref(_cfg()), None, None) == SDM_ERR_INVALID_ARG
     for f, n in (("sdm_forward", 8), ("sdm_score", 3), ("sdm_select", 3), ("sdm_address", 4),
-                 ("sdm_scan_with", 9), ("sdm_step", 8), ("sdm_forward_train", 9), ("sdm_backward", 16), ("sdm_broadcast_memory", 2)):
+                 ("sdm_address_pair", 7), ("sdm_scan_with", 9), ("sdm_step", 8), ("sdm_forward_train", 9),
+                 ("sdm_backward", 16), ("sdm_broadcast_memory", 2)):
         assert getattr(L, f)(None, *([None] * n)) == SDM_ERR_INVALID_ARG, f
     assert L.sdm_project(None, 64, *([None] * 8)) == SDM_ERR_INVALID_ARG
     assert L.sdm_overlap(None, None, None, None, None, 4, None, None, 0, None, None) == SDM_ERR_INVALID_ARG

@@ -55,6 +55,12 @@ def run_gpu(T, cfg, x, stages=True):
                 layer.address(q, dev["subkeys"], idx2, wt2)
                 res[f"scores_{name}"], res[f"idx_{name}"], res[f"wt_{name}"] = sc, idx, wt
                 res[f"idx2_{name}"], res[f"wt2_{name}"] = idx2, wt2
+            # both sets in the forward's own launches equal the one-set seam bit for bit
+            pair = [T.empty_like(res["idx2_w"]), T.empty_like(res["wt2_w"]), T.empty_like(res["idx2_r"]),
+                    T.empty_like(res["wt2_r"])]
+            layer.address_pair(dev["wq"], dev["rq"], dev["subkeys"], *pair)
+            for a, b in zip(pair, ("idx2_w", "wt2_w", "idx2_r", "wt2_r")):
+                assert T.equal(a.view(T.int32), res[b].view(T.int32)), f"sdm_address_pair differs from sdm_address: {b}"
         mem = dev["mem0"].clone()
         out = T.empty((cfg.B, cfg.T, cfg.H, cfg.d), dtype=T.float32, device="cuda")
         layer.forward(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem, out)
@@ -310,6 +316,11 @@ def full_gpu_run(T, cfg, label, padded=False) -> dict:
             layer.address(dev[s_ + "q"], dev["subkeys"], idx, wt)
             g[f"idx2_{s_}"], g[f"wt2_{s_}"] = to_host(idx), to_host(wt)
             del sc
+        pair = [T.empty((R, cfg.W), dtype=dt, device="cuda") for dt in (T.int32, T.float32, T.int32, T.float32)]
+        layer.address_pair(dev["wq"], dev["rq"], dev["subkeys"], *pair)
+        for a, b in zip(pair, ("idx2_w", "wt2_w", "idx2_r", "wt2_r")):
+            assert np.array_equal(to_host(a).view(np.int32), g[b].view(np.int32)), f"sdm_address_pair: {b}"
+        del pair
         layer.forward(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem, out)
         T.cuda.synchronize()
     if padded:

@@ -101,25 +101,40 @@ def _crafted_tables(S, dh, rng, kind):
     elif kind == "beyond_binary16":
         # scores past binary16's range: every score of the half is made exact
         K *= 300.0
+    elif kind == "shifted_mean":
+        # a common offset far above the spread: the fused scoring's threshold must follow the mean row
+        K += 3.0
+    elif kind == "low_rank":
+        # sub-keys along two directions only: scores far from the isotropic spread the threshold
+        # assumes, so many halves take the whole-half rescoring
+        K = (rng.standard_normal((1, 2, S, 2)) @ rng.standard_normal((2, dh)) * 0.25
+             + rng.standard_normal((1, 2, S, dh)) * 1e-3).astype(np.float32)
     return K
 
 
 @pytest.mark.parametrize("in_bf16", [False, True])
 @pytest.mark.parametrize("kind,S,k,W", [("cancellation", 8, 1, 1), ("cancellation", 8, 2, 3), ("equal_rows", 100, 6, 20),
                                          ("duplicate_rows", 48, 8, 30), ("random", 480, 32, 64),
-                                         ("near_binary16_limit", 480, 32, 64), ("beyond_binary16", 480, 32, 64)])
+                                         ("near_binary16_limit", 480, 32, 64), ("beyond_binary16", 480, 32, 64),
+                                         ("equal_rows", 480, 32, 64), ("duplicate_rows", 480, 32, 64),
+                                         ("shifted_mean", 480, 32, 64), ("low_rank", 480, 32, 64),
+                                         ("random_dh128", 640, 32, 64), ("low_rank_dh128", 480, 16, 40)])
 def test_forward_addressing_equals_the_oracle(kind, S, k, W, in_bf16):
     """sdm_address (the forward's addressing) against the oracle's addressing of the same queries:
     the same slots, weights within one float32 unit, also where float32 sums order scores wrongly
     (cancellation), where more than 64 scores of a half tie (every score made exact), and, for bf16
     inputs (whose forward stores binary16 scores), with scores near binary16's range limit, where
-    its rounding step is wide, and beyond it."""
+    its rounding step is wide, and beyond it.  With bf16 inputs, S a multiple of 32 and dh 64 or
+    128 the forward's scoring is fused with the candidate search: tables with equal or duplicated
+    rows, a large common offset or two directions only steer its threshold wrong on purpose, and
+    every row must still select exactly."""
     import torch
     from parity import to_dev, to_host
     from sdm_inputs import bf16_bits_from_f32, f32_from_bf16_bits
     from sparse_memory_linear_pk_amd import SDM
     orc = oracle.get()
-    dh = 16 if kind == "cancellation" else 64
+    dh = 16 if kind == "cancellation" else 128 if kind.endswith("_dh128") else 64
+    kind = kind.removesuffix("_dh128")
     T = 40
     cfg = gi.config(0).replace(B=1, H=1, T=T, d=8, S=S, dk=2 * dh, k=k, W=W, in_bf16=in_bf16)
     rng = np.random.default_rng(7)
