@@ -52,7 +52,10 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(SetOut s0, 
     __shared__ float s_val[kRowsPerBlock][2][64];        // sorted half lists: scores
     __shared__ uint32_t s_sub[kRowsPerBlock][2][64];     // and sub-key indices
     __shared__ uint16_t s_pairs[kPairsMax];              // restricted candidates
-    __shared__ double s_qd[EX ? kRowsPerBlock : 1][EX ? 512 : 1]; // the row's query as doubles (exact path)
+    // the rows' queries as doubles (exact path): dk per wave, dynamic, so that
+    // the workgroup's LDS stays small enough for two of them per CU beside a
+    // running scan
+    extern __shared__ double s_qd[];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     fill_pairs(s_pairs, k, W);
@@ -71,9 +74,10 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void pk_topk_kernel(SetOut s0, 
         constexpr bool BF16 = EX == 1 || EX == 3;
         const int h = (int)(row % rr.H), dh = ex.dh;
         const size_t es = BF16 ? 2 : 4;
-        stage_query<BF16>(static_cast<const char*>(ex.q) + (size_t)row * 2 * dh * es, s_qd[wave], 2 * dh, lane);
+        double* qd = s_qd + (size_t)wave * 2 * dh;
+        stage_query<BF16>(static_cast<const char*>(ex.q) + (size_t)row * 2 * dh * es, qd, 2 * dh, lane);
         const char* tab = static_cast<const char*>(ex.subkeys) + (size_t)h * 2 * S * dh * es;
-        Refine r0{s_qd[wave], tab, dh, 0.f}, r1{s_qd[wave] + dh, tab + (size_t)S * dh * es, dh, 0.f};
+        Refine r0{qd, tab, dh, 0.f}, r1{qd + dh, tab + (size_t)S * dh * es, dh, 0.f};
         r0.E = half_bound(r0, max_of_parts(ex.kmax + (h * 2 + 0) * kAbsmaxParts, kAbsmaxParts, lane), lane);
         r1.E = half_bound(r1, max_of_parts(ex.kmax + (h * 2 + 1) * kAbsmaxParts, kAbsmaxParts, lane), lane);
         using SC = std::conditional_t<BF16, uint16_t, float>;
@@ -127,9 +131,10 @@ hipError_t launch_j(const SetOut& s0, const SetOut& s1, int nsets, const Rows& r
                     const ExactIn& ex, hipStream_t stream)
 {
     dim3 grid((unsigned)((r.count() + kRowsPerBlock - 1) / kRowsPerBlock), (unsigned)nsets), block(kRowsPerBlock * 64);
+    const size_t qd_bytes = EX ? (size_t)kRowsPerBlock * 2 * ex.dh * sizeof(double) : 0;
 #define SDM_TOPK_R(Rv)                                                                                        \
     if (n_pairs <= 64 * Rv) {                                                                                 \
-        hipLaunchKernelGGL((pk_topk_kernel<J, Rv, EX>), grid, block, 0, stream, s0, s1, r, S, k, W, n_pairs, ex); \
+        hipLaunchKernelGGL((pk_topk_kernel<J, Rv, EX>), grid, block, qd_bytes, stream, s0, s1, r, S, k, W, n_pairs, ex); \
         return hipGetLastError();                                                                             \
     }
     SDM_TOPK_R(1)

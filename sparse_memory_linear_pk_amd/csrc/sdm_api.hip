@@ -53,9 +53,10 @@ std::mutex g_scratch_mu;
 // A forward longer than kChunk tokens runs its scan in chunks: two of kChunk /
 // 2 tokens, then kChunk each, the last taking any remainder shorter than
 // kChunk / 2.  The addressing and plan of chunk c + 1 run on a second stream
-// while chunk c scans; beside a running scan they take about 0.7 of the scan's
-// time per token, so a chunk may be at most about 1.4 times the one before it:
-// the second chunk is as short as the first, whose preparation nothing hides.
+// while chunk c scans; beside a running scan they get only the CU resources
+// the scan leaves free and stretch to most of its time, so a chunk may be at
+// most about twice the one before it, and the second chunk is as short as the
+// first, whose preparation nothing hides.
 constexpr int kChunk = 2048;
 
 struct Chunking {
@@ -69,15 +70,16 @@ Chunking chunking_of(const sdm_config& c)
 {
     Chunking k;
     k.start.push_back(0);
-    int t = c.T <= kChunk ? c.T : kChunk / 2;
+    int t = 0, len = c.T <= kChunk ? c.T : kChunk / 2;
     while (true) {
-        if (c.T - t < kChunk / 2)
-            t = c.T;
-        k.start.push_back(t);
-        if (t == c.T)
+        int next = t + len;
+        if (next > c.T || c.T - next < kChunk / 2)
+            next = c.T; // the remainder joins this chunk
+        k.start.push_back(next);
+        if (next == c.T)
             return k;
-        const int len = k.C() == 1 ? kChunk / 2 : kChunk; // the second chunk as long as the first
-        t += len < c.T - t ? len : c.T - t;
+        len = k.C() == 1 ? kChunk / 2 : kChunk; // the second chunk as long as the first
+        t = next;
     }
 }
 

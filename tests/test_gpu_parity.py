@@ -222,9 +222,9 @@ def test_chunked_calls_are_bitwise_equal(T):
     assert np.array_equal(to_host(mem), g["mem"])
 
 
-# Forwards longer than 2048 tokens scan in several launches (1024, then 2048
-# each, the last one taking a remainder below 1024) while the next chunk's
-# addressing runs on a second stream.
+# Forwards longer than 2048 tokens scan in several launches (1024, 1024, then
+# 2048 each, the last one taking a remainder below 1024: 1024 and 1576 at 2600
+# tokens) while the next chunk's addressing runs on a second stream.
 CHUNKED = {
     "f32_state_f32_in": _edge(T=2600, B=2, H=2, d=32, S=32, k=6, W=16),
     "f32_state_bf16_in": _edge(T=2700, B=1, H=3, d=64, S=48, k=8, W=24, in_bf16=True),
@@ -241,7 +241,7 @@ def test_chunked_forward_parity(orc, T, name):
     x = gi.make_inputs(cfg)
     rng = np.random.default_rng(11)
     pats = x["wq"][:, :6].copy()
-    for t0 in (500, 512, 2555, 2560):
+    for t0 in (1000, 1024, 2040, 2048):
         if t0 + 24 <= cfg.T:
             x["wq"][:, t0:t0 + 24] = pats[:, rng.integers(0, 6, 24)]
             x["rq"][:, t0:t0 + 24] = pats[:, rng.integers(0, 6, 24)]
