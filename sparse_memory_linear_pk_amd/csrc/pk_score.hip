@@ -523,6 +523,83 @@ __global__ __launch_bounds__(kStatThreads) void subkey_stats_kernel(const uint16
     }
 }
 
+// The fused scoring's per-call preparation of the sub-key tables in one pass:
+// workgroup t = h * 2 + half copies table t into MFMA operand order (as
+// pk_subkey_frag, S a multiple of 32), and from the same loads takes its
+// largest magnitude (into partial-maximum slot 0, the other slots zero, as the
+// selection reduces them) and the statistics of its threshold (mean row and
+// spread, as subkey_stats_kernel).  Thread t always loads the same 8 columns
+// (the lane of a 16-byte operand piece and its k-step repeat every 1024
+// pieces), so its column sums need no exchange until the end.
+template <int DH>
+__global__ __launch_bounds__(1024) void subkey_prepare_kernel(const uint16_t* __restrict__ subkeys,
+                                                              uint4* __restrict__ frag, float* __restrict__ kstat,
+                                                              float* __restrict__ kmax, int S)
+{
+    constexpr int KSTEPS = DH / 16, NTH = 1024;
+    static_assert(NTH % (64 * KSTEPS) == 0 || (64 * KSTEPS) % NTH == 0, "the column group of a thread is fixed");
+    __shared__ float s_sum[NTH][8], s_sq[NTH][8];
+    __shared__ float s_max[NTH / 64], s_var[DH];
+    const int tid = threadIdx.x, t = blockIdx.x;
+    const long n = (long)(S / 32) * KSTEPS * 64;
+    const uint16_t* tab = subkeys + (long)t * S * DH;
+    uint4* fo = frag + (long)t * n;
+    float sum[8] = {}, sq[8] = {}, mx = 0.f;
+    for (long e = tid; e < n; e += NTH) {
+        const int ln = (int)(e % 64), kk = (int)((e / 64) % KSTEPS), ct = (int)(e / (64 * KSTEPS));
+        const uint4 x = *reinterpret_cast<const uint4*>(tab + (long)(ct * 32 + (ln & 31)) * DH + kk * 16 +
+                                                        (ln >> 5) * 8);
+        fo[e] = x;
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+            sum[2 * i] += lo;
+            sum[2 * i + 1] += hi;
+            sq[2 * i] = fmaf(lo, lo, sq[2 * i]);
+            sq[2 * i + 1] = fmaf(hi, hi, sq[2 * i + 1]);
+            mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        s_sum[tid][i] = sum[i];
+        s_sq[tid][i] = sq[i];
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0)
+        s_max[tid >> 6] = mx;
+    __syncthreads();
+    if (tid < DH) {
+        // column c is element c % 8 of column group g = c / 8: k-step g / 2, lane half g % 2
+        const int c = tid, g = c >> 3, kk = g >> 1, hb = g & 1;
+        float m = 0.f, m2 = 0.f;
+        for (int j = kk; j < NTH / 64; j += KSTEPS)
+            for (int r = 0; r < 32; ++r) {
+                const int src = j * 64 + hb * 32 + r;
+                m += s_sum[src][c & 7];
+                m2 += s_sq[src][c & 7];
+            }
+        m /= (float)S;
+        kstat[(long)t * (DH + 4) + c] = m;
+        s_var[c] = fmaxf(m2 / (float)S - m * m, 0.f);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float v = 0.f, m = 0.f;
+        for (int i = 0; i < DH; ++i)
+            v += s_var[i];
+        kstat[(long)t * (DH + 4) + DH] = sqrtf(v / (float)DH);
+        for (int i = 0; i < NTH / 64; ++i)
+            m = fmaxf(m, s_max[i]);
+        kmax[(long)t * kAbsmaxParts] = m;
+    }
+    if (tid > 0 && tid < kAbsmaxParts)
+        kmax[(long)t * kAbsmaxParts + tid] = 0.f;
+}
+
 template <int DH>
 hipError_t launch_cand_dh(const void* q0, const void* q1, const void* frag, const float* kstat, void* rec0,
                           void* rec1, int nsets, const Rows& r, int S, float z, hipStream_t stream)
@@ -641,6 +718,20 @@ bool pk_cand_path(int S, int dh, int k, bool in_bf16)
 }
 
 size_t subkey_stats_floats(int H, int dh) { return (size_t)2 * H * (dh + 4); }
+
+hipError_t launch_subkey_prepare(const void* subkeys, void* frag, float* kstat, float* kmax, int H, int S, int dh,
+                                 hipStream_t stream)
+{
+    if (!pk_cand_path(S, dh, 1, true))
+        return hipErrorInvalidValue;
+    if (dh == 64)
+        hipLaunchKernelGGL(subkey_prepare_kernel<64>, dim3((unsigned)(2 * H)), dim3(1024), 0, stream,
+                           (const uint16_t*)subkeys, (uint4*)frag, kstat, kmax, S);
+    else
+        hipLaunchKernelGGL(subkey_prepare_kernel<128>, dim3((unsigned)(2 * H)), dim3(1024), 0, stream,
+                           (const uint16_t*)subkeys, (uint4*)frag, kstat, kmax, S);
+    return hipGetLastError();
+}
 
 hipError_t launch_subkey_stats(const void* subkeys, float* kstat, int H, int S, int dh, hipStream_t stream)
 {

@@ -280,13 +280,13 @@ hipError_t prepare_subkeys(sdm_ctx* h, const void* subkeys, hipStream_t st)
 {
     const sdm_config& c = h->cfg;
     const bool bf16 = c.in_dtype == SDM_BF16;
+    if (cand_path(c)) // all three in one pass over the tables
+        return sdm::launch_subkey_prepare(subkeys, h->frag, h->kstat, h->kmax, c.H, c.n_sub, c.dk / 2, st);
     hipError_t e = hipSuccess;
     if (bf16)
         e = sdm::launch_pk_subkey_frag(subkeys, h->frag, c.H, c.n_sub, c.dk / 2, st);
     if (e == hipSuccess)
         e = sdm::launch_subkey_absmax(subkeys, h->kmax, c.H, c.n_sub, c.dk / 2, bf16, st);
-    if (e == hipSuccess && cand_path(c))
-        e = sdm::launch_subkey_stats(subkeys, h->kstat, c.H, c.n_sub, c.dk / 2, st);
     return e;
 }
 

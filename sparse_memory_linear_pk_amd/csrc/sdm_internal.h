@@ -86,6 +86,11 @@ __host__ __device__ inline int cand_target(int k) { return (k + 64) / 2; }
 bool pk_cand_path(int S, int dh, int k, bool in_bf16);
 size_t subkey_stats_floats(int H, int dh);
 hipError_t launch_subkey_stats(const void* subkeys, float* kstat, int H, int S, int dh, hipStream_t stream);
+// The fused scoring's whole preparation in one launch: frag (as
+// launch_pk_subkey_frag), kmax (max |K| in part 0 of each table, the other
+// parts zero) and kstat (as launch_subkey_stats).
+hipError_t launch_subkey_prepare(const void* subkeys, void* frag, float* kstat, float* kmax, int H, int S, int dh,
+                                 hipStream_t stream);
 hipError_t launch_pk_score_cand(const void* q0, const void* q1, const void* frag, const float* kstat, void* rec0,
                                 void* rec1, int nsets, const Rows& r, int S, int dh, int k, hipStream_t stream);
 // The exact selection from candidate records (nsets query sets; q0, q1 the
