@@ -545,20 +545,33 @@ __global__ __launch_bounds__(1024) void subkey_prepare_kernel(const uint16_t* __
     const uint16_t* tab = subkeys + (long)t * S * DH;
     uint4* fo = frag + (long)t * n;
     float sum[8] = {}, sq[8] = {}, mx = 0.f;
-    for (long e = tid; e < n; e += NTH) {
-        const int ln = (int)(e % 64), kk = (int)((e / 64) % KSTEPS), ct = (int)(e / (64 * KSTEPS));
-        const uint4 x = *reinterpret_cast<const uint4*>(tab + (long)(ct * 32 + (ln & 31)) * DH + kk * 16 +
-                                                        (ln >> 5) * 8);
-        fo[e] = x;
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    // in rounds of 8 pieces per thread, all 8 loads in flight at once (pieces past
+    // the table read as zeros, which change no sum and no maximum)
+    for (long e0 = tid; e0 < n; e0 += 8 * NTH) {
+        uint4 xs[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
-            sum[2 * i] += lo;
-            sum[2 * i + 1] += hi;
-            sq[2 * i] = fmaf(lo, lo, sq[2 * i]);
-            sq[2 * i + 1] = fmaf(hi, hi, sq[2 * i + 1]);
-            mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
+        for (int u = 0; u < 8; ++u) {
+            const long e = e0 + (long)u * NTH;
+            const int ln = (int)(e % 64), kk = (int)((e / 64) % KSTEPS), ct = (int)(e / (64 * KSTEPS));
+            xs[u] = e < n ? *reinterpret_cast<const uint4*>(tab + (long)(ct * 32 + (ln & 31)) * DH + kk * 16 +
+                                                           (ln >> 5) * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const long e = e0 + (long)u * NTH;
+            if (e < n)
+                fo[e] = xs[u];
+            const uint32_t w[4] = {xs[u].x, xs[u].y, xs[u].z, xs[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+                sum[2 * i] += lo;
+                sum[2 * i + 1] += hi;
+                sq[2 * i] = fmaf(lo, lo, sq[2 * i]);
+                sq[2 * i + 1] = fmaf(hi, hi, sq[2 * i + 1]);
+                mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
+            }
         }
     }
 #pragma unroll

@@ -105,6 +105,12 @@ def _run(T, cfg, x, g, ms, m0):
                 out_s[:, t] = o
             res["mem_step"], res["out_step"] = mem_s, out_s
             intact.append(_padding_intact(T, mem_s, ms))
+            # T steps equal the T-token forward bit for bit; where not, name the first token that differs
+            same = (_bits(T, out_s) == _bits(T, out)).reshape(cfg.B, cfg.T, cfg.H, cfg.d).all(dim=-1)
+            bad = [(b, h, int((~same[b, :, h]).nonzero()[0])) for b in range(cfg.B) for h in range(cfg.H)
+                   if not bool(same[b, :, h].all())]
+            say(f"[stride ms={ms}] steps against the forward: first differing token per (b, h): {bad or 'none'}")
+            assert not bad, f"ms={ms}: the decode steps differ from the forward at (b, h, t) {bad}"
         if g:
             mem_t = _padded(T, dev["mem0"], ms)
             out_t = T.empty_like(out)
