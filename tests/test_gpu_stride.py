@@ -83,8 +83,16 @@ def _trains(cfg, ms):
     return _steps(cfg) and cfg.S ** 2 * max(ms, cfg.d) * 4 < 2 ** 32
 
 
+def _digest(T, t):
+    """Two sums over a tensor's bit patterns: a later write into it changes them."""
+    b = _bits(T, t).to(T.int64) if t.dtype in (T.float32, T.bfloat16) else t.to(T.int64)
+    return int(b.sum().item()), float((b.to(T.float64) ** 2).sum().item())
+
+
 def _run(T, cfg, x, g, ms, m0):
-    """Every state entry point with rows ms apart (ms = d: dense).  Returns device tensors (dense views)."""
+    """Every state entry point with rows ms apart (ms = d: dense).  Returns device tensors (dense views).
+    Each result is fingerprinted when it is produced and checked again at the end, so that a later
+    call writing outside its own tensors is caught."""
     from sparse_memory_linear_pk_amd import SDM
     dev = {k: to_dev(v) for k, v in x.items()}
     f32 = dict(dtype=T.float32, device="cuda")
@@ -94,6 +102,7 @@ def _run(T, cfg, x, g, ms, m0):
         out = T.empty((cfg.B, cfg.T, cfg.H, cfg.d), **f32)
         layer.forward(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem, out)
         res["mem"], res["out"] = mem, out
+        fp = {k: _digest(T, res[k]) for k in ("mem", "out")}
         intact.append(_padding_intact(T, mem, ms))
         if _steps(cfg):
             mem_s = _padded(T, dev["mem0"], ms)
@@ -104,6 +113,7 @@ def _run(T, cfg, x, g, ms, m0):
                 layer.step(tok["wq"], tok["rq"], tok["v"], tok["alpha"], tok["beta"], dev["subkeys"], mem_s, o)
                 out_s[:, t] = o
             res["mem_step"], res["out_step"] = mem_s, out_s
+            fp.update({k: _digest(T, res[k]) for k in ("mem_step", "out_step")})
             intact.append(_padding_intact(T, mem_s, ms))
             # T steps equal the T-token forward bit for bit; where not, name the first token that differs
             same = (_bits(T, out_s) == _bits(T, out)).reshape(cfg.B, cfg.T, cfg.H, cfg.d).all(dim=-1)
@@ -118,6 +128,7 @@ def _run(T, cfg, x, g, ms, m0):
             layer.forward_train(dev["wq"], dev["rq"], dev["v"], dev["alpha"], dev["beta"], dev["subkeys"], mem_t,
                                 out_t, log)
             res["mem_train"], res["out_train"], res["log"] = mem_t.clone(), out_t, log
+            fp.update({k: _digest(T, res[k]) for k in ("mem_train", "out_train", "log")})
             gd = {k: to_dev(v) for k, v in g.items()}
             dm = _padded(T, gd["dmem"], ms)
             outs = {"dwq": T.empty((cfg.B, cfg.T, cfg.H, cfg.dk), **f32),
@@ -131,11 +142,13 @@ def _run(T, cfg, x, g, ms, m0):
                            outs["dsub"])
             res.update(outs)
             res["mem_restored"], res["dmem0"] = mem_t, dm
+            fp.update({k: _digest(T, res[k]) for k in list(outs) + ["mem_restored", "dmem0"]})
             intact += [_padding_intact(T, mem_t, ms), _padding_intact(T, dm, ms)]
         src = _padded(T, m0, ms)
         dst = _padded(T, T.zeros((cfg.B, *m0.shape), dtype=m0.dtype, device="cuda"), ms)
         layer.broadcast_memory(src, dst)
         res["broadcast"] = dst
+        fp["broadcast"] = _digest(T, dst)
         intact.append(_padding_intact(T, dst, ms))
         if ms != cfg.d:
             R = cfg.B * cfg.T * cfg.H
@@ -145,6 +158,9 @@ def _run(T, cfg, x, g, ms, m0):
                 layer.address(dev[q], dev["subkeys"], idx, wt)
                 res["idx_" + s_], res["wt_" + s_] = idx, wt
         T.cuda.synchronize()
+        changed = [k for k in res if k in fp and _digest(T, res[k]) != fp[k]]
+        say(f"[stride ms={ms}] results changed after they were produced: {changed or 'none'}")
+        assert not changed, f"ms={ms}: later calls wrote into {changed}"
     return res, intact
 
 
