@@ -537,7 +537,7 @@ __global__ __launch_bounds__(1024) void subkey_prepare_kernel(const uint16_t* __
                                                               float* __restrict__ kmax, int S)
 {
     constexpr int KSTEPS = DH / 16, NTH = 1024;
-    static_assert(NTH % (64 * KSTEPS) == 0 || (64 * KSTEPS) % NTH == 0, "the column group of a thread is fixed");
+    static_assert((NTH / 64) % KSTEPS == 0, "a thread's pieces keep their lane and k-step: its 8 columns are fixed");
     __shared__ float s_sum[NTH][8], s_sq[NTH][8];
     __shared__ float s_max[NTH / 64], s_var[DH];
     const int tid = threadIdx.x, t = blockIdx.x;
