@@ -8,6 +8,7 @@
 #include "sdm.h"
 #include "sdm_internal.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -50,14 +51,18 @@ constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::mutex g_scratch_mu;
 
-// A forward longer than kChunk tokens runs its scan in chunks: two of kChunk /
-// 2 tokens, then kChunk each, the last taking any remainder shorter than
-// kChunk / 2.  The addressing and plan of chunk c + 1 run on a second stream
-// while chunk c scans; beside a running scan they get only the CU resources
-// the scan leaves free and stretch to most of its time, so a chunk may be at
-// most about twice the one before it, and the second chunk is as short as the
-// first, whose preparation nothing hides.
-constexpr int kChunk = 2048;
+// A forward longer than kOneChunk tokens runs its scan in chunks: kFirstChunk
+// tokens first, then each chunk 3/2 of the one before (rounded down to a
+// multiple of 64 tokens) up to kMaxChunk, the last taking any remainder
+// shorter than kMaxChunk / 2.  The addressing and plan of chunk c + 1 run on a
+// second stream while chunk c scans; beside a running scan they get only the
+// CU resources the scan leaves free and stretch to most of its time, so a
+// chunk may be only a little longer than the one before it.  The first chunk,
+// whose preparation nothing hides, is short; the later ones are long, since
+// every scan launch costs about 50 us of pipeline fill and drain.
+constexpr int kOneChunk = 2048;
+constexpr int kFirstChunk = 640;
+constexpr int kMaxChunk = 3072;
 
 struct Chunking {
     std::vector<int> start; // first token of each chunk, then T
@@ -70,16 +75,16 @@ Chunking chunking_of(const sdm_config& c)
 {
     Chunking k;
     k.start.push_back(0);
-    int t = 0, len = c.T <= kChunk ? c.T : kChunk / 2;
+    int t = 0, len = c.T <= kOneChunk ? c.T : kFirstChunk;
     while (true) {
         int next = t + len;
-        if (next > c.T || c.T - next < kChunk / 2)
+        if (next > c.T || c.T - next < kMaxChunk / 2)
             next = c.T; // the remainder joins this chunk
         k.start.push_back(next);
         if (next == c.T)
             return k;
-        len = k.C() == 1 ? kChunk / 2 : kChunk; // the second chunk as long as the first
         t = next;
+        len = std::min(kMaxChunk, (len * 3 / 2) & ~63);
     }
 }
 

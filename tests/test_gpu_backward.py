@@ -44,7 +44,7 @@ CASES = {
     "ragged_tiles": _cfg(B=1, H=3, T=33, d=96, S=40, dk=96, k=7, W=24),
     "one_slot": _cfg(B=2, H=1, T=17, d=32, S=8, dk=32, k=1, W=1),
     "k_eq_W_64": _cfg(B=1, H=1, T=20, d=32, S=64, dk=32, k=64, W=64),
-    # long enough to scan in chunks (1024 tokens, then the rest): the log of every chunk
+    # long enough to scan in chunks (640 tokens, then the rest): the log of every chunk
     "chunked_T2600": _cfg(B=2, H=1, T=2600, d=32, S=16, dk=32, k=4, W=8),
     # bf16 state (the 8B-shaped workload's): bf16 memory and log, float32 gradient
     "bf16_state": _cfg(B=2, H=2, T=48, d=64, S=16, dk=32, k=4, W=8, in_bf16=True, state_bf16=True),
