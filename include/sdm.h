@@ -173,7 +173,7 @@ SDM_API sdm_status sdm_step_static(const sdm_config* cfg, void* hip_stream, cons
  * sdm_backward consumes.  The log holds B*H*T*W*d*sizeof(state) bytes (17.2 GB
  * for B=4, H=1, T=8192, W=64, d=2048, float32), owned by the caller.
  * SDM_ERR_UNSUPPORTED unless d * sizeof(state) is a multiple of 128 bytes and
- * one memory's log of a scan chunk (up to 3071 tokens) stays below 4 GiB.  (SDM blog post, section "How does SDM
+ * one memory's log of a scan chunk (up to 3072 tokens) stays below 4 GiB.  (SDM blog post, section "How does SDM
  * work?": the decay and delta-rule write whose inputs the log keeps.) */
 SDM_API sdm_status sdm_forward_train(sdm_handle h, const void* wq, const void* rq, const void* v, const float* alpha,
                                      const float* beta, const void* subkeys, void* mem_inout, float* out, void* log);

@@ -53,8 +53,10 @@ std::mutex g_scratch_mu;
 
 // A forward longer than kOneChunk tokens runs its scan in chunks: kFirstChunk
 // tokens first, then each chunk 3/2 of the one before (rounded down to a
-// multiple of 64 tokens) up to kMaxChunk, the last taking any remainder
-// shorter than kMaxChunk / 2.  The addressing and plan of chunk c + 1 run on a
+// multiple of 64 tokens) up to kMaxChunk.  A remainder shorter than
+// kMaxChunk / 2 joins the chunk before it where the two fit in kMaxChunk;
+// otherwise those tokens form two chunks of about half each, so no chunk
+// exceeds kMaxChunk tokens.  The addressing and plan of chunk c + 1 run on a
 // second stream while chunk c scans; beside a running scan they get only the
 // CU resources the scan leaves free and stretch to most of its time, so a
 // chunk may be only a little longer than the one before it.  The first chunk,
@@ -78,8 +80,8 @@ Chunking chunking_of(const sdm_config& c)
     int t = 0, len = c.T <= kOneChunk ? c.T : kFirstChunk;
     while (true) {
         int next = t + len;
-        if (next > c.T || c.T - next < kMaxChunk / 2)
-            next = c.T; // the remainder joins this chunk
+        if (next >= c.T || c.T - next < kMaxChunk / 2)
+            next = c.T - t <= kMaxChunk ? c.T : t + (((c.T - t) / 2) & ~63);
         k.start.push_back(next);
         if (next == c.T)
             return k;

@@ -223,13 +223,16 @@ def test_chunked_calls_are_bitwise_equal(T):
 
 
 # Forwards longer than 2048 tokens scan in several launches (640 tokens first,
-# then each chunk 3/2 of the one before up to 3072, the last one taking a
-# remainder below 1536: 640 and 1960 at 2600 tokens, 640, 960 and 1700 at 3300)
-# while the next chunk's addressing runs on a second stream.
+# then each chunk 3/2 of the one before up to 3072, a remainder below 1536
+# joining the chunk before it: 640 and 1960 at 2600 tokens, 640, 960 and 1700
+# at 3300; where the two would exceed 3072 tokens they split in about half
+# instead: 640, 960, 1408, 2112, 1984 and 2088 at 9192) while the next chunk's
+# addressing runs on a second stream.
 CHUNKED = {
     "f32_state_f32_in": _edge(T=2600, B=2, H=2, d=32, S=32, k=6, W=16),
     "f32_state_bf16_in": _edge(T=3300, B=1, H=3, d=64, S=48, k=8, W=24, in_bf16=True),
     "bf16_state": _edge(T=2600, B=2, H=1, d=64, S=32, k=6, W=16, in_bf16=True, state_bf16=True),
+    "split_tail": _edge(T=9192, B=1, H=1, d=32, S=16, k=4, W=8),
 }
 
 
@@ -242,7 +245,7 @@ def test_chunked_forward_parity(orc, T, name):
     x = gi.make_inputs(cfg)
     rng = np.random.default_rng(11)
     pats = x["wq"][:, :6].copy()
-    for t0 in (620, 640, 1580, 1600):
+    for t0 in (620, 640, 1580, 1600, 7090, 7104):
         if t0 + 24 <= cfg.T:
             x["wq"][:, t0:t0 + 24] = pats[:, rng.integers(0, 6, 24)]
             x["rq"][:, t0:t0 + 24] = pats[:, rng.integers(0, 6, 24)]
